@@ -1,0 +1,214 @@
+"""CPU oracle for the lossless tensor codec (ctypes over libltc_oracle.so).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this package.  It is a plain, slow,
+scalar C implementation of the blob format described in ltc_oracle.h, written
+independently of the HIP library; the two share no code.
+
+The functions here only marshal numpy arrays to the C entry points.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+DTYPES = {"u8": 0, "bf16": 1, "fp16": 2, "fp32": 3}
+ELEM_BYTES = {0: 1, 1: 2, 2: 2, 3: 4}
+MODE_RAW, MODE_RANS, MODE_CONST = 0, 1, 2
+
+OK = 0
+ERR_INVALID_ARGUMENT = -1
+ERR_UNSUPPORTED_DTYPE = -2
+ERR_BAD_MAGIC = -3
+ERR_BAD_VERSION = -4
+ERR_CORRUPT = -5
+ERR_CAPACITY = -6
+
+_lib = None
+
+
+def _u8p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        c = ctypes
+        L.ltco_elem_bytes.argtypes = [c.c_int]
+        L.ltco_reorder.argtypes = [c.c_int, c.c_uint32]
+        L.ltco_reorder.restype = c.c_uint32
+        L.ltco_unreorder.argtypes = [c.c_int, c.c_uint32]
+        L.ltco_unreorder.restype = c.c_uint32
+        L.ltco_chunk_stream.argtypes = [u8p, c.c_uint64, c.c_int, c.c_uint32,
+                                        c.c_uint64, c.c_int, u8p]
+        L.ltco_chunk_stream.restype = c.c_uint64
+        L.ltco_histogram.argtypes = [u8p, c.c_uint64, u64p]
+        L.ltco_normalize.argtypes = [u64p, u16p]
+        L.ltco_p_max.argtypes = [c.c_uint64, c.c_double]
+        L.ltco_p_max.restype = c.c_uint64
+        L.ltco_rans_encode.argtypes = [u8p, c.c_uint64, u16p, u32p, u16p,
+                                       c.c_uint64, u64p]
+        L.ltco_rans_decode.argtypes = [u16p, c.c_uint64, u32p, u16p,
+                                       c.c_uint64, u8p]
+        L.ltco_compress_bound.argtypes = [c.c_uint64, c.c_int, c.c_uint32]
+        L.ltco_compress_bound.restype = c.c_uint64
+        L.ltco_compress.argtypes = [u8p, c.c_uint64, c.c_int, c.c_uint32,
+                                    c.c_double, u8p, c.c_uint64, u64p, c.c_int]
+        L.ltco_encode_chunk.argtypes = [u8p, c.c_uint64, c.c_int, c.c_uint32,
+                                        c.c_double, c.c_uint64, u8p, u8p, u32p,
+                                        u8p, c.c_uint64, u64p]
+        L.ltco_decompress.argtypes = [u8p, c.c_uint64, u8p, c.c_uint64, u64p,
+                                      c.c_int]
+        L.ltco_crc32.argtypes = [u8p, c.c_uint64]
+        L.ltco_crc32.restype = c.c_uint32
+        L.ltco_crc32_chunks.argtypes = [u8p, c.c_uint64, c.c_uint32, u32p]
+        _lib = L
+    return _lib
+
+
+def _as_bytes(a):
+    a = np.ascontiguousarray(a)
+    return a.reshape(-1).view(np.uint8)
+
+
+def reorder(dtype, x):
+    return lib().ltco_reorder(dtype, int(x))
+
+
+def unreorder(dtype, y):
+    return lib().ltco_unreorder(dtype, int(y))
+
+
+def chunk_stream(src, dtype, chunk_bytes, c, k):
+    b = _as_bytes(src)
+    out = np.zeros(chunk_bytes, dtype=np.uint8)
+    n = lib().ltco_chunk_stream(_u8p(b), b.size, dtype, chunk_bytes, c, k, _u8p(out))
+    return out[:n].copy()
+
+
+def histogram(sym):
+    s = np.ascontiguousarray(sym, dtype=np.uint8)
+    h = np.zeros(256, dtype=np.uint64)
+    lib().ltco_histogram(_u8p(s), s.size, h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)))
+    return h
+
+
+def normalize(h):
+    h = np.ascontiguousarray(h, dtype=np.uint64)
+    f = np.zeros(256, dtype=np.uint16)
+    rc = lib().ltco_normalize(h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                              f.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)))
+    if rc:
+        raise ValueError(f"normalize: status {rc}")
+    return f
+
+
+def p_max(n, theta):
+    return lib().ltco_p_max(n, theta)
+
+
+def rans_encode(sym, f):
+    s = np.ascontiguousarray(sym, dtype=np.uint8)
+    f = np.ascontiguousarray(f, dtype=np.uint16)
+    states = np.zeros(64, dtype=np.uint32)
+    words = np.zeros(max(1, s.size), dtype=np.uint16)
+    nw = ctypes.c_uint64(0)
+    rc = lib().ltco_rans_encode(_u8p(s), s.size,
+                                f.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                states.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                words.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                words.size, ctypes.byref(nw))
+    if rc:
+        raise ValueError(f"rans_encode: status {rc}")
+    return states, words[: nw.value].copy()
+
+
+def rans_decode(words, states, f, n):
+    w = np.ascontiguousarray(words, dtype=np.uint16)
+    st = np.ascontiguousarray(states, dtype=np.uint32)
+    f = np.ascontiguousarray(f, dtype=np.uint16)
+    out = np.zeros(max(1, n), dtype=np.uint8)
+    rc = lib().ltco_rans_decode(w.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), w.size,
+                                st.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                f.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                n, _u8p(out))
+    return rc, out[:n].copy()
+
+
+def compress_bound(nbytes, dtype, chunk_bytes=131072):
+    return lib().ltco_compress_bound(nbytes, dtype, chunk_bytes)
+
+
+def compress(src, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None):
+    """Blob (np.uint8) of the bytes of `src` read as `dtype` (a code)."""
+    b = _as_bytes(src)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    cap = max(64, compress_bound(b.size, dtype, chunk_bytes))
+    blob = np.zeros(cap, dtype=np.uint8)
+    nb = ctypes.c_uint64(0)
+    rc = lib().ltco_compress(_u8p(b), b.size, dtype, chunk_bytes, threshold,
+                             _u8p(blob), blob.size, ctypes.byref(nb), int(nthreads))
+    if rc:
+        raise ValueError(f"oracle compress: status {rc}")
+    return blob[: nb.value].copy()
+
+
+def encode_chunk(src, dtype, chunk_bytes, threshold, c):
+    """(modes, cvals, sizes, padded payload bytes) of chunk c alone."""
+    b = _as_bytes(src)
+    e = ELEM_BYTES[dtype]
+    modes = np.zeros(e, dtype=np.uint8)
+    cvals = np.zeros(e, dtype=np.uint8)
+    sizes = np.zeros(e, dtype=np.uint32)
+    out = np.zeros(chunk_bytes + 16 * e + 64, dtype=np.uint8)
+    nout = ctypes.c_uint64(0)
+    rc = lib().ltco_encode_chunk(_u8p(b), b.size, dtype, chunk_bytes, threshold, c,
+                                 _u8p(modes), _u8p(cvals),
+                                 sizes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                                 _u8p(out), out.size, ctypes.byref(nout))
+    if rc:
+        raise ValueError(f"oracle encode_chunk: status {rc}")
+    return modes, cvals, sizes, out[: nout.value].copy()
+
+
+def decompress(blob, capacity=None, nthreads=None):
+    """(status, decoded bytes as np.uint8)."""
+    bl = np.ascontiguousarray(blob, dtype=np.uint8)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    if capacity is None:
+        capacity = int.from_bytes(bytes(bl[8:16]), "little") if bl.size >= 16 else 0
+    dst = np.zeros(max(1, capacity), dtype=np.uint8)
+    nout = ctypes.c_uint64(0)
+    rc = lib().ltco_decompress(_u8p(bl), bl.size, _u8p(dst), capacity,
+                               ctypes.byref(nout), int(nthreads))
+    if rc:
+        return rc, None
+    return rc, dst[: nout.value].copy()
+
+
+def crc32(data):
+    b = _as_bytes(data)
+    return lib().ltco_crc32(_u8p(b), b.size)
+
+
+def crc32_chunks(data, chunk_bytes=16384):
+    b = _as_bytes(data)
+    count = (b.size + chunk_bytes - 1) // chunk_bytes
+    out = np.zeros(max(1, count), dtype=np.uint32)
+    rc = lib().ltco_crc32_chunks(_u8p(b), b.size, chunk_bytes,
+                                 out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)))
+    if rc:
+        raise ValueError(f"oracle crc32_chunks: status {rc}")
+    return out[:count].copy()

@@ -1,0 +1,640 @@
+/*
+ * ltc_oracle.c -- plain scalar reference for the lossless tensor codec.
+ *
+ * TEST INFRASTRUCTURE ONLY (see ltc_oracle.h for the format and the pages it
+ * follows).  Deliberately simple: one element, one byte, one symbol at a
+ * time, exact integer arithmetic, linear searches.  The only concession to
+ * speed is an optional OpenMP loop over independent chunks, which does not
+ * change any output byte.
+ */
+#include "ltc_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define M_TOTAL 4096u
+#define LANES 64
+#define RANS_LOW 65536u
+#define HDR_BYTES 64u
+#define DIR_BYTES 16u
+#define RANS_FIXED 272u /* 16-byte prefix + 64 u32 states */
+
+static uint64_t align16(uint64_t v) { return (v + 15u) & ~(uint64_t)15u; }
+
+int ltco_elem_bytes(int dtype) {
+  switch (dtype) {
+    case 0: return 1;
+    case 1: return 2;
+    case 2: return 2;
+    case 3: return 4;
+    default: return 0;
+  }
+}
+
+static int mantissa_bits(int dtype) {
+  switch (dtype) {
+    case 1: return 7;   /* bfloat16: 1 sign, 8 exponent, 7 mantissa */
+    case 2: return 10;  /* IEEE half: 1 sign, 5 exponent, 10 mantissa */
+    case 3: return 23;  /* IEEE single: 1 sign, 8 exponent, 23 mantissa */
+    default: return -1;
+  }
+}
+
+/* Exponent extraction (NOTE-241: ZipNN, "Method" item 1 and "Concepts"):
+ * move the exponent field to the top of the word so that for BF16 and FP32
+ * it fills the most significant byte; the sign goes directly below it. */
+uint32_t ltco_reorder(int dtype, uint32_t x) {
+  int wm = mantissa_bits(dtype);
+  if (wm < 0) return x;
+  int w = 8 * ltco_elem_bytes(dtype);
+  int we = w - 1 - wm;
+  uint32_t e = (x >> wm) & ((1u << we) - 1u);
+  uint32_t s = (x >> (w - 1)) & 1u;
+  uint32_t m = x & ((1u << wm) - 1u);
+  return (e << (wm + 1)) | (s << wm) | m;
+}
+
+uint32_t ltco_unreorder(int dtype, uint32_t y) {
+  int wm = mantissa_bits(dtype);
+  if (wm < 0) return y;
+  int w = 8 * ltco_elem_bytes(dtype);
+  int we = w - 1 - wm;
+  uint32_t e = (y >> (wm + 1)) & ((1u << we) - 1u);
+  uint32_t s = (y >> wm) & 1u;
+  uint32_t m = y & ((1u << wm) - 1u);
+  return (s << (w - 1)) | (e << wm) | m;
+}
+
+static uint32_t load_le(const uint8_t* p, int e) {
+  uint32_t x = 0;
+  for (int i = 0; i < e; i++) x |= (uint32_t)p[i] << (8 * i);
+  return x;
+}
+
+static void store_le(uint8_t* p, int e, uint32_t x) {
+  for (int i = 0; i < e; i++) p[i] = (uint8_t)(x >> (8 * i));
+}
+
+static void put_u16(uint8_t* p, uint32_t v) { store_le(p, 2, v); }
+static void put_u32(uint8_t* p, uint32_t v) { store_le(p, 4, v); }
+static void put_u64(uint8_t* p, uint64_t v) {
+  for (int i = 0; i < 8; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+static uint32_t get_u16(const uint8_t* p) { return load_le(p, 2); }
+static uint32_t get_u32(const uint8_t* p) { return load_le(p, 4); }
+static uint64_t get_u64(const uint8_t* p) {
+  uint64_t v = 0;
+  for (int i = 0; i < 8; i++) v |= (uint64_t)p[i] << (8 * i);
+  return v;
+}
+
+/* Byte grouping (NOTE-241: ZipNN, "Method" item 2): stream k of a chunk is
+ * byte k (little-endian position) of every reordered element. */
+uint64_t ltco_chunk_stream(const uint8_t* src, uint64_t nbytes, int dtype,
+                           uint32_t chunk_bytes, uint64_t c, int k, uint8_t* out) {
+  int e = ltco_elem_bytes(dtype);
+  uint64_t start = c * (uint64_t)chunk_bytes;
+  uint64_t end = start + chunk_bytes;
+  if (end > nbytes) end = nbytes;
+  uint64_t n = (end - start) / (uint64_t)e;
+  for (uint64_t t = 0; t < n; t++) {
+    uint32_t y = ltco_reorder(dtype, load_le(src + start + t * e, e));
+    out[t] = (uint8_t)(y >> (8 * k));
+  }
+  return n;
+}
+
+void ltco_histogram(const uint8_t* sym, uint64_t n, uint64_t h[256]) {
+  for (int v = 0; v < 256; v++) h[v] = 0;
+  for (uint64_t t = 0; t < n; t++) h[sym[t]] += 1;
+}
+
+/* Normalisation of a histogram to a 2^12 total (the pages fix only the
+ * total; the rule is this format's reading, stated in ltc_oracle.h). */
+int ltco_normalize(const uint64_t h[256], uint16_t f[256]) {
+  uint64_t n = 0;
+  int nonzero = 0;
+  for (int v = 0; v < 256; v++) {
+    n += h[v];
+    if (h[v]) nonzero++;
+  }
+  if (nonzero < 2) return LTCO_ERR_INVALID_ARGUMENT;
+  uint64_t g[256];
+  uint64_t total = 0;
+  for (int v = 0; v < 256; v++) {
+    if (h[v] == 0) {
+      g[v] = 0;
+    } else {
+      g[v] = h[v] * M_TOTAL / n;
+      if (g[v] < 1) g[v] = 1;
+    }
+    total += g[v];
+  }
+  while (total > M_TOTAL) {
+    int best = -1;
+    for (int v = 0; v < 256; v++)
+      if (g[v] > 1 && (best < 0 || g[v] > g[best])) best = v;
+    g[best] -= 1;
+    total -= 1;
+  }
+  if (total < M_TOTAL) {
+    int best = 0;
+    for (int v = 1; v < 256; v++)
+      if (h[v] > h[best]) best = v;
+    g[best] += M_TOTAL - total;
+  }
+  for (int v = 0; v < 256; v++) f[v] = (uint16_t)g[v];
+  return LTCO_OK;
+}
+
+/* passthrough_threshold (cuZipNN 0.1.0, "API"): a stream stays coded only if
+ * its payload is strictly below theta times its raw size, compared in IEEE
+ * double.  Returns the largest integer P with (double)P < theta*(double)n. */
+uint64_t ltco_p_max(uint64_t n, double theta) {
+  double t = theta * (double)n;
+  if (!(t > 0.0)) return 0;
+  double p = floor(t);
+  if (p >= t) p -= 1.0;
+  if (p < 0.0) return 0;
+  return (uint64_t)p;
+}
+
+static void cumulative(const uint16_t f[256], uint32_t cum[256]) {
+  uint32_t acc = 0;
+  for (int v = 0; v < 256; v++) {
+    cum[v] = acc;
+    acc += f[v];
+  }
+}
+
+/* Interleaved rANS encoder (lmz README, "On a GPU": interleaved states are
+ * lanes of work).  Walks the symbols in exactly the reverse of the decoder's
+ * order and records each emitted word; the final list is reversed so that
+ * it reads in decoder order. */
+int ltco_rans_encode(const uint8_t* sym, uint64_t n, const uint16_t f[256],
+                     uint32_t states[64], uint16_t* words, uint64_t words_cap,
+                     uint64_t* nwords) {
+  uint32_t cum[256];
+  cumulative(f, cum);
+  uint32_t x[LANES];
+  for (int l = 0; l < LANES; l++) x[l] = RANS_LOW;
+  uint64_t steps = (n + LANES - 1) / LANES;
+  uint16_t* emitted = (uint16_t*)malloc((n ? n : 1) * sizeof(uint16_t));
+  if (!emitted) return LTCO_ERR_INVALID_ARGUMENT;
+  uint64_t count = 0;
+  for (uint64_t j = steps; j-- > 0;) {
+    for (int l = LANES - 1; l >= 0; l--) {
+      uint64_t t = j * LANES + (uint64_t)l;
+      if (t >= n) continue;
+      uint32_t s = sym[t];
+      uint32_t fs = f[s];
+      if (fs == 0) {
+        free(emitted);
+        return LTCO_ERR_INVALID_ARGUMENT;
+      }
+      if ((uint64_t)x[l] >= ((uint64_t)fs << 20)) {
+        emitted[count++] = (uint16_t)(x[l] & 0xFFFFu);
+        x[l] >>= 16;
+      }
+      x[l] = (x[l] / fs) * M_TOTAL + (x[l] % fs) + cum[s];
+    }
+  }
+  if (count > words_cap) {
+    free(emitted);
+    return LTCO_ERR_CAPACITY;
+  }
+  for (uint64_t i = 0; i < count; i++) words[i] = emitted[count - 1 - i];
+  for (int l = 0; l < LANES; l++) states[l] = x[l];
+  *nwords = count;
+  free(emitted);
+  return LTCO_OK;
+}
+
+int ltco_rans_decode(const uint16_t* words, uint64_t nwords,
+                     const uint32_t states[64], const uint16_t f[256],
+                     uint64_t n, uint8_t* out) {
+  uint32_t cum[256];
+  uint32_t total = 0;
+  for (int v = 0; v < 256; v++) total += f[v];
+  if (total != M_TOTAL) return LTCO_ERR_CORRUPT;
+  cumulative(f, cum);
+  uint32_t x[LANES];
+  for (int l = 0; l < LANES; l++) x[l] = states[l];
+  uint64_t steps = (n + LANES - 1) / LANES;
+  uint64_t pos = 0;
+  for (uint64_t j = 0; j < steps; j++) {
+    for (int l = 0; l < LANES; l++) {
+      uint64_t t = j * LANES + (uint64_t)l;
+      if (t >= n) continue;
+      uint32_t slot = x[l] & (M_TOTAL - 1u);
+      int s = -1;
+      for (int v = 0; v < 256; v++) {
+        if (f[v] != 0 && cum[v] <= slot && slot < cum[v] + f[v]) {
+          s = v;
+          break;
+        }
+      }
+      if (s < 0) return LTCO_ERR_CORRUPT;
+      out[t] = (uint8_t)s;
+      x[l] = f[s] * (x[l] >> 12) + slot - cum[s];
+      if (x[l] < RANS_LOW) {
+        if (pos >= nwords) return LTCO_ERR_CORRUPT;
+        x[l] = (x[l] << 16) | words[pos];
+        pos++;
+      }
+    }
+  }
+  if (pos != nwords) return LTCO_ERR_CORRUPT;
+  for (int l = 0; l < LANES; l++)
+    if (x[l] != RANS_LOW) return LTCO_ERR_CORRUPT;
+  return LTCO_OK;
+}
+
+uint64_t ltco_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
+  int e = ltco_elem_bytes(dtype);
+  if (e == 0 || chunk_bytes == 0) return 0;
+  uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
+  uint64_t bound = HDR_BYTES + DIR_BYTES * k * (uint64_t)e;
+  for (uint64_t c = 0; c < k; c++) {
+    uint64_t len = nbytes - c * (uint64_t)chunk_bytes;
+    if (len > chunk_bytes) len = chunk_bytes;
+    bound += (uint64_t)e * align16(len / (uint64_t)e);
+  }
+  return bound;
+}
+
+typedef struct {
+  uint8_t mode;
+  uint8_t cval;
+  uint32_t size;
+  uint8_t* payload; /* malloc'd, size bytes (NULL for CONST) */
+} stream_result;
+
+/* One stream: histogram, CONST / RANS / RAW decision, payload bytes. */
+static int encode_stream(const uint8_t* sym, uint64_t n, double theta,
+                         stream_result* r) {
+  uint64_t h[256];
+  ltco_histogram(sym, n, h);
+  int nonzero = 0, only = 0;
+  for (int v = 0; v < 256; v++)
+    if (h[v]) {
+      nonzero++;
+      only = v;
+    }
+  r->payload = NULL;
+  r->cval = 0;
+  if (nonzero == 1) {
+    /* NOTE-241: ZipNN, "Method" item 3: a constant stream costs a header */
+    r->mode = LTCO_MODE_CONST;
+    r->cval = (uint8_t)only;
+    r->size = 0;
+    return LTCO_OK;
+  }
+  uint16_t f[256];
+  int rc = ltco_normalize(h, f);
+  if (rc) return rc;
+  uint32_t states[64];
+  uint16_t* words = (uint16_t*)malloc(n * sizeof(uint16_t));
+  if (!words) return LTCO_ERR_INVALID_ARGUMENT;
+  uint64_t nw = 0;
+  rc = ltco_rans_encode(sym, n, f, states, words, n, &nw);
+  if (rc) {
+    free(words);
+    return rc;
+  }
+  int lo = 0, hi = 255;
+  while (h[lo] == 0) lo++;
+  while (h[hi] == 0) hi--;
+  uint64_t tcount = (uint64_t)(hi - lo + 1);
+  uint64_t wo = align16(RANS_FIXED + 2 * tcount);
+  uint64_t p = wo + 2 * nw;
+  if (p <= ltco_p_max(n, theta)) {
+    uint8_t* pl = (uint8_t*)calloc(p, 1);
+    if (!pl) {
+      free(words);
+      return LTCO_ERR_INVALID_ARGUMENT;
+    }
+    put_u32(pl + 0, (uint32_t)nw);
+    pl[4] = (uint8_t)lo;
+    pl[5] = (uint8_t)hi;
+    for (int l = 0; l < LANES; l++) put_u32(pl + 16 + 4 * l, states[l]);
+    for (uint64_t i = 0; i < tcount; i++) put_u16(pl + RANS_FIXED + 2 * i, f[lo + i]);
+    for (uint64_t i = 0; i < nw; i++) put_u16(pl + wo + 2 * i, words[i]);
+    r->mode = LTCO_MODE_RANS;
+    r->size = (uint32_t)p;
+    r->payload = pl;
+  } else {
+    /* cuZipNN 0.1.0, "API", passthrough_threshold: stored raw */
+    uint8_t* pl = (uint8_t*)malloc(n);
+    if (!pl) {
+      free(words);
+      return LTCO_ERR_INVALID_ARGUMENT;
+    }
+    memcpy(pl, sym, n);
+    r->mode = LTCO_MODE_RAW;
+    r->size = (uint32_t)n;
+    r->payload = pl;
+  }
+  free(words);
+  return LTCO_OK;
+}
+
+static int encode_chunk_streams(const uint8_t* src, uint64_t nbytes, int dtype,
+                                uint32_t chunk_bytes, double theta, uint64_t c,
+                                stream_result* out) {
+  int e = ltco_elem_bytes(dtype);
+  uint8_t* sym = (uint8_t*)malloc(chunk_bytes / (uint32_t)e + 1);
+  if (!sym) return LTCO_ERR_INVALID_ARGUMENT;
+  int rc = LTCO_OK;
+  for (int k = 0; k < e && rc == LTCO_OK; k++) {
+    uint64_t n = ltco_chunk_stream(src, nbytes, dtype, chunk_bytes, c, k, sym);
+    rc = encode_stream(sym, n, theta, &out[k]);
+  }
+  free(sym);
+  return rc;
+}
+
+static int check_args(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                      double theta) {
+  int e = ltco_elem_bytes(dtype);
+  if (e == 0) return LTCO_ERR_UNSUPPORTED_DTYPE;
+  if (nbytes % (uint64_t)e) return LTCO_ERR_INVALID_ARGUMENT;
+  if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8)
+    return LTCO_ERR_INVALID_ARGUMENT;
+  if (!(theta > 0.0 && theta <= 1.0)) return LTCO_ERR_INVALID_ARGUMENT;
+  if ((nbytes + chunk_bytes - 1) / chunk_bytes >= (1ull << 32))
+    return LTCO_ERR_INVALID_ARGUMENT;
+  return LTCO_OK;
+}
+
+int ltco_encode_chunk(const uint8_t* src, uint64_t nbytes, int dtype,
+                      uint32_t chunk_bytes, double theta, uint64_t c,
+                      uint8_t* modes, uint8_t* cvals, uint32_t* sizes,
+                      uint8_t* out, uint64_t out_cap, uint64_t* nout) {
+  int rc = check_args(nbytes, dtype, chunk_bytes, theta);
+  if (rc) return rc;
+  int e = ltco_elem_bytes(dtype);
+  if (c * (uint64_t)chunk_bytes >= nbytes) return LTCO_ERR_INVALID_ARGUMENT;
+  stream_result r[4];
+  memset(r, 0, sizeof(r));
+  rc = encode_chunk_streams(src, nbytes, dtype, chunk_bytes, theta, c, r);
+  uint64_t cur = 0;
+  for (int k = 0; k < e && rc == LTCO_OK; k++) {
+    uint64_t next = align16(cur + r[k].size);
+    if (next > out_cap) {
+      rc = LTCO_ERR_CAPACITY;
+      break;
+    }
+    if (r[k].size) memcpy(out + cur, r[k].payload, r[k].size);
+    memset(out + cur + r[k].size, 0, next - cur - r[k].size);
+    modes[k] = r[k].mode;
+    cvals[k] = r[k].cval;
+    sizes[k] = r[k].size;
+    cur = next;
+  }
+  for (int k = 0; k < e; k++) free(r[k].payload);
+  *nout = cur;
+  return rc;
+}
+
+int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
+                  uint32_t chunk_bytes, double theta, uint8_t* blob,
+                  uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads) {
+  int rc = check_args(nbytes, dtype, chunk_bytes, theta);
+  if (rc) return rc;
+  int e = ltco_elem_bytes(dtype);
+  uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
+  uint64_t s = k * (uint64_t)e;
+  stream_result* res = (stream_result*)calloc(s ? s : 1, sizeof(stream_result));
+  if (!res) return LTCO_ERR_INVALID_ARGUMENT;
+  int failed = 0;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (long long c = 0; c < (long long)k; c++) {
+    int r = encode_chunk_streams(src, nbytes, dtype, chunk_bytes, theta,
+                                 (uint64_t)c, res + (uint64_t)c * e);
+    if (r) {
+#pragma omp atomic write
+      failed = r;
+    }
+  }
+  uint64_t base = HDR_BYTES + DIR_BYTES * s;
+  uint64_t cursor = base;
+  for (uint64_t i = 0; i < s; i++) cursor = align16(cursor + res[i].size);
+  if (failed) {
+    rc = failed;
+  } else if (cursor > blob_capacity) {
+    rc = LTCO_ERR_CAPACITY;
+  } else {
+    memset(blob, 0, cursor);
+    memcpy(blob, "LTCB", 4);
+    put_u16(blob + 4, 1);
+    blob[6] = (uint8_t)dtype;
+    blob[7] = (uint8_t)e;
+    put_u64(blob + 8, nbytes);
+    put_u32(blob + 16, chunk_bytes);
+    put_u32(blob + 20, (uint32_t)k);
+    put_u16(blob + 24, LANES);
+    blob[26] = 12;
+    blob[27] = 0;
+    put_u64(blob + 32, cursor);
+    put_u64(blob + 40, base);
+    uint64_t cur = base;
+    for (uint64_t i = 0; i < s; i++) {
+      uint8_t* d = blob + HDR_BYTES + DIR_BYTES * i;
+      put_u64(d, cur);
+      put_u32(d + 8, res[i].size);
+      d[12] = res[i].mode;
+      d[13] = res[i].cval;
+      if (res[i].size) memcpy(blob + cur, res[i].payload, res[i].size);
+      cur = align16(cur + res[i].size);
+    }
+    *blob_nbytes = cursor;
+  }
+  for (uint64_t i = 0; i < s; i++) free(res[i].payload);
+  free(res);
+  return rc;
+}
+
+typedef struct {
+  uint64_t off;
+  uint32_t size;
+  uint8_t mode;
+  uint8_t cval;
+} dir_entry;
+
+/* Structural checks of one RANS payload (lo, hi, zeros, table, states). */
+static int check_rans_payload(const uint8_t* pl, uint32_t size, uint16_t f[256],
+                              uint32_t states[64], uint64_t* nwords,
+                              uint64_t* words_off) {
+  if (size < RANS_FIXED + 16u) return LTCO_ERR_CORRUPT;
+  uint32_t nw = get_u32(pl);
+  int lo = pl[4], hi = pl[5];
+  if (lo >= hi) return LTCO_ERR_CORRUPT;
+  for (int i = 6; i < 16; i++)
+    if (pl[i]) return LTCO_ERR_CORRUPT;
+  uint64_t tcount = (uint64_t)(hi - lo + 1);
+  uint64_t wo = align16(RANS_FIXED + 2 * tcount);
+  if (wo > size) return LTCO_ERR_CORRUPT;
+  if ((uint64_t)size - wo != 2 * (uint64_t)nw) return LTCO_ERR_CORRUPT;
+  for (uint64_t i = RANS_FIXED + 2 * tcount; i < wo; i++)
+    if (pl[i]) return LTCO_ERR_CORRUPT;
+  memset(f, 0, 256 * sizeof(uint16_t));
+  uint32_t total = 0;
+  for (uint64_t i = 0; i < tcount; i++) {
+    f[lo + i] = (uint16_t)get_u16(pl + RANS_FIXED + 2 * i);
+    total += f[lo + i];
+  }
+  if (f[lo] == 0 || f[hi] == 0 || total != M_TOTAL) return LTCO_ERR_CORRUPT;
+  for (int l = 0; l < LANES; l++) {
+    states[l] = get_u32(pl + 16 + 4 * l);
+    if (states[l] < RANS_LOW) return LTCO_ERR_CORRUPT;
+  }
+  *nwords = nw;
+  *words_off = wo;
+  return LTCO_OK;
+}
+
+static int decode_chunk(const uint8_t* blob, const dir_entry* ent, int dtype,
+                        int e, uint64_t n, uint8_t* dst) {
+  uint8_t* planes = (uint8_t*)malloc((uint64_t)e * (n ? n : 1));
+  if (!planes) return LTCO_ERR_INVALID_ARGUMENT;
+  int rc = LTCO_OK;
+  for (int k = 0; k < e && rc == LTCO_OK; k++) {
+    uint8_t* plane = planes + (uint64_t)k * n;
+    const uint8_t* pl = blob + ent[k].off;
+    if (ent[k].mode == LTCO_MODE_CONST) {
+      memset(plane, ent[k].cval, n);
+    } else if (ent[k].mode == LTCO_MODE_RAW) {
+      memcpy(plane, pl, n);
+    } else {
+      uint16_t f[256];
+      uint32_t states[64];
+      uint64_t nw = 0, wo = 0;
+      rc = check_rans_payload(pl, ent[k].size, f, states, &nw, &wo);
+      if (rc) break;
+      uint16_t* words = (uint16_t*)malloc((nw ? nw : 1) * sizeof(uint16_t));
+      if (!words) {
+        rc = LTCO_ERR_INVALID_ARGUMENT;
+        break;
+      }
+      for (uint64_t i = 0; i < nw; i++) words[i] = (uint16_t)get_u16(pl + wo + 2 * i);
+      rc = ltco_rans_decode(words, nw, states, f, n, plane);
+      free(words);
+    }
+  }
+  if (rc == LTCO_OK) {
+    for (uint64_t t = 0; t < n; t++) {
+      uint32_t y = 0;
+      for (int k = 0; k < e; k++) y |= (uint32_t)planes[(uint64_t)k * n + t] << (8 * k);
+      store_le(dst + t * e, e, ltco_unreorder(dtype, y));
+    }
+  }
+  free(planes);
+  return rc;
+}
+
+int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
+                    uint64_t dst_capacity, uint64_t* out_nbytes, int nthreads) {
+  if (blob_nbytes < HDR_BYTES) return LTCO_ERR_CORRUPT;
+  if (memcmp(blob, "LTCB", 4) != 0) return LTCO_ERR_BAD_MAGIC;
+  if (get_u16(blob + 4) != 1) return LTCO_ERR_BAD_VERSION;
+  int dtype = blob[6];
+  int e = ltco_elem_bytes(dtype);
+  if (e == 0) return LTCO_ERR_UNSUPPORTED_DTYPE;
+  if (blob[7] != e) return LTCO_ERR_CORRUPT;
+  uint64_t nbytes = get_u64(blob + 8);
+  uint32_t chunk_bytes = get_u32(blob + 16);
+  uint64_t k = get_u32(blob + 20);
+  if (get_u16(blob + 24) != LANES || blob[26] != 12 || blob[27] != 0 ||
+      get_u32(blob + 28) != 0)
+    return LTCO_ERR_CORRUPT;
+  for (int i = 48; i < 64; i++)
+    if (blob[i]) return LTCO_ERR_CORRUPT;
+  if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8)
+    return LTCO_ERR_CORRUPT;
+  if (nbytes % (uint64_t)e) return LTCO_ERR_CORRUPT;
+  if (k != (nbytes + chunk_bytes - 1) / chunk_bytes) return LTCO_ERR_CORRUPT;
+  uint64_t s = k * (uint64_t)e;
+  uint64_t base = HDR_BYTES + DIR_BYTES * s;
+  if (get_u64(blob + 40) != base) return LTCO_ERR_CORRUPT;
+  if (get_u64(blob + 32) != blob_nbytes) return LTCO_ERR_CORRUPT;
+  if (base > blob_nbytes) return LTCO_ERR_CORRUPT;
+  if (dst_capacity < nbytes) return LTCO_ERR_CAPACITY;
+
+  dir_entry* ent = (dir_entry*)malloc((s ? s : 1) * sizeof(dir_entry));
+  if (!ent) return LTCO_ERR_INVALID_ARGUMENT;
+  uint64_t cursor = base;
+  for (uint64_t i = 0; i < s; i++) {
+    const uint8_t* d = blob + HDR_BYTES + DIR_BYTES * i;
+    ent[i].off = get_u64(d);
+    ent[i].size = get_u32(d + 8);
+    ent[i].mode = d[12];
+    ent[i].cval = d[13];
+    uint64_t c = i / (uint64_t)e;
+    uint64_t len = nbytes - c * (uint64_t)chunk_bytes;
+    if (len > chunk_bytes) len = chunk_bytes;
+    uint64_t n = len / (uint64_t)e;
+    int bad = ent[i].off != cursor || get_u16(d + 14) != 0 || ent[i].mode > 2 ||
+              (ent[i].mode != LTCO_MODE_CONST && ent[i].cval != 0) ||
+              (ent[i].mode == LTCO_MODE_RAW && ent[i].size != n) ||
+              (ent[i].mode == LTCO_MODE_CONST && ent[i].size != 0) ||
+              ent[i].size > blob_nbytes - ent[i].off;
+    if (bad) {
+      free(ent);
+      return LTCO_ERR_CORRUPT;
+    }
+    cursor = align16(ent[i].off + ent[i].size);
+  }
+  if (cursor != blob_nbytes) {
+    free(ent);
+    return LTCO_ERR_CORRUPT;
+  }
+  int failed = 0;
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (long long c = 0; c < (long long)k; c++) {
+    uint64_t start = (uint64_t)c * chunk_bytes;
+    uint64_t len = nbytes - start;
+    if (len > chunk_bytes) len = chunk_bytes;
+    int r = decode_chunk(blob, ent + (uint64_t)c * e, dtype, e, len / (uint64_t)e,
+                         dst + start);
+    if (r) {
+#pragma omp atomic write
+      failed = r;
+    }
+  }
+  free(ent);
+  if (failed) return failed;
+  *out_nbytes = nbytes;
+  return LTCO_OK;
+}
+
+/* CRC-32 as zlib computes it (cuZipNN 0.1.0, "API": checksums match
+ * zlib.crc32): reflected polynomial 0xEDB88320, one bit at a time. */
+uint32_t ltco_crc32(const uint8_t* p, uint64_t n) {
+  uint32_t c = 0xFFFFFFFFu;
+  for (uint64_t i = 0; i < n; i++) {
+    c ^= p[i];
+    for (int b = 0; b < 8; b++) c = (c >> 1) ^ (0xEDB88320u & (0u - (c & 1u)));
+  }
+  return c ^ 0xFFFFFFFFu;
+}
+
+int ltco_crc32_chunks(const uint8_t* p, uint64_t n, uint32_t chunk_bytes,
+                      uint32_t* out) {
+  if (chunk_bytes == 0) return LTCO_ERR_INVALID_ARGUMENT;
+  uint64_t count = (n + chunk_bytes - 1) / chunk_bytes;
+#pragma omp parallel for schedule(static)
+  for (long long i = 0; i < (long long)count; i++) {
+    uint64_t start = (uint64_t)i * chunk_bytes;
+    uint64_t len = n - start;
+    if (len > chunk_bytes) len = chunk_bytes;
+    out[i] = ltco_crc32(p + start, len);
+  }
+  return LTCO_OK;
+}
