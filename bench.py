@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 lossless tensor codec on one GPU.
+
+A step is one pass of the whole hot path over the workload, inputs resident
+in HBM: batch compress (histogram, normalise, rANS encode, scan, pack),
+batch decompress (validate, decode, inverse regroup and reorder), and the
+CRC-32 of every blob in 16 KiB chunks.  Prints one JSON line.
+
+Default workload: 28 BF16 tensors shaped like four Llama-3-8B-style layers
+(1.74 GB), generated on the GPU from a fixed seed (see workloads.py).
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decompress GB/s (orig bytes, HBM-resident) + compress GB/s + ratio, BF16"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+CHUNK = 131072
+THRESHOLD = 0.95
+CRC_CHUNK = 16384
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all, max 16)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device-to-device copy of 1 GiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent_t helpers on the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        path = None
+        for line in open("/proc/self/maps"):
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+        self.L = ctypes.CDLL(path or "libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.L.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        self.L.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+
+    def ms(self, a, b):
+        v = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(v.value)
+
+
+def make_workload(name, torch, workloads):
+    dev = "cuda"
+    if name == "c3":
+        ts = workloads.c3_gpu(dev)
+        desc = {"workload": "C3: 28 BF16 tensors of a 4-layer Llama-3-8B-like stack, "
+                            "N(0, sigma), sigma log-uniform [0.005, 0.05]",
+                "tensors": len(ts), "dtype": "bf16"}
+    elif name == "c5":
+        buf = workloads.c5_gpu(dev)
+        ts = [buf.view(torch.bfloat16)]
+        desc = {"workload": "C5: 8 GiB BF16 stream of 64 tensors 8192x8192, every 8th random bytes",
+                "tensors": 1, "dtype": "bf16"}
+    elif name == "c1":
+        ts = [torch.from_numpy(workloads.c1().view("int16")).cuda().view(torch.bfloat16)]
+        desc = {"workload": "C1: BF16 2**20 elements N(0, 0.02)", "tensors": 1, "dtype": "bf16"}
+    elif name == "c2":
+        ts = [torch.from_numpy(workloads.c2()).cuda()]
+        desc = {"workload": "C2: FP32 4096x4096 N(0, 0.02)", "tensors": 1, "dtype": "fp32"}
+    else:
+        clean, h = workloads.c4()
+        ts = [torch.from_numpy(clean).cuda()]
+        desc = {"workload": "C4 (clean FP32 part): bf16-rounded values widened to FP32, 2048x8192",
+                "tensors": 1, "dtype": "fp32"}
+    return ts, desc
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    for _ in range(20):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.time() - t0) / 20
+    print(json.dumps({"copy_bytes": n, "copy_read_plus_write_gbs": 2 * n / dt / 1e9}), flush=True)
+
+
+def traffic_from_profiles(kernel, launches_per_step):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(args, ts, torch):
+    import numpy as np
+
+    import oracle
+    threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+    # bounded sample: whole tensors from the start of the workload, ~64 MiB
+    sample, taken = [], 0
+    for t in ts:
+        b = t.contiguous().view(-1).view(torch.uint8)
+        if taken and taken + b.numel() > (64 << 20):
+            break
+        take = min(b.numel(), 64 << 20)
+        sample.append(b[:take].cpu().numpy())
+        taken += take
+        if taken >= (64 << 20):
+            break
+    code = {torch.bfloat16: 1, torch.float16: 2, torch.float32: 3, torch.uint8: 0}[ts[0].dtype]
+    t0 = time.time()
+    total = 0
+    for s in sample:
+        blob = oracle.compress(s, code, CHUNK, THRESHOLD, nthreads=threads)
+        rc, out = oracle.decompress(blob, nthreads=threads)
+        assert rc == 0 and np.array_equal(out, s)
+        oracle.crc32_chunks(blob, CRC_CHUNK)
+        total += s.size
+    dt = time.time() - t0
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {total / 2**20:.0f} MiB of the workload: compress + decompress + "
+                      f"CRC-32 per step, OpenMP over chunks, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import lossless_tensor_compression_amd as ltc
+    import workloads
+
+    ltc.lib()
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    torch.cuda.set_device(0)
+    ts, desc = make_workload(args.workload, torch, workloads)
+    code = ltc.DTYPE_CODE[ts[0].dtype]
+    count = len(ts)
+    nbytes = [t.numel() * t.element_size() for t in ts]
+    N = sum(nbytes)
+    caps = [ltc.compress_bound(n, code, CHUNK) for n in nbytes]
+    blobs = [torch.empty(c, dtype=torch.uint8, device="cuda") for c in caps]
+    ws_n = ltc.workspace_size(nbytes, code, CHUNK)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    sizes = torch.zeros(count, dtype=torch.int64, device="cuda")
+    outs = [torch.empty(n, dtype=torch.uint8, device="cuda") for n in nbytes]
+    status = torch.zeros(count, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    src_ptrs = [t.data_ptr() for t in ts]
+    blob_ptrs = [b.data_ptr() for b in blobs]
+    out_ptrs = [o.data_ptr() for o in outs]
+
+    # first pass: sizes and headers (host copies) for the decode and CRC launches
+    ltc.compress_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, blob_ptrs, caps, sizes.data_ptr(),
+                     ws.data_ptr(), ws_n)
+    bsz = sizes.cpu().tolist()
+    headers = [bytes(b[:64].cpu().numpy().tobytes()) for b in blobs]
+    B = sum(bsz)
+    ncrc = [(s + CRC_CHUNK - 1) // CRC_CHUNK for s in bsz]
+    crcs = torch.empty(sum(ncrc), dtype=torch.int32, device="cuda")
+    crc_off = [sum(ncrc[:i]) for i in range(count)]
+    L = ltc.lib()
+
+    hip = Hip()
+    ev_c = hip.events(5)
+    ev_d = hip.events(3)
+    ev_x = hip.events(2)
+
+    def step(prof):
+        ltc.compress_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, blob_ptrs, caps, sizes.data_ptr(),
+                         ws.data_ptr(), ws_n, events=ev_c if prof else None)
+        ltc.decompress_raw(headers, blob_ptrs, bsz, out_ptrs, nbytes, status.data_ptr(),
+                           events=ev_d if prof else None)
+        if prof:
+            hip.record(ev_x[0], sptr)
+        for i in range(count):
+            rc = L.ltc_crc32_chunks(ctypes.c_void_p(blob_ptrs[i]), bsz[i], CRC_CHUNK,
+                                    ctypes.c_void_p(crcs.data_ptr() + 4 * crc_off[i]),
+                                    ctypes.c_void_p(sptr))
+            if rc:
+                raise RuntimeError(f"crc32_chunks: {rc}")
+        if prof:
+            hip.record(ev_x[1], sptr)
+
+    for _ in range(max(1, args.warmup)):
+        step(False)
+    torch.cuda.synchronize()
+    # correctness of what is timed: sizes stable, status OK, exact round trip
+    assert sizes.cpu().tolist() == bsz, "blob sizes changed between steps"
+    assert status.cpu().tolist() == [0] * count, f"decode status {status.cpu().tolist()}"
+    for t, o in zip(ts, outs):
+        assert torch.equal(t.contiguous().view(-1).view(torch.uint8), o), "round trip mismatch"
+
+    # timed region: K whole steps bracketed by synchronisation
+    torch.cuda.synchronize()
+    t_wall = time.time()
+    hip.record(ev_x[0], sptr)
+    start_ev = hip.events(2)
+    hip.record(start_ev[0], sptr)
+    for _ in range(args.steps):
+        step(False)
+    hip.record(start_ev[1], sptr)
+    torch.cuda.synchronize()
+    wall = time.time() - t_wall
+    ms_step = hip.ms(start_ev[0], start_ev[1]) / args.steps
+
+    # per-kernel durations (same work, events between the kernels)
+    k = {"k_hist": 0.0, "k_encode": 0.0, "k_scan": 0.0, "k_pack": 0.0, "k_decode": 0.0,
+         "k_decode_multi": 0.0, "k_crc32": 0.0}
+    reps = max(3, min(args.steps, 10))
+    for _ in range(reps):
+        step(True)
+        torch.cuda.synchronize()
+        k["k_hist"] += hip.ms(ev_c[0], ev_c[1])
+        k["k_encode"] += hip.ms(ev_c[1], ev_c[2])
+        k["k_scan"] += hip.ms(ev_c[2], ev_c[3])
+        k["k_pack"] += hip.ms(ev_c[3], ev_c[4])
+        k["k_decode"] += hip.ms(ev_d[0], ev_d[1])
+        k["k_decode_multi"] += hip.ms(ev_d[1], ev_d[2])
+        k["k_crc32"] += hip.ms(ev_x[0], ev_x[1])
+    k = {n: v / reps for n, v in k.items()}
+    t_comp = k["k_hist"] + k["k_encode"] + k["k_scan"] + k["k_pack"]
+    t_dec = k["k_decode"] + k["k_decode_multi"]
+    t_crc = k["k_crc32"]
+
+    # algorithmic bytes per launch (what the method must move):
+    #   k_decode reads the blob and writes the original bytes: B + N
+    #   k_hist reads the input once: N;  k_crc32 reads the blobs: B
+    #   k_encode reads the elements of the streams it codes; k_pack writes
+    #   the blob and reads the input for RAW streams: B + N
+    algo = {"k_decode": B + N, "k_hist": N, "k_pack": B + N, "k_crc32": B, "k_encode": N,
+            "k_scan": 0, "k_decode_multi": 0}
+    dom = max((n for n in k if algo[n]), key=lambda n: k[n])
+    achieved = algo[dom] / (k[dom] * 1e-3) / 1e9
+    traffic = traffic_from_profiles(dom, 1)
+
+    value = N / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {**desc, "global_batch": count, "orig_bytes": N, "blob_bytes": B,
+                   "chunk_bytes": CHUNK, "passthrough_threshold": THRESHOLD,
+                   "crc_chunk_bytes": CRC_CHUNK, "parallelism": "single GPU"},
+        "decompress_gbs": round(N / (t_dec * 1e-3) / 1e9, 2),
+        "compress_gbs": round(N / (t_comp * 1e-3) / 1e9, 2),
+        "crc32_blob_gbs": round(B / (t_crc * 1e-3) / 1e9, 2),
+        "ratio": round(B / N, 5),
+        "decompress_roofline_frac": round((N + B) / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "compress_roofline_frac": round((N + B) / (t_comp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_ms": {n: round(v, 4) for n, v in k.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args, ts, torch)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * ltc.h -- C ABI of the MI355X (gfx950) lossless tensor codec.
+ *
+ * The library compresses the bytes of a tensor of model weights the way
+ * ZipNN does ("NOTE-241: ZipNN" (nucleation notes), section "Method",
+ * items 1-3 and 5): each element's bits are reordered so that the exponent
+ * fills the top byte, the bytes are split into one stream per byte position
+ * inside fixed-size chunks, and every stream is stored CONST (one repeated
+ * value), RAW, or entropy coded with 64-lane interleaved rANS over a 256-bin
+ * order-0 model normalised to a 4096 total.  The arguments and defaults
+ * follow cuZipNN 0.1.0 (PyPI page, section "API": chunk_bytes = 131072, a
+ * multiple of 8 and at most 16 MiB; passthrough_threshold = 0.95 in (0, 1];
+ * CRC-32 per 16 KiB matching zlib.crc32, the last chunk shorter); the blob is
+ * versioned and other versions are rejected (same page, "Blob format").  The
+ * device-pointer, caller-stream, no-allocation convention follows lmz's
+ * device entry point (lmz README, section "Building on lmz": "The caller owns
+ * the device").
+ *
+ * OWNERSHIP AND ASYNCHRONY.  Arguments named d_* are device pointers, h_*
+ * host pointers.  The caller allocates every buffer and owns the stream.
+ * The library allocates no memory, creates no context and never
+ * synchronises: work is enqueued on `stream` and the call returns at once.
+ * Results that only the device knows (*d_blob_nbytes, *d_status) are written
+ * to device memory; read them after synchronising the stream.  Argument
+ * errors the host can see are returned before anything is enqueued.  A HIP
+ * launch failure returns LTC_ERR_HIP.  Calls on different streams are
+ * independent; the library has no mutable global state.
+ *
+ * BLOB FORMAT v1 (byte exact; all integers little-endian).
+ *   dtype codes: LTC_U8 (element 1 byte), LTC_BF16, LTC_FP16 (2 bytes),
+ *   LTC_FP32 (4 bytes).  E = element bytes, C = chunk_bytes, N = input bytes,
+ *   K = ceil(N / C) chunks, S = K*E streams.
+ *   Reorder: for BF16/FP16/FP32 (mantissa bits w_m = 7/10/23, W = 8E) the
+ *   element x becomes y = e << (w_m+1) | s << w_m | m, i.e. the exponent
+ *   field moves to the top and the sign sits just below it (for BF16 and
+ *   FP32 the top byte is exactly the biased exponent).  U8 is not reordered.
+ *   Stream k of chunk c holds byte k of y for every element of the chunk.
+ *   Header, 64 bytes:
+ *     0 'L','T','C','B' | 4 u16 version = 1 | 6 u8 dtype | 7 u8 E |
+ *     8 u64 N | 16 u32 C | 20 u32 K | 24 u16 lanes = 64 | 26 u8 prob_bits
+ *     = 12 | 27 u8 flags = 0 | 28 u32 0 | 32 u64 blob_nbytes |
+ *     40 u64 payload_base = 64 + 16*S | 48 16 zero bytes
+ *   Directory: S entries of 16 bytes, entry c*E + k:
+ *     0 u64 offset from blob start | 8 u32 payload bytes | 12 u8 mode
+ *     (0 RAW, 1 RANS, 2 CONST) | 13 u8 const value (0 unless CONST) | 14 u16 0
+ *   Payloads in directory order, each at a multiple of 16: cursor starts at
+ *   payload_base; offset = cursor; cursor = align16(cursor + size); the
+ *   final cursor is blob_nbytes; every gap byte is zero.
+ *   Mode choice for a stream of n bytes with histogram h: CONST if one value
+ *   occurs; else the rANS payload size P is computed and the stream is RANS
+ *   if P <= P_max(n), the largest integer strictly below
+ *   passthrough_threshold * n in IEEE double, otherwise RAW (the n bytes).
+ *   Frequencies: f[v] = 0 if h[v] = 0, else max(1, floor(h[v]*4096/n));
+ *   while sum f > 4096, decrement the largest f > 1 (ties: smallest v); if
+ *   sum f < 4096, add the shortfall to the largest h (ties: smallest v).
+ *   rANS: 32-bit states, lower bound 2^16, 16-bit words, 64 lanes; symbol t
+ *   belongs to lane t mod 64, step t / 64.  Encoding starts each lane at
+ *   65536 and runs steps last to first, lanes 63 to 0: if x >= f[s] << 20,
+ *   emit x & 0xFFFF and x >>= 16; then x = (x/f)*4096 + x%f + cum[s].
+ *   Words are stored in decoding order: step by step, lanes ascending.
+ *   RANS payload: 0 u32 W | 4 u8 sym_lo | 5 u8 sym_hi | 6 ten zero bytes |
+ *     16 u32 states[64] | 272 u16 f[sym_lo..sym_hi] | zero pad to
+ *     WO = align16(272 + 2*(sym_hi - sym_lo + 1)) | WO u16 words[W];
+ *     payload bytes = WO + 2W.
+ *   Decoding reverses this; a RANS stream must consume exactly W words and
+ *   end with every state at 65536.
+ */
+#ifndef LTC_H
+#define LTC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { LTC_U8 = 0, LTC_BF16 = 1, LTC_FP16 = 2, LTC_FP32 = 3 };
+
+enum {
+  LTC_OK = 0,
+  LTC_ERR_INVALID_ARGUMENT = -1, /* bad size, chunk_bytes, threshold, pointer */
+  LTC_ERR_UNSUPPORTED_DTYPE = -2,
+  LTC_ERR_BAD_MAGIC = -3,
+  LTC_ERR_BAD_VERSION = -4,      /* cuZipNN "Blob format": other versions rejected */
+  LTC_ERR_CORRUPT = -5,          /* structural check failed */
+  LTC_ERR_CAPACITY = -6,         /* output buffer too small */
+  LTC_ERR_WORKSPACE = -7,        /* workspace too small */
+  LTC_ERR_HIP = -8               /* a HIP call or launch failed */
+};
+
+enum { LTC_MODE_RAW = 0, LTC_MODE_RANS = 1, LTC_MODE_CONST = 2 };
+
+#define LTC_HEADER_BYTES 64
+#define LTC_DEFAULT_CHUNK_BYTES 131072u
+#define LTC_DEFAULT_THRESHOLD 0.95
+#define LTC_DEFAULT_CRC_CHUNK_BYTES 16384u
+#define LTC_BATCH_MAX 32 /* tensors per batch call */
+
+/* Parsed header (ltc_blob_info). */
+typedef struct {
+  int32_t dtype;
+  uint32_t elem_bytes;
+  uint64_t nbytes;       /* N: decoded size */
+  uint32_t chunk_bytes;  /* C */
+  uint32_t nchunks;      /* K */
+  uint64_t blob_nbytes;
+  uint64_t payload_base;
+} ltc_info;
+
+/* Element size of a dtype code, 0 if unknown. */
+uint32_t ltc_elem_bytes(int dtype);
+
+/* Upper bound of the blob size for an input of `nbytes` bytes:
+ * 64 + 16*S + sum over streams of align16(stream bytes).  0 on bad args. */
+uint64_t ltc_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes);
+
+/* Device workspace (bytes) that ltc_compress needs for this input. */
+int ltc_compress_workspace_size(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                                uint64_t* ws_nbytes);
+
+/* Compress `nbytes` bytes at d_src (read as `dtype`, row-major) into d_blob.
+ * d_src must be aligned to the element size; blob_capacity must be at least
+ * ltc_compress_bound(); d_ws/ws_nbytes at least ltc_compress_workspace_size().
+ * The blob size is written to *d_blob_nbytes (device u64).  The blob is
+ * identical byte for byte to the format above for the same arguments.
+ * Errors: INVALID_ARGUMENT (nbytes % E, chunk_bytes not a multiple of 8 or
+ * outside [8, 2^24], threshold outside (0, 1], NULL pointers, K >= 2^32),
+ * UNSUPPORTED_DTYPE, CAPACITY, WORKSPACE, HIP. */
+int ltc_compress(const void* d_src, uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                 double passthrough_threshold, void* d_blob, uint64_t blob_capacity,
+                 uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
+                 hipStream_t stream);
+
+/* Batch of `count` (1..LTC_BATCH_MAX) tensors of one dtype, one launch
+ * sequence; each blob is identical to what ltc_compress gives for that
+ * tensor alone.  Host arrays hold the per-tensor device pointers and sizes;
+ * d_blob_nbytes is a device array of `count` u64.  The workspace is
+ * ltc_compress_batch_workspace_size(). */
+int ltc_compress_batch_workspace_size(int count, const uint64_t* h_nbytes, int dtype,
+                                      uint32_t chunk_bytes, uint64_t* ws_nbytes);
+int ltc_compress_batch(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                       int dtype, uint32_t chunk_bytes, double passthrough_threshold,
+                       void* const* h_blob_ptrs, const uint64_t* h_blob_capacity,
+                       uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
+                       hipStream_t stream);
+
+/* Parse and check the 64-byte header (a host copy of the blob's first bytes).
+ * Errors: BAD_MAGIC, BAD_VERSION (cuZipNN "Blob format": blobs of other
+ * versions are rejected), UNSUPPORTED_DTYPE, CORRUPT (inconsistent fields). */
+int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out);
+
+/* Decode a blob into d_dst (dst_capacity >= N).  h_header is a host copy of
+ * the blob's first 64 bytes (the host needs N, C and K to size the launch);
+ * blob_nbytes must equal the header's blob_nbytes.  The kernels validate the
+ * directory and every payload against the format (offset chain, sizes,
+ * modes, table sums, states, word counts, end states) without ever reading
+ * or writing out of bounds, and write LTC_OK or LTC_ERR_CORRUPT to *d_status
+ * (device i32).  After CORRUPT the contents of d_dst are unspecified.  A
+ * checksum is still the way to detect a corrupted payload that happens to
+ * decode (cuZipNN "API": verify untrusted blobs with CRC-32 first). */
+int ltc_decompress(const void* h_header, const void* d_blob, uint64_t blob_nbytes,
+                   void* d_dst, uint64_t dst_capacity, int32_t* d_status,
+                   hipStream_t stream);
+
+/* Batch decode of `count` (1..LTC_BATCH_MAX) blobs of one dtype and chunk
+ * size; d_status is a device array of `count` i32. */
+int ltc_decompress_batch(int count, const void* const* h_headers,
+                         const void* const* h_blob_ptrs, const uint64_t* h_blob_nbytes,
+                         void* const* h_dst_ptrs, const uint64_t* h_dst_capacity,
+                         int32_t* d_status, hipStream_t stream);
+
+/* CRC-32 (zlib's: reflected 0xEDB88320, init and final xor 0xFFFFFFFF) of
+ * every chunk_bytes-byte chunk of d_src, the last one possibly shorter
+ * (cuZipNN 0.1.0 "API", hash_tensor_with_crc32).  d_crc receives
+ * ceil(nbytes / chunk_bytes) u32 values.  chunk_bytes >= 1. */
+int ltc_crc32_chunks(const void* d_src, uint64_t nbytes, uint32_t chunk_bytes,
+                     uint32_t* d_crc, hipStream_t stream);
+
+/* Statistics from a host copy of the header and directory (the first
+ * payload_base bytes): per stream-index mode counts and payload bytes (the
+ * per-byte-group layout of ZipNN's Table II) and the whole-blob ratio. */
+typedef struct {
+  uint32_t elem_bytes;
+  uint64_t nbytes;
+  uint64_t blob_nbytes;
+  uint64_t mode_count[4][3];     /* [stream index k][mode] */
+  uint64_t payload_bytes[4];     /* sum of payload sizes per stream index */
+  uint64_t stream_bytes[4];      /* sum of raw stream sizes per stream index */
+} ltc_stats;
+int ltc_blob_stats(const void* h_prefix, uint64_t h_nbytes, ltc_stats* out);
+
+/* Profiling variants: identical work and results, plus hipEventRecord on
+ * `stream` around each kernel so a caller can time one kernel alone.
+ * Compress: 5 events (before k_hist, before k_encode, before k_scan, before
+ * k_pack, after k_pack).  Decompress: 3 events (before the single-table
+ * decode kernel, between it and the multi-table one, after). */
+int ltc_compress_batch_prof(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                            int dtype, uint32_t chunk_bytes, double passthrough_threshold,
+                            void* const* h_blob_ptrs, const uint64_t* h_blob_capacity,
+                            uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
+                            hipStream_t stream, const hipEvent_t* h_events);
+int ltc_decompress_batch_prof(int count, const void* const* h_headers,
+                              const void* const* h_blob_ptrs, const uint64_t* h_blob_nbytes,
+                              void* const* h_dst_ptrs, const uint64_t* h_dst_capacity,
+                              int32_t* d_status, hipStream_t stream, const hipEvent_t* h_events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

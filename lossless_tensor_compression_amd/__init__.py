@@ -1,0 +1,258 @@
+"""MI355X-native ZipNN-style lossless compression of model-weight tensors.
+
+A thin ctypes binding over libltc.so (HIP kernels for gfx950 behind the C ABI
+in include/ltc.h).  Every step of compression, decompression and checksum
+runs in the library's kernels; this module only marshals torch tensors
+(device memory and the current stream) to the C entry points.  There is no
+CPU fallback: without the built library, or without a GPU, calls raise.
+
+API (names as in cuZipNN 0.1.0, "API", and the C ABI):
+  compress(t, chunk_bytes=131072, passthrough_threshold=0.95) -> uint8 blob
+  decompress(blob, shape=None) -> tensor of the recorded dtype
+  crc32_chunks(t, chunk_bytes=16384) -> int32 tensor holding CRC-32 bits
+  compress_batch / decompress_batch for many tensors in one launch sequence
+  blob_info / blob_stats for host-side inspection of a blob's header
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libltc.so")
+
+U8, BF16, FP16, FP32 = 0, 1, 2, 3
+DTYPE_CODE = {torch.uint8: U8, torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}
+CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
+ERRORS = {0: "OK", -1: "INVALID_ARGUMENT", -2: "UNSUPPORTED_DTYPE", -3: "BAD_MAGIC",
+          -4: "BAD_VERSION", -5: "CORRUPT", -6: "CAPACITY", -7: "WORKSPACE", -8: "HIP"}
+BATCH_MAX = 32
+DEFAULT_CHUNK_BYTES = 131072
+DEFAULT_THRESHOLD = 0.95
+DEFAULT_CRC_CHUNK_BYTES = 16384
+
+
+class LTCError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({code})")
+        self.code = code
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("elem_bytes", ctypes.c_uint32),
+                ("nbytes", ctypes.c_uint64), ("chunk_bytes", ctypes.c_uint32),
+                ("nchunks", ctypes.c_uint32), ("blob_nbytes", ctypes.c_uint64),
+                ("payload_base", ctypes.c_uint64)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("elem_bytes", ctypes.c_uint32), ("nbytes", ctypes.c_uint64),
+                ("blob_nbytes", ctypes.c_uint64),
+                ("mode_count", (ctypes.c_uint64 * 3) * 4),
+                ("payload_bytes", ctypes.c_uint64 * 4),
+                ("stream_bytes", ctypes.c_uint64 * 4)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libltc.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python lossless_tensor_compression_amd/build.py` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, u64, u32, i32, dbl = (ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
+                                  ctypes.c_int, ctypes.c_double)
+        pvp = ctypes.POINTER(ctypes.c_void_p)
+        pu64 = ctypes.POINTER(ctypes.c_uint64)
+        L.ltc_elem_bytes.argtypes = [i32]
+        L.ltc_elem_bytes.restype = u32
+        L.ltc_compress_bound.argtypes = [u64, i32, u32]
+        L.ltc_compress_bound.restype = u64
+        L.ltc_compress_workspace_size.argtypes = [u64, i32, u32, pu64]
+        L.ltc_compress_batch_workspace_size.argtypes = [i32, pu64, i32, u32, pu64]
+        L.ltc_compress.argtypes = [vp, u64, i32, u32, dbl, vp, u64, vp, vp, u64, vp]
+        L.ltc_compress_batch.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp, vp, u64, vp]
+        L.ltc_compress_batch_prof.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp, vp,
+                                              u64, vp, pvp]
+        L.ltc_blob_info.argtypes = [ctypes.c_char_p, u64, ctypes.POINTER(Info)]
+        L.ltc_decompress.argtypes = [ctypes.c_char_p, vp, u64, vp, u64, vp, vp]
+        L.ltc_decompress_batch.argtypes = [i32, pvp, pvp, pu64, pvp, pu64, vp, vp]
+        L.ltc_decompress_batch_prof.argtypes = [i32, pvp, pvp, pu64, pvp, pu64, vp, vp, pvp]
+        L.ltc_crc32_chunks.argtypes = [vp, u64, u32, vp, vp]
+        L.ltc_blob_stats.argtypes = [ctypes.c_char_p, u64, ctypes.POINTER(Stats)]
+        for name in ("ltc_compress_workspace_size", "ltc_compress_batch_workspace_size",
+                     "ltc_compress", "ltc_compress_batch", "ltc_compress_batch_prof",
+                     "ltc_blob_info", "ltc_decompress", "ltc_decompress_batch",
+                     "ltc_decompress_batch_prof", "ltc_crc32_chunks", "ltc_blob_stats"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise LTCError(rc, what)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptrs(seq):
+    return (ctypes.c_void_p * len(seq))(*[ctypes.c_void_p(p) for p in seq])
+
+
+def _u64s(seq):
+    return (ctypes.c_uint64 * len(seq))(*seq)
+
+
+def _flat_bytes(t):
+    if not t.is_cuda:
+        raise ValueError("tensor must be on a GPU")
+    if t.dtype not in DTYPE_CODE:
+        raise LTCError(-2, f"dtype {t.dtype}")
+    return t.contiguous()
+
+
+def compress_bound(nbytes, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES):
+    return int(lib().ltc_compress_bound(nbytes, dtype_code, chunk_bytes))
+
+
+def workspace_size(nbytes_list, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES):
+    out = ctypes.c_uint64(0)
+    _check(lib().ltc_compress_batch_workspace_size(len(nbytes_list), _u64s(nbytes_list), dtype_code,
+                                                   chunk_bytes, ctypes.byref(out)), "workspace size")
+    return out.value
+
+
+def compress_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blob_ptrs, caps,
+                 nbytes_out_ptr, ws_ptr, ws_nbytes, stream=None, events=None):
+    """Pointer-level batch compress on `stream` (no allocation, no sync)."""
+    count = len(src_ptrs)
+    args = [count, _ptrs(src_ptrs), _u64s(nbytes), dtype_code, chunk_bytes, threshold,
+            _ptrs(blob_ptrs), _u64s(caps), ctypes.c_void_p(nbytes_out_ptr),
+            ctypes.c_void_p(ws_ptr), ws_nbytes, _stream(stream)]
+    if events is None:
+        _check(lib().ltc_compress_batch(*args), "compress")
+    else:
+        _check(lib().ltc_compress_batch_prof(*args, _ptrs(events)), "compress")
+
+
+def decompress_raw(headers, blob_ptrs, blob_nbytes, dst_ptrs, caps, status_ptr, stream=None,
+                   events=None):
+    """Pointer-level batch decompress on `stream`; headers are 64-byte host bytes."""
+    count = len(blob_ptrs)
+    hdr = (ctypes.c_void_p * count)(*[ctypes.cast(ctypes.c_char_p(h), ctypes.c_void_p) for h in headers])
+    args = [count, hdr, _ptrs(blob_ptrs), _u64s(blob_nbytes), _ptrs(dst_ptrs), _u64s(caps),
+            ctypes.c_void_p(status_ptr), _stream(stream)]
+    if events is None:
+        _check(lib().ltc_decompress_batch(*args), "decompress")
+    else:
+        _check(lib().ltc_decompress_batch_prof(*args, _ptrs(events)), "decompress")
+
+
+def compress_batch(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
+                   passthrough_threshold=DEFAULT_THRESHOLD):
+    """Blobs (uint8 GPU tensors) for up to 32 tensors of one dtype."""
+    if not 1 <= len(tensors) <= BATCH_MAX:
+        raise ValueError(f"1..{BATCH_MAX} tensors per batch")
+    ts = [_flat_bytes(t) for t in tensors]
+    code = DTYPE_CODE[ts[0].dtype]
+    if any(DTYPE_CODE[t.dtype] != code for t in ts):
+        raise ValueError("one dtype per batch")
+    dev = ts[0].device
+    nbytes = [t.numel() * t.element_size() for t in ts]
+    caps = [compress_bound(n, code, chunk_bytes) for n in nbytes]
+    if any(c == 0 for c in caps):
+        raise LTCError(-1, "compress_bound")
+    blobs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
+    ws_n = workspace_size(nbytes, code, chunk_bytes)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+    sizes = torch.zeros(len(ts), dtype=torch.int64, device=dev)
+    compress_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
+                 [b.data_ptr() for b in blobs], caps, sizes.data_ptr(), ws.data_ptr(), ws.numel())
+    host_sizes = sizes.cpu().tolist()
+    return [b[:s] for b, s in zip(blobs, host_sizes)]
+
+
+def compress(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD):
+    """Blob (1-D uint8 tensor on t's device) of a GPU tensor's bytes."""
+    return compress_batch([t], chunk_bytes, passthrough_threshold)[0]
+
+
+def blob_info(blob_or_header):
+    """Header fields as a dict; accepts a blob tensor (any device) or bytes."""
+    hdr = _header_bytes(blob_or_header)
+    info = Info()
+    _check(lib().ltc_blob_info(hdr, len(hdr), ctypes.byref(info)), "blob_info")
+    return {f: getattr(info, f) for f, _ in Info._fields_}
+
+
+def _header_bytes(b):
+    if isinstance(b, (bytes, bytearray)):
+        return bytes(b[:64])
+    return bytes(b[:64].cpu().numpy().tobytes())
+
+
+def decompress_batch(blobs, shapes=None, check=True):
+    """Decoded tensors (on the blobs' device) for up to 32 blobs."""
+    if not 1 <= len(blobs) <= BATCH_MAX:
+        raise ValueError(f"1..{BATCH_MAX} blobs per batch")
+    headers = [_header_bytes(b) for b in blobs]
+    infos = [blob_info(h) for h in headers]
+    dev = blobs[0].device
+    outs = [torch.empty(i["nbytes"], dtype=torch.uint8, device=dev) for i in infos]
+    status = torch.full((len(blobs),), -99, dtype=torch.int32, device=dev)
+    decompress_raw(headers, [b.data_ptr() for b in blobs], [b.numel() for b in blobs],
+                   [o.data_ptr() for o in outs], [o.numel() for o in outs], status.data_ptr())
+    if check:
+        st = status.cpu().tolist()
+        for s in st:
+            _check(s, "decompress (device status)")
+    res = []
+    for k, (o, i) in enumerate(zip(outs, infos)):
+        t = o.view(CODE_DTYPE[i["dtype"]])
+        if shapes is not None and shapes[k] is not None:
+            t = t.view(shapes[k])
+        res.append(t)
+    return res
+
+
+def decompress(blob, shape=None):
+    return decompress_batch([blob], [shape])[0]
+
+
+def crc32_chunks(t, chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):
+    """CRC-32 (zlib's) of every chunk_bytes bytes of a GPU tensor, as int32 bits."""
+    if not t.is_cuda:
+        raise ValueError("tensor must be on a GPU")
+    t = t.contiguous()
+    nbytes = t.numel() * t.element_size()
+    count = (nbytes + chunk_bytes - 1) // chunk_bytes if chunk_bytes else 0
+    out = torch.empty(max(count, 1), dtype=torch.int32, device=t.device)
+    _check(lib().ltc_crc32_chunks(ctypes.c_void_p(t.data_ptr()), nbytes, chunk_bytes,
+                                  ctypes.c_void_p(out.data_ptr()), _stream()), "crc32_chunks")
+    return out[:count]
+
+
+def blob_stats(blob):
+    """Mode counts and payload bytes per stream index (ZipNN Table II layout)."""
+    info = blob_info(blob)
+    prefix = bytes(blob[:info["payload_base"]].cpu().numpy().tobytes())
+    st = Stats()
+    _check(lib().ltc_blob_stats(prefix, len(prefix), ctypes.byref(st)), "blob_stats")
+    e = st.elem_bytes
+    return {
+        "nbytes": st.nbytes, "blob_nbytes": st.blob_nbytes,
+        "ratio": st.blob_nbytes / st.nbytes if st.nbytes else 0.0,
+        "modes": [{"raw": st.mode_count[k][0], "rans": st.mode_count[k][1],
+                   "const": st.mode_count[k][2]} for k in range(e)],
+        "group_percent": [100.0 * st.payload_bytes[k] / st.stream_bytes[k]
+                          if st.stream_bytes[k] else 0.0 for k in range(e)],
+    }

@@ -1,0 +1,390 @@
+// ltc_api.hip -- host side of the C ABI declared in include/ltc.h:
+// argument checks, sizes, workspace carving, header parsing and launches.
+// Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "ltc_internal.h"
+#include "ltc_launch.h"
+
+namespace ltc {
+namespace {
+
+constexpr uint64_t kAlign = 256;
+constexpr uint32_t kWordsGranule = 1024;
+
+uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+uint32_t elem_bytes(int dtype) {
+  switch (dtype) {
+    case LTC_U8: return 1;
+    case LTC_BF16: return 2;
+    case LTC_FP16: return 2;
+    case LTC_FP32: return 4;
+    default: return 0;
+  }
+}
+
+// Largest integer P with (double)P < theta * (double)n: cuZipNN 0.1.0, "API":
+// a chunk stays compressed only if it shrinks below the threshold fraction.
+uint32_t p_max(uint64_t n, double theta) {
+  const double lim = theta * (double)n;
+  if (!(lim > 0.0)) return 0;
+  double p = floor(lim);
+  if (p >= lim) p -= 1.0;
+  return p < 0.0 ? 0u : (uint32_t)p;
+}
+
+int check_shape(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
+  const uint32_t e = elem_bytes(dtype);
+  if (!e) return LTC_ERR_UNSUPPORTED_DTYPE;
+  if (nbytes % e) return LTC_ERR_INVALID_ARGUMENT;
+  if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8) return LTC_ERR_INVALID_ARGUMENT;
+  const uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
+  if (k >= (1ull << 32)) return LTC_ERR_INVALID_ARGUMENT;
+  return LTC_OK;
+}
+
+// words per stream reserved in the workspace: enough for any threshold <= 1
+uint32_t words_capacity(uint32_t chunk_bytes, uint32_t e) {
+  const uint32_t n = chunk_bytes / e;
+  const uint32_t pmax = n - 1;  // theta = 1
+  const uint32_t w = pmax > kRansFixed ? (pmax - kRansFixed) / 2 + 1 : 1;
+  return (uint32_t)round_up(w, kWordsGranule);
+}
+
+struct Layout {
+  uint64_t sinfo, freq, states, offsets, blobn, words, total;
+};
+
+Layout layout(uint64_t streams, int count, uint32_t wcap) {
+  Layout l;
+  uint64_t cur = 0;
+  l.sinfo = cur;   cur = round_up(cur + 16 * streams, kAlign);
+  l.freq = cur;    cur = round_up(cur + 512 * streams, kAlign);
+  l.states = cur;  cur = round_up(cur + 256 * streams, kAlign);
+  l.offsets = cur; cur = round_up(cur + 8 * streams, kAlign);
+  l.blobn = cur;   cur = round_up(cur + 8 * (uint64_t)count, kAlign);
+  l.words = cur;   cur = round_up(cur + 2ull * wcap * streams, kAlign);
+  l.total = cur;
+  return l;
+}
+
+uint64_t bound_of(uint64_t nbytes, uint32_t e, uint32_t chunk_bytes) {
+  const uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
+  if (k == 0) return kHeader;
+  const uint64_t full = nbytes / chunk_bytes;
+  const uint64_t tail = nbytes - full * chunk_bytes;
+  uint64_t b = kHeader + kDirEntry * k * e + full * e * align16(chunk_bytes / e);
+  if (tail) b += e * align16(tail / e);
+  return b;
+}
+
+int64_t batch_streams(int count, const uint64_t* nbytes, uint32_t e, uint32_t chunk_bytes) {
+  uint64_t chunks = 0;
+  for (int i = 0; i < count; ++i) chunks += (nbytes[i] + chunk_bytes - 1) / chunk_bytes;
+  // grid limit: chunks * 256 work-items per launch must stay below 2^32
+  if (chunks >= (1ull << 24)) return -1;
+  return (int64_t)(chunks * e);
+}
+
+int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, int dtype,
+                  uint32_t chunk_bytes, double theta, void* const* blobs, const uint64_t* caps,
+                  uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes, hipStream_t stream,
+                  const hipEvent_t* ev) {
+  if (count < 1 || count > kMaxJobs || !srcs || !nbytes || !blobs || !caps || !d_blob_nbytes)
+    return LTC_ERR_INVALID_ARGUMENT;
+  if (!(theta > 0.0 && theta <= 1.0)) return LTC_ERR_INVALID_ARGUMENT;
+  const uint32_t e = elem_bytes(dtype);
+  for (int i = 0; i < count; ++i) {
+    const int rc = check_shape(nbytes[i], dtype, chunk_bytes);
+    if (rc) return rc;
+    if (!blobs[i] || (nbytes[i] && !srcs[i])) return LTC_ERR_INVALID_ARGUMENT;
+    if (reinterpret_cast<uintptr_t>(srcs[i]) % e) return LTC_ERR_INVALID_ARGUMENT;
+    if (reinterpret_cast<uintptr_t>(blobs[i]) % 16) return LTC_ERR_INVALID_ARGUMENT;
+    if (caps[i] < bound_of(nbytes[i], e, chunk_bytes)) return LTC_ERR_CAPACITY;
+  }
+  const int64_t streams = batch_streams(count, nbytes, e, chunk_bytes);
+  if (streams < 0) return LTC_ERR_INVALID_ARGUMENT;
+  const uint32_t wcap = words_capacity(chunk_bytes, e);
+  const Layout l = layout((uint64_t)streams, count, wcap);
+  if (!d_ws || ws_nbytes < l.total || reinterpret_cast<uintptr_t>(d_ws) % kAlign)
+    return LTC_ERR_WORKSPACE;
+
+  CTable t;
+  memset(&t, 0, sizeof(t));
+  t.count = (uint32_t)count;
+  t.chunk_bytes = chunk_bytes;
+  t.n_full = chunk_bytes / e;
+  t.wcap = wcap;
+  t.dtype = (uint32_t)dtype;
+  bool vec = chunk_bytes % 16 == 0;
+  uint64_t chunk0 = 0;
+  for (int i = 0; i < count; ++i) {
+    CJob& jb = t.jobs[i];
+    jb.src = static_cast<const uint8_t*>(srcs[i]);
+    jb.blob = static_cast<uint8_t*>(blobs[i]);
+    jb.blob_nbytes_out = d_blob_nbytes + i;
+    jb.nbytes = nbytes[i];
+    jb.chunk0 = chunk0;
+    jb.nchunks = (uint32_t)((nbytes[i] + chunk_bytes - 1) / chunk_bytes);
+    const uint64_t tail_bytes = nbytes[i] - (uint64_t)(jb.nchunks ? jb.nchunks - 1 : 0) * chunk_bytes;
+    jb.n_tail = (uint32_t)(tail_bytes / e);
+    jb.pmax_full = p_max(t.n_full, theta);
+    jb.pmax_tail = p_max(jb.n_tail, theta);
+    chunk0 += jb.nchunks;
+    if (nbytes[i] && reinterpret_cast<uintptr_t>(srcs[i]) % 16) vec = false;
+  }
+  t.total_chunks = chunk0;
+  t.vec16 = vec ? 1u : 0u;
+  uint8_t* ws = static_cast<uint8_t*>(d_ws);
+  CWork w;
+  w.sinfo = reinterpret_cast<uint32_t*>(ws + l.sinfo);
+  w.freq = reinterpret_cast<uint16_t*>(ws + l.freq);
+  w.states = reinterpret_cast<uint32_t*>(ws + l.states);
+  w.offsets = reinterpret_cast<uint64_t*>(ws + l.offsets);
+  w.blob_nbytes = reinterpret_cast<uint64_t*>(ws + l.blobn);
+  w.words = reinterpret_cast<uint16_t*>(ws + l.words);
+  return launch_compress(t, w, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+}
+
+uint64_t rd64(const uint8_t* p) {
+  uint64_t v;
+  memcpy(&v, p, 8);
+  return v;
+}
+uint32_t rd32(const uint8_t* p) {
+  uint32_t v;
+  memcpy(&v, p, 4);
+  return v;
+}
+uint16_t rd16(const uint8_t* p) {
+  uint16_t v;
+  memcpy(&v, p, 2);
+  return v;
+}
+
+int decompress_impl(int count, const void* const* headers, const void* const* blobs,
+                    const uint64_t* blob_nbytes, void* const* dsts, const uint64_t* caps,
+                    int32_t* d_status, hipStream_t stream, const hipEvent_t* ev) {
+  if (count < 1 || count > kMaxJobs || !headers || !blobs || !blob_nbytes || !dsts || !caps || !d_status)
+    return LTC_ERR_INVALID_ARGUMENT;
+  DTable t;
+  memset(&t, 0, sizeof(t));
+  t.count = (uint32_t)count;
+  int dtype = -1;
+  uint32_t chunk_bytes = 0, e = 0;
+  bool vec = true;
+  uint64_t chunk0 = 0;
+  for (int i = 0; i < count; ++i) {
+    ltc_info info;
+    const int rc = ltc_blob_info(headers[i], kHeader, &info);
+    if (rc) return rc;
+    if (i == 0) {
+      dtype = info.dtype;
+      chunk_bytes = info.chunk_bytes;
+      e = info.elem_bytes;
+    } else if (info.dtype != dtype || info.chunk_bytes != chunk_bytes) {
+      return LTC_ERR_INVALID_ARGUMENT;
+    }
+    if (info.blob_nbytes != blob_nbytes[i]) return LTC_ERR_CORRUPT;
+    if (caps[i] < info.nbytes) return LTC_ERR_CAPACITY;
+    if (!blobs[i] || (info.nbytes && !dsts[i])) return LTC_ERR_INVALID_ARGUMENT;
+    if (reinterpret_cast<uintptr_t>(blobs[i]) % 16) return LTC_ERR_INVALID_ARGUMENT;
+    DJob& jb = t.jobs[i];
+    jb.blob = static_cast<const uint8_t*>(blobs[i]);
+    jb.dst = static_cast<uint8_t*>(dsts[i]);
+    jb.status = d_status + i;
+    jb.blob_nbytes = info.blob_nbytes;
+    jb.nbytes = info.nbytes;
+    jb.chunk0 = chunk0;
+    jb.nchunks = info.nchunks;
+    const uint64_t tail_bytes = info.nbytes - (uint64_t)(info.nchunks ? info.nchunks - 1 : 0) * chunk_bytes;
+    jb.n_tail = (uint32_t)(tail_bytes / e);
+    chunk0 += info.nchunks;
+    if (info.nbytes && reinterpret_cast<uintptr_t>(dsts[i]) % 16) vec = false;
+  }
+  if (chunk0 >= (1ull << 26)) return LTC_ERR_INVALID_ARGUMENT;  // 64 work-items per chunk
+  t.chunk_bytes = chunk_bytes;
+  t.n_full = chunk_bytes / e;
+  t.vec16 = (vec && chunk_bytes % 16 == 0) ? 1u : 0u;
+  t.total_chunks = chunk0;
+  return launch_decompress(dtype, t, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+}
+
+uint32_t gf2_mulmod_host(uint32_t a, uint32_t b) {
+  uint32_t r = 0;
+  for (int i = 0; i < 32; ++i) {
+    if (a & (0x80000000u >> i)) r ^= b;
+    b = (b >> 1) ^ (0xEDB88320u & (0u - (b & 1u)));
+  }
+  return r;
+}
+
+// x^(8n) mod P in the reflected representation (bit 31 - d = x^d)
+uint32_t xpow8(uint64_t n) {
+  uint32_t r = 0x80000000u, sq = 0x00800000u;
+  while (n) {
+    if (n & 1) r = gf2_mulmod_host(r, sq);
+    sq = gf2_mulmod_host(sq, sq);
+    n >>= 1;
+  }
+  return r;
+}
+
+}  // namespace
+}  // namespace ltc
+
+using namespace ltc;
+
+extern "C" {
+
+uint32_t ltc_elem_bytes(int dtype) { return elem_bytes(dtype); }
+
+uint64_t ltc_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
+  if (check_shape(nbytes, dtype, chunk_bytes)) return 0;
+  return bound_of(nbytes, elem_bytes(dtype), chunk_bytes);
+}
+
+int ltc_compress_workspace_size(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                                uint64_t* ws_nbytes) {
+  return ltc_compress_batch_workspace_size(1, &nbytes, dtype, chunk_bytes, ws_nbytes);
+}
+
+int ltc_compress_batch_workspace_size(int count, const uint64_t* h_nbytes, int dtype,
+                                      uint32_t chunk_bytes, uint64_t* ws_nbytes) {
+  if (count < 1 || count > kMaxJobs || !h_nbytes || !ws_nbytes) return LTC_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < count; ++i) {
+    const int rc = check_shape(h_nbytes[i], dtype, chunk_bytes);
+    if (rc) return rc;
+  }
+  const uint32_t e = elem_bytes(dtype);
+  const int64_t streams = batch_streams(count, h_nbytes, e, chunk_bytes);
+  if (streams < 0) return LTC_ERR_INVALID_ARGUMENT;
+  *ws_nbytes = layout((uint64_t)streams, count, words_capacity(chunk_bytes, e)).total;
+  return LTC_OK;
+}
+
+int ltc_compress(const void* d_src, uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                 double passthrough_threshold, void* d_blob, uint64_t blob_capacity,
+                 uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes, hipStream_t stream) {
+  return compress_impl(1, &d_src, &nbytes, dtype, chunk_bytes, passthrough_threshold, &d_blob,
+                       &blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, nullptr);
+}
+
+int ltc_compress_batch(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                       int dtype, uint32_t chunk_bytes, double passthrough_threshold,
+                       void* const* h_blob_ptrs, const uint64_t* h_blob_capacity,
+                       uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
+                       hipStream_t stream) {
+  return compress_impl(count, h_src_ptrs, h_nbytes, dtype, chunk_bytes, passthrough_threshold,
+                       h_blob_ptrs, h_blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, nullptr);
+}
+
+int ltc_compress_batch_prof(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                            int dtype, uint32_t chunk_bytes, double passthrough_threshold,
+                            void* const* h_blob_ptrs, const uint64_t* h_blob_capacity,
+                            uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
+                            hipStream_t stream, const hipEvent_t* h_events) {
+  return compress_impl(count, h_src_ptrs, h_nbytes, dtype, chunk_bytes, passthrough_threshold,
+                       h_blob_ptrs, h_blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, h_events);
+}
+
+int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {
+  if (!h_header || !out) return LTC_ERR_INVALID_ARGUMENT;
+  if (h_nbytes < kHeader) return LTC_ERR_CORRUPT;
+  const uint8_t* h = static_cast<const uint8_t*>(h_header);
+  if (memcmp(h, "LTCB", 4) != 0) return LTC_ERR_BAD_MAGIC;
+  if (rd16(h + 4) != 1) return LTC_ERR_BAD_VERSION;
+  const int dtype = h[6];
+  const uint32_t e = elem_bytes(dtype);
+  if (!e) return LTC_ERR_UNSUPPORTED_DTYPE;
+  if (h[7] != e) return LTC_ERR_CORRUPT;
+  const uint64_t nbytes = rd64(h + 8);
+  const uint32_t chunk_bytes = rd32(h + 16);
+  const uint64_t k = rd32(h + 20);
+  if (rd16(h + 24) != kLanes || h[26] != 12 || h[27] != 0 || rd32(h + 28) != 0) return LTC_ERR_CORRUPT;
+  for (int i = 48; i < 64; ++i)
+    if (h[i]) return LTC_ERR_CORRUPT;
+  if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8) return LTC_ERR_CORRUPT;
+  if (nbytes % e) return LTC_ERR_CORRUPT;
+  if (k != (nbytes + chunk_bytes - 1) / chunk_bytes) return LTC_ERR_CORRUPT;
+  const uint64_t base = kHeader + kDirEntry * k * e;
+  const uint64_t blob_nbytes = rd64(h + 32);
+  if (rd64(h + 40) != base || blob_nbytes < base || blob_nbytes % 16) return LTC_ERR_CORRUPT;
+  out->dtype = dtype;
+  out->elem_bytes = e;
+  out->nbytes = nbytes;
+  out->chunk_bytes = chunk_bytes;
+  out->nchunks = (uint32_t)k;
+  out->blob_nbytes = blob_nbytes;
+  out->payload_base = base;
+  return LTC_OK;
+}
+
+int ltc_decompress(const void* h_header, const void* d_blob, uint64_t blob_nbytes, void* d_dst,
+                   uint64_t dst_capacity, int32_t* d_status, hipStream_t stream) {
+  return decompress_impl(1, &h_header, &d_blob, &blob_nbytes, &d_dst, &dst_capacity, d_status,
+                         stream, nullptr);
+}
+
+int ltc_decompress_batch(int count, const void* const* h_headers, const void* const* h_blob_ptrs,
+                         const uint64_t* h_blob_nbytes, void* const* h_dst_ptrs,
+                         const uint64_t* h_dst_capacity, int32_t* d_status, hipStream_t stream) {
+  return decompress_impl(count, h_headers, h_blob_ptrs, h_blob_nbytes, h_dst_ptrs, h_dst_capacity,
+                         d_status, stream, nullptr);
+}
+
+int ltc_decompress_batch_prof(int count, const void* const* h_headers, const void* const* h_blob_ptrs,
+                              const uint64_t* h_blob_nbytes, void* const* h_dst_ptrs,
+                              const uint64_t* h_dst_capacity, int32_t* d_status, hipStream_t stream,
+                              const hipEvent_t* h_events) {
+  return decompress_impl(count, h_headers, h_blob_ptrs, h_blob_nbytes, h_dst_ptrs, h_dst_capacity,
+                         d_status, stream, h_events);
+}
+
+int ltc_crc32_chunks(const void* d_src, uint64_t nbytes, uint32_t chunk_bytes, uint32_t* d_crc,
+                     hipStream_t stream) {
+  if (chunk_bytes == 0) return LTC_ERR_INVALID_ARGUMENT;
+  if (nbytes == 0) return LTC_OK;
+  if (!d_src || !d_crc) return LTC_ERR_INVALID_ARGUMENT;
+  CrcArgs a;
+  memset(&a, 0, sizeof(a));
+  a.src = static_cast<const uint8_t*>(d_src);
+  a.out = d_crc;
+  a.chunk_bytes = chunk_bytes;
+  a.nchunks = (nbytes + chunk_bytes - 1) / chunk_bytes;
+  a.tail_len = nbytes - (a.nchunks - 1) * (uint64_t)chunk_bytes;
+  a.seg = round_up(chunk_bytes, 256) / 64;
+  for (int l = 0; l < 6; ++l) a.lvl[l] = xpow8(a.seg << l);
+  a.init_full = gf2_mulmod_host(0xFFFFFFFFu, xpow8(chunk_bytes));
+  a.init_tail = gf2_mulmod_host(0xFFFFFFFFu, xpow8(a.tail_len));
+  return launch_crc32(a, stream) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+}
+
+int ltc_blob_stats(const void* h_prefix, uint64_t h_nbytes, ltc_stats* out) {
+  ltc_info info;
+  const int rc = ltc_blob_info(h_prefix, h_nbytes, &info);
+  if (rc) return rc;
+  if (!out || h_nbytes < info.payload_base) return LTC_ERR_INVALID_ARGUMENT;
+  memset(out, 0, sizeof(*out));
+  out->elem_bytes = info.elem_bytes;
+  out->nbytes = info.nbytes;
+  out->blob_nbytes = info.blob_nbytes;
+  const uint8_t* d = static_cast<const uint8_t*>(h_prefix) + kHeader;
+  const uint32_t e = info.elem_bytes;
+  for (uint64_t c = 0; c < info.nchunks; ++c) {
+    const uint64_t len = c + 1 < info.nchunks ? info.chunk_bytes : info.nbytes - c * (uint64_t)info.chunk_bytes;
+    for (uint32_t k = 0; k < e; ++k) {
+      const uint8_t* ent = d + kDirEntry * (c * e + k);
+      const uint32_t mode = ent[12];
+      if (mode > 2) return LTC_ERR_CORRUPT;
+      out->mode_count[k][mode] += 1;
+      out->payload_bytes[k] += rd32(ent + 8);
+      out->stream_bytes[k] += len / e;
+    }
+  }
+  return LTC_OK;
+}
+
+}  // extern "C"

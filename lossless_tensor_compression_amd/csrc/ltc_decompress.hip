@@ -1,0 +1,348 @@
+// ltc_decompress.hip -- gfx950 decoding kernel.
+//
+// One wave64 workgroup per chunk.  The 64 interleaved rANS lanes of a coded
+// stream are the 64 lanes of the wave (lmz README, "On a GPU": the
+// interleaved states are the lanes of work, so parallelism comes from many
+// streams at once).  Per chunk the wave
+//   1. checks its directory entries (offset chain, modes, sizes) and the
+//      RANS payload headers (symbol range, zero fields, table sum, states),
+//   2. builds, per coded stream, a 4096-slot symbol table (u8) and a
+//      per-symbol (f, cum) table in LDS,
+//   3. streams the coded words through a 512-word LDS ring refilled 256
+//      words ahead of use,
+//   4. decodes 8 steps (512 symbols) at a time into an LDS stage, and
+//   5. rebuilds the elements from the stage (coded streams), direct loads
+//      (RAW streams) and constants (CONST streams), undoes the exponent
+//      extraction and writes 8 elements per lane with one vector store.
+// The decoding loop is a dependent chain (table lookup -> state update ->
+// conditional word fetch), which lmz's README calls latency-bound; many
+// resident waves hide it.  Chunks with more than one coded stream go to a
+// second instantiation that holds several tables.
+#include "ltc_internal.h"
+#include "ltc_launch.h"
+
+namespace ltc {
+
+constexpr uint32_t kDecRing = 512;  // words
+constexpr uint32_t kHalf = 256;     // words per refill (64 lanes x 8 bytes)
+
+__device__ __forceinline__ uint2 load_half(const uint16_t* wp, uint32_t nw, uint32_t h) {
+  const uint32_t idx = kHalf * h + 4 * lane_id();
+  if (idx + 4 <= nw) return *reinterpret_cast<const uint2*>(wp + idx);
+  uint32_t v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = idx + q < nw ? wp[idx + q] : 0u;
+  return make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+}
+
+template <int DT, int MAXR>
+__global__ __launch_bounds__(64) void k_decode(DTable t) {
+  constexpr int E = Dt<DT>::E;
+  __shared__ uint8_t lut[MAXR][4096];
+  __shared__ uint32_t symt[MAXR][256];
+  __shared__ __attribute__((aligned(16))) uint16_t ring[MAXR][kDecRing];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[MAXR][512];
+
+  const uint64_t g = blockIdx.x;
+  const int j = find_job(t, g);
+  const DJob& job = t.jobs[j];
+  const uint64_t c = g - job.chunk0;
+  const bool last = c + 1 == job.nchunks;
+  const uint32_t n = last ? job.n_tail : t.n_full;
+  const uint8_t* blob = job.blob;
+  const uint64_t B = job.blob_nbytes;
+  const uint64_t S = (uint64_t)job.nchunks * E;
+  const uint64_t s0 = c * E;
+  const uint32_t lane = lane_id();
+
+  // ---- directory
+  const uint4* dir = reinterpret_cast<const uint4*>(blob + kHeader);
+  uint64_t off[E];
+  uint32_t size[E], mode[E], cval[E];
+  bool bad = false;
+  int nr = 0;
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    const uint4 e = dir[s0 + k];
+    off[k] = (uint64_t)e.x | ((uint64_t)e.y << 32);
+    size[k] = e.z;
+    mode[k] = e.w & 0xFFu;
+    cval[k] = (e.w >> 8) & 0xFFu;
+    bad |= (e.w >> 16) != 0 || mode[k] > 2 || (mode[k] != LTC_MODE_CONST && cval[k] != 0) ||
+           (mode[k] == LTC_MODE_RAW && size[k] != n) || (mode[k] == LTC_MODE_CONST && size[k] != 0) ||
+           (mode[k] == LTC_MODE_RANS && size[k] < kRansFixed + 16) || off[k] > B ||
+           (uint64_t)size[k] > B - off[k];
+    if (k == 0 && c == 0) bad |= off[0] != kHeader + kDirEntry * S;
+    if (k > 0) bad |= off[k] != align16(off[k - 1] + size[k - 1]);
+    nr += mode[k] == LTC_MODE_RANS;
+  }
+  {
+    const uint64_t end = align16(off[E - 1] + size[E - 1]);
+    if (s0 + E < S) {
+      const uint4 e = dir[s0 + E];
+      bad |= ((uint64_t)e.x | ((uint64_t)e.y << 32)) != end;
+    } else {
+      bad |= end != B;
+    }
+  }
+  if (MAXR == 1) {
+    if (bad) {
+      if (lane == 0) *job.status = LTC_ERR_CORRUPT;
+      return;
+    }
+    if (nr > 1) return;  // the multi-table instantiation takes it
+  } else if (bad || nr <= 1) {
+    return;
+  }
+
+  // ---- coded-stream headers and tables
+  int rstream[MAXR];
+  uint32_t x[MAXR], nwords[MAXR], pos[MAXR], hcur[MAXR];
+  uint2 staged[MAXR];
+  const uint16_t* wp[MAXR];
+  int slot_of[E];
+  {
+    int rr = 0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      slot_of[k] = -1;
+      if (mode[k] == LTC_MODE_RANS && rr < MAXR) {
+        slot_of[k] = rr;
+        rstream[rr] = k;
+        ++rr;
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < MAXR; ++rr) {
+    x[rr] = kRansLow;
+    nwords[rr] = 0;
+    pos[rr] = 0;
+    hcur[rr] = 0;
+    wp[rr] = nullptr;
+    if (rr >= nr) continue;
+    const int k = rstream[rr];
+    const uint8_t* p = blob + off[k];
+    const uint4 h = *reinterpret_cast<const uint4*>(p);
+    const uint32_t lo = h.y & 0xFFu, hi = (h.y >> 8) & 0xFFu;
+    const uint32_t tcount = hi - lo + 1u;
+    const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * tcount);
+    bad |= lo >= hi || (h.y >> 16) != 0 || h.z != 0 || h.w != 0 || wo > size[k] ||
+           (uint64_t)(size[k] - wo) != 2ull * h.x;
+    if (bad) break;
+    nwords[rr] = h.x;
+    wp[rr] = reinterpret_cast<const uint16_t*>(p + wo);
+    x[rr] = reinterpret_cast<const uint32_t*>(p + 16)[lane];
+    bad |= __ballot(x[rr] < kRansLow) != 0;
+    const uint16_t* ft = reinterpret_cast<const uint16_t*>(p + kRansFixed);
+    uint32_t f[4], cum[4], acc = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t i = 4 * lane + q;
+      f[q] = i < tcount ? ft[i] : 0u;
+      cum[q] = acc;
+      acc += f[q];
+    }
+    const uint32_t base = wave_exclusive_scan_u32(acc);
+    const uint32_t total = wave_sum_u32(acc);
+    uint32_t flast = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (4 * lane + q == tcount - 1) flast = f[q];
+    const uint32_t f_lo = __shfl(f[0], 0, 64);
+    const uint32_t f_hi = wave_max_u32(flast);
+    const uint32_t pad = wo - (kRansFixed + 2 * tcount);
+    const bool padbad = lane < pad && p[kRansFixed + 2 * tcount + lane] != 0;
+    bad |= total != kTotal || f_lo == 0 || f_hi == 0 || __ballot(padbad) != 0;
+    if (bad) break;
+    uint16_t* cumt = ring[rr];  // the ring doubles as the cum table while building
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t i = 4 * lane + q;
+      if (i < tcount) {
+        symt[rr][lo + i] = f[q] | ((base + cum[q]) << 16);
+        cumt[i] = (uint16_t)(base + cum[q]);
+      }
+    }
+    if (lane == 0) cumt[tcount] = (uint16_t)kTotal;
+  }
+  if (bad) {
+    if (lane == 0) *job.status = LTC_ERR_CORRUPT;
+    return;
+  }
+  __syncthreads();
+  // slot -> symbol table: lane l fills slots 64l .. 64l+63
+#pragma unroll
+  for (int rr = 0; rr < MAXR; ++rr) {
+    if (rr >= nr) continue;
+    const uint8_t* p = blob + off[rstream[rr]];
+    const uint32_t lo = p[4], hi = p[5];
+    const uint32_t tcount = hi - lo + 1u;
+    const uint16_t* cumt = ring[rr];
+    const uint32_t slot0 = 64 * lane;
+    uint32_t a = 0, z = tcount - 1;  // largest i with cumt[i] <= slot0
+    while (a < z) {
+      const uint32_t mid = (a + z + 1) / 2;
+      if (cumt[mid] <= slot0) a = mid;
+      else z = mid - 1;
+    }
+    uint32_t v = a, nextc = cumt[a + 1];
+    uint32_t* lw = reinterpret_cast<uint32_t*>(&lut[rr][slot0]);
+    for (uint32_t q4 = 0; q4 < 16; ++q4) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t sl = slot0 + 4 * q4 + b;
+        while (nextc <= sl) {
+          ++v;
+          nextc = cumt[v + 1];
+        }
+        word |= (lo + v) << (8 * b);
+      }
+      lw[q4] = word;
+    }
+  }
+  __syncthreads();
+  // word rings: halves 0 and 1 resident, half 2 staged in registers
+#pragma unroll
+  for (int rr = 0; rr < MAXR; ++rr) {
+    if (rr >= nr) continue;
+    *reinterpret_cast<uint2*>(&ring[rr][4 * lane]) = load_half(wp[rr], nwords[rr], 0);
+    *reinterpret_cast<uint2*>(&ring[rr][kHalf + 4 * lane]) = load_half(wp[rr], nwords[rr], 1);
+    staged[rr] = load_half(wp[rr], nwords[rr], 2);
+  }
+  __syncthreads();
+
+  // ---- main loop: 8 steps (512 symbols) per block
+  const bool vec = t.vec16 != 0;
+  uint8_t* dst = job.dst + c * t.chunk_bytes;
+  const uint32_t steps = (n + 63) / 64;
+  const uint32_t nblk = (steps + 7) / 8;
+  bool wbad = false;
+  for (uint32_t b = 0; b < nblk; ++b) {
+    const uint32_t e0 = 512 * b + 8 * lane;
+    uint64_t rawv[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      rawv[k] = 0;
+      if (mode[k] != LTC_MODE_RAW) continue;
+      const uint8_t* rp = blob + off[k] + e0;
+      if (e0 + 8 <= n) {
+        rawv[k] = *reinterpret_cast<const uint64_t*>(rp);
+      } else {
+        for (uint32_t i = 0; e0 + i < n && i < 8; ++i) rawv[k] |= (uint64_t)rp[i] << (8 * i);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < MAXR; ++rr) {
+      if (rr >= nr) continue;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t step = 8 * b + q;
+        if (step >= steps) break;
+        const bool active = 64 * step + lane < n;
+        const uint32_t xs = x[rr];
+        const uint32_t sl = xs & (kTotal - 1);
+        const uint32_t v = lut[rr][sl];
+        const uint32_t e = symt[rr][v];
+        uint32_t xn = __umul24(e & 0xFFFFu, xs >> 12) + sl - (e >> 16);
+        if (!active) xn = xs;
+        const bool need = active && xn < kRansLow;
+        const uint64_t mask = __ballot(need);
+        if (need) {
+          const uint32_t idx = pos[rr] + lanes_below(mask);
+          wbad |= idx >= nwords[rr];
+          xn = (xn << 16) | ring[rr][idx & (kDecRing - 1)];
+        }
+        pos[rr] += (uint32_t)__popcll(mask);
+        x[rr] = xn;
+        stage[rr][64 * q + lane] = (uint8_t)v;
+        if (pos[rr] >= kHalf * (hcur[rr] + 1)) {
+          ++hcur[rr];
+          __syncthreads();
+          *reinterpret_cast<uint2*>(&ring[rr][kHalf * ((hcur[rr] + 1) & 1) + 4 * lane]) = staged[rr];
+          staged[rr] = load_half(wp[rr], nwords[rr], hcur[rr] + 2);
+          __syncthreads();
+        }
+      }
+    }
+    __syncthreads();
+    if (e0 < n) {
+      uint64_t pb[E];
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        if (mode[k] == LTC_MODE_RANS) pb[k] = *reinterpret_cast<const uint64_t*>(&stage[slot_of[k]][8 * lane]);
+        else if (mode[k] == LTC_MODE_RAW) pb[k] = rawv[k];
+        else pb[k] = 0x0101010101010101ull * cval[k];
+      }
+      uint32_t xe[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t y = 0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) y |= (uint32_t)((pb[k] >> (8 * i)) & 0xFFu) << (8 * k);
+        xe[i] = unreorder<DT>(y);
+      }
+      uint8_t* op = dst + (uint64_t)e0 * E;
+      if (vec && e0 + 8 <= n) {
+        if constexpr (E == 1) {
+          *reinterpret_cast<uint2*>(op) =
+              make_uint2(xe[0] | (xe[1] << 8) | (xe[2] << 16) | (xe[3] << 24),
+                         xe[4] | (xe[5] << 8) | (xe[6] << 16) | (xe[7] << 24));
+        } else if constexpr (E == 2) {
+          *reinterpret_cast<uint4*>(op) = make_uint4(xe[0] | (xe[1] << 16), xe[2] | (xe[3] << 16),
+                                                     xe[4] | (xe[5] << 16), xe[6] | (xe[7] << 16));
+        } else {
+          reinterpret_cast<uint4*>(op)[0] = make_uint4(xe[0], xe[1], xe[2], xe[3]);
+          reinterpret_cast<uint4*>(op)[1] = make_uint4(xe[4], xe[5], xe[6], xe[7]);
+        }
+      } else {
+        for (uint32_t i = 0; i < 8 && e0 + i < n; ++i) {
+#pragma unroll
+          for (int bb = 0; bb < E; ++bb) op[i * E + bb] = (uint8_t)(xe[i] >> (8 * bb));
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // ---- end checks: every coded stream consumed exactly its words and
+  // returned to the initial state
+  bool endbad = wbad;
+#pragma unroll
+  for (int rr = 0; rr < MAXR; ++rr) {
+    if (rr >= nr) continue;
+    endbad |= pos[rr] != nwords[rr] || x[rr] != kRansLow;
+  }
+  if (__ballot(endbad) != 0 && lane == 0) *job.status = LTC_ERR_CORRUPT;
+}
+
+__global__ void k_status_init(DTable t) {
+  const uint32_t j = threadIdx.x;
+  if (j < t.count) *t.jobs[j].status = LTC_OK;
+}
+
+template <int DT>
+static hipError_t launch_decompress_t(const DTable& t, hipStream_t st, const hipEvent_t* ev) {
+  constexpr int E = Dt<DT>::E;
+  hipLaunchKernelGGL(k_status_init, dim3(1), dim3(64), 0, st, t);
+  record(ev, 0, st);
+  if (t.total_chunks) hipLaunchKernelGGL((k_decode<DT, 1>), dim3((uint32_t)t.total_chunks), dim3(64), 0, st, t);
+  record(ev, 1, st);
+  if constexpr (E > 1) {
+    if (t.total_chunks) hipLaunchKernelGGL((k_decode<DT, E>), dim3((uint32_t)t.total_chunks), dim3(64), 0, st, t);
+  }
+  record(ev, 2, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_decompress(int dtype, const DTable& t, hipStream_t st, const hipEvent_t* ev) {
+  switch (dtype) {
+    case LTC_U8: return launch_decompress_t<LTC_U8>(t, st, ev);
+    case LTC_BF16: return launch_decompress_t<LTC_BF16>(t, st, ev);
+    case LTC_FP16: return launch_decompress_t<LTC_FP16>(t, st, ev);
+    case LTC_FP32: return launch_decompress_t<LTC_FP32>(t, st, ev);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ltc

@@ -1,0 +1,168 @@
+// ltc_internal.h -- device-side types and helpers of the gfx950 codec.
+// Not installed; the public contract is include/ltc.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ltc.h"
+
+namespace ltc {
+
+constexpr uint32_t kTotal = 4096;       // normalised frequency total (2^12)
+constexpr uint32_t kLanes = 64;         // interleaved rANS lanes = one wave64
+constexpr uint32_t kRansLow = 65536;    // state lower bound 2^16
+constexpr uint32_t kHeader = 64;
+constexpr uint32_t kDirEntry = 16;
+constexpr uint32_t kRansFixed = 272;    // 16-byte prefix + 64 u32 states
+constexpr uint32_t kModeCand = 3;       // internal: histogram done, encode pending
+constexpr int kMaxJobs = LTC_BATCH_MAX;
+
+__host__ __device__ constexpr uint64_t align16(uint64_t v) { return (v + 15) & ~uint64_t(15); }
+
+template <int DT> struct Dt;
+template <> struct Dt<LTC_U8> { static constexpr int E = 1, WM = -1; };
+template <> struct Dt<LTC_BF16> { static constexpr int E = 2, WM = 7; };
+template <> struct Dt<LTC_FP16> { static constexpr int E = 2, WM = 10; };
+template <> struct Dt<LTC_FP32> { static constexpr int E = 4, WM = 23; };
+
+// Exponent extraction ("NOTE-241: ZipNN", Method item 1): the exponent field
+// moves to the top of the element, the sign directly below it, the mantissa
+// stays in place.  U8 is the identity.
+template <int DT> __device__ __forceinline__ uint32_t reorder(uint32_t x) {
+  constexpr int E = Dt<DT>::E, WM = Dt<DT>::WM;
+  if constexpr (WM < 0) {
+    return x;
+  } else {
+    constexpr int W = 8 * E, WE = W - 1 - WM;
+    const uint32_t e = (x >> WM) & ((1u << WE) - 1u);
+    const uint32_t s = (x >> (W - 1)) & 1u;
+    return (e << (WM + 1)) | (s << WM) | (x & ((1u << WM) - 1u));
+  }
+}
+
+template <int DT> __device__ __forceinline__ uint32_t unreorder(uint32_t y) {
+  constexpr int E = Dt<DT>::E, WM = Dt<DT>::WM;
+  if constexpr (WM < 0) {
+    return y;
+  } else {
+    constexpr int W = 8 * E, WE = W - 1 - WM;
+    const uint32_t e = (y >> (WM + 1)) & ((1u << WE) - 1u);
+    const uint32_t s = (y >> WM) & 1u;
+    return (s << (W - 1)) | (e << WM) | (y & ((1u << WM) - 1u));
+  }
+}
+
+// ---------------------------------------------------------------- jobs
+// A launch covers up to kMaxJobs tensors of one dtype and chunk size; the
+// table travels as a kernel argument.
+
+struct CJob {
+  const uint8_t* src;
+  uint8_t* blob;
+  uint64_t* blob_nbytes_out;  // device u64
+  uint64_t nbytes;
+  uint64_t chunk0;            // first global chunk index of this job
+  uint32_t nchunks;
+  uint32_t n_tail;            // elements in the last chunk
+  uint32_t pmax_full;         // P_max for a full chunk's stream
+  uint32_t pmax_tail;         // P_max for the last chunk's stream
+};
+
+struct CTable {
+  CJob jobs[kMaxJobs];
+  uint32_t count;
+  uint32_t chunk_bytes;
+  uint32_t n_full;     // elements per full chunk
+  uint32_t wcap;       // word capacity per stream in the workspace (multiple of 1024)
+  uint64_t total_chunks;
+  uint32_t vec16;      // every src 16-byte aligned and chunk_bytes % 16 == 0
+  uint32_t dtype;
+};
+
+struct CWork {
+  uint32_t* sinfo;      // [S][4]: size, mode | cval<<8 | lo<<16 | hi<<24, W, 0
+  uint16_t* freq;       // [S][256]
+  uint32_t* states;     // [S][64]
+  uint16_t* words;      // [S][wcap]  (a stream's words end at its slot's end)
+  uint64_t* offsets;    // [S]
+  uint64_t* blob_nbytes;  // [count]
+};
+
+struct DJob {
+  const uint8_t* blob;
+  uint8_t* dst;
+  int32_t* status;
+  uint64_t blob_nbytes;
+  uint64_t nbytes;
+  uint64_t chunk0;
+  uint32_t nchunks;
+  uint32_t n_tail;
+};
+
+struct DTable {
+  DJob jobs[kMaxJobs];
+  uint32_t count;
+  uint32_t chunk_bytes;
+  uint32_t n_full;
+  uint32_t vec16;       // every dst 16-byte aligned and chunk_bytes % 16 == 0
+  uint64_t total_chunks;
+};
+
+template <class T>
+__device__ __forceinline__ int find_job(const T& t, uint64_t g) {
+  int j = 0;
+  while (j + 1 < (int)t.count && g >= t.jobs[j + 1].chunk0) ++j;
+  return j;
+}
+
+// ------------------------------------------------------- wave64 helpers
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// exclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_exclusive_scan_u32(uint32_t v) {
+  const uint32_t lane = lane_id();
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t up = __shfl_up(inc, o, 64);
+    if (lane >= (uint32_t)o) inc += up;
+  }
+  return inc - v;
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+}  // namespace ltc

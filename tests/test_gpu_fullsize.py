@@ -1,0 +1,117 @@
+"""GPU parity at the benchmark sizes, in the launch configuration bench.py
+times: C3 (28 BF16 tensors, 1.74 GB, one batch call) and C5 (one 8 GiB BF16
+buffer, 1/8 random bytes) plus CRC-32 of the C5 blob.  Whole outputs are
+checked by properties that hold at any size (exact round trip on the GPU,
+the directory's offset chain, per-stream modes, determinism); the oracle
+recomputes sampled tensors (C3) and sampled chunks (C5) byte for byte; zlib
+recomputes sampled CRC chunks."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import banner
+
+pytestmark = pytest.mark.gpu
+CHUNK = 131072
+
+
+@pytest.fixture(scope="module")
+def ltc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import lossless_tensor_compression_amd as m
+    m.lib()
+    return m
+
+
+def _directory(blob):
+    info_k = int.from_bytes(blob[20:24].cpu().numpy().tobytes(), "little")
+    e = int(blob[7].item())
+    d = blob[64:64 + 16 * info_k * e].cpu().numpy().reshape(-1, 16)
+    offs = d[:, :8].copy().view(np.uint64).ravel().astype(np.int64)
+    sizes = d[:, 8:12].copy().view(np.uint32).ravel().astype(np.int64)
+    return e, info_k, offs, sizes, d[:, 12].copy(), d[:, 13].copy()
+
+
+def _check_chain(blob):
+    e, k, offs, sizes, modes, cvals = _directory(blob)
+    base = 64 + 16 * k * e
+    ends = (offs + sizes + 15) // 16 * 16
+    assert offs[0] == base
+    assert np.array_equal(offs[1:], ends[:-1])
+    assert ends[-1] == blob.numel()
+    assert set(np.unique(modes).tolist()) <= {0, 1, 2}
+    return e, k, offs, sizes, modes, cvals
+
+
+def test_c3_batch_full_size(ltc):
+    banner("C3 generate")
+    ts = workloads.c3_gpu()
+    banner("C3 compress_batch (28 tensors, one launch sequence)")
+    blobs = ltc.compress_batch(ts)
+    banner("C3 decompress_batch")
+    outs = ltc.decompress_batch(blobs)
+    for t, o in zip(ts, outs):
+        assert torch.equal(t.view(-1).view(torch.int16), o.view(torch.int16))
+    del outs
+    n = sum(t.numel() * 2 for t in ts)
+    b = sum(x.numel() for x in blobs)
+    banner(f"C3 ratio {b / n:.4f}")
+    assert 0.64 < b / n < 0.68
+    for bl in blobs:
+        _, _, _, _, modes, _ = _check_chain(bl)
+        assert (modes.reshape(-1, 2)[:, 1] == 1).all()
+    assert torch.equal(ltc.compress(ts[2]), blobs[2])      # batch == single call
+    assert torch.equal(ltc.compress_batch(ts)[5], blobs[5])  # deterministic
+    for i in (0, 1, 4, 27):  # q, k, gate of layer 0 and down of layer 3
+        banner(f"C3 oracle parity tensor {i} {workloads.C3_SHAPES[i]}")
+        host = ts[i].view(torch.int16).cpu().numpy()
+        want = oracle.compress(host, 1, CHUNK, 0.95, nthreads=16)
+        assert np.array_equal(blobs[i].cpu().numpy(), want)
+
+
+def test_c5_full_size_with_crc(ltc):
+    banner("C5 generate (8 GiB)")
+    buf = workloads.c5_gpu()
+    t = buf.view(torch.bfloat16)
+    banner("C5 compress")
+    blob = ltc.compress(t)
+    banner("C5 decompress")
+    out = ltc.decompress(blob)
+    assert torch.equal(out.view(torch.uint8), buf)
+    del out
+    torch.cuda.empty_cache()
+    e, k, offs, sizes, modes, cvals = _check_chain(blob)
+    assert k == 65536
+    m = modes.reshape(k, 2)
+    per_tensor = 1024
+    rnd = np.zeros(k, dtype=bool)
+    for ti in range(7, 64, 8):
+        rnd[ti * per_tensor:(ti + 1) * per_tensor] = True
+    assert (m[rnd] == 0).all()                 # random bytes: both streams RAW
+    assert (m[~rnd, 1] == 1).all() and (m[~rnd, 0] == 0).all()
+    ratio = blob.numel() / buf.numel()
+    banner(f"C5 ratio {ratio:.4f}")
+    rng = np.random.default_rng(0)
+    sample = sorted(set([0, 1, 1023, 1024, 7 * 1024, 7 * 1024 + 511, 8 * 1024 - 1, k - 1] +
+                        rng.integers(0, k, 40).tolist()))
+    for c in sample:
+        src = buf[c * CHUNK:(c + 1) * CHUNK].cpu().numpy()
+        w_modes, w_cvals, w_sizes, payload = oracle.encode_chunk(src, 1, CHUNK, 0.95, 0)
+        assert m[c].tolist() == w_modes.tolist(), c
+        assert sizes[2 * c:2 * c + 2].tolist() == w_sizes.tolist(), c
+        got = blob[int(offs[2 * c]):int(offs[2 * c]) + payload.size].cpu().numpy()
+        assert np.array_equal(got, payload), c
+    banner("C5 CRC-32 of the blob")
+    crc = ltc.crc32_chunks(blob, 16384).cpu().numpy().view(np.uint32)
+    nb = blob.numel()
+    assert crc.size == (nb + 16383) // 16384
+    idx = sorted(set([0, 1, crc.size - 2, crc.size - 1] + rng.integers(0, crc.size, 2000).tolist()))
+    for i in idx:
+        lo = i * 16384
+        seg = blob[lo:min(nb, lo + 16384)].cpu().numpy()
+        assert int(crc[i]) == zlib.crc32(seg.tobytes()), i

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Blobs must be byte-identical to the oracle's, decoded bytes identical to the
+input, CRC-32 values identical to zlib's, and corrupted blobs must get the
+same verdict (and, when they still decode, the same bytes) as the oracle.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import banner, to_gpu, to_np_bytes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ltc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import lossless_tensor_compression_amd as m
+    m.lib()  # raises if the HIP library is missing
+    return m
+
+
+def gpu_blob(ltc, arr, dtype, chunk=131072, thr=0.95):
+    t = to_gpu(arr, dtype)
+    return to_np_bytes(ltc.compress(t, chunk, thr))
+
+
+def gpu_decode(ltc, blob_np):
+    b = torch.from_numpy(np.ascontiguousarray(blob_np).copy()).cuda()
+    return to_np_bytes(ltc.decompress(b))
+
+
+def check_case(ltc, arr, dtype, chunk=131072, thr=0.95, label=""):
+    banner(f"case {label} dtype={dtype} chunk={chunk} thr={thr} bytes={np.asarray(arr).nbytes}")
+    src = np.ascontiguousarray(arr).reshape(-1).view(np.uint8)
+    want = oracle.compress(src, dtype, chunk, thr)
+    got = gpu_blob(ltc, src, dtype, chunk, thr)
+    assert got.size == want.size, (got.size, want.size)
+    if not np.array_equal(got, want):
+        bad = np.nonzero(got != want)[0]
+        raise AssertionError(f"blob differs at {bad.size} bytes, first {bad[:8].tolist()}")
+    assert np.array_equal(gpu_decode(ltc, want), src)
+    return want
+
+
+def test_c1_bf16(ltc):
+    blob = check_case(ltc, workloads.c1(), 1, label="C1")
+    st = ltc.blob_stats(torch.from_numpy(blob))
+    assert st["modes"][0]["raw"] == 16 and st["modes"][1]["rans"] == 16
+
+
+def test_c2_fp32(ltc):
+    check_case(ltc, workloads.c2(), 3, label="C2")
+
+
+def test_c4_clean_fp32_and_fp16(ltc):
+    clean, h = workloads.c4()
+    check_case(ltc, clean, 3, label="C4 clean fp32")
+    check_case(ltc, h, 2, label="C4 fp16")
+
+
+def _pattern(kind, dtype, nelem, rng):
+    e = oracle.ELEM_BYTES[dtype]
+    if kind == "normal":
+        x = rng.standard_normal(nelem) * 0.02
+        if dtype == 0:
+            return np.clip(np.rint(x * 2000) + 128, 0, 255).astype(np.uint8)
+        if dtype == 1:
+            return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+        return x.astype(np.float16 if dtype == 2 else np.float32)
+    if kind == "const":
+        return np.full(nelem * e, 0x3C, dtype=np.uint8)
+    if kind == "two":
+        return rng.choice(np.array([0x11, 0xEE], dtype=np.uint8), nelem * e)
+    if kind == "random":
+        return rng.integers(0, 256, nelem * e, dtype=np.uint8)
+    if kind == "special":
+        pats = {0: [0, 255, 1], 1: [0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0x0001, 0x3F80],
+                2: [0x0000, 0x8000, 0x7C00, 0xFC00, 0x7E00, 0x0001, 0x3C00],
+                3: [0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 1, 0x3F800000]}[dtype]
+        dt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[e]
+        return rng.choice(np.array(pats, dtype=np.uint64), nelem).astype(dt)
+    raise ValueError(kind)
+
+
+AWKWARD = [(d, n, c, k) for d in (0, 1, 2, 3)
+           for n in (0, 1, 63, 64, 65, 129, 1000, 5003, 70001)
+           for c in (8, 24, 4096, 131072)
+           for k in ("normal", "const", "two", "random", "special")
+           if not (c == 8 and n > 5003)]
+
+
+@pytest.mark.parametrize("dtype,nelem,chunk,kind", AWKWARD,
+                         ids=lambda v: str(v))
+def test_awkward(ltc, dtype, nelem, chunk, kind):
+    rng = np.random.default_rng(nelem * 7 + chunk + dtype)
+    arr = _pattern(kind, dtype, nelem, rng)
+    check_case(ltc, arr, dtype, chunk, label=f"{kind} n={nelem}")
+
+
+@pytest.mark.parametrize("thr", [1e-6, 0.3, 0.5, 0.9, 0.95, 1.0])
+def test_threshold_variants(ltc, thr):
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(300000) * np.repeat([0.02, 0.5, 1e-3], 100000)).astype(np.float32)
+    check_case(ltc, x, 3, 65536, thr, label="threshold")
+    check_case(ltc, x.astype(np.float16), 2, 65536, thr, label="threshold fp16")
+
+
+def test_batch_equals_single(ltc):
+    rng = np.random.default_rng(8)
+    arrs = [(rng.standard_normal(n) * s).astype(np.float32)
+            for n, s in ((1, 1.0), (1000, 0.02), (70000, 0.1), (32768, 0.02), (100003, 3.0),
+                         (0, 1.0), (262144, 1e-3))]
+    ts = [to_gpu(a, 3) for a in arrs]
+    blobs = ltc.compress_batch(ts, 65536)
+    for a, b in zip(arrs, blobs):
+        assert np.array_equal(to_np_bytes(b), oracle.compress(a, 3, 65536))
+    outs = ltc.decompress_batch(blobs)
+    for a, o in zip(arrs, outs):
+        assert np.array_equal(to_np_bytes(o), a.view(np.uint8))
+
+
+def test_determinism_and_recompress(ltc):
+    x = workloads.c1()
+    t = to_gpu(x, 1)
+    b1 = ltc.compress(t)
+    b2 = ltc.compress(t)
+    assert torch.equal(b1, b2)
+    out = ltc.decompress(b1)
+    assert torch.equal(ltc.compress(out), b1)
+
+
+@pytest.mark.parametrize("n", [0, 1, 100, 4095, 16383, 16384, 16385, 1000007])
+@pytest.mark.parametrize("k", [1, 7, 256, 1000, 16384, 65536])
+def test_crc32_matches_zlib(ltc, n, k):
+    if k == 1 and n > 20000:
+        n = 20000
+    rng = np.random.default_rng(n + k)
+    data = rng.integers(0, 256, n + 3, dtype=np.uint8)
+    d = torch.from_numpy(data).cuda()
+    for start in (0, 3):  # aligned and misaligned starting address
+        view = d[start:start + n]
+        got = ltc.crc32_chunks(view, k).cpu().numpy().view(np.uint32).tolist()
+        seg = data[start:start + n]
+        want = [zlib.crc32(seg[i:i + k].tobytes()) for i in range(0, n, k)]
+        assert got == want
+
+
+def test_crc32_check_value(ltc):
+    d = torch.frombuffer(bytearray(b"123456789"), dtype=torch.uint8).cuda()
+    assert ltc.crc32_chunks(d, 16384).cpu().numpy().view(np.uint32).tolist() == [0xCBF43926]
+
+
+def _verdicts_agree(ltc, blob_np):
+    """GPU verdict (host return code or device status) == oracle verdict, and
+    identical decoded bytes whenever both accept the blob."""
+    want_rc, want = oracle.decompress(blob_np)
+    hdr = bytes(blob_np[:64])
+    try:
+        info = ltc.blob_info(hdr)
+    except ltc.LTCError as e:
+        assert e.code == want_rc, (e.code, want_rc)
+        return want_rc
+    b = torch.from_numpy(np.ascontiguousarray(blob_np).copy()).cuda()
+    dst = torch.empty(max(1, info["nbytes"]), dtype=torch.uint8, device="cuda")
+    status = torch.full((1,), -99, dtype=torch.int32, device="cuda")
+    try:
+        ltc.decompress_raw([hdr], [b.data_ptr()], [b.numel()], [dst.data_ptr()],
+                           [info["nbytes"]], status.data_ptr())
+    except ltc.LTCError as e:
+        assert e.code == want_rc, (e.code, want_rc)
+        return want_rc
+    st = int(status.item())
+    assert st == want_rc, (st, want_rc)
+    if st == 0:
+        assert np.array_equal(dst[:info["nbytes"]].cpu().numpy(), want)
+    return st
+
+
+def test_corruption_verdicts_match_oracle(ltc):
+    x = workloads.c1()[:200000]
+    blob = oracle.compress(x, 1, 16384)
+    assert _verdicts_agree(ltc, blob) == 0
+    e, k = 2, int.from_bytes(blob[20:24].tobytes(), "little")
+    d = blob[64:64 + 16 * k * e].reshape(-1, 16)
+    modes = d[:, 12]
+    offs = d[:, :8].copy().view(np.uint64).ravel()
+    rans = np.nonzero(modes == 1)[0]
+    cases = []
+    b = blob.copy(); b[64 + 12] = 5; cases.append(("bad mode", b))
+    b = blob.copy(); b[64 + 8] ^= 1; cases.append(("size breaks chain", b))
+    b = blob.copy(); b[64 + 16 * 3] ^= 0x10; cases.append(("offset breaks chain", b))
+    b = blob.copy(); b[64 + 14] = 1; cases.append(("reserved", b))
+    o = int(offs[rans[0]])
+    b = blob.copy(); b[o + 16 + 2:o + 16 + 4] = 0; cases.append(("state < 2^16", b))
+    b = blob.copy(); b[o + 272] ^= 1; cases.append(("table sum", b))
+    b = blob.copy(); b[o] ^= 2; cases.append(("word count", b))
+    b = blob.copy(); b[o + 6] = 1; cases.append(("prefix zeros", b))
+    b = blob.copy(); b[o + 4], b[o + 5] = b[o + 5], b[o + 4]; cases.append(("lo >= hi", b))
+    o2 = int(offs[rans[-1]])
+    b = blob.copy(); b[o2 + 300] ^= 0x40; cases.append(("word flip", b))
+    b = blob.copy(); b[o2 + 16 + 4 * 7] ^= 0x01; cases.append(("state flip", b))
+    cases.append(("truncated", blob[:-16]))
+    b = blob.copy(); b[4] = 2; cases.append(("version", b))
+    b = blob.copy(); b[0] = 0; cases.append(("magic", b))
+    for name, cb in cases:
+        banner(f"corruption {name}")
+        _verdicts_agree(ltc, cb)
+
+
+def test_random_payload_flips_match_oracle(ltc):
+    x = workloads.c1()[:100000]
+    blob = oracle.compress(x, 1, 16384)
+    base = 64 + 16 * 2 * int.from_bytes(blob[20:24].tobytes(), "little")
+    rng = np.random.default_rng(1)
+    verdicts = set()
+    for i in range(120):
+        b = blob.copy()
+        pos = int(rng.integers(base, b.size))
+        b[pos] ^= 1 << int(rng.integers(0, 8))
+        verdicts.add(_verdicts_agree(ltc, b))
+    assert -5 in verdicts
