@@ -178,6 +178,11 @@ int ltc_decompress_batch(int count, const void* const* h_headers,
 int ltc_crc32_chunks(const void* d_src, uint64_t nbytes, uint32_t chunk_bytes,
                      uint32_t* d_crc, hipStream_t stream);
 
+/* The same for `count` (1..LTC_BATCH_MAX) buffers in one launch; buffer i's
+ * checksums go to h_crc_ptrs[i] (a device pointer held in a host array). */
+int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                           uint32_t chunk_bytes, uint32_t* const* h_crc_ptrs, hipStream_t stream);
+
 /* Statistics from a host copy of the header and directory (the first
  * payload_base bytes): per stream-index mode counts and payload bytes (the
  * per-byte-group layout of ZipNN's Table II) and the whole-blob ratio. */

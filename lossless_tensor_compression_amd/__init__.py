@@ -84,11 +84,13 @@ def lib():
         L.ltc_decompress_batch.argtypes = [i32, pvp, pvp, pu64, pvp, pu64, vp, vp]
         L.ltc_decompress_batch_prof.argtypes = [i32, pvp, pvp, pu64, pvp, pu64, vp, vp, pvp]
         L.ltc_crc32_chunks.argtypes = [vp, u64, u32, vp, vp]
+        L.ltc_crc32_chunks_batch.argtypes = [i32, pvp, pu64, u32, pvp, vp]
         L.ltc_blob_stats.argtypes = [ctypes.c_char_p, u64, ctypes.POINTER(Stats)]
         for name in ("ltc_compress_workspace_size", "ltc_compress_batch_workspace_size",
                      "ltc_compress", "ltc_compress_batch", "ltc_compress_batch_prof",
                      "ltc_blob_info", "ltc_decompress", "ltc_decompress_batch",
-                     "ltc_decompress_batch_prof", "ltc_crc32_chunks", "ltc_blob_stats"):
+                     "ltc_decompress_batch_prof", "ltc_crc32_chunks", "ltc_crc32_chunks_batch",
+                     "ltc_blob_stats"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -239,6 +241,24 @@ def crc32_chunks(t, chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):
     _check(lib().ltc_crc32_chunks(ctypes.c_void_p(t.data_ptr()), nbytes, chunk_bytes,
                                   ctypes.c_void_p(out.data_ptr()), _stream()), "crc32_chunks")
     return out[:count]
+
+
+def crc32_raw(src_ptrs, nbytes, chunk_bytes, crc_ptrs, stream=None):
+    """Pointer-level batch CRC-32 on `stream` (no allocation, no sync)."""
+    _check(lib().ltc_crc32_chunks_batch(len(src_ptrs), _ptrs(src_ptrs), _u64s(nbytes), chunk_bytes,
+                                        _ptrs(crc_ptrs), _stream(stream)), "crc32_chunks_batch")
+
+
+def crc32_chunks_batch(tensors, chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):
+    """crc32_chunks for up to 32 GPU tensors in one launch."""
+    ts = [t.contiguous() for t in tensors]
+    if not 1 <= len(ts) <= BATCH_MAX or any(not t.is_cuda for t in ts):
+        raise ValueError(f"1..{BATCH_MAX} GPU tensors per batch")
+    nbytes = [t.numel() * t.element_size() for t in ts]
+    counts = [(n + chunk_bytes - 1) // chunk_bytes if chunk_bytes else 0 for n in nbytes]
+    outs = [torch.empty(max(c, 1), dtype=torch.int32, device=ts[0].device) for c in counts]
+    crc32_raw([t.data_ptr() for t in ts], nbytes, chunk_bytes, [o.data_ptr() for o in outs])
+    return [o[:c] for o, c in zip(outs, counts)]
 
 
 def blob_stats(blob):

@@ -343,23 +343,39 @@ int ltc_decompress_batch_prof(int count, const void* const* h_headers, const voi
                          d_status, stream, h_events);
 }
 
+int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                           uint32_t chunk_bytes, uint32_t* const* h_crc_ptrs, hipStream_t stream) {
+  if (count < 1 || count > kMaxJobs || !h_src_ptrs || !h_nbytes || !h_crc_ptrs || chunk_bytes == 0)
+    return LTC_ERR_INVALID_ARGUMENT;
+  CrcArgs a;
+  memset(&a, 0, sizeof(a));
+  a.count = (uint32_t)count;
+  a.chunk_bytes = chunk_bytes;
+  a.seg = round_up(chunk_bytes, 256) / 64;
+  for (int l = 0; l < 6; ++l) a.lvl[l] = xpow8(a.seg << l);
+  a.init_full = gf2_mulmod_host(0xFFFFFFFFu, xpow8(chunk_bytes));
+  uint64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    CrcJob& jb = a.jobs[i];
+    jb.src = static_cast<const uint8_t*>(h_src_ptrs[i]);
+    jb.out = h_crc_ptrs[i];
+    jb.chunk0 = total;
+    jb.nchunks = (h_nbytes[i] + chunk_bytes - 1) / chunk_bytes;
+    if (jb.nchunks && (!jb.src || !jb.out)) return LTC_ERR_INVALID_ARGUMENT;
+    jb.tail_len = jb.nchunks ? h_nbytes[i] - (jb.nchunks - 1) * (uint64_t)chunk_bytes : 0;
+    jb.init_tail = gf2_mulmod_host(0xFFFFFFFFu, xpow8(jb.tail_len));
+    total += jb.nchunks;
+  }
+  a.total_chunks = total;
+  return launch_crc32(a, stream) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+}
+
 int ltc_crc32_chunks(const void* d_src, uint64_t nbytes, uint32_t chunk_bytes, uint32_t* d_crc,
                      hipStream_t stream) {
   if (chunk_bytes == 0) return LTC_ERR_INVALID_ARGUMENT;
   if (nbytes == 0) return LTC_OK;
   if (!d_src || !d_crc) return LTC_ERR_INVALID_ARGUMENT;
-  CrcArgs a;
-  memset(&a, 0, sizeof(a));
-  a.src = static_cast<const uint8_t*>(d_src);
-  a.out = d_crc;
-  a.chunk_bytes = chunk_bytes;
-  a.nchunks = (nbytes + chunk_bytes - 1) / chunk_bytes;
-  a.tail_len = nbytes - (a.nchunks - 1) * (uint64_t)chunk_bytes;
-  a.seg = round_up(chunk_bytes, 256) / 64;
-  for (int l = 0; l < 6; ++l) a.lvl[l] = xpow8(a.seg << l);
-  a.init_full = gf2_mulmod_host(0xFFFFFFFFu, xpow8(chunk_bytes));
-  a.init_tail = gf2_mulmod_host(0xFFFFFFFFu, xpow8(a.tail_len));
-  return launch_crc32(a, stream) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+  return ltc_crc32_chunks_batch(1, &d_src, &nbytes, chunk_bytes, &d_crc, stream);
 }
 
 int ltc_blob_stats(const void* h_prefix, uint64_t h_nbytes, ltc_stats* out) {

@@ -18,6 +18,8 @@
 // Method: "NOTE-241: ZipNN", Method items 1-3 and 5; chunk size and
 // passthrough rule: cuZipNN 0.1.0, API; interleaved rANS lanes and a table per
 // stream: lmz README, "On a GPU" and "Building on lmz".
+#include <type_traits>
+
 #include "ltc_internal.h"
 #include "ltc_launch.h"
 
@@ -29,6 +31,7 @@ constexpr int kPackThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr uint32_t kRingWords = 1024;   // encoder word ring (LDS)
 constexpr uint32_t kFlushWords = 512;   // one flush = 64 lanes x 16 bytes
+constexpr int kEncBlock = 16;          // encoder steps per prefetched block
 
 __device__ __forceinline__ uint32_t pack_info(uint32_t mode, uint32_t cval, uint32_t lo,
                                               uint32_t hi) {
@@ -165,15 +168,19 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   for (uint32_t i = tid; i < E * 256 * kHistCopies; i += kHistThreads) hs[i] = 0;
   __syncthreads();
   uint32_t done = 0;
-  if (t.vec16) {
-    const uint32_t nvec = len / 16;
+  if (t.vec16 && len >= 16) {
+    const uint32_t nvec = len / 16, lastv = nvec - 1;
     const uint4* v = reinterpret_cast<const uint4*>(src);
+    // one 16-byte load in flight ahead of the one being counted; the index
+    // is clamped instead of branched so the wait lands at the use
+    uint4 q = v[min(tid, lastv)];
     for (uint32_t i = tid; i < nvec; i += kHistThreads) {
-      const uint4 q = v[i];
+      const uint4 nq = v[min(i + kHistThreads, lastv)];
       hist_word<DT>(hs, q.x, copy);
       hist_word<DT>(hs, q.y, copy);
       hist_word<DT>(hs, q.z, copy);
       hist_word<DT>(hs, q.w, copy);
+      q = nq;
     }
     done = nvec * 16;
   }
@@ -197,8 +204,10 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
 template <int DT>
 __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
-  __shared__ uint2 tab[256];
-  __shared__ __attribute__((aligned(16))) uint16_t ring[kRingWords];
+  __shared__ uint4 tab[256];
+  // word ring plus one private dummy slot per lane: a lane that emits
+  // nothing writes its dummy slot, so the store needs no branch
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kRingWords + 64];
   const uint64_t s = blockIdx.x;
   const uint32_t info = w.sinfo[4 * s + 1];
   if ((info & 0xFFu) != kModeCand) return;
@@ -214,10 +223,13 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * (hi - lo + 1u));
   const uint32_t lane = lane_id();
 
-  // encoder table: f | cum << 12 | sh2 << 24 | sh1 << 28, and the
-  // Granlund-Montgomery multiplier for exact division by f
-  // (Granlund & Montgomery 1994, "Division by invariant integers using
-  // multiplication", unsigned case with an (N+1)-bit multiplier).
+  // Encoder table, one 16-byte entry per symbol:
+  //   x: f << 20, the renormalisation bound
+  //   y: Granlund-Montgomery multiplier m for exact division by f
+  //      (Granlund & Montgomery 1994, "Division by invariant integers using
+  //      multiplication": q = (t + ((x - t) >> sh1)) >> sh2, t = mulhi(m, x))
+  //   z: (4096 - f) | sh2 << 24   (the 24-bit multiply ignores the top byte)
+  //   w: cum | sh1 << 24
   {
     const uint64_t fq = *reinterpret_cast<const uint64_t*>(w.freq + 256 * s + 4 * lane);
     uint32_t f[4], cum[4], acc = 0;
@@ -234,7 +246,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
       const uint32_t ell = fv <= 1 ? 0u : 32u - __clz(fv - 1u);
       const uint32_t m = fv ? (uint32_t)(((((uint64_t)1) << 32) * ((1ull << ell) - fv)) / fv + 1u) : 0u;
       const uint32_t sh1 = ell > 0 ? 1u : 0u, sh2 = ell > 0 ? ell - 1u : 0u;
-      tab[4 * lane + i] = make_uint2(fv | ((base + cum[i]) << 12) | (sh2 << 24) | (sh1 << 28), m);
+      tab[4 * lane + i] = make_uint4(fv << 20, m, (kTotal - fv) | (sh2 << 24), (base + cum[i]) | (sh1 << 24));
     }
   }
   __syncthreads();
@@ -243,14 +255,16 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   uint16_t* wout = w.words + s * wcap;
   const uint32_t wlimit = (pmax - wo) / 2;  // more words than this cannot beat the threshold
   const uint8_t* src = job.src + c * t.chunk_bytes;
+  const uint32_t full = n / 64;             // steps in which every lane codes a symbol
   const uint32_t steps = (n + 63) / 64;
-  const uint32_t nblk = (steps + 7) / 8;
   uint32_t x = kRansLow, top = wcap, nw = 0, flushed = 0;
-  bool aborted = false;
 
-  auto sym_at = [&](uint32_t step) -> uint32_t {
+  // Elements are fetched one block of steps ahead, unconditionally: lanes
+  // past the end read the last element instead (their state is not
+  // updated), so no branch forces an early wait on the loads.
+  auto elem_at = [&](uint32_t step) -> uint32_t {
     const uint32_t e = 64 * step + lane;
-    return e < n ? (reorder<DT>(load_elem<DT>(src + (uint64_t)e * E)) >> (8 * k)) & 0xFFu : 0u;
+    return load_elem<DT>(src + (uint64_t)(e < n ? e : n - 1) * E);
   };
   auto flush = [&](uint32_t b) {
     __syncthreads();
@@ -258,51 +272,58 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     const uint4 v = *reinterpret_cast<const uint4*>(&ring[base & (kRingWords - 1)]);
     *reinterpret_cast<uint4*>(wout + base) = v;
   };
+  // One coding step of the wave.  Steps run from the last to the first and,
+  // within a step, the emitted words take decoder order (lanes ascending):
+  // lane l's word goes to top - cnt + (number of emitting lanes below l).
+  // Returns false once the payload can no longer beat the threshold.
+  auto code = [&](auto guarded, uint32_t raw) -> bool {
+    constexpr bool G = decltype(guarded)::value;
+    const bool active = !G || 64 * full + lane < n;
+    const uint4 e = tab[(reorder<DT>(raw) >> (8 * k)) & 0xFFu];
+    const bool need = active && x >= e.x;
+    const uint64_t mask = ballot(need);
+    const uint32_t cnt = (uint32_t)__popcll(mask);
+    nw += cnt;
+    if (nw > wlimit) return false;
+    const uint32_t slot = need ? ((top - cnt + lanes_below(mask)) & (kRingWords - 1)) : kRingWords + lane;
+    ring[slot] = (uint16_t)x;
+    const uint32_t xr = need ? x >> 16 : x;
+    top -= cnt;
+    const uint32_t t1 = __umulhi(e.y, xr);
+    const uint32_t q = (t1 + ((xr - t1) >> (e.w >> 24))) >> (e.z >> 24);
+    const uint32_t xn = __umul24(q, e.z) + xr + (e.w & 0xFFFFFFu);
+    x = active ? xn : x;
+    if (nw >= kFlushWords * (flushed + 1)) {
+      flush(flushed);
+      ++flushed;
+    }
+    return true;
+  };
 
-  uint32_t cur[8];
+  bool ok = true;
+  if (steps > full) ok = code(std::true_type{}, elem_at(full));  // the partial step comes first
+  if (ok && full > 0) {
+    const uint32_t nblk = (full + kEncBlock - 1) / kEncBlock;
+    uint32_t cur[kEncBlock];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) cur[q] = sym_at(8 * (nblk - 1) + q);
-  for (int b = (int)nblk - 1; b >= 0 && !aborted; --b) {
-    uint32_t nxt[8];
-    if (b > 0) {
+    for (int q = 0; q < kEncBlock; ++q) cur[q] = elem_at(kEncBlock * (nblk - 1) + q);
+    for (int b = (int)nblk - 1; b >= 0 && ok; --b) {
+      uint32_t nxt[kEncBlock];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) nxt[q] = sym_at(8 * (b - 1) + q);
+      for (int q = 0; q < kEncBlock; ++q) nxt[q] = elem_at(kEncBlock * (b > 0 ? b - 1 : 0) + q);
+#pragma unroll
+      for (int q = kEncBlock - 1; q >= 0; --q) {
+        if (kEncBlock * (uint32_t)b + q >= full) continue;
+        if (!code(std::false_type{}, cur[q])) {
+          ok = false;
+          break;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kEncBlock; ++q) cur[q] = nxt[q];
     }
-#pragma unroll
-    for (int q = 7; q >= 0; --q) {
-      const uint32_t step = 8 * (uint32_t)b + q;
-      if (step >= steps) continue;
-      const bool active = 64 * step + lane < n;
-      const uint2 e = tab[cur[q]];
-      const uint32_t f = e.x & 0xFFFu, cum = (e.x >> 12) & 0xFFFu;
-      const uint32_t sh2 = (e.x >> 24) & 0xFu, sh1 = e.x >> 28;
-      const bool need = active && x >= (f << 20);
-      const uint64_t mask = __ballot(need);
-      const uint32_t cnt = (uint32_t)__popcll(mask);
-      nw += cnt;
-      if (nw > wlimit) {
-        aborted = true;
-        break;
-      }
-      if (need) {
-        ring[(top - cnt + lanes_below(mask)) & (kRingWords - 1)] = (uint16_t)(x & 0xFFFFu);
-        x >>= 16;
-      }
-      top -= cnt;
-      if (active) {
-        const uint32_t t1 = __umulhi(e.y, x);
-        const uint32_t qd = (t1 + ((x - t1) >> sh1)) >> sh2;
-        x = x + __umul24(qd, kTotal - f) + cum;
-      }
-      if (nw >= kFlushWords * (flushed + 1)) {
-        flush(flushed);
-        ++flushed;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
   }
-  if (aborted) {
+  if (!ok) {
     if (lane == 0)
       *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(n, pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
     return;

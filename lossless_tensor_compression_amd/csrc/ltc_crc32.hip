@@ -37,6 +37,7 @@ __device__ __forceinline__ uint32_t gf2_mulmod(uint32_t a, uint32_t b) {
 __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
   __shared__ uint32_t t8[8][256];
   __shared__ uint32_t tl[6][4][256];
+  __shared__ uint32_t basis[6][32];
   const uint32_t tid = threadIdx.x;
   {
     // t8[m][b] = CRC register of byte b followed by m zero bytes
@@ -46,20 +47,33 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
       t8[m][tid] = c;
     }
   }
+  // multiplication by the level constant is linear: tabulate it per byte
+  // position from the images of the 32 single-bit words
+  if (tid < 6 * 32) basis[tid / 32][tid % 32] = gf2_mulmod(1u << (tid % 32), a.lvl[tid / 32]);
+  __syncthreads();
   for (uint32_t idx = tid; idx < 6 * 4 * 256; idx += kCrcThreads) {
     const uint32_t l = idx / 1024, p = (idx / 256) & 3, b = idx & 255;
-    tl[l][p][b] = gf2_mulmod(b << (8 * p), a.lvl[l]);
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (b & (1u << i)) v ^= basis[l][8 * p + i];
+    tl[l][p][b] = v;
   }
   __syncthreads();
 
   const uint32_t lane = lane_id(), wave = tid / 64;
   const uint64_t frame = 64 * a.seg;
-  for (uint64_t i = (uint64_t)blockIdx.x * 4 + wave; i < a.nchunks; i += (uint64_t)gridDim.x * 4) {
-    const bool last = i + 1 == a.nchunks;
-    const uint64_t len = last ? a.tail_len : a.chunk_bytes;
+  for (uint64_t gi = (uint64_t)blockIdx.x * 4 + wave; gi < a.total_chunks;
+       gi += (uint64_t)gridDim.x * 4) {
+    int jb = 0;
+    while (jb + 1 < (int)a.count && gi >= a.jobs[jb + 1].chunk0) ++jb;
+    const CrcJob& job = a.jobs[jb];
+    const uint64_t i = gi - job.chunk0;
+    const bool last = i + 1 == job.nchunks;
+    const uint64_t len = last ? job.tail_len : a.chunk_bytes;
     const uint64_t pad = frame - len;  // leading virtual zero bytes
     const uint64_t vs = lane * a.seg, ve = vs + a.seg;
-    const uint8_t* base = a.src + i * a.chunk_bytes;
+    const uint8_t* base = job.src + i * a.chunk_bytes;
     const uint8_t* p = base;
     const uint8_t* end = base;
     if (ve > pad) {
@@ -71,17 +85,26 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
       crc = t8[0][(crc ^ *p) & 0xFFu] ^ (crc >> 8);
       ++p;
     }
-    for (; p + 16 <= end; p += 16) {
-      const uint4 q = *reinterpret_cast<const uint4*>(p);
-      crc ^= q.x;
-      crc = t8[7][crc & 0xFFu] ^ t8[6][(crc >> 8) & 0xFFu] ^ t8[5][(crc >> 16) & 0xFFu] ^
-            t8[4][crc >> 24] ^ t8[3][q.y & 0xFFu] ^ t8[2][(q.y >> 8) & 0xFFu] ^
-            t8[1][(q.y >> 16) & 0xFFu] ^ t8[0][q.y >> 24];
-      crc ^= q.z;
-      crc = t8[7][crc & 0xFFu] ^ t8[6][(crc >> 8) & 0xFFu] ^ t8[5][(crc >> 16) & 0xFFu] ^
-            t8[4][crc >> 24] ^ t8[3][q.w & 0xFFu] ^ t8[2][(q.w >> 8) & 0xFFu] ^
-            t8[1][(q.w >> 16) & 0xFFu] ^ t8[0][q.w >> 24];
+    auto step16 = [&](uint32_t c, const uint4 q) {
+      c ^= q.x;
+      c = t8[7][c & 0xFFu] ^ t8[6][(c >> 8) & 0xFFu] ^ t8[5][(c >> 16) & 0xFFu] ^
+          t8[4][c >> 24] ^ t8[3][q.y & 0xFFu] ^ t8[2][(q.y >> 8) & 0xFFu] ^
+          t8[1][(q.y >> 16) & 0xFFu] ^ t8[0][q.y >> 24];
+      c ^= q.z;
+      c = t8[7][c & 0xFFu] ^ t8[6][(c >> 8) & 0xFFu] ^ t8[5][(c >> 16) & 0xFFu] ^
+          t8[4][c >> 24] ^ t8[3][q.w & 0xFFu] ^ t8[2][(q.w >> 8) & 0xFFu] ^
+          t8[1][(q.w >> 16) & 0xFFu] ^ t8[0][q.w >> 24];
+      return c;
+    };
+    // all sixteen 16-byte loads of a 256-byte segment are in flight together
+    for (; p + 256 <= end; p += 256) {
+      uint4 q[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) q[u] = reinterpret_cast<const uint4*>(p)[u];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) crc = step16(crc, q[u]);
     }
+    for (; p + 16 <= end; p += 16) crc = step16(crc, *reinterpret_cast<const uint4*>(p));
     for (; p < end; ++p) crc = t8[0][(crc ^ *p) & 0xFFu] ^ (crc >> 8);
 #pragma unroll
     for (int l = 0; l < 6; ++l) {
@@ -90,13 +113,13 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
         crc = tl[l][0][crc & 0xFFu] ^ tl[l][1][(crc >> 8) & 0xFFu] ^ tl[l][2][(crc >> 16) & 0xFFu] ^
               tl[l][3][crc >> 24] ^ right;
     }
-    if (lane == 0) a.out[i] = crc ^ (last ? a.init_tail : a.init_full) ^ 0xFFFFFFFFu;
+    if (lane == 0) job.out[i] = crc ^ (last ? job.init_tail : a.init_full) ^ 0xFFFFFFFFu;
   }
 }
 
 hipError_t launch_crc32(const CrcArgs& a, hipStream_t st) {
-  if (a.nchunks == 0) return hipSuccess;
-  const uint64_t want = (a.nchunks + 3) / 4;
+  if (a.total_chunks == 0) return hipSuccess;
+  const uint64_t want = (a.total_chunks + 3) / 4;
   const uint32_t grid = (uint32_t)(want < 1280 ? want : 1280);
   hipLaunchKernelGGL(k_crc32, dim3(grid), dim3(kCrcThreads), 0, st, a);
   return hipGetLastError();

@@ -9,7 +9,7 @@
 //   2. builds, per coded stream, a 4096-slot symbol table (u8) and a
 //      per-symbol (f, cum) table in LDS,
 //   3. streams the coded words through a 512-word LDS ring refilled 256
-//      words ahead of use,
+//      words at a time from registers loaded a refill ahead,
 //   4. decodes 8 steps (512 symbols) at a time into an LDS stage, and
 //   5. rebuilds the elements from the stage (coded streams), direct loads
 //      (RAW streams) and constants (CONST streams), undoes the exponent
@@ -18,6 +18,8 @@
 // conditional word fetch), which lmz's README calls latency-bound; many
 // resident waves hide it.  Chunks with more than one coded stream go to a
 // second instantiation that holds several tables.
+#include <type_traits>
+
 #include "ltc_internal.h"
 #include "ltc_launch.h"
 
@@ -26,13 +28,56 @@ namespace ltc {
 constexpr uint32_t kDecRing = 512;  // words
 constexpr uint32_t kHalf = 256;     // words per refill (64 lanes x 8 bytes)
 
+// Words 256h + 4l .. +3 of a coded stream (lane l).  An 8-byte read that
+// starts at a word index below W stays inside the payload's 16-byte padded
+// slot, so only the start index is clamped (no branch, no early wait); a
+// stream with W = 0 passes a pointer into the directory instead.  Words past
+// W are never consumed by a valid blob, and reading one marks it corrupt.
 __device__ __forceinline__ uint2 load_half(const uint16_t* wp, uint32_t nw, uint32_t h) {
   const uint32_t idx = kHalf * h + 4 * lane_id();
-  if (idx + 4 <= nw) return *reinterpret_cast<const uint2*>(wp + idx);
-  uint32_t v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = idx + q < nw ? wp[idx + q] : 0u;
-  return make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+  return *reinterpret_cast<const uint2*>(wp + (idx < nw ? idx : 0u));
+}
+
+// 8 bytes of a RAW stream at element e0; the 16-byte padding of the payload
+// slot covers a read that starts below n, lanes past the end read offset 0.
+__device__ __forceinline__ uint64_t load_raw8(const uint8_t* rp, uint32_t e0, uint32_t n) {
+  return *reinterpret_cast<const uint64_t*>(rp + (e0 < n ? e0 : 0u));
+}
+
+__device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t a, uint32_t b) {
+  return (a & mask) | (b & ~mask);  // v_bfi_b32
+}
+
+// Four elements from their E stream bytes (one 32-bit word per stream, byte
+// i belongs to element i): undoes the byte grouping and the exponent
+// extraction with bit inserts and byte permutes on packed bytes.
+template <int DT> __device__ __forceinline__ void planes_to_words(const uint32_t* p, uint32_t* o) {
+  if constexpr (DT == LTC_U8) {
+    o[0] = p[0];
+  } else if constexpr (DT == LTC_BF16) {
+    // stream 1 = e, stream 0 = s<<7 | m; element = s<<15 | e<<7 | m
+    const uint32_t hi = bit_insert(0x80808080u, p[0], p[1] >> 1);  // s<<7 | e>>1
+    const uint32_t lo = bit_insert(0x80808080u, p[1] << 7, p[0]);  // (e&1)<<7 | m
+    o[0] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    o[1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  } else if constexpr (DT == LTC_FP16) {
+    // stream 1 = e<<3 | s<<2 | m[9:8]; high byte = s<<7 | e<<2 | m[9:8]
+    const uint32_t hi = bit_insert(0x80808080u, p[1] << 5, bit_insert(0x7C7C7C7Cu, p[1] >> 1, p[1]));
+    o[0] = __builtin_amdgcn_perm(hi, p[0], 0x05010400u);
+    o[1] = __builtin_amdgcn_perm(hi, p[0], 0x07030602u);
+  } else {
+    // stream 3 = e, stream 2 = s<<7 | m[22:16], streams 1, 0 = m[15:8], m[7:0]
+    const uint32_t b3 = bit_insert(0x80808080u, p[2], p[3] >> 1);
+    const uint32_t b2 = bit_insert(0x80808080u, p[3] << 7, p[2]);
+    const uint32_t a = __builtin_amdgcn_perm(p[1], p[0], 0x05010400u);
+    const uint32_t b = __builtin_amdgcn_perm(p[1], p[0], 0x07030602u);
+    const uint32_t c = __builtin_amdgcn_perm(b3, b2, 0x05010400u);
+    const uint32_t d = __builtin_amdgcn_perm(b3, b2, 0x07030602u);
+    o[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(c, a, 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(d, b, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
+  }
 }
 
 template <int DT, int MAXR>
@@ -131,9 +176,11 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
            (uint64_t)(size[k] - wo) != 2ull * h.x;
     if (bad) break;
     nwords[rr] = h.x;
-    wp[rr] = reinterpret_cast<const uint16_t*>(p + wo);
+    // with no words, refills (reached only by a corrupt stream) read the
+    // directory, which is always inside the blob
+    wp[rr] = reinterpret_cast<const uint16_t*>(h.x ? p + wo : blob + kHeader);
     x[rr] = reinterpret_cast<const uint32_t*>(p + 16)[lane];
-    bad |= __ballot(x[rr] < kRansLow) != 0;
+    bad |= ballot(x[rr] < kRansLow) != 0;
     const uint16_t* ft = reinterpret_cast<const uint16_t*>(p + kRansFixed);
     uint32_t f[4], cum[4], acc = 0;
 #pragma unroll
@@ -153,7 +200,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     const uint32_t f_hi = wave_max_u32(flast);
     const uint32_t pad = wo - (kRansFixed + 2 * tcount);
     const bool padbad = lane < pad && p[kRansFixed + 2 * tcount + lane] != 0;
-    bad |= total != kTotal || f_lo == 0 || f_hi == 0 || __ballot(padbad) != 0;
+    bad |= total != kTotal || f_lo == 0 || f_hi == 0 || ballot(padbad) != 0;
     if (bad) break;
     uint16_t* cumt = ring[rr];  // the ring doubles as the cum table while building
 #pragma unroll
@@ -206,7 +253,8 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   // word rings: halves 0 and 1 resident, half 2 staged in registers
 #pragma unroll
   for (int rr = 0; rr < MAXR; ++rr) {
-    if (rr >= nr) continue;
+    staged[rr] = make_uint2(0, 0);
+    if (rr >= nr || nwords[rr] == 0) continue;
     *reinterpret_cast<uint2*>(&ring[rr][4 * lane]) = load_half(wp[rr], nwords[rr], 0);
     *reinterpret_cast<uint2*>(&ring[rr][kHalf + 4 * lane]) = load_half(wp[rr], nwords[rr], 1);
     staged[rr] = load_half(wp[rr], nwords[rr], 2);
@@ -217,103 +265,121 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   const bool vec = t.vec16 != 0;
   uint8_t* dst = job.dst + c * t.chunk_bytes;
   const uint32_t steps = (n + 63) / 64;
+  const uint32_t full = n / 64;  // steps in which every lane decodes a symbol
   const uint32_t nblk = (steps + 7) / 8;
-  bool wbad = false;
+  // RAW bytes for block b are loaded while block b-1 decodes.  Non-RAW
+  // streams read 8 bytes of the directory (always inside the blob) and never
+  // use them, so the loads carry no branch.
+  const uint8_t* rbase[E];
+  uint32_t rlim[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    const bool raw = mode[k] == LTC_MODE_RAW;
+    rbase[k] = raw ? blob + off[k] : blob + kHeader;
+    rlim[k] = raw ? n : 0u;
+  }
+  uint64_t rawv[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) rawv[k] = load_raw8(rbase[k], 8 * lane, rlim[k]);
+
+  // One decoding step of coded stream rr.  Every lane reads a ring word at
+  // pos + (renormalising lanes below it) and keeps it only if it
+  // renormalises, so there is no branch; a read past W cannot go unnoticed
+  // because it leaves pos > W for the end check.
+  auto dstep = [&](auto guarded, int rr, int q) {
+    constexpr bool G = decltype(guarded)::value;
+    const bool active = !G || 64 * full + lane < n;
+    const uint32_t xs = x[rr];
+    const uint32_t sl = xs & (kTotal - 1);
+    const uint32_t v = lut[rr][sl];
+    const uint32_t e = symt[rr][v];
+    const uint32_t xd = __umul24(e & 0xFFFFu, xs >> 12) + sl - (e >> 16);
+    const bool need = active && xd < kRansLow;
+    const uint64_t mask = ballot(need);
+    const uint32_t wv = ring[rr][(pos[rr] + lanes_below(mask)) & (kDecRing - 1)];
+    const uint32_t xn = need ? (xd << 16) | wv : xd;
+    x[rr] = active ? xn : xs;
+    pos[rr] += (uint32_t)__popcll(mask);
+    stage[rr][64 * q + lane] = (uint8_t)v;
+  };
+  // Ring refill, checked after every 4 steps: halves hcur and hcur+1 are
+  // resident and pos < 256*(hcur+1) holds at every check, and 4 steps read
+  // at most 256 words, so no read leaves the resident halves and at most one
+  // half is retired per check.  The retired half's slot receives the staged
+  // half hcur+2 and the next half is loaded into registers a check ahead.
+  auto refill = [&](int rr) {
+    if (pos[rr] >= kHalf * (hcur[rr] + 1)) {
+      ++hcur[rr];
+      __syncthreads();
+      *reinterpret_cast<uint2*>(&ring[rr][kHalf * ((hcur[rr] + 1) & 1) + 4 * lane]) = staged[rr];
+      staged[rr] = load_half(wp[rr], nwords[rr], hcur[rr] + 2);
+      __syncthreads();
+    }
+  };
+
   for (uint32_t b = 0; b < nblk; ++b) {
     const uint32_t e0 = 512 * b + 8 * lane;
-    uint64_t rawv[E];
+    uint64_t rawn[E];
 #pragma unroll
-    for (int k = 0; k < E; ++k) {
-      rawv[k] = 0;
-      if (mode[k] != LTC_MODE_RAW) continue;
-      const uint8_t* rp = blob + off[k] + e0;
-      if (e0 + 8 <= n) {
-        rawv[k] = *reinterpret_cast<const uint64_t*>(rp);
-      } else {
-        for (uint32_t i = 0; e0 + i < n && i < 8; ++i) rawv[k] |= (uint64_t)rp[i] << (8 * i);
-      }
-    }
+    for (int k = 0; k < E; ++k) rawn[k] = load_raw8(rbase[k], e0 + 512, rlim[k]);
 #pragma unroll
     for (int rr = 0; rr < MAXR; ++rr) {
       if (rr >= nr) continue;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t step = 8 * b + q;
-        if (step >= steps) break;
-        const bool active = 64 * step + lane < n;
-        const uint32_t xs = x[rr];
-        const uint32_t sl = xs & (kTotal - 1);
-        const uint32_t v = lut[rr][sl];
-        const uint32_t e = symt[rr][v];
-        uint32_t xn = __umul24(e & 0xFFFFu, xs >> 12) + sl - (e >> 16);
-        if (!active) xn = xs;
-        const bool need = active && xn < kRansLow;
-        const uint64_t mask = __ballot(need);
-        if (need) {
-          const uint32_t idx = pos[rr] + lanes_below(mask);
-          wbad |= idx >= nwords[rr];
-          xn = (xn << 16) | ring[rr][idx & (kDecRing - 1)];
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int q = 4 * sb; q < 4 * sb + 4; ++q) {
+          const uint32_t step = 8 * b + q;
+          if (step >= steps) break;
+          if (step < full) dstep(std::false_type{}, rr, q);
+          else dstep(std::true_type{}, rr, q);
         }
-        pos[rr] += (uint32_t)__popcll(mask);
-        x[rr] = xn;
-        stage[rr][64 * q + lane] = (uint8_t)v;
-        if (pos[rr] >= kHalf * (hcur[rr] + 1)) {
-          ++hcur[rr];
-          __syncthreads();
-          *reinterpret_cast<uint2*>(&ring[rr][kHalf * ((hcur[rr] + 1) & 1) + 4 * lane]) = staged[rr];
-          staged[rr] = load_half(wp[rr], nwords[rr], hcur[rr] + 2);
-          __syncthreads();
-        }
+        refill(rr);
       }
     }
     __syncthreads();
     if (e0 < n) {
-      uint64_t pb[E];
+      uint32_t pl[2][E];
 #pragma unroll
       for (int k = 0; k < E; ++k) {
-        if (mode[k] == LTC_MODE_RANS) pb[k] = *reinterpret_cast<const uint64_t*>(&stage[slot_of[k]][8 * lane]);
-        else if (mode[k] == LTC_MODE_RAW) pb[k] = rawv[k];
-        else pb[k] = 0x0101010101010101ull * cval[k];
+        uint64_t v;
+        if (mode[k] == LTC_MODE_RANS) v = *reinterpret_cast<const uint64_t*>(&stage[slot_of[k]][8 * lane]);
+        else if (mode[k] == LTC_MODE_RAW) v = rawv[k];
+        else v = 0x0101010101010101ull * cval[k];
+        pl[0][k] = (uint32_t)v;
+        pl[1][k] = (uint32_t)(v >> 32);
       }
-      uint32_t xe[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t y = 0;
-#pragma unroll
-        for (int k = 0; k < E; ++k) y |= (uint32_t)((pb[k] >> (8 * i)) & 0xFFu) << (8 * k);
-        xe[i] = unreorder<DT>(y);
-      }
+      uint32_t ow[2 * E];
+      planes_to_words<DT>(pl[0], ow);
+      planes_to_words<DT>(pl[1], ow + E);
       uint8_t* op = dst + (uint64_t)e0 * E;
       if (vec && e0 + 8 <= n) {
         if constexpr (E == 1) {
-          *reinterpret_cast<uint2*>(op) =
-              make_uint2(xe[0] | (xe[1] << 8) | (xe[2] << 16) | (xe[3] << 24),
-                         xe[4] | (xe[5] << 8) | (xe[6] << 16) | (xe[7] << 24));
+          *reinterpret_cast<uint2*>(op) = make_uint2(ow[0], ow[1]);
         } else if constexpr (E == 2) {
-          *reinterpret_cast<uint4*>(op) = make_uint4(xe[0] | (xe[1] << 16), xe[2] | (xe[3] << 16),
-                                                     xe[4] | (xe[5] << 16), xe[6] | (xe[7] << 16));
+          *reinterpret_cast<uint4*>(op) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
         } else {
-          reinterpret_cast<uint4*>(op)[0] = make_uint4(xe[0], xe[1], xe[2], xe[3]);
-          reinterpret_cast<uint4*>(op)[1] = make_uint4(xe[4], xe[5], xe[6], xe[7]);
+          reinterpret_cast<uint4*>(op)[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+          reinterpret_cast<uint4*>(op)[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
         }
       } else {
-        for (uint32_t i = 0; i < 8 && e0 + i < n; ++i) {
-#pragma unroll
-          for (int bb = 0; bb < E; ++bb) op[i * E + bb] = (uint8_t)(xe[i] >> (8 * bb));
-        }
+        const uint32_t nb = (n - e0 < 8 ? n - e0 : 8) * E;
+        for (uint32_t i = 0; i < nb; ++i) op[i] = (uint8_t)(ow[i / 4] >> (8 * (i & 3)));
       }
     }
+#pragma unroll
+    for (int k = 0; k < E; ++k) rawv[k] = rawn[k];
     __syncthreads();
   }
   // ---- end checks: every coded stream consumed exactly its words and
   // returned to the initial state
-  bool endbad = wbad;
+  bool endbad = false;
 #pragma unroll
   for (int rr = 0; rr < MAXR; ++rr) {
     if (rr >= nr) continue;
     endbad |= pos[rr] != nwords[rr] || x[rr] != kRansLow;
   }
-  if (__ballot(endbad) != 0 && lane == 0) *job.status = LTC_ERR_CORRUPT;
+  if (ballot(endbad) != 0 && lane == 0) *job.status = LTC_ERR_CORRUPT;
 }
 
 __global__ void k_status_init(DTable t) {

@@ -120,6 +120,9 @@ __device__ __forceinline__ int find_job(const T& t, uint64_t g) {
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+// lane mask of a predicate (the builtin avoids a round trip through a VGPR)
+__device__ __forceinline__ uint64_t ballot(bool b) { return __builtin_amdgcn_ballot_w64(b); }
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -12,16 +12,23 @@ hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, cons
 // multi-table decode kernels
 hipError_t launch_decompress(int dtype, const DTable& t, hipStream_t st, const hipEvent_t* ev);
 
-struct CrcArgs {
+struct CrcJob {
   const uint8_t* src;
   uint32_t* out;
+  uint64_t chunk0;       // first global chunk index of this buffer
   uint64_t nchunks;
+  uint64_t tail_len;     // length of the buffer's last chunk
+  uint32_t init_tail;    // 0xFFFFFFFF * x^(8*tail_len) mod P
+};
+
+struct CrcArgs {
+  CrcJob jobs[kMaxJobs];
+  uint32_t count;
+  uint64_t total_chunks;
   uint64_t chunk_bytes;  // K
   uint64_t seg;          // bytes per lane segment (K rounded up to 256, / 64)
-  uint64_t tail_len;     // length of the last chunk
   uint32_t lvl[6];       // x^(8*seg*2^l) mod P, reflected
   uint32_t init_full;    // 0xFFFFFFFF * x^(8K) mod P
-  uint32_t init_tail;    // 0xFFFFFFFF * x^(8*tail_len) mod P
 };
 
 hipError_t launch_crc32(const CrcArgs& a, hipStream_t st);

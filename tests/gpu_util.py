@@ -8,8 +8,9 @@ TORCH_DTYPE = {0: torch.uint8, 1: torch.bfloat16, 2: torch.float16, 3: torch.flo
 
 def to_gpu(arr, dtype_code):
     b = np.ascontiguousarray(arr).reshape(-1).view(np.uint8)
-    t = torch.from_numpy(b.copy()).cuda()
-    return t.view(TORCH_DTYPE[dtype_code]) if b.size else t.view(TORCH_DTYPE[dtype_code])
+    if b.size == 0:
+        return torch.empty(0, dtype=TORCH_DTYPE[dtype_code], device="cuda")
+    return torch.from_numpy(b.copy()).cuda().view(TORCH_DTYPE[dtype_code])
 
 
 def to_np_bytes(t):

@@ -226,3 +226,15 @@ def test_random_payload_flips_match_oracle(ltc):
         b[pos] ^= 1 << int(rng.integers(0, 8))
         verdicts.add(_verdicts_agree(ltc, b))
     assert -5 in verdicts
+
+
+def test_crc32_batch_matches_single(ltc):
+    rng = np.random.default_rng(3)
+    sizes = [0, 1, 16384, 100000, 16384 * 7 + 5, 333]
+    ts = [torch.from_numpy(rng.integers(0, 256, n, dtype=np.uint8)).cuda() for n in sizes]
+    for k in (16384, 1000):
+        outs = ltc.crc32_chunks_batch(ts, k)
+        for t, o in zip(ts, outs):
+            d = t.cpu().numpy()
+            want = [zlib.crc32(d[i:i + k].tobytes()) for i in range(0, d.size, k)]
+            assert o.cpu().numpy().view(np.uint32).tolist() == want
