@@ -26,12 +26,14 @@
 namespace ltc {
 
 constexpr int kHistThreads = 256;
-constexpr int kHistCopies = 4;   // sub-histograms, picked by lane & 3
+constexpr int kHistCopies = 32;  // sub-histograms, picked by lane & 31
+constexpr uint32_t kHistSeg = 1u << 20;  // elements between sub-histogram flushes
 constexpr int kPackThreads = 256;
 constexpr int kScanThreads = 1024;
-constexpr uint32_t kRingWords = 1024;   // encoder word ring (LDS)
-constexpr uint32_t kFlushWords = 512;   // one flush = 64 lanes x 16 bytes
-constexpr int kEncBlock = 16;          // encoder steps per prefetched block
+constexpr uint32_t kRingWords = 512;    // encoder word ring per stream (LDS)
+constexpr uint32_t kFlushWords = 256;   // one flush = 64 lanes x 8 bytes
+constexpr int kEncBlock = 8;            // steps per prefetched block (a multiple of 4)
+constexpr int kEncStreams = 2;          // streams one wave codes, interleaved
 
 __device__ __forceinline__ uint32_t pack_info(uint32_t mode, uint32_t cval, uint32_t lo,
                                               uint32_t hi) {
@@ -47,13 +49,19 @@ template <int DT> __device__ __forceinline__ uint32_t load_elem(const uint8_t* p
 
 // ------------------------------------------------------------------ k_hist
 
+// Sub-histograms: 32 copies, copy = lane & 31, laid out so that the copy
+// index is the LDS bank (word address = (k*128 + bin/2)*32 + copy): the 32
+// lanes of a half-wave always hit 32 different banks, whatever their bins, so
+// the skewed exponent bytes cost no bank conflicts.  Two bins share a word as
+// 16-bit counters; a copy counts at most kHistSeg/32 elements between
+// flushes into the 32-bit histogram, so no counter overflows.
 template <int DT>
 __device__ __forceinline__ void hist_elem(uint32_t* hs, uint32_t y, uint32_t copy) {
   constexpr int E = Dt<DT>::E;
 #pragma unroll
   for (int k = 0; k < E; ++k) {
     const uint32_t bin = (y >> (8 * k)) & 0xFFu;
-    atomicAdd(&hs[(k * 256 + bin) * kHistCopies + copy], 1u);
+    atomicAdd(&hs[((k * 128 + (bin >> 1)) << 5) | copy], 1u << ((bin & 1u) << 4));
   }
 }
 
@@ -70,6 +78,14 @@ __device__ __forceinline__ void hist_word(uint32_t* hs, uint32_t v, uint32_t cop
 #pragma unroll
     for (int b = 0; b < 4; ++b) hist_elem<DT>(hs, (v >> (8 * b)) & 0xFFu, copy);
   }
+}
+
+template <int DT>
+__device__ __forceinline__ void hist_vec(uint32_t* hs, const uint4 q, uint32_t copy) {
+  hist_word<DT>(hs, q.x, copy);
+  hist_word<DT>(hs, q.y, copy);
+  hist_word<DT>(hs, q.z, copy);
+  hist_word<DT>(hs, q.w, copy);
 }
 
 // Normalise one stream's histogram (one wave; lane l owns symbols 4l..4l+3),
@@ -152,7 +168,8 @@ __device__ void normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, u
 template <int DT>
 __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
-  __shared__ uint32_t hs[E * 256 * kHistCopies];
+  constexpr uint32_t kWords = E * 128 * kHistCopies;
+  __shared__ uint32_t hs[kWords];
   __shared__ uint32_t hf[E * 256];
   const uint64_t g = blockIdx.x;
   const int j = find_job(t, g);
@@ -160,40 +177,50 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   const uint64_t c = g - job.chunk0;
   const bool last = c + 1 == job.nchunks;
   const uint32_t n = last ? job.n_tail : t.n_full;
-  const uint32_t len = n * E;
-  const uint8_t* src = job.src + c * t.chunk_bytes;
+  const uint8_t* chunk = job.src + c * t.chunk_bytes;
   const uint32_t tid = threadIdx.x;
   const uint32_t copy = tid & (kHistCopies - 1);
 
-  for (uint32_t i = tid; i < E * 256 * kHistCopies; i += kHistThreads) hs[i] = 0;
-  __syncthreads();
-  uint32_t done = 0;
-  if (t.vec16 && len >= 16) {
-    const uint32_t nvec = len / 16, lastv = nvec - 1;
-    const uint4* v = reinterpret_cast<const uint4*>(src);
-    // one 16-byte load in flight ahead of the one being counted; the index
-    // is clamped instead of branched so the wait lands at the use
-    uint4 q = v[min(tid, lastv)];
-    for (uint32_t i = tid; i < nvec; i += kHistThreads) {
-      const uint4 nq = v[min(i + kHistThreads, lastv)];
-      hist_word<DT>(hs, q.x, copy);
-      hist_word<DT>(hs, q.y, copy);
-      hist_word<DT>(hs, q.z, copy);
-      hist_word<DT>(hs, q.w, copy);
-      q = nq;
+  for (uint32_t i = tid; i < E * 256; i += kHistThreads) hf[i] = 0;
+  for (uint32_t seg = 0; seg < n; seg += kHistSeg) {
+    const uint32_t sn = n - seg < kHistSeg ? n - seg : kHistSeg;
+    const uint32_t len = sn * E;
+    const uint8_t* src = chunk + (uint64_t)seg * E;
+    for (uint32_t i = tid; i < kWords; i += kHistThreads) hs[i] = 0;
+    __syncthreads();
+    uint32_t done = 0;
+    if (t.vec16 && len >= 32) {
+      const uint32_t nvec = len / 16, lastv = nvec - 1;
+      const uint4* v = reinterpret_cast<const uint4*>(src);
+      // two 16-byte loads in flight ahead of the two being counted; indices
+      // are clamped instead of branched so the waits land at the uses
+      uint4 q0 = v[min(tid, lastv)], q1 = v[min(tid + kHistThreads, lastv)];
+      for (uint32_t i = tid; i < nvec; i += 2 * kHistThreads) {
+        const uint4 n0 = v[min(i + 2 * kHistThreads, lastv)];
+        const uint4 n1 = v[min(i + 3 * kHistThreads, lastv)];
+        hist_vec<DT>(hs, q0, copy);
+        if (i + kHistThreads < nvec) hist_vec<DT>(hs, q1, copy);
+        q0 = n0;
+        q1 = n1;
+      }
+      done = nvec * 16;
     }
-    done = nvec * 16;
+    for (uint32_t e = done / E + tid; e < sn; e += kHistThreads)
+      hist_elem<DT>(hs, reorder<DT>(load_elem<DT>(src + (uint64_t)e * E)), copy);
+    __syncthreads();
+    // fold the 32 copies; the copy index rotates with the thread so the 32
+    // reads of a half-wave hit 32 different banks
+    for (uint32_t i = tid; i < E * 256; i += kHistThreads) {
+      const uint32_t k = i >> 8, b = i & 255u;
+      const uint32_t* row = hs + ((k * 128 + (b >> 1)) << 5);
+      const uint32_t sh = (b & 1u) << 4;
+      uint32_t sum = 0;
+#pragma unroll 8
+      for (uint32_t r = 0; r < kHistCopies; ++r) sum += (row[(r + tid) & (kHistCopies - 1)] >> sh) & 0xFFFFu;
+      hf[i] += sum;
+    }
+    __syncthreads();
   }
-  for (uint32_t e = done / E + tid; e < n; e += kHistThreads)
-    hist_elem<DT>(hs, reorder<DT>(load_elem<DT>(src + (uint64_t)e * E)), copy);
-  __syncthreads();
-  for (uint32_t i = tid; i < E * 256; i += kHistThreads) {
-    uint32_t sum = 0;
-#pragma unroll
-    for (int r = 0; r < kHistCopies; ++r) sum += hs[i * kHistCopies + r];
-    hf[i] = sum;
-  }
-  __syncthreads();
   const uint32_t wave = tid / 64;
   if (wave < (uint32_t)E)
     normalize_stream(hf + 256 * wave, n, last ? job.pmax_tail : job.pmax_full, g * E + wave, w);
@@ -201,37 +228,84 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
 
 // ---------------------------------------------------------------- k_encode
 
+// Byte k of the reordered element.  For BF16 and FP32 the top byte is the
+// biased exponent field itself, one bit-field extract.
+template <int DT, bool TOP>
+__device__ __forceinline__ uint32_t stream_byte(uint32_t x, uint32_t k) {
+  if constexpr (TOP) return (x >> Dt<DT>::WM) & 0xFFu;
+  else return (reorder<DT>(x) >> (8 * k)) & 0xFFu;
+}
+
+// One wave codes stream k of two neighbouring chunks, interleaving their
+// independent state chains (instruction-level parallelism for a loop whose
+// every step is a dependent chain).  Per stream:
+//   tab   one 8-byte entry per symbol: f | cum << 12 | sh2 << 24 | sh1 << 31
+//         and the Granlund-Montgomery multiplier m for exact division by f
+//         (Granlund & Montgomery 1994, "Division by invariant integers using
+//         multiplication": q = (t + ((x - t) >> sh1)) >> sh2, t = mulhi(m, x));
+//   ring  a 512-word LDS ring for the emitted words plus a private dummy slot
+//         per lane, so a lane that emits nothing writes without a branch; the
+//         ring drains to the workspace 256 words at a time.
+// Abort and drain checks run every 4 steps: 4 steps emit at most 256 words,
+// so a drained block is never overwritten before it leaves, and an abort is
+// seen before any word past the stream's limit reaches the workspace.
 template <int DT>
 __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
-  __shared__ uint4 tab[256];
-  // word ring plus one private dummy slot per lane: a lane that emits
-  // nothing writes its dummy slot, so the store needs no branch
-  __shared__ __attribute__((aligned(16))) uint16_t ring[kRingWords + 64];
-  const uint64_t s = blockIdx.x;
-  const uint32_t info = w.sinfo[4 * s + 1];
-  if ((info & 0xFFu) != kModeCand) return;
-  const uint64_t g = s / E;
-  const uint32_t k = (uint32_t)(s % E);
-  const int j = find_job(t, g);
-  const CJob& job = t.jobs[j];
-  const uint64_t c = g - job.chunk0;
-  const bool last = c + 1 == job.nchunks;
-  const uint32_t n = last ? job.n_tail : t.n_full;
-  const uint32_t pmax = last ? job.pmax_tail : job.pmax_full;
-  const uint32_t lo = (info >> 16) & 0xFFu, hi = info >> 24;
-  const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * (hi - lo + 1u));
+  constexpr int U = kEncStreams;
+  __shared__ uint2 tab[U][256];
+  // one block of elements per stream, staged for the transpose to lane order
+  __shared__ __attribute__((aligned(16))) uint32_t stg[U][128 * E];
+  __shared__ __attribute__((aligned(16))) uint16_t ring[U][kRingWords + 64];
   const uint32_t lane = lane_id();
+  const uint32_t k = blockIdx.x % E;
+  const uint64_t g0 = (uint64_t)(blockIdx.x / E) * U;
+  const uint32_t wcap = t.wcap;
 
-  // Encoder table, one 16-byte entry per symbol:
-  //   x: f << 20, the renormalisation bound
-  //   y: Granlund-Montgomery multiplier m for exact division by f
-  //      (Granlund & Montgomery 1994, "Division by invariant integers using
-  //      multiplication": q = (t + ((x - t) >> sh1)) >> sh2, t = mulhi(m, x))
-  //   z: (4096 - f) | sh2 << 24   (the 24-bit multiply ignores the top byte)
-  //   w: cum | sh1 << 24
-  {
-    const uint64_t fq = *reinterpret_cast<const uint64_t*>(w.freq + 256 * s + 4 * lane);
+  bool on[U];
+  uint64_t sid[U];
+  uint32_t n[U], full[U], wlimit[U], wo[U], lo[U], hi[U];
+  const uint8_t* src[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    on[u] = false;
+    sid[u] = 0;
+    n[u] = full[u] = wlimit[u] = wo[u] = lo[u] = hi[u] = 0;
+    src[u] = nullptr;
+    const uint64_t g = g0 + u;
+    if (g >= t.total_chunks) continue;
+    const uint64_t s = g * E + k;
+    const uint32_t info = w.sinfo[4 * s + 1];
+    if ((info & 0xFFu) != kModeCand) continue;
+    const int j = find_job(t, g);
+    const CJob& job = t.jobs[j];
+    const uint64_t c = g - job.chunk0;
+    const bool last = c + 1 == job.nchunks;
+    on[u] = true;
+    sid[u] = s;
+    n[u] = last ? job.n_tail : t.n_full;
+    full[u] = n[u] / 64;
+    lo[u] = (info >> 16) & 0xFFu;
+    hi[u] = info >> 24;
+    wo[u] = (uint32_t)align16(kRansFixed + 2u * (hi[u] - lo[u] + 1u));
+    wlimit[u] = ((last ? job.pmax_tail : job.pmax_full) - wo[u]) / 2;
+    src[u] = job.src + c * t.chunk_bytes;
+  }
+  if (!on[0] && !on[1]) return;
+  // The element prefetch below loads for both slots unconditionally; a slot
+  // without a stream reads the other slot's chunk so every load stays in
+  // bounds (its values are never used).
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (on[u]) continue;
+    src[u] = src[1 - u];
+    n[u] = n[1 - u];
+  }
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!on[u]) continue;
+    const uint64_t fq = *reinterpret_cast<const uint64_t*>(w.freq + 256 * sid[u] + 4 * lane);
     uint32_t f[4], cum[4], acc = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -246,93 +320,217 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
       const uint32_t ell = fv <= 1 ? 0u : 32u - __clz(fv - 1u);
       const uint32_t m = fv ? (uint32_t)(((((uint64_t)1) << 32) * ((1ull << ell) - fv)) / fv + 1u) : 0u;
       const uint32_t sh1 = ell > 0 ? 1u : 0u, sh2 = ell > 0 ? ell - 1u : 0u;
-      tab[4 * lane + i] = make_uint4(fv << 20, m, (kTotal - fv) | (sh2 << 24), (base + cum[i]) | (sh1 << 24));
+      tab[u][4 * lane + i] = make_uint2(fv | ((base + cum[i]) << 12) | (sh2 << 24) | (sh1 << 31), m);
     }
   }
   __syncthreads();
 
-  const uint32_t wcap = t.wcap;
-  uint16_t* wout = w.words + s * wcap;
-  const uint32_t wlimit = (pmax - wo) / 2;  // more words than this cannot beat the threshold
-  const uint8_t* src = job.src + c * t.chunk_bytes;
-  const uint32_t full = n / 64;             // steps in which every lane codes a symbol
-  const uint32_t steps = (n + 63) / 64;
-  uint32_t x = kRansLow, top = wcap, nw = 0, flushed = 0;
+  uint32_t x[U], top[U], nw[U], flushed[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    x[u] = kRansLow;
+    top[u] = wcap;
+    nw[u] = 0;
+    flushed[u] = 0;
+  }
 
-  // Elements are fetched one block of steps ahead, unconditionally: lanes
-  // past the end read the last element instead (their state is not
-  // updated), so no branch forces an early wait on the loads.
-  auto elem_at = [&](uint32_t step) -> uint32_t {
-    const uint32_t e = 64 * step + lane;
-    return load_elem<DT>(src + (uint64_t)(e < n ? e : n - 1) * E);
-  };
-  auto flush = [&](uint32_t b) {
-    __syncthreads();
-    const uint32_t base = wcap - kFlushWords * (b + 1) + 8 * lane;
-    const uint4 v = *reinterpret_cast<const uint4*>(&ring[base & (kRingWords - 1)]);
-    *reinterpret_cast<uint4*>(wout + base) = v;
-  };
-  // One coding step of the wave.  Steps run from the last to the first and,
-  // within a step, the emitted words take decoder order (lanes ascending):
-  // lane l's word goes to top - cnt + (number of emitting lanes below l).
-  // Returns false once the payload can no longer beat the threshold.
-  auto code = [&](auto guarded, uint32_t raw) -> bool {
-    constexpr bool G = decltype(guarded)::value;
-    const bool active = !G || 64 * full + lane < n;
-    const uint4 e = tab[(reorder<DT>(raw) >> (8 * k)) & 0xFFu];
-    const bool need = active && x >= e.x;
-    const uint64_t mask = ballot(need);
-    const uint32_t cnt = (uint32_t)__popcll(mask);
-    nw += cnt;
-    if (nw > wlimit) return false;
-    const uint32_t slot = need ? ((top - cnt + lanes_below(mask)) & (kRingWords - 1)) : kRingWords + lane;
-    ring[slot] = (uint16_t)x;
-    const uint32_t xr = need ? x >> 16 : x;
-    top -= cnt;
-    const uint32_t t1 = __umulhi(e.y, xr);
-    const uint32_t q = (t1 + ((xr - t1) >> (e.w >> 24))) >> (e.z >> 24);
-    const uint32_t xn = __umul24(q, e.z) + xr + (e.w & 0xFFFFFFu);
-    x = active ? xn : x;
-    if (nw >= kFlushWords * (flushed + 1)) {
-      flush(flushed);
-      ++flushed;
+  const bool vec = t.vec16 != 0;
+  auto body = [&](auto topexp) {
+    constexpr bool TOP = decltype(topexp)::value;
+    // element of stream u at step `step` (index clamped inside the chunk)
+    auto elem_at = [&](int u, uint32_t step) -> uint32_t {
+      const uint32_t e = 64 * step + lane;
+      return load_elem<DT>(src[u] + (uint64_t)(e < n[u] ? e : n[u] - 1) * E);
+    };
+    auto flush = [&](int u, uint32_t b) {
+      __syncthreads();
+      const uint32_t base = wcap - kFlushWords * (b + 1) + 4 * lane;
+      const uint2 v = *reinterpret_cast<const uint2*>(&ring[u][base & (kRingWords - 1)]);
+      *reinterpret_cast<uint2*>(w.words + sid[u] * wcap + base) = v;
+    };
+    // abort once the payload can no longer beat the threshold, else drain
+    auto check = [&](int u) {
+      if (nw[u] > wlimit[u]) {
+        on[u] = false;
+        if (lane == 0)
+          *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =
+              make_uint4(n[u], pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
+        return;
+      }
+      while (nw[u] >= kFlushWords * (flushed[u] + 1)) {
+        flush(u, flushed[u]);
+        ++flushed[u];
+      }
+    };
+    // One coding step of stream u: steps run from the last to the first and
+    // the words of a step take decoder order (lanes ascending), so lane l's
+    // word lands at top - cnt + (number of emitting lanes below l).
+    auto code = [&](auto guarded, int u, const uint2 e) {
+      constexpr bool G = decltype(guarded)::value;
+      const bool active = !G || 64 * full[u] + lane < n[u];
+      const uint32_t f = e.x & 0xFFFu;
+      const bool need = active && x[u] >= (f << 20);
+      const uint64_t mask = ballot(need);
+      const uint32_t cnt = (uint32_t)__popcll(mask);
+      const uint32_t slot = need ? ((top[u] - cnt + lanes_below(mask)) & (kRingWords - 1))
+                                 : kRingWords + lane;
+      ring[u][slot] = (uint16_t)x[u];
+      const uint32_t xr = need ? x[u] >> 16 : x[u];
+      const uint32_t t1 = __umulhi(e.y, xr);
+      const uint32_t q = (t1 + ((xr - t1) >> (e.x >> 31))) >> ((e.x >> 24) & 0xFu);
+      const uint32_t xn = xr + __umul24(q, kTotal - f) + ((e.x >> 12) & 0xFFFu);
+      x[u] = active ? xn : x[u];
+      top[u] -= cnt;
+      nw[u] += cnt;
+    };
+
+    auto entry = [&](int u, uint32_t raw) { return tab[u][stream_byte<DT, TOP>(raw, k)]; };
+    // the partial step (the last one) is coded first
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (on[u] && n[u] > 64 * full[u]) {
+        code(std::true_type{}, u, entry(u, elem_at(u, full[u])));
+        check(u);
+      }
     }
-    return true;
-  };
-
-  bool ok = true;
-  if (steps > full) ok = code(std::true_type{}, elem_at(full));  // the partial step comes first
-  if (ok && full > 0) {
-    const uint32_t nblk = (full + kEncBlock - 1) / kEncBlock;
-    uint32_t cur[kEncBlock];
+    // Full steps, both streams in lock step from their last full step down.
+    // A block of 8 steps covers 512 consecutive elements of a stream: each
+    // lane loads 8*E contiguous bytes of the next block with wide coalesced
+    // loads (one block ahead), the block goes through an LDS tile, and every
+    // lane reads back its own element of each step (64 q + lane).  A block's
+    // table entries are read into registers before its steps, so the state
+    // chains hold no LDS read.  When both streams have the same number of
+    // steps (the common case) a full block runs without any per-step branch
+    // and the two chains interleave; a stream that aborted keeps computing
+    // there but is never drained or finalised.
+    const bool lock = on[0] && on[1] && full[0] == full[1];
+    const uint32_t iters = max(on[0] ? full[0] : 0u, on[1] ? full[1] : 0u);
+    const uint32_t nblk = (iters + kEncBlock - 1) / kEncBlock;
+    // first element of block bi of stream u (the block's lowest step)
+    auto block_lo = [&](int u, uint32_t bi) -> uint32_t {
+      const uint32_t top_step = full[u] > kEncBlock * bi ? full[u] - 1 - kEncBlock * bi : 0u;
+      return 64u * (top_step >= kEncBlock - 1 ? top_step - (kEncBlock - 1) : 0u);
+    };
+    // A lane whose 8 elements reach past the stream's full steps (the lowest
+    // block of a short stream) loads the chunk's first 8 elements instead,
+    // which it never reads back.  A slot with no full step of its own fetches
+    // from the other slot's chunk.
+    const uint8_t* fsrc[U];
+    uint32_t flim[U];
 #pragma unroll
-    for (int q = 0; q < kEncBlock; ++q) cur[q] = elem_at(kEncBlock * (nblk - 1) + q);
-    for (int b = (int)nblk - 1; b >= 0 && ok; --b) {
-      uint32_t nxt[kEncBlock];
+    for (int u = 0; u < U; ++u) {
+      const bool own = on[u] && full[u] > 0;
+      fsrc[u] = own ? src[u] : src[1 - u];
+      flim[u] = 64 * (own ? full[u] : full[1 - u]);
+    }
+    uint32_t pf[U][2 * E];
+    auto fetch = [&](int u, uint32_t bi) {
+      uint32_t e0 = block_lo(u, bi) + 8 * lane;
+      e0 = e0 + 8 <= flim[u] ? e0 : 0u;
+      if (vec) {
+        const uint4* p = reinterpret_cast<const uint4*>(fsrc[u] + (uint64_t)e0 * E);
+        if constexpr (E == 1) {
+          const uint2 v = *reinterpret_cast<const uint2*>(fsrc[u] + e0);
+          pf[u][0] = v.x;
+          pf[u][1] = v.y;
+        } else {
 #pragma unroll
-      for (int q = 0; q < kEncBlock; ++q) nxt[q] = elem_at(kEncBlock * (b > 0 ? b - 1 : 0) + q);
+          for (int h = 0; h < E / 2; ++h) {
+            const uint4 v = p[h];
+            pf[u][4 * h] = v.x;
+            pf[u][4 * h + 1] = v.y;
+            pf[u][4 * h + 2] = v.z;
+            pf[u][4 * h + 3] = v.w;
+          }
+        }
+      } else {
 #pragma unroll
-      for (int q = kEncBlock - 1; q >= 0; --q) {
-        if (kEncBlock * (uint32_t)b + q >= full) continue;
-        if (!code(std::false_type{}, cur[q])) {
-          ok = false;
-          break;
+        for (int i = 0; i < 2 * E; ++i) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) word |= (uint32_t)fsrc[u][(uint64_t)e0 * E + 4 * i + b] << (8 * b);
+          pf[u][i] = word;
         }
       }
+    };
+    auto stage_elem = [&](int u, uint32_t pos) -> uint32_t {
+      if constexpr (E == 1) return reinterpret_cast<const uint8_t*>(stg[u])[pos];
+      else if constexpr (E == 2) return reinterpret_cast<const uint16_t*>(stg[u])[pos];
+      else return stg[u][pos];
+    };
+    if (nblk > 0) {
 #pragma unroll
-      for (int q = 0; q < kEncBlock; ++q) cur[q] = nxt[q];
+      for (int u = 0; u < U; ++u) fetch(u, 0);
     }
-  }
-  if (!ok) {
-    if (lane == 0)
-      *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(n, pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
-    return;
-  }
-  if (nw > kFlushWords * flushed) flush(flushed);
-  w.states[64 * s + lane] = x;
-  if (lane == 0)
-    *reinterpret_cast<uint4*>(w.sinfo + 4 * s) =
-        make_uint4(wo + 2 * nw, pack_info(LTC_MODE_RANS, 0, lo, hi), nw, 0);
+    for (uint32_t bi = 0; bi < nblk; ++bi) {
+      if (!on[0] && !on[1]) break;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if constexpr (E == 1) {
+          reinterpret_cast<uint2*>(stg[u])[lane] = make_uint2(pf[u][0], pf[u][1]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < E / 2; ++h)
+            reinterpret_cast<uint4*>(stg[u])[(E / 2) * lane + h] =
+                make_uint4(pf[u][4 * h], pf[u][4 * h + 1], pf[u][4 * h + 2], pf[u][4 * h + 3]);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < U; ++u) fetch(u, bi + 1 < nblk ? bi + 1 : bi);
+      uint2 te[U][kEncBlock];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t top_step = full[u] > kEncBlock * bi ? full[u] - 1 - kEncBlock * bi : 0u;
+        const uint32_t lo_step = block_lo(u, bi) / 64;
+#pragma unroll
+        for (int q = 0; q < kEncBlock; ++q) {
+          const uint32_t step = top_step >= (uint32_t)q ? top_step - q : lo_step;
+          te[u][q] = entry(u, stage_elem(u, 64 * (step - lo_step) + lane));
+        }
+      }
+      if (lock && kEncBlock * (bi + 1) <= iters) {
+#pragma unroll
+        for (int q = 0; q < kEncBlock; ++q) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) code(std::false_type{}, u, te[u][q]);
+          if ((q & 3) == 3) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              if (on[u]) check(u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < kEncBlock; ++q) {
+          const uint32_t i = kEncBlock * bi + q;
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (on[u] && i < full[u]) code(std::false_type{}, u, te[u][q]);
+          if ((q & 3) == 3) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              if (on[u]) check(u);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!on[u]) continue;
+      check(u);
+      if (!on[u]) continue;
+      if (nw[u] > kFlushWords * flushed[u]) flush(u, flushed[u]);
+      w.states[64 * sid[u] + lane] = x[u];
+      if (lane == 0)
+        *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =
+            make_uint4(wo[u] + 2 * nw[u], pack_info(LTC_MODE_RANS, 0, lo[u], hi[u]), nw[u], 0);
+    }
+  };
+  const bool topexp = (DT == LTC_BF16 || DT == LTC_FP32) && k == (uint32_t)(E - 1);
+  if (topexp) body(std::true_type{});
+  else body(std::false_type{});
 }
 
 // ------------------------------------------------------------------ k_scan
@@ -535,7 +733,9 @@ static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t
   record(ev, 0, st);
   if (chunks) hipLaunchKernelGGL(k_hist<DT>, dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
   record(ev, 1, st);
-  if (chunks) hipLaunchKernelGGL(k_encode<DT>, dim3((uint32_t)(chunks * E)), dim3(64), 0, st, t, w);
+  if (chunks)
+    hipLaunchKernelGGL(k_encode<DT>, dim3((uint32_t)((chunks + kEncStreams - 1) / kEncStreams * E)), dim3(64), 0,
+                       st, t, w);
   record(ev, 2, st);
   hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E);
   record(ev, 3, st);

@@ -238,3 +238,22 @@ def test_crc32_batch_matches_single(ltc):
             d = t.cpu().numpy()
             want = [zlib.crc32(d[i:i + k].tobytes()) for i in range(0, d.size, k)]
             assert o.cpu().numpy().view(np.uint32).tolist() == want
+
+
+@pytest.mark.parametrize("nchunks", [1, 2, 3, 7])
+def test_mixed_stream_pairs(ltc, nchunks):
+    """Neighbouring chunks alternate between compressible values and random
+    bytes (so a wave codes one stream of a pair and not the other), with an
+    odd number of chunks as well; blobs must equal the oracle's."""
+    rng = np.random.default_rng(nchunks)
+    chunk = 16384
+    parts = []
+    for c in range(nchunks):
+        if c % 2 == 0:
+            x = (rng.standard_normal(chunk // 2) * 0.02).astype(np.float32)
+            parts.append(torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint8))
+        else:
+            parts.append(rng.integers(0, 256, chunk, dtype=np.uint8))
+    data = np.concatenate(parts)[: nchunks * chunk - 6]
+    check_case(ltc, data, 1, chunk, label=f"mixed pairs {nchunks}")
+    check_case(ltc, data[: data.size // 4 * 4], 3, chunk, label=f"mixed pairs fp32 {nchunks}")
