@@ -6,10 +6,11 @@
 //             sub-histograms against same-bin contention), then one wave per
 //             stream normalises its histogram to a 4096 total and decides
 //             CONST / RAW (by an exact lower bound on the rANS size) / encode.
-//   k_encode  one wave per stream still to encode: 64-lane interleaved rANS
-//             from the last step to the first, words staged in an LDS ring
-//             and flushed 1 KiB at a time to the workspace; aborts to RAW as
-//             soon as the payload can no longer beat the threshold.
+//   k_encode  one wave per two streams still to encode: 64-lane interleaved
+//             rANS from the last step to the first, exact division by one
+//             double multiply, words staged in an LDS ring and drained 512
+//             bytes at a time to the workspace in decoder order; aborts to
+//             RAW as soon as the payload can no longer beat the threshold.
 //   k_scan    one workgroup per tensor: exclusive scan of the 16-byte-aligned
 //             payload sizes into offsets; writes the 64-byte header.
 //   k_pack    one workgroup per chunk: directory entries, RANS payloads from
@@ -31,7 +32,7 @@ constexpr uint32_t kHistSeg = 1u << 20;  // elements between sub-histogram flush
 constexpr int kPackThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr uint32_t kRingWords = 512;    // encoder word ring per stream (LDS)
-constexpr uint32_t kFlushWords = 256;   // one flush = 64 lanes x 8 bytes
+constexpr uint32_t kFlushWords = 256;   // one drain = 64 lanes x 8 bytes
 constexpr int kEncBlock = 8;            // steps per prefetched block (a multiple of 4)
 constexpr int kEncStreams = 2;          // streams one wave codes, interleaved
 
@@ -228,6 +229,15 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
 
 // ---------------------------------------------------------------- k_encode
 
+// 24-bit multiply (v_mul_u32_u24, full rate).  The compiler rewrites the
+// builtin into a 32-bit multiply whenever it can prove an operand narrow,
+// which then issues at quarter rate, so the instruction is named directly.
+__device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_mul_u32_u24 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 // Byte k of the reordered element.  For BF16 and FP32 the top byte is the
 // biased exponent field itself, one bit-field extract.
 template <int DT, bool TOP>
@@ -238,24 +248,35 @@ __device__ __forceinline__ uint32_t stream_byte(uint32_t x, uint32_t k) {
 
 // One wave codes stream k of two neighbouring chunks, interleaving their
 // independent state chains (instruction-level parallelism for a loop whose
-// every step is a dependent chain).  Per stream:
-//   tab   one 8-byte entry per symbol: f | cum << 12 | sh2 << 24 | sh1 << 31
-//         and the Granlund-Montgomery multiplier m for exact division by f
-//         (Granlund & Montgomery 1994, "Division by invariant integers using
-//         multiplication": q = (t + ((x - t) >> sh1)) >> sh2, t = mulhi(m, x));
-//   ring  a 512-word LDS ring for the emitted words plus a private dummy slot
-//         per lane, so a lane that emits nothing writes without a branch; the
-//         ring drains to the workspace 256 words at a time.
+// every step is a dependent chain).
+//
+// Division.  A coding step needs q = floor(x / f) for a 32-bit x and
+// 1 <= f <= 4095.  With r = 1/f rounded up to a double, x * r >= x / f, and
+// the excess x/f * 2^-52 < 2^-20, while a non-integral x/f sits at least 1/f
+// >= 2^-12 below the next integer; so truncating the rounded product gives q
+// exactly (rounding is monotone and q is representable).  The same quotient
+// decides renormalisation: x >= f * 2^20 exactly when floor(x / f) >= 2^20,
+// and then floor((x >> 16) / f) = floor(x / f) >> 16.
+//
+// Per stream, in LDS:
+//   tab   one 16-byte entry per symbol: {r (double), 4096 - f, cum};
+//   stg   one block of 512 elements, loaded with wide coalesced loads one
+//         block ahead, stored as their symbols' table offsets and read back
+//         transposed to lane order;
+//   ring  512 emitted words.  The words of a step take decoder order (lanes
+//         ascending), so lane l's word lands at top - cnt + (number of
+//         emitting lanes below l); complete 256-word blocks drain to the
+//         workspace with 8-byte stores, and a stream's words end at the end
+//         of its workspace slot.
 // Abort and drain checks run every 4 steps: 4 steps emit at most 256 words,
-// so a drained block is never overwritten before it leaves, and an abort is
-// seen before any word past the stream's limit reaches the workspace.
+// so a block is never overwritten before it drains, and an abort is seen
+// before any word past the stream's limit reaches the workspace.
 template <int DT>
 __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
   constexpr int U = kEncStreams;
-  __shared__ uint2 tab[U][256];
-  // one block of elements per stream, staged for the transpose to lane order
-  __shared__ __attribute__((aligned(16))) uint32_t stg[U][128 * E];
+  __shared__ uint4 tab[U][256];
+  __shared__ __attribute__((aligned(16))) uint32_t stg[U][256];  // 512 u16 entry offsets
   __shared__ __attribute__((aligned(16))) uint16_t ring[U][kRingWords + 64];
   const uint32_t lane = lane_id();
   const uint32_t k = blockIdx.x % E;
@@ -292,15 +313,6 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     src[u] = job.src + c * t.chunk_bytes;
   }
   if (!on[0] && !on[1]) return;
-  // The element prefetch below loads for both slots unconditionally; a slot
-  // without a stream reads the other slot's chunk so every load stays in
-  // bounds (its values are never used).
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (on[u]) continue;
-    src[u] = src[1 - u];
-    n[u] = n[1 - u];
-  }
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -316,204 +328,187 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     const uint32_t base = wave_exclusive_scan_u32(acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t fv = f[i];
-      const uint32_t ell = fv <= 1 ? 0u : 32u - __clz(fv - 1u);
-      const uint32_t m = fv ? (uint32_t)(((((uint64_t)1) << 32) * ((1ull << ell) - fv)) / fv + 1u) : 0u;
-      const uint32_t sh1 = ell > 0 ? 1u : 0u, sh2 = ell > 0 ? ell - 1u : 0u;
-      tab[u][4 * lane + i] = make_uint2(fv | ((base + cum[i]) << 12) | (sh2 << 24) | (sh1 << 31), m);
+      double r = 0.0;
+      if (f[i]) {
+        const double fd = (double)f[i];
+        r = 1.0 / fd;                                  // correctly rounded
+        if (fma(r, fd, -1.0) < 0.0)                    // below 1/f: one ulp up
+          r = __longlong_as_double(__double_as_longlong(r) + 1);
+      }
+      const uint64_t rb = (uint64_t)__double_as_longlong(r);
+      tab[u][4 * lane + i] = make_uint4((uint32_t)rb, (uint32_t)(rb >> 32), kTotal - f[i], base + cum[i]);
     }
   }
   __syncthreads();
 
-  uint32_t x[U], top[U], nw[U], flushed[U];
+  uint32_t x[U], top[U], flushed[U];  // words emitted so far: wcap - top
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     x[u] = kRansLow;
     top[u] = wcap;
-    nw[u] = 0;
     flushed[u] = 0;
   }
 
-  const bool vec = t.vec16 != 0;
+  auto flush = [&](int u, uint32_t b) {
+    const uint32_t base = wcap - kFlushWords * (b + 1) + 4 * lane;
+    const uint2 v = *reinterpret_cast<const uint2*>(&ring[u][base & (kRingWords - 1)]);
+    *reinterpret_cast<uint2*>(w.words + sid[u] * wcap + base) = v;
+  };
+  // abort once the payload can no longer beat the threshold, else drain
+  auto check = [&](int u) {
+    const uint32_t nw = wcap - top[u];
+    if (nw > wlimit[u]) {
+      on[u] = false;
+      if (lane == 0)
+        *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =
+            make_uint4(n[u], pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
+      return;
+    }
+    while (nw >= kFlushWords * (flushed[u] + 1)) {
+      flush(u, flushed[u]);
+      flushed[u] = uniform(flushed[u] + 1);
+    }
+  };
+  // One coding step of stream u (steps run from the last to the first).  A
+  // lane that emits nothing writes its private slot past the ring, so the
+  // step has no branch.
+  auto code = [&](auto guarded, int u, const uint4 e) {
+    constexpr bool G = decltype(guarded)::value;
+    const bool active = !G || lane < (n[u] & 63u);
+    const uint32_t xo = x[u];
+    const double r = __hiloint2double((int)e.y, (int)e.x);
+    const uint32_t q1 = (uint32_t)((double)xo * r);
+    const bool need = active && q1 >= (1u << 20);
+    const uint64_t mask = ballot(need);
+    const uint32_t sh = need ? 16u : 0u;
+    const uint32_t xn = mul_u24(q1 >> sh, e.z) + (xo >> sh) + e.w;
+    x[u] = active ? xn : xo;
+    top[u] = uniform(top[u] - (uint32_t)__popcll(mask));
+    const uint32_t slot = (top[u] + lanes_below(mask)) & (kRingWords - 1);
+    ring[u][need ? slot : kRingWords + lane] = (uint16_t)xo;
+  };
+
   auto body = [&](auto topexp) {
     constexpr bool TOP = decltype(topexp)::value;
-    // element of stream u at step `step` (index clamped inside the chunk)
-    auto elem_at = [&](int u, uint32_t step) -> uint32_t {
+    auto sym_at = [&](int u, uint32_t step) -> uint32_t {  // direct load, index clamped
       const uint32_t e = 64 * step + lane;
-      return load_elem<DT>(src[u] + (uint64_t)(e < n[u] ? e : n[u] - 1) * E);
+      return stream_byte<DT, TOP>(load_elem<DT>(src[u] + (uint64_t)(e < n[u] ? e : n[u] - 1) * E), k);
     };
-    auto flush = [&](int u, uint32_t b) {
-      __syncthreads();
-      const uint32_t base = wcap - kFlushWords * (b + 1) + 4 * lane;
-      const uint2 v = *reinterpret_cast<const uint2*>(&ring[u][base & (kRingWords - 1)]);
-      *reinterpret_cast<uint2*>(w.words + sid[u] * wcap + base) = v;
-    };
-    // abort once the payload can no longer beat the threshold, else drain
-    auto check = [&](int u) {
-      if (nw[u] > wlimit[u]) {
-        on[u] = false;
-        if (lane == 0)
-          *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =
-              make_uint4(n[u], pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
-        return;
-      }
-      while (nw[u] >= kFlushWords * (flushed[u] + 1)) {
-        flush(u, flushed[u]);
-        ++flushed[u];
-      }
-    };
-    // One coding step of stream u: steps run from the last to the first and
-    // the words of a step take decoder order (lanes ascending), so lane l's
-    // word lands at top - cnt + (number of emitting lanes below l).
-    auto code = [&](auto guarded, int u, const uint2 e) {
-      constexpr bool G = decltype(guarded)::value;
-      const bool active = !G || 64 * full[u] + lane < n[u];
-      const uint32_t f = e.x & 0xFFFu;
-      const bool need = active && x[u] >= (f << 20);
-      const uint64_t mask = ballot(need);
-      const uint32_t cnt = (uint32_t)__popcll(mask);
-      const uint32_t slot = need ? ((top[u] - cnt + lanes_below(mask)) & (kRingWords - 1))
-                                 : kRingWords + lane;
-      ring[u][slot] = (uint16_t)x[u];
-      const uint32_t xr = need ? x[u] >> 16 : x[u];
-      const uint32_t t1 = __umulhi(e.y, xr);
-      const uint32_t q = (t1 + ((xr - t1) >> (e.x >> 31))) >> ((e.x >> 24) & 0xFu);
-      const uint32_t xn = xr + __umul24(q, kTotal - f) + ((e.x >> 12) & 0xFFFu);
-      x[u] = active ? xn : x[u];
-      top[u] -= cnt;
-      nw[u] += cnt;
-    };
-
-    auto entry = [&](int u, uint32_t raw) { return tab[u][stream_byte<DT, TOP>(raw, k)]; };
     // the partial step (the last one) is coded first
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (on[u] && n[u] > 64 * full[u]) {
-        code(std::true_type{}, u, entry(u, elem_at(u, full[u])));
+        code(std::true_type{}, u, tab[u][sym_at(u, full[u])]);
         check(u);
       }
     }
-    // Full steps, both streams in lock step from their last full step down.
-    // A block of 8 steps covers 512 consecutive elements of a stream: each
-    // lane loads 8*E contiguous bytes of the next block with wide coalesced
-    // loads (one block ahead), the block goes through an LDS tile, and every
-    // lane reads back its own element of each step (64 q + lane).  A block's
-    // table entries are read into registers before its steps, so the state
-    // chains hold no LDS read.  When both streams have the same number of
-    // steps (the common case) a full block runs without any per-step branch
-    // and the two chains interleave; a stream that aborted keeps computing
-    // there but is never drained or finalised.
-    const bool lock = on[0] && on[1] && full[0] == full[1];
-    const uint32_t iters = max(on[0] ? full[0] : 0u, on[1] ? full[1] : 0u);
-    const uint32_t nblk = (iters + kEncBlock - 1) / kEncBlock;
-    // first element of block bi of stream u (the block's lowest step)
-    auto block_lo = [&](int u, uint32_t bi) -> uint32_t {
-      const uint32_t top_step = full[u] > kEncBlock * bi ? full[u] - 1 - kEncBlock * bi : 0u;
-      return 64u * (top_step >= kEncBlock - 1 ? top_step - (kEncBlock - 1) : 0u);
-    };
-    // A lane whose 8 elements reach past the stream's full steps (the lowest
-    // block of a short stream) loads the chunk's first 8 elements instead,
-    // which it never reads back.  A slot with no full step of its own fetches
-    // from the other slot's chunk.
-    const uint8_t* fsrc[U];
-    uint32_t flim[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool own = on[u] && full[u] > 0;
-      fsrc[u] = own ? src[u] : src[1 - u];
-      flim[u] = 64 * (own ? full[u] : full[1 - u]);
-    }
+    // Fast loop: both streams have the same number of full steps (the common
+    // case) and code them in lock step, 8 steps (512 elements per stream) per
+    // block.  Each lane loads 8*E contiguous bytes of the next block with one
+    // wide load, the block goes through the LDS tile, and every lane reads
+    // back its own element of each step at a fixed offset.  Table entries for
+    // 4 steps are read into registers ahead of those steps, so the state
+    // chains hold no LDS read.
+    uint32_t done = 0;  // full steps coded, counted from the last one down
+    const bool lock = on[0] && on[1] && full[0] == full[1] && t.vec16 != 0;
+    const uint32_t nfb = lock ? full[0] / kEncBlock : 0u;
     uint32_t pf[U][2 * E];
-    auto fetch = [&](int u, uint32_t bi) {
-      uint32_t e0 = block_lo(u, bi) + 8 * lane;
-      e0 = e0 + 8 <= flim[u] ? e0 : 0u;
-      if (vec) {
-        const uint4* p = reinterpret_cast<const uint4*>(fsrc[u] + (uint64_t)e0 * E);
-        if constexpr (E == 1) {
-          const uint2 v = *reinterpret_cast<const uint2*>(fsrc[u] + e0);
-          pf[u][0] = v.x;
-          pf[u][1] = v.y;
-        } else {
-#pragma unroll
-          for (int h = 0; h < E / 2; ++h) {
-            const uint4 v = p[h];
-            pf[u][4 * h] = v.x;
-            pf[u][4 * h + 1] = v.y;
-            pf[u][4 * h + 2] = v.z;
-            pf[u][4 * h + 3] = v.w;
-          }
-        }
+    auto fetch = [&](int u, uint32_t bi) {  // block bi: elements 64*(full - 8(bi+1)) + 8 lane ...
+      const uint32_t e0 = 64u * (full[u] - kEncBlock * (bi + 1)) + 8u * lane;
+      if constexpr (E == 1) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src[u] + e0);
+        pf[u][0] = v.x;
+        pf[u][1] = v.y;
       } else {
+        const uint4* p = reinterpret_cast<const uint4*>(src[u] + (uint64_t)e0 * E);
 #pragma unroll
-        for (int i = 0; i < 2 * E; ++i) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) word |= (uint32_t)fsrc[u][(uint64_t)e0 * E + 4 * i + b] << (8 * b);
-          pf[u][i] = word;
+        for (int h = 0; h < E / 2; ++h) {
+          const uint4 v = p[h];
+          pf[u][4 * h] = v.x;
+          pf[u][4 * h + 1] = v.y;
+          pf[u][4 * h + 2] = v.z;
+          pf[u][4 * h + 3] = v.w;
         }
       }
     };
-    auto stage_elem = [&](int u, uint32_t pos) -> uint32_t {
-      if constexpr (E == 1) return reinterpret_cast<const uint8_t*>(stg[u])[pos];
-      else if constexpr (E == 2) return reinterpret_cast<const uint16_t*>(stg[u])[pos];
-      else return stg[u][pos];
+    // The tile holds, per element, the byte offset of its symbol's table
+    // entry (symbol * 16) as a u16: the steps then read their entry address
+    // straight from LDS.
+    auto entry_offsets = [&](int u) -> uint4 {
+      uint32_t o[4];
+      if constexpr (DT == LTC_BF16 && TOP) {
+        // the exponent of each half-word sits in bits 7..14: (x >> 3) & 0xFF0
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (pf[u][i] >> 3) & 0x0FF00FF0u;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t a, b;
+          if constexpr (E == 1) {
+            a = ((pf[u][i >> 1] >> (16 * (i & 1))) & 0xFFu) << 4;
+            b = ((pf[u][i >> 1] >> (16 * (i & 1) + 8)) & 0xFFu) << 4;
+          } else if constexpr (E == 2) {
+            a = stream_byte<DT, TOP>(pf[u][i] & 0xFFFFu, k) << 4;
+            b = stream_byte<DT, TOP>(pf[u][i] >> 16, k) << 4;
+          } else {
+            a = stream_byte<DT, TOP>(pf[u][2 * i], k) << 4;
+            b = stream_byte<DT, TOP>(pf[u][2 * i + 1], k) << 4;
+          }
+          o[i] = a | (b << 16);
+        }
+      }
+      return make_uint4(o[0], o[1], o[2], o[3]);
     };
-    if (nblk > 0) {
+    if (nfb > 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) fetch(u, 0);
     }
-    for (uint32_t bi = 0; bi < nblk; ++bi) {
-      if (!on[0] && !on[1]) break;
+    for (uint32_t bi = 0; bi < nfb; ++bi) {
       __syncthreads();
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if constexpr (E == 1) {
-          reinterpret_cast<uint2*>(stg[u])[lane] = make_uint2(pf[u][0], pf[u][1]);
-        } else {
-#pragma unroll
-          for (int h = 0; h < E / 2; ++h)
-            reinterpret_cast<uint4*>(stg[u])[(E / 2) * lane + h] =
-                make_uint4(pf[u][4 * h], pf[u][4 * h + 1], pf[u][4 * h + 2], pf[u][4 * h + 3]);
-        }
-      }
+      for (int u = 0; u < U; ++u) reinterpret_cast<uint4*>(stg[u])[lane] = entry_offsets(u);
       __syncthreads();
+      if (bi + 1 < nfb) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) fetch(u, bi + 1 < nblk ? bi + 1 : bi);
-      uint2 te[U][kEncBlock];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t top_step = full[u] > kEncBlock * bi ? full[u] - 1 - kEncBlock * bi : 0u;
-        const uint32_t lo_step = block_lo(u, bi) / 64;
-#pragma unroll
-        for (int q = 0; q < kEncBlock; ++q) {
-          const uint32_t step = top_step >= (uint32_t)q ? top_step - q : lo_step;
-          te[u][q] = entry(u, stage_elem(u, 64 * (step - lo_step) + lane));
-        }
+        for (int u = 0; u < U; ++u) fetch(u, bi + 1);
       }
-      if (lock && kEncBlock * (bi + 1) <= iters) {
+      // step full-1-8bi-q sits at element 64*(7-q) + lane of the tile
+      uint32_t sy[U][kEncBlock];
 #pragma unroll
-        for (int q = 0; q < kEncBlock; ++q) {
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < kEncBlock; ++q)
+          sy[u][q] = reinterpret_cast<const uint16_t*>(stg[u])[64 * (kEncBlock - 1 - q) + lane];
+#pragma unroll
+      for (int h = 0; h < kEncBlock / 4; ++h) {
+        uint4 te[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            te[u][q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(tab[u]) + sy[u][4 * h + q]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int u = 0; u < U; ++u) code(std::false_type{}, u, te[u][q]);
-          if ((q & 3) == 3) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-              if (on[u]) check(u);
-          }
-        }
-      } else {
+        for (int u = 0; u < U; ++u) check(u);
+      }
+      done = kEncBlock * (bi + 1);
+      if (!on[0] || !on[1]) break;  // the survivor finishes below
+    }
+    // General path: whatever the fast loop left (streams of different
+    // lengths, unaligned inputs, the last full % 8 steps, the partner of a
+    // stream that aborted), one step at a time with direct element loads.
+    const uint32_t rest = max(on[0] ? full[0] - done : 0u, on[1] ? full[1] - done : 0u);
+    for (uint32_t i = 0; i < rest; ++i) {
 #pragma unroll
-        for (int q = 0; q < kEncBlock; ++q) {
-          const uint32_t i = kEncBlock * bi + q;
+      for (int u = 0; u < U; ++u)
+        if (on[u] && done + i < full[u]) code(std::false_type{}, u, tab[u][sym_at(u, full[u] - 1 - done - i)]);
+      if ((i & 3) == 3) {
 #pragma unroll
-          for (int u = 0; u < U; ++u)
-            if (on[u] && i < full[u]) code(std::false_type{}, u, te[u][q]);
-          if ((q & 3) == 3) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-              if (on[u]) check(u);
-          }
-        }
+        for (int u = 0; u < U; ++u)
+          if (on[u]) check(u);
       }
     }
 #pragma unroll
@@ -521,11 +516,12 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
       if (!on[u]) continue;
       check(u);
       if (!on[u]) continue;
-      if (nw[u] > kFlushWords * flushed[u]) flush(u, flushed[u]);
+      const uint32_t nw = wcap - top[u];
+      if (nw > kFlushWords * flushed[u]) flush(u, flushed[u]);
       w.states[64 * sid[u] + lane] = x[u];
       if (lane == 0)
         *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =
-            make_uint4(wo[u] + 2 * nw[u], pack_info(LTC_MODE_RANS, 0, lo[u], hi[u]), nw[u], 0);
+            make_uint4(wo[u] + 2 * nw, pack_info(LTC_MODE_RANS, 0, lo[u], hi[u]), nw, 0);
     }
   };
   const bool topexp = (DT == LTC_BF16 || DT == LTC_FP32) && k == (uint32_t)(E - 1);
