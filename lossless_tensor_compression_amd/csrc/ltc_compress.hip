@@ -341,32 +341,35 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   }
   __syncthreads();
 
-  uint32_t x[U], top[U], flushed[U];  // words emitted so far: wcap - top
+  // Words emitted so far: wcap - top.  A stream aborts once top < atop
+  // (more than wlimit words) and drains the 256 words at [ftop, ftop + 256)
+  // once top <= ftop.
+  uint32_t x[U], top[U], ftop[U], atop[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     x[u] = kRansLow;
     top[u] = wcap;
-    flushed[u] = 0;
+    ftop[u] = wcap - kFlushWords;
+    atop[u] = wcap - wlimit[u];
   }
 
-  auto flush = [&](int u, uint32_t b) {
-    const uint32_t base = wcap - kFlushWords * (b + 1) + 4 * lane;
+  auto flush = [&](int u) {
+    wave_sync();  // the block's words were written by other lanes
+    const uint32_t base = ftop[u] + 4 * lane;
     const uint2 v = *reinterpret_cast<const uint2*>(&ring[u][base & (kRingWords - 1)]);
     *reinterpret_cast<uint2*>(w.words + sid[u] * wcap + base) = v;
   };
-  // abort once the payload can no longer beat the threshold, else drain
+  // Every 4 steps: 4 steps emit at most 256 words, so at most one block is
+  // complete and none is overwritten before it drains.
   auto check = [&](int u) {
-    const uint32_t nw = wcap - top[u];
-    if (nw > wlimit[u]) {
+    if (top[u] < atop[u]) {
       on[u] = false;
       if (lane == 0)
         *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =
             make_uint4(n[u], pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
-      return;
-    }
-    while (nw >= kFlushWords * (flushed[u] + 1)) {
-      flush(u, flushed[u]);
-      flushed[u] = uniform(flushed[u] + 1);
+    } else if (top[u] <= ftop[u]) {
+      flush(u);
+      ftop[u] = uniform(ftop[u] - kFlushWords);
     }
   };
   // One coding step of stream u (steps run from the last to the first).  A
@@ -406,9 +409,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     // case) and code them in lock step, 8 steps (512 elements per stream) per
     // block.  Each lane loads 8*E contiguous bytes of the next block with one
     // wide load, the block goes through the LDS tile, and every lane reads
-    // back its own element of each step at a fixed offset.  Table entries for
-    // 4 steps are read into registers ahead of those steps, so the state
-    // chains hold no LDS read.
+    // back its own element of each step at a fixed offset.
     uint32_t done = 0;  // full steps coded, counted from the last one down
     const bool lock = on[0] && on[1] && full[0] == full[1] && t.vec16 != 0;
     const uint32_t nfb = lock ? full[0] / kEncBlock : 0u;
@@ -459,43 +460,81 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
       }
       return make_uint4(o[0], o[1], o[2], o[3]);
     };
-    if (nfb > 0) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) fetch(u, 0);
-    }
-    for (uint32_t bi = 0; bi < nfb; ++bi) {
-      __syncthreads();
+    // Software pipeline, per block of 8 steps: the entries of a half-block's
+    // 4 steps are read while the previous 4 steps compute, and the next block
+    // is staged (and the one after it loaded) between the two halves, so the
+    // state chains never wait on LDS or HBM.  A tile staged past the last
+    // block repeats in-bounds data and is never coded.
+    auto stage = [&]() {
+      wave_sync();
 #pragma unroll
       for (int u = 0; u < U; ++u) reinterpret_cast<uint4*>(stg[u])[lane] = entry_offsets(u);
-      __syncthreads();
-      if (bi + 1 < nfb) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) fetch(u, bi + 1);
-      }
-      // step full-1-8bi-q sits at element 64*(7-q) + lane of the tile
-      uint32_t sy[U][kEncBlock];
+      wave_sync();
+    };
+    // step full-1-8bi-q sits at element 64*(7-q) + lane of the tile
+    auto read_offsets = [&](uint32_t (&sy)[U][kEncBlock]) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int q = 0; q < kEncBlock; ++q)
           sy[u][q] = reinterpret_cast<const uint16_t*>(stg[u])[64 * (kEncBlock - 1 - q) + lane];
+    };
+    auto entry_at = [&](int u, uint32_t off) {
+      return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(tab[u]) + off);
+    };
+    if (nfb > 0) {
+      uint32_t sy[U][kEncBlock], sn[U][kEncBlock];
+      uint4 ta[U][4], tb[U][4];
 #pragma unroll
-      for (int h = 0; h < kEncBlock / 4; ++h) {
-        uint4 te[U][4];
+      for (int u = 0; u < U; ++u) fetch(u, 0);
+      stage();
+      read_offsets(sy);
+#pragma unroll
+      for (int u = 0; u < U; ++u) fetch(u, nfb > 1 ? 1u : 0u);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ta[u][q] = entry_at(u, sy[u][q]);
+      for (uint32_t bi = 0; bi < nfb; ++bi) {
+        // steps 0..3 of the block; the entries of steps 4..7 load meanwhile
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            code(std::false_type{}, u, ta[u][q]);
+            tb[u][q] = entry_at(u, sy[u][4 + q]);
+          }
+        }
+        // stage block bi+1 (loaded one block ago), load block bi+2; the
+        // drain check comes after, so its stores are a half-block old by the
+        // time the next staging waits on the loads (one counter covers both)
+        stage();
+        read_offsets(sn);
+        const uint32_t nxt = bi + 2 < nfb ? bi + 2 : nfb - 1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) fetch(u, nxt);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (on[u]) check(u);
+        // steps 4..7; the entries of the next block's steps 0..3 load meanwhile
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            code(std::false_type{}, u, tb[u][q]);
+            ta[u][q] = entry_at(u, sn[u][q]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (on[u]) check(u);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            te[u][q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(tab[u]) + sy[u][4 * h + q]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int u = 0; u < U; ++u) code(std::false_type{}, u, te[u][q]);
-#pragma unroll
-        for (int u = 0; u < U; ++u) check(u);
+          for (int q = 0; q < kEncBlock; ++q) sy[u][q] = sn[u][q];
+        done = kEncBlock * (bi + 1);
+        if (!on[0] || !on[1]) break;  // the survivor finishes below
       }
-      done = kEncBlock * (bi + 1);
-      if (!on[0] || !on[1]) break;  // the survivor finishes below
     }
     // General path: whatever the fast loop left (streams of different
     // lengths, unaligned inputs, the last full % 8 steps, the partner of a
@@ -517,7 +556,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
       check(u);
       if (!on[u]) continue;
       const uint32_t nw = wcap - top[u];
-      if (nw > kFlushWords * flushed[u]) flush(u, flushed[u]);
+      if (top[u] < ftop[u] + kFlushWords) flush(u);  // the last, partial block
       w.states[64 * sid[u] + lane] = x[u];
       if (lane == 0)
         *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =

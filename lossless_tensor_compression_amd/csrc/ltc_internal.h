@@ -164,6 +164,15 @@ __device__ __forceinline__ uint32_t wave_exclusive_scan_u32(uint32_t v) {
   return inc - v;
 }
 
+// Orders LDS accesses across the lanes of one wave (a workgroup of a single
+// wave needs no s_barrier): LDS executes a wave's accesses in order, so only
+// the compiler must not move them across this point.  Unlike __syncthreads()
+// it waits for nothing, in particular not for outstanding global stores.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
