@@ -217,7 +217,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     if (lane == 0) *job.status = LTC_ERR_CORRUPT;
     return;
   }
-  __syncthreads();
+  wave_sync();
   // slot -> symbol table: lane l fills slots 64l .. 64l+63
 #pragma unroll
   for (int rr = 0; rr < MAXR; ++rr) {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
       lw[q4] = word;
     }
   }
-  __syncthreads();
+  wave_sync();
   // word rings: halves 0 and 1 resident, half 2 staged in registers
 #pragma unroll
   for (int rr = 0; rr < MAXR; ++rr) {
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     *reinterpret_cast<uint2*>(&ring[rr][kHalf + 4 * lane]) = load_half(wp[rr], nwords[rr], 1);
     staged[rr] = load_half(wp[rr], nwords[rr], 2);
   }
-  __syncthreads();
+  wave_sync();
 
   // ---- main loop: 8 steps (512 symbols) per block
   const bool vec = t.vec16 != 0;
@@ -310,10 +310,10 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   auto refill = [&](int rr) {
     if (pos[rr] >= kHalf * (hcur[rr] + 1)) {
       ++hcur[rr];
-      __syncthreads();
+      wave_sync();
       *reinterpret_cast<uint2*>(&ring[rr][kHalf * ((hcur[rr] + 1) & 1) + 4 * lane]) = staged[rr];
       staged[rr] = load_half(wp[rr], nwords[rr], hcur[rr] + 2);
-      __syncthreads();
+      wave_sync();
     }
   };
 
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
         refill(rr);
       }
     }
-    __syncthreads();
+    wave_sync();
     if (e0 < n) {
       uint32_t pl[2][E];
 #pragma unroll
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     }
 #pragma unroll
     for (int k = 0; k < E; ++k) rawv[k] = rawn[k];
-    __syncthreads();
+    wave_sync();
   }
   // ---- end checks: every coded stream consumed exactly its words and
   // returned to the initial state
