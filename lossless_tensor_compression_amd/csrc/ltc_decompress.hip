@@ -296,7 +296,8 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     const uint32_t xd = __umul24(e & 0xFFFFu, xs >> 12) + sl - (e >> 16);
     const bool need = active && xd < kRansLow;
     const uint64_t mask = ballot(need);
-    const uint32_t wv = ring[rr][(pos[rr] + lanes_below(mask)) & (kDecRing - 1)];
+    uint32_t wv = ring[rr][(pos[rr] + lanes_below(mask)) & (kDecRing - 1)];
+    asm volatile("" : "+v"(wv));  // keep the read unconditional (no exec branch)
     const uint32_t xn = need ? (xd << 16) | wv : xd;
     x[rr] = active ? xn : xs;
     pos[rr] += (uint32_t)__popcll(mask);
@@ -325,16 +326,25 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
 #pragma unroll
     for (int rr = 0; rr < MAXR; ++rr) {
       if (rr >= nr) continue;
+      if (8 * (b + 1) <= full) {  // every step of the block is full
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+        for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-        for (int q = 4 * sb; q < 4 * sb + 4; ++q) {
-          const uint32_t step = 8 * b + q;
-          if (step >= steps) break;
-          if (step < full) dstep(std::false_type{}, rr, q);
-          else dstep(std::true_type{}, rr, q);
+          for (int q = 4 * sb; q < 4 * sb + 4; ++q) dstep(std::false_type{}, rr, q);
+          refill(rr);
         }
-        refill(rr);
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+          for (int q = 4 * sb; q < 4 * sb + 4; ++q) {
+            const uint32_t step = 8 * b + q;
+            if (step >= steps) break;
+            if (step < full) dstep(std::false_type{}, rr, q);
+            else dstep(std::true_type{}, rr, q);
+          }
+          refill(rr);
+        }
       }
     }
     wave_sync();
