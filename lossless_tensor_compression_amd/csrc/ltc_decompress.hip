@@ -86,7 +86,8 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   __shared__ uint8_t lut[MAXR][4096];
   __shared__ uint32_t symt[MAXR][256];
   __shared__ __attribute__((aligned(16))) uint16_t ring[MAXR][kDecRing];
-  __shared__ __attribute__((aligned(16))) uint8_t stage[MAXR][512];
+  // decoded symbols of a block: dword 64*(q/4) + l holds steps q..q+3 of lane l
+  __shared__ __attribute__((aligned(16))) uint32_t stage[MAXR][128];
 
   const uint64_t g = blockIdx.x;
   const int j = find_job(t, g);
@@ -282,6 +283,26 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
 #pragma unroll
   for (int k = 0; k < E; ++k) rawv[k] = load_raw8(rbase[k], 8 * lane, rlim[k]);
 
+  // Output lane l writes elements 8l .. 8l+7 of the block: step l / 8, lanes
+  // 8(l % 8) .. 8(l % 8)+7, i.e. byte (l / 8) % 4 of 8 consecutive stage
+  // dwords starting at 64 * (l / 32) + 8 * (l % 8).
+  uint32_t sacc[MAXR];
+#pragma unroll
+  for (int rr = 0; rr < MAXR; ++rr) sacc[rr] = 0;
+  const uint32_t sbyte = (lane >> 3) & 3u;
+  const uint32_t sel_pair = sbyte | ((sbyte + 4) << 8) | 0x0C0C0000u;  // bytes 0,1 from d0,d1; 2,3 zero
+  auto stage_bytes = [&](int rr) -> uint64_t {
+    const uint4* sp = reinterpret_cast<const uint4*>(&stage[rr][64 * (lane >> 5) + 8 * (lane & 7)]);
+    const uint4 a = sp[0], b = sp[1];
+    const uint32_t p01 = __builtin_amdgcn_perm(a.y, a.x, sel_pair);
+    const uint32_t p23 = __builtin_amdgcn_perm(a.w, a.z, sel_pair);
+    const uint32_t p45 = __builtin_amdgcn_perm(b.y, b.x, sel_pair);
+    const uint32_t p67 = __builtin_amdgcn_perm(b.w, b.z, sel_pair);
+    const uint32_t lo = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    const uint32_t hi = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+  };
+
   // One decoding step of coded stream rr.  Every lane reads a ring word at
   // pos + (renormalising lanes below it) and keeps it only if it
   // renormalises, so there is no branch; a read past W cannot go unnoticed
@@ -301,7 +322,13 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     const uint32_t xn = need ? (xd << 16) | wv : xd;
     x[rr] = active ? xn : xs;
     pos[rr] += (uint32_t)__popcll(mask);
-    stage[rr][64 * q + lane] = (uint8_t)v;
+    sacc[rr] = __builtin_amdgcn_alignbit(v, sacc[rr], 8);  // step q in byte q % 4
+    if ((q & 3) == 3) stage[rr][64 * (q >> 2) + lane] = sacc[rr];
+  };
+  // a step past the stream's end keeps the byte positions aligned
+  auto dskip = [&](int rr, int q) {
+    sacc[rr] = sacc[rr] >> 8;
+    if ((q & 3) == 3) stage[rr][64 * (q >> 2) + lane] = sacc[rr];
   };
   // Ring refill, checked after every 4 steps: halves hcur and hcur+1 are
   // resident and pos < 256*(hcur+1) holds at every check, and 4 steps read
@@ -339,8 +366,8 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
 #pragma unroll
           for (int q = 4 * sb; q < 4 * sb + 4; ++q) {
             const uint32_t step = 8 * b + q;
-            if (step >= steps) break;
-            if (step < full) dstep(std::false_type{}, rr, q);
+            if (step >= steps) dskip(rr, q);
+            else if (step < full) dstep(std::false_type{}, rr, q);
             else dstep(std::true_type{}, rr, q);
           }
           refill(rr);
@@ -353,7 +380,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
 #pragma unroll
       for (int k = 0; k < E; ++k) {
         uint64_t v;
-        if (mode[k] == LTC_MODE_RANS) v = *reinterpret_cast<const uint64_t*>(&stage[slot_of[k]][8 * lane]);
+        if (mode[k] == LTC_MODE_RANS) v = stage_bytes(slot_of[k]);
         else if (mode[k] == LTC_MODE_RAW) v = rawv[k];
         else v = 0x0101010101010101ull * cval[k];
         pl[0][k] = (uint32_t)v;
