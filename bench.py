@@ -6,6 +6,12 @@ in HBM: batch compress (histogram, normalise, rANS encode, scan, pack),
 batch decompress (validate, decode, inverse regroup and reorder), and the
 CRC-32 of every blob in 16 KiB chunks.  Prints one JSON line.
 
+compress/decompress/CRC throughputs come from HIP events between the three
+calls of the timed steps; per-kernel times (kernel_ms, roofline) come from a
+separate pass that launches the kernels one by one on one stream.  With
+--isolated the timed steps run that way too (the mode the committed
+rocprofv3 kernel summary is taken in).
+
 Default workload: 28 BF16 tensors shaped like four Llama-3-8B-style layers
 (1.74 GB), generated on the GPU from a fixed seed (see workloads.py).
 """
@@ -37,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all, max 16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB (HBM counter calibration)")
+    ap.add_argument("--isolated", action="store_true",
+                    help="run every step kernel by kernel on one stream (for per-kernel profiles)")
     return ap.parse_args()
 
 
@@ -214,19 +222,32 @@ def main():
     ev_d = hip.events(3)
     ev_x = hip.events(2)
 
-    def step(prof):
+    ev_p = hip.events(4)
+
+    def step(prof, phases=False):
+        """One pass of the hot path.  prof: kernel by kernel on one stream with
+        events between the kernels; otherwise a compress call over many chunks
+        runs its chunk groups on several streams (library-internal)."""
+        if phases:
+            hip.record(ev_p[0], sptr)
         ltc.compress_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, blob_ptrs, caps, sizes.data_ptr(),
                          ws.data_ptr(), ws_n, events=ev_c if prof else None)
+        if phases:
+            hip.record(ev_p[1], sptr)
         ltc.decompress_raw(headers, blob_ptrs, bsz, out_ptrs, nbytes, status.data_ptr(),
                            events=ev_d if prof else None)
         if prof:
             hip.record(ev_x[0], sptr)
+        if phases:
+            hip.record(ev_p[2], sptr)
         ltc.crc32_raw(blob_ptrs, bsz, CRC_CHUNK, crc_ptrs)
         if prof:
             hip.record(ev_x[1], sptr)
+        if phases:
+            hip.record(ev_p[3], sptr)
 
     for _ in range(max(1, args.warmup)):
-        step(False)
+        step(args.isolated)
     torch.cuda.synchronize()
     # correctness of what is timed: sizes stable, status OK, exact round trip
     assert sizes.cpu().tolist() == bsz, "blob sizes changed between steps"
@@ -240,16 +261,25 @@ def main():
     start_ev = hip.events(2)
     hip.record(start_ev[0], sptr)
     for _ in range(args.steps):
-        step(False)
+        step(args.isolated)
     hip.record(start_ev[1], sptr)
     torch.cuda.synchronize()
     wall = time.time() - t_wall
     ms_step = hip.ms(start_ev[0], start_ev[1]) / args.steps
 
+    # phase times of the same steps, with events between the three calls
+    reps = max(3, min(args.steps, 10))
+    ph = [0.0, 0.0, 0.0]
+    for _ in range(reps):
+        step(args.isolated, phases=True)
+        torch.cuda.synchronize()
+        for i in range(3):
+            ph[i] += hip.ms(ev_p[i], ev_p[i + 1]) / reps
+    t_comp, t_dec, t_crc = ph
+
     # per-kernel durations (same work, events between the kernels)
     k = {"k_hist": 0.0, "k_encode": 0.0, "k_scan": 0.0, "k_pack": 0.0, "k_decode": 0.0,
          "k_decode_multi": 0.0, "k_crc32": 0.0}
-    reps = max(3, min(args.steps, 10))
     for _ in range(reps):
         step(True)
         torch.cuda.synchronize()
@@ -261,9 +291,6 @@ def main():
         k["k_decode_multi"] += hip.ms(ev_d[1], ev_d[2])
         k["k_crc32"] += hip.ms(ev_x[0], ev_x[1])
     k = {n: v / reps for n, v in k.items()}
-    t_comp = k["k_hist"] + k["k_encode"] + k["k_scan"] + k["k_pack"]
-    t_dec = k["k_decode"] + k["k_decode_multi"]
-    t_crc = k["k_crc32"]
 
     # algorithmic bytes per launch (what the method must move):
     #   k_decode reads the blob and writes the original bytes: B + N
@@ -292,13 +319,17 @@ def main():
         "data": "synthetic",
         "config": {**desc, "global_batch": count, "orig_bytes": N, "blob_bytes": B,
                    "chunk_bytes": CHUNK, "passthrough_threshold": THRESHOLD,
-                   "crc_chunk_bytes": CRC_CHUNK, "parallelism": "single GPU"},
+                   "crc_chunk_bytes": CRC_CHUNK, "parallelism": "single GPU",
+                   "launch": "kernel by kernel, one stream" if args.isolated
+                             else "compress in 4 chunk groups on 4 streams"},
         "decompress_gbs": round(N / (t_dec * 1e-3) / 1e9, 2),
         "compress_gbs": round(N / (t_comp * 1e-3) / 1e9, 2),
         "crc32_blob_gbs": round(B / (t_crc * 1e-3) / 1e9, 2),
         "ratio": round(B / N, 5),
         "decompress_roofline_frac": round((N + B) / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "compress_roofline_frac": round((N + B) / (t_comp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "phase_ms": {"compress": round(t_comp, 4), "decompress": round(t_dec, 4),
+                     "crc32": round(t_crc, 4)},
         "kernel_ms": {n: round(v, 4) for n, v in k.items()},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -18,13 +18,26 @@
  *
  * OWNERSHIP AND ASYNCHRONY.  Arguments named d_* are device pointers, h_*
  * host pointers.  The caller allocates every buffer and owns the stream.
- * The library allocates no memory, creates no context and never
+ * The library allocates no device memory, creates no context and never
  * synchronises: work is enqueued on `stream` and the call returns at once.
  * Results that only the device knows (*d_blob_nbytes, *d_status) are written
  * to device memory; read them after synchronising the stream.  Argument
  * errors the host can see are returned before anything is enqueued.  A HIP
  * launch failure returns LTC_ERR_HIP.  Calls on different streams are
- * independent; the library has no mutable global state.
+ * independent.
+ *
+ * PIPELINED COMPRESSION.  A compress call over 512 chunks or more (all
+ * tensors of a batch together) splits its chunks into four chunk-ordered
+ * groups: the first runs on `stream`, the others on internal streams that
+ * wait for `stream` at the call and that `stream` waits for before anything
+ * enqueued after the call, so the call still behaves as work on `stream`.
+ * One group's compute-bound encoding then overlaps another's memory-bound
+ * passes.  The groups' offset scans run in chunk order, so blobs are the same
+ * as from one group.  The internal streams (default priority) and events
+ * are the library's only state: created once per device on first use, kept
+ * until the process ends, and used under a lock while a call enqueues.  A
+ * stream of another device than the current one, or the *_prof variants,
+ * run all chunks on `stream` alone.
  *
  * BLOB FORMAT v1 (byte exact; all integers little-endian).
  *   dtype codes: LTC_U8 (element 1 byte), LTC_BF16, LTC_FP16 (2 bytes),
@@ -196,8 +209,9 @@ typedef struct {
 } ltc_stats;
 int ltc_blob_stats(const void* h_prefix, uint64_t h_nbytes, ltc_stats* out);
 
-/* Profiling variants: identical work and results, plus hipEventRecord on
- * `stream` around each kernel so a caller can time one kernel alone.
+/* Profiling variants: identical work and results, all on `stream` kernel by
+ * kernel (never pipelined), plus hipEventRecord on `stream` around each kernel
+ * so a caller can time one kernel alone.
  * Compress: 5 events (before k_hist, before k_encode, before k_scan, before
  * k_pack, after k_pack).  Decompress: 3 events (before the single-table
  * decode kernel, between it and the multi-table one, after). */

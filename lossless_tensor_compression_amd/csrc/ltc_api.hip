@@ -4,6 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "ltc_internal.h"
 #include "ltc_launch.h"
 
@@ -12,6 +15,70 @@ namespace {
 
 constexpr uint64_t kAlign = 256;
 constexpr uint32_t kWordsGranule = 1024;
+
+// ---- pipelined compression
+// A compress call over at least kPipeMinChunks chunks splits them into
+// kPipeGroups chunk-ordered groups.  Group 0 runs on the caller's stream, the
+// others on internal streams forked from it and joined back to it, so one
+// group's compute-bound encoding overlaps another's memory-bound histogram and
+// packing.  The groups' scans run in chunk order (each waits for the previous
+// one), so offsets and blobs are the same as with one group.  The streams
+// (default priority, non-blocking) and events are created once per device on
+// first use and kept until the process ends; the enqueue is serialised.
+constexpr int kPipeGroups = 4;
+constexpr uint64_t kPipeMinChunks = 512;
+
+struct PipeRes {
+  hipStream_t s[kPipeGroups] = {};
+  hipEvent_t fork = nullptr, scan[kPipeGroups] = {}, done[kPipeGroups] = {};
+  bool ok = false;
+};
+std::mutex g_pipe_mu;
+std::vector<PipeRes*> g_pipe;  // per device
+
+// the current device's streams and events; call with g_pipe_mu held
+PipeRes* pipe_res(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  hipDevice_t sdev = 0;  // the caller's stream must belong to the current device
+  if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return nullptr;
+  if ((int)g_pipe.size() <= dev) g_pipe.resize(dev + 1, nullptr);
+  if (!g_pipe[dev]) {
+    PipeRes* r = new PipeRes();
+    bool ok = hipEventCreateWithFlags(&r->fork, hipEventDisableTiming) == hipSuccess;
+    for (int g = 0; g < kPipeGroups; ++g) {
+      if (g > 0) ok = ok && hipStreamCreateWithFlags(&r->s[g], hipStreamNonBlocking) == hipSuccess;
+      ok = ok && hipEventCreateWithFlags(&r->scan[g], hipEventDisableTiming) == hipSuccess;
+      ok = ok && hipEventCreateWithFlags(&r->done[g], hipEventDisableTiming) == hipSuccess;
+    }
+    r->ok = ok;
+    g_pipe[dev] = r;
+  }
+  return g_pipe[dev]->ok ? g_pipe[dev] : nullptr;
+}
+
+// all chunks on one stream, or groups as above
+hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipEvent_t* ev) {
+  const uint64_t total = t.total_chunks;
+  t.c_begin = 0;
+  t.c_end = total;
+  if (ev || total < kPipeMinChunks) return launch_compress(t, w, stream, ev);
+  std::lock_guard<std::mutex> lock(g_pipe_mu);
+  PipeRes* r = pipe_res(stream);
+  if (!r) return launch_compress(t, w, stream, nullptr);
+  hipError_t err = hipEventRecord(r->fork, stream);
+  for (int g = 1; g < kPipeGroups && err == hipSuccess; ++g) err = hipStreamWaitEvent(r->s[g], r->fork, 0);
+  for (int g = 0; g < kPipeGroups && err == hipSuccess; ++g) {
+    CTable tg = t;
+    tg.c_begin = total * g / kPipeGroups;
+    tg.c_end = total * (g + 1) / kPipeGroups;
+    hipStream_t st = g == 0 ? stream : r->s[g];
+    err = launch_compress(tg, w, st, nullptr, g > 0 ? r->scan[g - 1] : nullptr, r->scan[g]);
+    if (err == hipSuccess && g > 0) err = hipEventRecord(r->done[g], st);
+  }
+  for (int g = 1; g < kPipeGroups && err == hipSuccess; ++g) err = hipStreamWaitEvent(stream, r->done[g], 0);
+  return err;
+}
 
 uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
@@ -145,7 +212,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   w.offsets = reinterpret_cast<uint64_t*>(ws + l.offsets);
   w.blob_nbytes = reinterpret_cast<uint64_t*>(ws + l.blobn);
   w.words = reinterpret_cast<uint16_t*>(ws + l.words);
-  return launch_compress(t, w, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+  return run_compress(t, w, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 }
 
 uint64_t rd64(const uint8_t* p) {

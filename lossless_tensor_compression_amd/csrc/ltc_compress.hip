@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   constexpr uint32_t kWords = E * 128 * kHistCopies;
   __shared__ uint32_t hs[kWords];
   __shared__ uint32_t hf[E * 256];
-  const uint64_t g = blockIdx.x;
+  const uint64_t g = t.c_begin + blockIdx.x;
   const int j = find_job(t, g);
   const CJob& job = t.jobs[j];
   const uint64_t c = g - job.chunk0;
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   __shared__ __attribute__((aligned(16))) uint16_t ring[U][kRingWords + 64];
   const uint32_t lane = lane_id();
   const uint32_t k = blockIdx.x % E;
-  const uint64_t g0 = (uint64_t)(blockIdx.x / E) * U;
+  const uint64_t g0 = t.c_begin + (uint64_t)(blockIdx.x / E) * U;
   const uint32_t wcap = t.wcap;
 
   bool on[U];
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     n[u] = full[u] = wlimit[u] = wo[u] = lo[u] = hi[u] = 0;
     src[u] = nullptr;
     const uint64_t g = g0 + u;
-    if (g >= t.total_chunks) continue;
+    if (g >= t.c_end) continue;
     const uint64_t s = g * E + k;
     const uint32_t info = w.sinfo[4 * s + 1];
     if ((info & 0xFFu) != kModeCand) continue;
@@ -576,15 +576,29 @@ __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int o) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// One workgroup per tensor: exclusive scan of the 16-byte-aligned payload
+// sizes of the tensor's streams inside this launch's chunk range.  A
+// pipelined call scans its groups in chunk order; the running offset passes
+// from one group to the next through blob_nbytes[j], and the group holding
+// the tensor's last chunk writes the blob size and the header.
 __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32_t E) {
   __shared__ uint64_t wave_tot[kScanThreads / 64];
   const int j = blockIdx.x;
   const CJob& job = t.jobs[j];
-  const uint64_t s0 = job.chunk0 * E;
-  const uint64_t S = (uint64_t)job.nchunks * E;
-  const uint64_t base = kHeader + kDirEntry * S;
+  uint64_t c_lo = max(t.c_begin, job.chunk0);
+  uint64_t c_hi = min(t.c_end, job.chunk0 + job.nchunks);
+  if (job.nchunks == 0) {  // an empty tensor is only a header: the first group writes it
+    if (t.c_begin != 0) return;
+    c_lo = c_hi = job.chunk0;
+  } else if (c_lo >= c_hi) {
+    return;  // no chunk of this tensor in this launch
+  }
+  const bool first = c_lo == job.chunk0, final = c_hi == job.chunk0 + job.nchunks;
+  const uint64_t s0 = c_lo * E;
+  const uint64_t S = (c_hi - c_lo) * E;
+  const uint64_t base = kHeader + kDirEntry * (uint64_t)job.nchunks * E;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
-  uint64_t running = base;
+  uint64_t running = first ? base : w.blob_nbytes[j];
   for (uint64_t tile = 0; tile < S; tile += 4 * kScanThreads) {
     uint64_t sz[4], local = 0;
 #pragma unroll
@@ -616,10 +630,9 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
     running += tile_total;
     __syncthreads();
   }
-  if (tid == 0) {
-    w.blob_nbytes[j] = running;
-    *job.blob_nbytes_out = running;
-  }
+  if (tid == 0) w.blob_nbytes[j] = running;
+  if (!final) return;
+  if (tid == 0) *job.blob_nbytes_out = running;
   if (tid < 4) {  // header
     uint4 v;
     if (tid == 0)
@@ -712,7 +725,7 @@ __device__ void write_rans(uint8_t* dst, uint64_t s, uint32_t info, uint32_t siz
 template <int DT>
 __global__ __launch_bounds__(kPackThreads) void k_pack(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
-  const uint64_t g = blockIdx.x;
+  const uint64_t g = t.c_begin + blockIdx.x;
   const int j = find_job(t, g);
   const CJob& job = t.jobs[j];
   const uint64_t c = g - job.chunk0;
@@ -762,9 +775,10 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(CTable t, CWork w) {
 
 template <int DT>
 static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t st,
-                                    const hipEvent_t* ev) {
+                                    const hipEvent_t* ev, hipEvent_t scan_after,
+                                    hipEvent_t scan_done) {
   constexpr int E = Dt<DT>::E;
-  const uint64_t chunks = t.total_chunks;
+  const uint64_t chunks = t.c_end - t.c_begin;
   record(ev, 0, st);
   if (chunks) hipLaunchKernelGGL(k_hist<DT>, dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
   record(ev, 1, st);
@@ -772,19 +786,22 @@ static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t
     hipLaunchKernelGGL(k_encode<DT>, dim3((uint32_t)((chunks + kEncStreams - 1) / kEncStreams * E)), dim3(64), 0,
                        st, t, w);
   record(ev, 2, st);
+  if (scan_after) (void)hipStreamWaitEvent(st, scan_after, 0);
   hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E);
+  if (scan_done) (void)hipEventRecord(scan_done, st);
   record(ev, 3, st);
   if (chunks) hipLaunchKernelGGL(k_pack<DT>, dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
   record(ev, 4, st);
   return hipGetLastError();
 }
 
-hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev) {
+hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                           hipEvent_t scan_after, hipEvent_t scan_done) {
   switch (t.dtype) {
-    case LTC_U8: return launch_compress_t<LTC_U8>(t, w, st, ev);
-    case LTC_BF16: return launch_compress_t<LTC_BF16>(t, w, st, ev);
-    case LTC_FP16: return launch_compress_t<LTC_FP16>(t, w, st, ev);
-    case LTC_FP32: return launch_compress_t<LTC_FP32>(t, w, st, ev);
+    case LTC_U8: return launch_compress_t<LTC_U8>(t, w, st, ev, scan_after, scan_done);
+    case LTC_BF16: return launch_compress_t<LTC_BF16>(t, w, st, ev, scan_after, scan_done);
+    case LTC_FP16: return launch_compress_t<LTC_FP16>(t, w, st, ev, scan_after, scan_done);
+    case LTC_FP32: return launch_compress_t<LTC_FP32>(t, w, st, ev, scan_after, scan_done);
     default: return hipErrorInvalidValue;
   }
 }

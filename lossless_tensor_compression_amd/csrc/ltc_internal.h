@@ -78,6 +78,9 @@ struct CTable {
   uint64_t total_chunks;
   uint32_t vec16;      // every src 16-byte aligned and chunk_bytes % 16 == 0
   uint32_t dtype;
+  // the launch covers global chunks [c_begin, c_end) (a group of a pipelined
+  // call, or all of them)
+  uint64_t c_begin, c_end;
 };
 
 struct CWork {

@@ -5,8 +5,12 @@
 
 namespace ltc {
 
-// ev (optional): 5 events recorded around k_hist, k_encode, k_scan, k_pack
-hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev);
+// Launches k_hist, k_encode, k_scan and k_pack for chunks [t.c_begin,
+// t.c_end) on st.  ev (optional): 5 events recorded around the kernels.
+// scan_after (optional): the scan waits for it (the previous group's scan);
+// scan_done (optional): recorded right after the scan.
+hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                           hipEvent_t scan_after = nullptr, hipEvent_t scan_done = nullptr);
 
 // ev (optional): 3 events recorded around the single-table and the
 // multi-table decode kernels

@@ -257,3 +257,55 @@ def test_mixed_stream_pairs(ltc, nchunks):
     data = np.concatenate(parts)[: nchunks * chunk - 6]
     check_case(ltc, data, 1, chunk, label=f"mixed pairs {nchunks}")
     check_case(ltc, data[: data.size // 4 * 4], 3, chunk, label=f"mixed pairs fp32 {nchunks}")
+
+
+# ---- pipelined compression: calls over 512 chunks or more run in four
+# chunk-ordered groups on several streams; blobs must not change.
+
+@pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (2, 2048), (0, 512)])
+def test_grouped_single_tensor(ltc, dtype, chunk):
+    rng = np.random.default_rng(100 + dtype)
+    nbytes = 700 * chunk + 3 * 8  # 701 chunks, a ragged last one: four uneven groups
+    if dtype == 0:
+        data = rng.integers(0, 6, nbytes, dtype=np.uint8)
+        data[: nbytes // 3] = 7  # const chunks too
+    else:
+        x = rng.standard_normal(nbytes // 4) * np.repeat([0.02, 1e-3, 3.0], nbytes // 12 + 1)[: nbytes // 4]
+        x = x.astype(np.float32)
+        if dtype == 1:
+            data = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint8)
+            data = np.concatenate([data, data])[:nbytes]
+        elif dtype == 2:
+            data = np.concatenate([x.astype(np.float16).view(np.uint8)] * 2)[:nbytes]
+        else:
+            data = x.view(np.uint8)[:nbytes]
+        # every 5th chunk random bytes: a RAW and a coded stream in one pair
+        for c in range(0, nbytes // chunk, 5):
+            data[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
+    data = data[: nbytes // oracle.ELEM_BYTES[dtype] * oracle.ELEM_BYTES[dtype]]
+    check_case(ltc, data, dtype, chunk, label=f"grouped dtype {dtype}")
+
+
+def test_grouped_batch_with_empty_and_tiny(ltc):
+    """A batch whose tensors straddle the group boundaries, with an empty and
+    a one-element tensor; every blob must equal the single-tensor oracle blob."""
+    rng = np.random.default_rng(77)
+    chunk = 1024
+    sizes = (90000, 0, 1, 123457, 2, 40000, 250001, 17, 60000)
+    arrs = [(rng.standard_normal(n) * rng.choice([0.02, 1.0, 1e-4])).astype(np.float32) for n in sizes]
+    total_chunks = sum((a.nbytes + chunk - 1) // chunk for a in arrs)
+    assert total_chunks >= 512
+    ts = [to_gpu(a, 3) for a in arrs]
+    banner(f"grouped batch: {len(arrs)} tensors, {total_chunks} chunks")
+    blobs = ltc.compress_batch(ts, chunk)
+    for a, b in zip(arrs, blobs):
+        want = oracle.compress(a, 3, chunk)
+        got = to_np_bytes(b)
+        assert got.size == want.size and np.array_equal(got, want)
+    outs = ltc.decompress_batch(blobs)
+    for a, o in zip(arrs, outs):
+        assert np.array_equal(to_np_bytes(o), a.view(np.uint8))
+    # the same call twice on one stream, and grouped equals a repeat
+    again = ltc.compress_batch(ts, chunk)
+    for b1, b2 in zip(blobs, again):
+        assert torch.equal(b1, b2)
