@@ -345,7 +345,15 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     }
   };
 
-  for (uint32_t b = 0; b < nblk; ++b) {
+  // Output of NB blocks is written together: every wait on a load (a ring
+  // refill, the next block's RAW bytes) also waits for all older stores,
+  // since one counter covers both, so fewer store bursts mean fewer waits
+  // on store completion (measured: 4 blocks 0.74 ms, 1 or 2 blocks 0.89 ms
+  // for 13,312 BF16 chunks).
+  constexpr int NB = 4;
+  uint32_t obuf[NB][2 * E];
+  auto block = [&](uint32_t b, auto subc) {
+    constexpr int SUB = decltype(subc)::value;
     const uint32_t e0 = 512 * b + 8 * lane;
     uint64_t rawn[E];
 #pragma unroll
@@ -386,20 +394,11 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
         pl[0][k] = (uint32_t)v;
         pl[1][k] = (uint32_t)(v >> 32);
       }
-      uint32_t ow[2 * E];
+      uint32_t* ow = obuf[SUB];
       planes_to_words<DT>(pl[0], ow);
       planes_to_words<DT>(pl[1], ow + E);
-      uint8_t* op = dst + (uint64_t)e0 * E;
-      if (vec && e0 + 8 <= n) {
-        if constexpr (E == 1) {
-          *reinterpret_cast<uint2*>(op) = make_uint2(ow[0], ow[1]);
-        } else if constexpr (E == 2) {
-          *reinterpret_cast<uint4*>(op) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-        } else {
-          reinterpret_cast<uint4*>(op)[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-          reinterpret_cast<uint4*>(op)[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
-        }
-      } else {
+      if (!(vec && e0 + 8 <= n)) {  // a ragged or unaligned block: bytes, now
+        uint8_t* op = dst + (uint64_t)e0 * E;
         const uint32_t nb = (n - e0 < 8 ? n - e0 : 8) * E;
         for (uint32_t i = 0; i < nb; ++i) op[i] = (uint8_t)(ow[i / 4] >> (8 * (i & 3)));
       }
@@ -407,6 +406,30 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
 #pragma unroll
     for (int k = 0; k < E; ++k) rawv[k] = rawn[k];
     wave_sync();
+  };
+  // vector stores of block b's elements 8 lane .. 8 lane + 7
+  auto store_block = [&](uint32_t b, auto subc) {
+    constexpr int SUB = decltype(subc)::value;
+    const uint32_t e0 = 512 * b + 8 * lane;
+    if (!(e0 < n && vec && e0 + 8 <= n)) return;
+    const uint32_t* ow = obuf[SUB];
+    uint8_t* op = dst + (uint64_t)e0 * E;
+    if constexpr (E == 1) {
+      *reinterpret_cast<uint2*>(op) = make_uint2(ow[0], ow[1]);
+    } else if constexpr (E == 2) {
+      *reinterpret_cast<uint4*>(op) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    } else {
+      reinterpret_cast<uint4*>(op)[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      reinterpret_cast<uint4*>(op)[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+    }
+  };
+  for (uint32_t b = 0; b < nblk; b += NB) {
+    static_for<NB>([&](auto i) {
+      if (b + i < nblk) block(b + i, i);
+    });
+    static_for<NB>([&](auto i) {
+      if (b + i < nblk) store_block(b + i, i);
+    });
   }
   // ---- end checks: every coded stream consumed exactly its words and
   // returned to the initial state
