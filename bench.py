@@ -28,6 +28,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decompress GB/s (orig bytes, HBM-resident) + compress GB/s + ratio, BF16"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+# 32-bit integer VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64
+# VALU instruction occupies a 16-lane SIMD for 4 cycles)
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# integer operations one rANS encode step needs (table read, renormalisation
+# test, word emit, shift, quotient, remainder (multiply + subtract), scale by
+# M, two adds)
+ENC_OPS_PER_SYMBOL = 10
 CHUNK = 131072
 THRESHOLD = 0.95
 CRC_CHUNK = 16384
@@ -130,13 +137,16 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": n, "copy_read_plus_write_gbs": 2 * n / dt / 1e9}), flush=True)
 
 
-def traffic_from_profiles(kernel, launches_per_step):
+def traffic_from_profiles(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the summary is missing or the kernel source changed since."""
+    None when the summary is missing, was taken on another workload, or the
+    kernel source changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if rec.get("bench_workload") != workload:
+        return None
     src = os.path.join(ROOT, rec.get("source", ""))
     if not os.path.exists(src):
         return None
@@ -319,8 +329,27 @@ def main():
     algo = {"k_decode": B + N, "k_hist": N, "k_pack": B + N, "k_crc32": B, "k_encode": N,
             "k_scan": 0, "k_decode_multi": 0}
     dom = max((n for n in k if algo[n]), key=lambda n: k[n])
-    achieved = algo[dom] / (k[dom] * 1e-3) / 1e9
-    traffic = traffic_from_profiles(dom, 1)
+    traffic = traffic_from_profiles(dom, args.workload)
+    if dom == "k_encode":
+        # the encoder is bound by integer issue, not by HBM: count the
+        # operations of every symbol it codes (streams that end in RANS mode;
+        # every chunk of the bench workloads is full, so a stream holds
+        # CHUNK / E symbols)
+        e = ts[0].element_size()
+        coded = 0
+        for b, s in zip(blobs, bsz):
+            st = ltc.blob_stats(b[:s])
+            coded += sum(m["rans"] for m in st["modes"]) * (CHUNK // e)
+        achieved = coded * ENC_OPS_PER_SYMBOL / (k[dom] * 1e-3) / 1e12
+        roof = {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3),
+                "peak": round(ALU_PEAK_TOPS, 2), "unit": "Top/s",
+                "frac": round(achieved / ALU_PEAK_TOPS, 4), "traffic": traffic,
+                "coded_symbols": coded, "ops_per_symbol": ENC_OPS_PER_SYMBOL}
+    else:
+        achieved = algo[dom] / (k[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
     value = N / (ms_step * 1e-3) / 1e9
     rec = {
@@ -350,9 +379,7 @@ def main():
         "phase_ms": {"compress": round(t_comp, 4), "decompress": round(t_dec, 4),
                      "crc32": round(t_crc, 4)},
         "kernel_ms": {n: round(v, 4) for n, v in k.items()},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "roofline": roof,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
