@@ -6,8 +6,13 @@ in HBM: batch compress (histogram, normalise, rANS encode, scan, pack),
 batch decompress (validate, decode, inverse regroup and reorder), and the
 CRC-32 of every blob in 16 KiB chunks.  Prints one JSON line.
 
-compress/decompress/CRC throughputs come from HIP events between the three
-calls of the timed steps; per-kernel times (kernel_ms, roofline) come from a
+--crc fused (default): the step is compress_with_crc32 (the pack kernel
+checksums the payload as it writes it) then decompress.  --crc beside: plain
+compress, then the CRC kernel over the blobs on a second stream beside the
+decompression.
+
+compress/decompress/CRC throughputs come from HIP events between the calls,
+run one after another; per-kernel times (kernel_ms, roofline) come from a
 separate pass that launches the kernels one by one on one stream.  With
 --isolated the timed steps run that way too (the mode the committed
 rocprofv3 kernel summary is taken in).
@@ -52,6 +57,8 @@ def parse():
                     help="only run a device-to-device copy of 1 GiB (HBM counter calibration)")
     ap.add_argument("--isolated", action="store_true",
                     help="run every step kernel by kernel on one stream (for per-kernel profiles)")
+    ap.add_argument("--crc", default="fused", choices=["fused", "beside"],
+                    help="CRC-32 of the blobs computed while packing, or by its own kernel")
     return ap.parse_args()
 
 
@@ -236,18 +243,36 @@ def main():
     ncrc = [(s + CRC_CHUNK - 1) // CRC_CHUNK for s in bsz]
     crcs = torch.empty(sum(ncrc), dtype=torch.int32, device="cuda")
     crc_ptrs = [crcs.data_ptr() + 4 * sum(ncrc[:i]) for i in range(count)]
+    # compress_with_crc32 writes into capacity for the bound
+    fcap = [(c + CRC_CHUNK - 1) // CRC_CHUNK for c in caps]
+    fcrcs = torch.empty(sum(fcap), dtype=torch.int32, device="cuda")
+    fcrc_ptrs = [fcrcs.data_ptr() + 4 * sum(fcap[:i]) for i in range(count)]
+    ev_f = hip.events(6)
+    fused = args.crc == "fused"
+
+    def compress_crc(events=None):
+        ltc.compress_crc32_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, blob_ptrs, caps,
+                               sizes.data_ptr(), CRC_CHUNK, fcrc_ptrs, fcap, ws.data_ptr(), ws_n,
+                               events=events)
 
     ev_p = hip.events(4)
     side = torch.cuda.Stream()  # default priority
     ev_fork, ev_join = hip.events(2)
 
-    def step(prof, phases=False):
-        """One pass of the hot path.  prof or phases: the three calls one after
-        another on one stream (prof: kernel by kernel, with events between the
-        kernels).  Otherwise a compress call over many chunks runs its chunk
-        groups on several streams (library-internal), and the CRC-32 of the
-        blobs runs on a second stream beside the decompression, which does
-        not depend on it."""
+    def step(prof, phases=False, plain=False):
+        """One pass of the hot path.  Fused CRC (unless phases or plain):
+        compress_with_crc32 then decompress.  Otherwise compress, decompress
+        and the CRC kernel: with prof or phases one after another on one
+        stream (prof: kernel by kernel, with events between the kernels),
+        else the CRC-32 of the blobs runs on a second stream beside the
+        decompression, which does not depend on it.  A compress call over
+        many chunks runs its chunk groups on several streams
+        (library-internal) unless prof."""
+        if fused and not phases and not plain:
+            compress_crc(ev_f if prof else None)
+            ltc.decompress_raw(headers, blob_ptrs, bsz, out_ptrs, nbytes, status.data_ptr(),
+                               events=ev_d if prof else None)
+            return
         serial = prof or phases
         if phases:
             hip.record(ev_p[0], sptr)
@@ -283,6 +308,14 @@ def main():
     assert status.cpu().tolist() == [0] * count, f"decode status {status.cpu().tolist()}"
     for t, o in zip(ts, outs):
         assert torch.equal(t.contiguous().view(-1).view(torch.uint8), o), "round trip mismatch"
+    # both checksum paths agree on the blobs
+    compress_crc()
+    ltc.crc32_raw(blob_ptrs, bsz, CRC_CHUNK, crc_ptrs)
+    torch.cuda.synchronize()
+    for i in range(count):
+        a = crcs[sum(ncrc[:i]):sum(ncrc[:i + 1])]
+        b = fcrcs[sum(fcap[:i]):sum(fcap[:i]) + ncrc[i]]
+        assert torch.equal(a, b), f"CRC-32 of blob {i} differs between the two paths"
 
     # timed region: K whole steps bracketed by synchronisation
     torch.cuda.synchronize()
@@ -305,12 +338,20 @@ def main():
         for i in range(3):
             ph[i] += hip.ms(ev_p[i], ev_p[i + 1]) / reps
     t_comp, t_dec, t_crc = ph
+    # compress_with_crc32 alone (the fused path's first call)
+    t_fused = 0.0
+    for _ in range(reps):
+        hip.record(ev_p[0], sptr)
+        compress_crc()
+        hip.record(ev_p[1], sptr)
+        torch.cuda.synchronize()
+        t_fused += hip.ms(ev_p[0], ev_p[1]) / reps
 
     # per-kernel durations (same work, events between the kernels)
     k = {"k_hist": 0.0, "k_encode": 0.0, "k_scan": 0.0, "k_pack": 0.0, "k_decode": 0.0,
          "k_decode_multi": 0.0, "k_crc32": 0.0}
     for _ in range(reps):
-        step(True)
+        step(True, plain=True)
         torch.cuda.synchronize()
         k["k_hist"] += hip.ms(ev_c[0], ev_c[1])
         k["k_encode"] += hip.ms(ev_c[1], ev_c[2])
@@ -320,6 +361,12 @@ def main():
         k["k_decode_multi"] += hip.ms(ev_d[1], ev_d[2])
         k["k_crc32"] += hip.ms(ev_x[0], ev_x[1])
     k = {n: v / reps for n, v in k.items()}
+    kf = {"k_pack_crc": 0.0, "k_crc32_finish": 0.0}
+    for _ in range(reps):
+        compress_crc(ev_f)
+        torch.cuda.synchronize()
+        kf["k_pack_crc"] += hip.ms(ev_f[3], ev_f[4]) / reps
+        kf["k_crc32_finish"] += hip.ms(ev_f[4], ev_f[5]) / reps
 
     # algorithmic bytes per launch (what the method must move):
     #   k_decode reads the blob and writes the original bytes: B + N
@@ -368,17 +415,21 @@ def main():
         "config": {**desc, "global_batch": count, "orig_bytes": N, "blob_bytes": B,
                    "chunk_bytes": CHUNK, "passthrough_threshold": THRESHOLD,
                    "crc_chunk_bytes": CRC_CHUNK, "parallelism": "single GPU",
+                   "crc": "computed while packing (compress_with_crc32)" if fused
+                          else "own kernel beside decompress",
                    "launch": "kernel by kernel, one stream" if args.isolated
-                             else "compress in 4 chunk groups on 4 streams; CRC-32 beside decompress"},
+                             else "compress in 4 chunk groups on 4 streams"},
         "decompress_gbs": round(N / (t_dec * 1e-3) / 1e9, 2),
         "compress_gbs": round(N / (t_comp * 1e-3) / 1e9, 2),
         "crc32_blob_gbs": round(B / (t_crc * 1e-3) / 1e9, 2),
         "ratio": round(B / N, 5),
         "decompress_roofline_frac": round((N + B) / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "compress_roofline_frac": round((N + B) / (t_comp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "compress_with_crc32_gbs": round(N / (t_fused * 1e-3) / 1e9, 2),
         "phase_ms": {"compress": round(t_comp, 4), "decompress": round(t_dec, 4),
-                     "crc32": round(t_crc, 4)},
-        "kernel_ms": {n: round(v, 4) for n, v in k.items()},
+                     "crc32": round(t_crc, 4), "compress_with_crc32": round(t_fused, 4)},
+        "kernel_ms": {**{n: round(v, 4) for n, v in k.items()},
+                      **{n: round(v, 4) for n, v in kf.items()}},
         "roofline": roof,
         "wall_s_timed": round(wall, 3),
     }

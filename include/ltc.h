@@ -196,6 +196,37 @@ int ltc_crc32_chunks(const void* d_src, uint64_t nbytes, uint32_t chunk_bytes,
 int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
                            uint32_t chunk_bytes, uint32_t* const* h_crc_ptrs, hipStream_t stream);
 
+/* Compress and checksum the blob in one call (cuZipNN 0.1.0 "API",
+ * compress_tensor_with_crc32): the same blob as ltc_compress, and in d_crc
+ * the CRC-32 of every checksum_chunk_bytes-byte chunk of the blob, the last
+ * one possibly shorter, exactly as ltc_crc32_chunks would give for the
+ * finished blob.  The blob size is known only on the device, so d_crc must
+ * hold crc_capacity >= ceil(ltc_compress_bound() / checksum_chunk_bytes)
+ * u32 values; the first ceil(*d_blob_nbytes / checksum_chunk_bytes) are
+ * written and the rest are left as they were.  When checksum_chunk_bytes is a
+ * multiple of 1 KiB and at most 1 MiB, the payload is checksummed while it
+ * is written (k_pack) and only the chunks holding header or directory bytes
+ * and the blob's last chunk are read back; otherwise the CRC kernel reads
+ * the blob back after packing.  The workspace is the same
+ * as for ltc_compress.  Errors: those of ltc_compress, INVALID_ARGUMENT for
+ * checksum_chunk_bytes = 0 or a NULL or misaligned d_crc, CAPACITY for a
+ * short crc_capacity. */
+int ltc_compress_with_crc32(const void* d_src, uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                            double passthrough_threshold, void* d_blob, uint64_t blob_capacity,
+                            uint64_t* d_blob_nbytes, uint32_t checksum_chunk_bytes, uint32_t* d_crc,
+                            uint64_t crc_capacity, void* d_ws, uint64_t ws_nbytes,
+                            hipStream_t stream);
+
+/* Batch form: tensor i's checksums go to h_crc_ptrs[i] (a device pointer in
+ * a host array) with h_crc_capacity[i] entries; the workspace is
+ * ltc_compress_batch_workspace_size(). */
+int ltc_compress_batch_with_crc32(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                                  int dtype, uint32_t chunk_bytes, double passthrough_threshold,
+                                  void* const* h_blob_ptrs, const uint64_t* h_blob_capacity,
+                                  uint64_t* d_blob_nbytes, uint32_t checksum_chunk_bytes,
+                                  uint32_t* const* h_crc_ptrs, const uint64_t* h_crc_capacity,
+                                  void* d_ws, uint64_t ws_nbytes, hipStream_t stream);
+
 /* Statistics from a host copy of the header and directory (the first
  * payload_base bytes): per stream-index mode counts and payload bytes (the
  * per-byte-group layout of ZipNN's Table II) and the whole-blob ratio. */
@@ -213,13 +244,22 @@ int ltc_blob_stats(const void* h_prefix, uint64_t h_nbytes, ltc_stats* out);
  * kernel (never pipelined), plus hipEventRecord on `stream` around each kernel
  * so a caller can time one kernel alone.
  * Compress: 5 events (before k_hist, before k_encode, before k_scan, before
- * k_pack, after k_pack).  Decompress: 3 events (before the single-table
- * decode kernel, between it and the multi-table one, after). */
+ * k_pack, after k_pack); compress with CRC-32: 6, the sixth after the CRC
+ * kernel that finishes the checksums.  Decompress: 3 events (before the
+ * single-table decode kernel, between it and the multi-table one, after). */
 int ltc_compress_batch_prof(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
                             int dtype, uint32_t chunk_bytes, double passthrough_threshold,
                             void* const* h_blob_ptrs, const uint64_t* h_blob_capacity,
                             uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
                             hipStream_t stream, const hipEvent_t* h_events);
+int ltc_compress_batch_with_crc32_prof(int count, const void* const* h_src_ptrs,
+                                       const uint64_t* h_nbytes, int dtype, uint32_t chunk_bytes,
+                                       double passthrough_threshold, void* const* h_blob_ptrs,
+                                       const uint64_t* h_blob_capacity, uint64_t* d_blob_nbytes,
+                                       uint32_t checksum_chunk_bytes, uint32_t* const* h_crc_ptrs,
+                                       const uint64_t* h_crc_capacity, void* d_ws,
+                                       uint64_t ws_nbytes, hipStream_t stream,
+                                       const hipEvent_t* h_events);
 int ltc_decompress_batch_prof(int count, const void* const* h_headers,
                               const void* const* h_blob_ptrs, const uint64_t* h_blob_nbytes,
                               void* const* h_dst_ptrs, const uint64_t* h_dst_capacity,

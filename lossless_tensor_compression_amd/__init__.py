@@ -10,6 +10,8 @@ API (names as in cuZipNN 0.1.0, "API", and the C ABI):
   compress(t, chunk_bytes=131072, passthrough_threshold=0.95) -> uint8 blob
   decompress(blob, shape=None) -> tensor of the recorded dtype
   crc32_chunks(t, chunk_bytes=16384) -> int32 tensor holding CRC-32 bits
+  compress_with_crc32(t, ..., checksum_chunk_bytes=16384) -> (blob, CRC-32 of
+      the blob's chunks), the checksums computed while the blob is written
   compress_batch / decompress_batch for many tensors in one launch sequence
   blob_info / blob_stats for host-side inspection of a blob's header
 """
@@ -79,6 +81,12 @@ def lib():
         L.ltc_compress_batch.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp, vp, u64, vp]
         L.ltc_compress_batch_prof.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp, vp,
                                               u64, vp, pvp]
+        L.ltc_compress_with_crc32.argtypes = [vp, u64, i32, u32, dbl, vp, u64, vp, u32, vp, u64,
+                                              vp, u64, vp]
+        L.ltc_compress_batch_with_crc32.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp,
+                                                    u32, pvp, pu64, vp, u64, vp]
+        L.ltc_compress_batch_with_crc32_prof.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64,
+                                                         vp, u32, pvp, pu64, vp, u64, vp, pvp]
         L.ltc_blob_info.argtypes = [ctypes.c_char_p, u64, ctypes.POINTER(Info)]
         L.ltc_decompress.argtypes = [ctypes.c_char_p, vp, u64, vp, u64, vp, vp]
         L.ltc_decompress_batch.argtypes = [i32, pvp, pvp, pu64, pvp, pu64, vp, vp]
@@ -88,6 +96,8 @@ def lib():
         L.ltc_blob_stats.argtypes = [ctypes.c_char_p, u64, ctypes.POINTER(Stats)]
         for name in ("ltc_compress_workspace_size", "ltc_compress_batch_workspace_size",
                      "ltc_compress", "ltc_compress_batch", "ltc_compress_batch_prof",
+                     "ltc_compress_with_crc32", "ltc_compress_batch_with_crc32",
+                     "ltc_compress_batch_with_crc32_prof",
                      "ltc_blob_info", "ltc_decompress", "ltc_decompress_batch",
                      "ltc_decompress_batch_prof", "ltc_crc32_chunks", "ltc_crc32_chunks_batch",
                      "ltc_blob_stats"):
@@ -146,6 +156,21 @@ def compress_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blob_ptrs
         _check(lib().ltc_compress_batch_prof(*args, _ptrs(events)), "compress")
 
 
+def compress_crc32_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blob_ptrs, caps,
+                       nbytes_out_ptr, crc_chunk_bytes, crc_ptrs, crc_caps, ws_ptr, ws_nbytes,
+                       stream=None, events=None):
+    """Pointer-level batch compress plus CRC-32 of each blob (6 events with
+    `events`)."""
+    count = len(src_ptrs)
+    args = [count, _ptrs(src_ptrs), _u64s(nbytes), dtype_code, chunk_bytes, threshold,
+            _ptrs(blob_ptrs), _u64s(caps), ctypes.c_void_p(nbytes_out_ptr), crc_chunk_bytes,
+            _ptrs(crc_ptrs), _u64s(crc_caps), ctypes.c_void_p(ws_ptr), ws_nbytes, _stream(stream)]
+    if events is None:
+        _check(lib().ltc_compress_batch_with_crc32(*args), "compress_with_crc32")
+    else:
+        _check(lib().ltc_compress_batch_with_crc32_prof(*args, _ptrs(events)), "compress_with_crc32")
+
+
 def decompress_raw(headers, blob_ptrs, blob_nbytes, dst_ptrs, caps, status_ptr, stream=None,
                    events=None):
     """Pointer-level batch decompress on `stream`; headers are 64-byte host bytes."""
@@ -181,6 +206,47 @@ def compress_batch(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
                  [b.data_ptr() for b in blobs], caps, sizes.data_ptr(), ws.data_ptr(), ws.numel())
     host_sizes = sizes.cpu().tolist()
     return [b[:s] for b, s in zip(blobs, host_sizes)]
+
+
+def compress_batch_with_crc32(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
+                              passthrough_threshold=DEFAULT_THRESHOLD,
+                              checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):
+    """(blobs, checksums): the blobs of compress_batch and, per blob, the
+    CRC-32 of each checksum_chunk_bytes-byte chunk (int32 GPU tensors holding
+    the CRC bits)."""
+    if not 1 <= len(tensors) <= BATCH_MAX:
+        raise ValueError(f"1..{BATCH_MAX} tensors per batch")
+    ts = [_flat_bytes(t) for t in tensors]
+    code = DTYPE_CODE[ts[0].dtype]
+    if any(DTYPE_CODE[t.dtype] != code for t in ts):
+        raise ValueError("one dtype per batch")
+    if checksum_chunk_bytes <= 0:
+        raise LTCError(-1, "checksum_chunk_bytes")
+    dev = ts[0].device
+    nbytes = [t.numel() * t.element_size() for t in ts]
+    caps = [compress_bound(n, code, chunk_bytes) for n in nbytes]
+    if any(c == 0 for c in caps):
+        raise LTCError(-1, "compress_bound")
+    blobs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
+    ccaps = [(c + checksum_chunk_bytes - 1) // checksum_chunk_bytes for c in caps]
+    crcs = [torch.empty(n, dtype=torch.int32, device=dev) for n in ccaps]
+    ws_n = workspace_size(nbytes, code, chunk_bytes)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+    sizes = torch.zeros(len(ts), dtype=torch.int64, device=dev)
+    compress_crc32_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
+                       [b.data_ptr() for b in blobs], caps, sizes.data_ptr(), checksum_chunk_bytes,
+                       [c.data_ptr() for c in crcs], ccaps, ws.data_ptr(), ws.numel())
+    host_sizes = sizes.cpu().tolist()
+    return ([b[:s] for b, s in zip(blobs, host_sizes)],
+            [c[:(s + checksum_chunk_bytes - 1) // checksum_chunk_bytes] for c, s in zip(crcs, host_sizes)])
+
+
+def compress_with_crc32(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
+                        checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):
+    """(blob, checksums) of one GPU tensor (cuZipNN's compress_tensor_with_crc32)."""
+    blobs, crcs = compress_batch_with_crc32([t], chunk_bytes, passthrough_threshold,
+                                            checksum_chunk_bytes)
+    return blobs[0], crcs[0]
 
 
 def compress(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD):

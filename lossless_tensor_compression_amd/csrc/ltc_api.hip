@@ -82,6 +82,27 @@ hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipE
 
 uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
+uint32_t gf2_mulmod_host(uint32_t a, uint32_t b) {
+  uint32_t r = 0;
+  for (int i = 0; i < 32; ++i) {
+    if (a & (0x80000000u >> i)) r ^= b;
+    b = (b >> 1) ^ (0xEDB88320u & (0u - (b & 1u)));
+  }
+  return r;
+}
+
+// x^(8n) mod P in the reflected representation (bit 31 - d = x^d)
+uint32_t xpow8(uint64_t n) {
+  uint32_t r = 0x80000000u, sq = 0x00800000u;
+  while (n) {
+    if (n & 1) r = gf2_mulmod_host(r, sq);
+    sq = gf2_mulmod_host(sq, sq);
+    n >>= 1;
+  }
+  return r;
+}
+
+
 uint32_t elem_bytes(int dtype) {
   switch (dtype) {
     case LTC_U8: return 1;
@@ -121,10 +142,11 @@ uint32_t words_capacity(uint32_t chunk_bytes, uint32_t e) {
 }
 
 struct Layout {
-  uint64_t sinfo, freq, states, offsets, blobn, words, total;
+  uint64_t sinfo, freq, states, offsets, blobn, frames, words, total;
 };
 
-Layout layout(uint64_t streams, int count, uint32_t wcap) {
+// frames: one u32 per KiB of every blob's bound (compress_with_crc32)
+Layout layout(uint64_t streams, int count, uint32_t wcap, uint64_t frames) {
   Layout l;
   uint64_t cur = 0;
   l.sinfo = cur;   cur = round_up(cur + 16 * streams, kAlign);
@@ -132,6 +154,7 @@ Layout layout(uint64_t streams, int count, uint32_t wcap) {
   l.states = cur;  cur = round_up(cur + 256 * streams, kAlign);
   l.offsets = cur; cur = round_up(cur + 8 * streams, kAlign);
   l.blobn = cur;   cur = round_up(cur + 8 * (uint64_t)count, kAlign);
+  l.frames = cur;  cur = round_up(cur + 4 * frames, kAlign);
   l.words = cur;   cur = round_up(cur + 2ull * wcap * streams, kAlign);
   l.total = cur;
   return l;
@@ -147,6 +170,12 @@ uint64_t bound_of(uint64_t nbytes, uint32_t e, uint32_t chunk_bytes) {
   return b;
 }
 
+uint64_t batch_frames(int count, const uint64_t* nbytes, uint32_t e, uint32_t chunk_bytes) {
+  uint64_t f = 0;
+  for (int i = 0; i < count; ++i) f += (bound_of(nbytes[i], e, chunk_bytes) + 1023) / 1024;
+  return f;
+}
+
 int64_t batch_streams(int count, const uint64_t* nbytes, uint32_t e, uint32_t chunk_bytes) {
   uint64_t chunks = 0;
   for (int i = 0; i < count; ++i) chunks += (nbytes[i] + chunk_bytes - 1) / chunk_bytes;
@@ -155,10 +184,17 @@ int64_t batch_streams(int count, const uint64_t* nbytes, uint32_t e, uint32_t ch
   return (int64_t)(chunks * e);
 }
 
+// checksums requested with a compress call (compress_with_crc32)
+struct CrcReq {
+  uint32_t chunk_bytes;      // K; 0: none
+  uint32_t* const* outs;     // per tensor, ceil(bound / K) entries at least
+  const uint64_t* caps;      // entries available per tensor
+};
+
 int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, int dtype,
                   uint32_t chunk_bytes, double theta, void* const* blobs, const uint64_t* caps,
                   uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes, hipStream_t stream,
-                  const hipEvent_t* ev) {
+                  const hipEvent_t* ev, const CrcReq& crc = CrcReq{0, nullptr, nullptr}) {
   if (count < 1 || count > kMaxJobs || !srcs || !nbytes || !blobs || !caps || !d_blob_nbytes)
     return LTC_ERR_INVALID_ARGUMENT;
   if (!(theta > 0.0 && theta <= 1.0)) return LTC_ERR_INVALID_ARGUMENT;
@@ -171,10 +207,18 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
     if (reinterpret_cast<uintptr_t>(blobs[i]) % 16) return LTC_ERR_INVALID_ARGUMENT;
     if (caps[i] < bound_of(nbytes[i], e, chunk_bytes)) return LTC_ERR_CAPACITY;
   }
+  if (crc.chunk_bytes) {
+    if (!crc.outs || !crc.caps) return LTC_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < count; ++i) {
+      if (!crc.outs[i] || reinterpret_cast<uintptr_t>(crc.outs[i]) % 4) return LTC_ERR_INVALID_ARGUMENT;
+      const uint64_t need = (bound_of(nbytes[i], e, chunk_bytes) + crc.chunk_bytes - 1) / crc.chunk_bytes;
+      if (crc.caps[i] < need) return LTC_ERR_CAPACITY;
+    }
+  }
   const int64_t streams = batch_streams(count, nbytes, e, chunk_bytes);
   if (streams < 0) return LTC_ERR_INVALID_ARGUMENT;
   const uint32_t wcap = words_capacity(chunk_bytes, e);
-  const Layout l = layout((uint64_t)streams, count, wcap);
+  const Layout l = layout((uint64_t)streams, count, wcap, batch_frames(count, nbytes, e, chunk_bytes));
   if (!d_ws || ws_nbytes < l.total || reinterpret_cast<uintptr_t>(d_ws) % kAlign)
     return LTC_ERR_WORKSPACE;
 
@@ -212,7 +256,61 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   w.offsets = reinterpret_cast<uint64_t*>(ws + l.offsets);
   w.blob_nbytes = reinterpret_cast<uint64_t*>(ws + l.blobn);
   w.words = reinterpret_cast<uint16_t*>(ws + l.words);
-  return run_compress(t, w, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+  if (!crc.chunk_bytes) return run_compress(t, w, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+
+  // compress_with_crc32: when checksum chunks are whole 1 KiB frames, k_pack
+  // accumulates the payload's frame remainders, k_crc_frames combines the
+  // full payload chunks from them, and k_crc32 reads back the leading chunks
+  // (header and directory) and each blob's last chunk; otherwise k_crc32
+  // reads back every chunk of the finished blobs.
+  const uint64_t K = crc.chunk_bytes;
+  const bool fused = crc_frames_usable(K);
+  uint32_t* frames = reinterpret_cast<uint32_t*>(ws + l.frames);
+  CrcArgs a;  // k_crc32
+  memset(&a, 0, sizeof(a));
+  a.count = (uint32_t)count;
+  a.chunk_bytes = K;
+  a.seg = round_up(K, 256) / 64;
+  for (int lv = 0; lv < 6; ++lv) a.lvl[lv] = xpow8(a.seg << lv);
+  a.init_full = gf2_mulmod_host(0xFFFFFFFFu, xpow8(K));
+  a.x1k = xpow8(1024);
+  a.tail_slot = fused ? 1u : 0u;
+  CrcArgs af = a;  // k_crc_frames
+  if (fused) {
+    t.crc = 1;
+    t.crc_frames = (uint32_t)(K / 1024);
+    for (int lv = 0; lv < 7; ++lv) t.crc_lvl[lv] = xpow8(16ull << lv);
+  }
+  uint64_t fcur = 0, scur = 0, ccur = 0;
+  for (int i = 0; i < count; ++i) {
+    const uint64_t bound = bound_of(nbytes[i], e, chunk_bytes);
+    const uint64_t chunks = (bound + K - 1) / K;
+    t.jobs[i].frames = frames + fcur;
+    CrcJob& jb = a.jobs[i];
+    jb.src = t.jobs[i].blob;
+    jb.out = crc.outs[i];
+    jb.len = d_blob_nbytes + i;
+    jb.frames = fused ? frames + fcur : nullptr;
+    jb.frames_from = kHeader + kDirEntry * (uint64_t)t.jobs[i].nchunks * e;
+    jb.lead = (jb.frames_from + K - 1) / K;
+    if (jb.lead > chunks) jb.lead = chunks;
+    af.jobs[i] = jb;
+    af.jobs[i].chunk0 = ccur;
+    af.jobs[i].nchunks = chunks;
+    jb.chunk0 = scur;
+    jb.nchunks = fused ? jb.lead + 1 : chunks;
+    fcur += (bound + 1023) / 1024;
+    scur += jb.nchunks;
+    ccur += chunks;
+  }
+  a.total_chunks = scur;
+  af.total_chunks = ccur;
+  hipError_t err = fused ? launch_zero_u32(frames, fcur, stream) : hipSuccess;
+  if (err == hipSuccess) err = run_compress(t, w, stream, ev);
+  if (err == hipSuccess && fused) err = launch_crc32_frames(af, stream);
+  if (err == hipSuccess) err = launch_crc32(a, stream);
+  if (ev) record(ev, 5, stream);
+  return err == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 }
 
 uint64_t rd64(const uint8_t* p) {
@@ -279,26 +377,6 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
   return launch_decompress(dtype, t, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 }
 
-uint32_t gf2_mulmod_host(uint32_t a, uint32_t b) {
-  uint32_t r = 0;
-  for (int i = 0; i < 32; ++i) {
-    if (a & (0x80000000u >> i)) r ^= b;
-    b = (b >> 1) ^ (0xEDB88320u & (0u - (b & 1u)));
-  }
-  return r;
-}
-
-// x^(8n) mod P in the reflected representation (bit 31 - d = x^d)
-uint32_t xpow8(uint64_t n) {
-  uint32_t r = 0x80000000u, sq = 0x00800000u;
-  while (n) {
-    if (n & 1) r = gf2_mulmod_host(r, sq);
-    sq = gf2_mulmod_host(sq, sq);
-    n >>= 1;
-  }
-  return r;
-}
-
 }  // namespace
 }  // namespace ltc
 
@@ -328,7 +406,8 @@ int ltc_compress_batch_workspace_size(int count, const uint64_t* h_nbytes, int d
   const uint32_t e = elem_bytes(dtype);
   const int64_t streams = batch_streams(count, h_nbytes, e, chunk_bytes);
   if (streams < 0) return LTC_ERR_INVALID_ARGUMENT;
-  *ws_nbytes = layout((uint64_t)streams, count, words_capacity(chunk_bytes, e)).total;
+  *ws_nbytes = layout((uint64_t)streams, count, words_capacity(chunk_bytes, e),
+                      batch_frames(count, h_nbytes, e, chunk_bytes)).total;
   return LTC_OK;
 }
 
@@ -355,6 +434,44 @@ int ltc_compress_batch_prof(int count, const void* const* h_src_ptrs, const uint
                             hipStream_t stream, const hipEvent_t* h_events) {
   return compress_impl(count, h_src_ptrs, h_nbytes, dtype, chunk_bytes, passthrough_threshold,
                        h_blob_ptrs, h_blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, h_events);
+}
+
+int ltc_compress_with_crc32(const void* d_src, uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                            double passthrough_threshold, void* d_blob, uint64_t blob_capacity,
+                            uint64_t* d_blob_nbytes, uint32_t checksum_chunk_bytes, uint32_t* d_crc,
+                            uint64_t crc_capacity, void* d_ws, uint64_t ws_nbytes,
+                            hipStream_t stream) {
+  if (checksum_chunk_bytes == 0) return LTC_ERR_INVALID_ARGUMENT;
+  const CrcReq crc{checksum_chunk_bytes, &d_crc, &crc_capacity};
+  return compress_impl(1, &d_src, &nbytes, dtype, chunk_bytes, passthrough_threshold, &d_blob,
+                       &blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, nullptr, crc);
+}
+
+int ltc_compress_batch_with_crc32(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                                  int dtype, uint32_t chunk_bytes, double passthrough_threshold,
+                                  void* const* h_blob_ptrs, const uint64_t* h_blob_capacity,
+                                  uint64_t* d_blob_nbytes, uint32_t checksum_chunk_bytes,
+                                  uint32_t* const* h_crc_ptrs, const uint64_t* h_crc_capacity,
+                                  void* d_ws, uint64_t ws_nbytes, hipStream_t stream) {
+  if (checksum_chunk_bytes == 0) return LTC_ERR_INVALID_ARGUMENT;
+  const CrcReq crc{checksum_chunk_bytes, h_crc_ptrs, h_crc_capacity};
+  return compress_impl(count, h_src_ptrs, h_nbytes, dtype, chunk_bytes, passthrough_threshold,
+                       h_blob_ptrs, h_blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, nullptr, crc);
+}
+
+int ltc_compress_batch_with_crc32_prof(int count, const void* const* h_src_ptrs,
+                                       const uint64_t* h_nbytes, int dtype, uint32_t chunk_bytes,
+                                       double passthrough_threshold, void* const* h_blob_ptrs,
+                                       const uint64_t* h_blob_capacity, uint64_t* d_blob_nbytes,
+                                       uint32_t checksum_chunk_bytes, uint32_t* const* h_crc_ptrs,
+                                       const uint64_t* h_crc_capacity, void* d_ws,
+                                       uint64_t ws_nbytes, hipStream_t stream,
+                                       const hipEvent_t* h_events) {
+  if (checksum_chunk_bytes == 0 || !h_events) return LTC_ERR_INVALID_ARGUMENT;
+  const CrcReq crc{checksum_chunk_bytes, h_crc_ptrs, h_crc_capacity};
+  return compress_impl(count, h_src_ptrs, h_nbytes, dtype, chunk_bytes, passthrough_threshold,
+                       h_blob_ptrs, h_blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, h_events,
+                       crc);
 }
 
 int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {

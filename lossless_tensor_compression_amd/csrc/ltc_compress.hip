@@ -21,6 +21,7 @@
 // stream: lmz README, "On a GPU" and "Building on lmz".
 #include <type_traits>
 
+#include "ltc_crc.h"
 #include "ltc_internal.h"
 #include "ltc_launch.h"
 
@@ -30,6 +31,10 @@ constexpr int kHistThreads = 256;
 constexpr int kHistCopies = 32;  // sub-histograms, picked by lane & 31
 constexpr uint32_t kHistSeg = 1u << 20;  // elements between sub-histogram flushes
 constexpr int kPackThreads = 256;
+// CRC variant: larger workgroups share one copy of the 37 KiB of tables, two
+// per CU, so that LDS stays free for the encoder of a concurrent chunk group
+constexpr int kPackCrcThreads = 512;
+constexpr uint64_t kPackCrcGrid = 512;
 constexpr int kScanThreads = 1024;
 constexpr uint32_t kRingWords = 512;    // encoder word ring per stream (LDS)
 constexpr uint32_t kFlushWords = 256;   // one drain = 64 lanes x 8 bytes
@@ -689,43 +694,121 @@ __device__ __forceinline__ uint32_t pack4(const uint32_t* y, int k) {
 
 __device__ __forceinline__ uint32_t pack_u16x2(uint32_t a, uint32_t b) { return a | (b << 16); }
 
-__device__ void write_rans(uint8_t* dst, uint64_t s, uint32_t info, uint32_t size, uint32_t nw,
-                           const CTable& t, const CWork& w) {
+// ---- CRC-32 of the blob as it is written (compress_with_crc32)
+// Payload bytes are checksummed in 16-byte units: a unit's remainder comes
+// from slicing-by-8 tables, the 64 units of a 1 KiB frame sit in the 64 lanes
+// of a wave (lane = position in the frame), and a 6-level tree combines them
+// (ltc_crc.h).  A wave walks consecutive frames, so each lane first chains
+// its units across frames (multiply by x^(8*1024), then add) and the tree
+// runs once per run of frames; a run ends at the last frame of a checksum
+// chunk or of the wave's share, and its remainder, relative to the end of its
+// last frame, is XORed into frames[last frame].  Several workgroups can add
+// to one frame where payloads meet; CRC linearity makes the XOR of the parts
+// the remainder of the whole.
+
+template <bool CRC> struct PackLds {};
+template <> struct PackLds<true> { CrcLdsT<7> c; };
+
+struct FrameRun {
+  uint32_t acc;    // per lane
+  uint64_t last;   // last frame added (uniform)
+  uint32_t wpos;   // its position in its checksum chunk (uniform)
+  bool open;
+};
+
+__device__ __forceinline__ void run_flush(FrameRun& r, const CrcLdsT<7>& s, uint32_t* frames,
+                                          uint32_t lane) {
+  if (!r.open) return;
+  const uint32_t v = crc_tree64(s, r.acc, lane);
+  if (lane == 0 && v) atomicXor(frames + r.last, v);
+  r.open = false;
+}
+
+// lane l's unit remainder c at position l of frame f
+__device__ __forceinline__ void run_add(FrameRun& r, const CrcLdsT<7>& s, uint32_t* frames,
+                                        uint64_t f, uint32_t c, uint32_t per_chunk, uint32_t lane) {
+  if (r.open && (f != r.last + 1 || r.wpos + 1 == per_chunk)) run_flush(r, s, frames, lane);
+  if (r.open) {
+    r.acc = crc_mul_level(s, 6, r.acc) ^ c;
+    r.wpos += 1;
+  } else {
+    r.acc = c;
+    r.wpos = (uint32_t)(f % per_chunk);
+    r.open = true;
+  }
+  r.last = f;
+}
+
+// frames [fb, fe) of a payload of `units` units starting at blob unit index a
+// that this wave takes (contiguous shares, one per wave of the workgroup)
+__device__ __forceinline__ void wave_frames(uint64_t a, uint32_t units, uint64_t& fb, uint64_t& fe) {
+  constexpr uint64_t kWaves = kPackCrcThreads / 64;
+  const uint64_t f0 = a >> 6, nf = ((a + units + 63) >> 6) - f0;
+  const uint64_t q = (nf + kWaves - 1) / kWaves, wave = threadIdx.x / 64;
+  fb = f0 + min(nf, wave * q);
+  fe = f0 + min(nf, wave * q + q);
+}
+
+// unit u (16 bytes) of a RANS payload: prefix, states, frequencies, words
+__device__ __forceinline__ uint4 rans_unit(uint32_t u, uint64_t s, uint32_t lo, uint32_t tcount,
+                                           uint32_t wo, uint32_t nw, const uint16_t* fr,
+                                           const uint16_t* words, const CWork& w) {
+  const uint32_t pos = 16 * u;
+  if (u == 0) return make_uint4(nw, lo | ((lo + tcount - 1) << 8), 0, 0);
+  if (pos < kRansFixed) return *reinterpret_cast<const uint4*>(w.states + 64 * s + (pos - 16) / 4);
+  uint32_t h[8];
+  if (pos < wo) {
+    const uint32_t i0 = (pos - kRansFixed) / 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = i0 + i < tcount ? fr[i0 + i] : 0u;
+  } else {
+    const uint32_t i0 = (pos - wo) / 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = i0 + i < nw ? words[i0 + i] : 0u;
+  }
+  return make_uint4(pack_u16x2(h[0], h[1]), pack_u16x2(h[2], h[3]), pack_u16x2(h[4], h[5]),
+                    pack_u16x2(h[6], h[7]));
+}
+
+template <bool CRC>
+__device__ void write_rans(uint8_t* blob, uint64_t off, uint64_t s, uint32_t info, uint32_t size,
+                           uint32_t nw, const CTable& t, const CWork& w, uint32_t* frames,
+                           const PackLds<CRC>& L) {
   const uint32_t lo = (info >> 16) & 0xFFu, hi = info >> 24;
   const uint32_t tcount = hi - lo + 1u;
   const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * tcount);
   const uint32_t units = (uint32_t)(align16(size) / 16);
   const uint16_t* fr = w.freq + 256 * s + lo;
   const uint16_t* words = w.words + s * t.wcap + (t.wcap - nw);
-  for (uint32_t u = threadIdx.x; u < units; u += kPackThreads) {
-    const uint32_t pos = 16 * u;
-    uint4 v;
-    if (u == 0) {
-      v = make_uint4(nw, lo | (hi << 8), 0, 0);
-    } else if (pos < kRansFixed) {
-      v = *reinterpret_cast<const uint4*>(w.states + 64 * s + (pos - 16) / 4);
-    } else {
-      uint32_t h[8];
-      if (pos < wo) {
-        const uint32_t i0 = (pos - kRansFixed) / 2;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = i0 + i < tcount ? fr[i0 + i] : 0u;
-      } else {
-        const uint32_t i0 = (pos - wo) / 2;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = i0 + i < nw ? words[i0 + i] : 0u;
+  uint8_t* dst = blob + off;
+  if constexpr (!CRC) {
+    for (uint32_t u = threadIdx.x; u < units; u += kPackThreads)
+      *reinterpret_cast<uint4*>(dst + 16 * u) = rans_unit(u, s, lo, tcount, wo, nw, fr, words, w);
+  } else {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t a = off / 16;
+    uint64_t fb, fe;
+    wave_frames(a, units, fb, fe);
+    FrameRun r{0, 0, 0, false};
+    for (uint64_t f = fb; f < fe; ++f) {
+      const uint64_t ua = 64 * f + lane;
+      uint32_t c = 0;
+      if (ua >= a && ua < a + units) {
+        const uint32_t u = (uint32_t)(ua - a);
+        const uint4 v = rans_unit(u, s, lo, tcount, wo, nw, fr, words, w);
+        *reinterpret_cast<uint4*>(dst + 16 * u) = v;
+        c = crc_step16(L.c, 0u, v);
       }
-      v = make_uint4(pack_u16x2(h[0], h[1]), pack_u16x2(h[2], h[3]), pack_u16x2(h[4], h[5]),
-                     pack_u16x2(h[6], h[7]));
+      run_add(r, L.c, frames, f, c, t.crc_frames, lane);
     }
-    *reinterpret_cast<uint4*>(dst + pos) = v;
+    run_flush(r, L.c, frames, lane);
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kPackThreads) void k_pack(CTable t, CWork w) {
+template <int DT, bool CRC>
+__device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint64_t g,
+                                           const PackLds<CRC>& L) {
   constexpr int E = Dt<DT>::E;
-  const uint64_t g = t.c_begin + blockIdx.x;
   const int j = find_job(t, g);
   const CJob& job = t.jobs[j];
   const uint64_t c = g - job.chunk0;
@@ -754,10 +837,12 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(CTable t, CWork w) {
     const uint32_t mode = si.y & 0xFFu;
     raw_off[k] = w.offsets[s];
     if (mode == LTC_MODE_RAW) rawmask |= 1u << k;
-    else if (mode == LTC_MODE_RANS) write_rans(blob + raw_off[k], s, si.y, si.x, si.z, t, w);
+    else if (mode == LTC_MODE_RANS)
+      write_rans<CRC>(blob, raw_off[k], s, si.y, si.x, si.z, t, w, job.frames, L);
   }
-  if (rawmask) {
-    const uint32_t units = (n + 15) / 16;
+  if (!rawmask) return;
+  const uint32_t units = (n + 15) / 16;
+  if constexpr (!CRC) {
     for (uint32_t u = tid; u < units; u += kPackThreads) {
       uint32_t y[16];
       load16<DT>(src, 16 * u, n, t.vec16 != 0, y);
@@ -768,7 +853,61 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(CTable t, CWork w) {
         *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = v;
       }
     }
+  } else {
+    // frames follow the first RAW stream; another RAW stream at the same
+    // position within its frames chains like it, one at another position
+    // splits each wave's units over two frames (rotated, two trees per frame)
+    const uint32_t lane = tid & 63;
+    const int k0 = __builtin_ctz(rawmask);
+    const uint64_t a0 = raw_off[k0] / 16;
+    uint64_t fb, fe;
+    wave_frames(a0, units, fb, fe);
+    FrameRun r[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) r[k] = FrameRun{0, 0, 0, false};
+    for (uint64_t f = fb; f < fe; ++f) {
+      const uint64_t ua = 64 * f + lane;
+      const bool have = ua >= a0 && ua < a0 + units;
+      const uint32_t u = (uint32_t)(ua - a0);
+      uint32_t y[16];
+      if (have) load16<DT>(src, 16 * u, n, t.vec16 != 0, y);
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        if (!(rawmask & (1u << k))) continue;
+        uint32_t cr = 0;
+        if (have) {
+          const uint4 v = make_uint4(pack4(y, k), pack4(y + 4, k), pack4(y + 8, k), pack4(y + 12, k));
+          *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = v;
+          cr = crc_step16(L.c, 0u, v);
+        }
+        const uint64_t d = raw_off[k] / 16 - a0;  // >= 0: streams are laid out in order
+        const uint32_t rot = (uint32_t)(d & 63);
+        const uint64_t fk = f + (d >> 6);
+        if (rot == 0) {
+          run_add(r[k], L.c, job.frames, fk, cr, t.crc_frames, lane);
+        } else {
+          const uint32_t v = __shfl(cr, (lane - rot) & 63u, 64);
+          uint32_t lo = lane >= rot ? v : 0u, hi = lane < rot ? v : 0u;
+          crc_tree64x2(L.c, lo, hi, lane);
+          if (lane == 0) {
+            if (lo) atomicXor(job.frames + fk, lo);
+            if (hi) atomicXor(job.frames + fk + 1, hi);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < E; ++k) run_flush(r[k], L.c, job.frames, lane);
   }
+}
+
+// One workgroup per chunk (a grid-stride loop; the CRC variant runs a grid
+// of at most kPackCrcGrid workgroups, which build their tables once).
+template <int DT, bool CRC>
+__global__ __launch_bounds__(CRC ? kPackCrcThreads : kPackThreads) void k_pack(CTable t, CWork w) {
+  __shared__ PackLds<CRC> lds;
+  if constexpr (CRC) crc_build_tables(lds.c, t.crc_lvl, threadIdx.x, kPackCrcThreads);
+  for (uint64_t g = t.c_begin + blockIdx.x; g < t.c_end; g += gridDim.x) pack_chunk<DT, CRC>(t, w, g, lds);
 }
 
 // ------------------------------------------------------------------ launch
@@ -790,7 +929,11 @@ static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t
   hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E);
   if (scan_done) (void)hipEventRecord(scan_done, st);
   record(ev, 3, st);
-  if (chunks) hipLaunchKernelGGL(k_pack<DT>, dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
+  if (chunks && t.crc)
+    hipLaunchKernelGGL((k_pack<DT, true>), dim3((uint32_t)(chunks < kPackCrcGrid ? chunks : kPackCrcGrid)),
+                       dim3(kPackCrcThreads), 0, st, t, w);
+  else if (chunks)
+    hipLaunchKernelGGL((k_pack<DT, false>), dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
   record(ev, 4, st);
   return hipGetLastError();
 }

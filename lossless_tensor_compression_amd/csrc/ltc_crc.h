@@ -1,0 +1,139 @@
+// ltc_crc.h -- CRC-32 (zlib's: reflected polynomial 0xEDB88320, register
+// preset to all ones, result complemented) building blocks shared by the
+// per-chunk CRC kernel and the pack kernel that checksums the blob while it
+// writes it.
+//
+// CRC is linear over GF(2).  With crc_raw(M) the remainder of a register that
+// starts at zero,
+//   crc_raw(A || B) = crc_raw(A) * x^(8|B|) mod P  xor  crc_raw(B),
+// and leading zero bytes leave crc_raw unchanged.  zlib's preset adds
+// 0xFFFFFFFF * x^(8L) mod P for a message of L bytes, and the result is
+// complemented.  Multiplication by a constant power of x is itself a linear
+// map of the 32-bit remainder, tabulated per operand byte (four 256-entry
+// tables); remainders of 16-byte units come from slicing-by-8 tables
+// (Kounavis & Berry, "A Systematic Approach to Building High Performance
+// Software-based CRC Generators", 2005).
+#pragma once
+
+#include "ltc_internal.h"
+
+namespace ltc {
+
+constexpr uint32_t kPoly = 0xEDB88320u;  // reflected CRC-32 polynomial
+constexpr int kCrcLevels = 6;            // tree levels over the 64 lanes of a wave
+
+// LDS tables: t8[m][b] (8 x 256) and, per multiplication constant l,
+// tl[l][p][b] (4 x 256).  Constants 0..5 are the tree levels; a seventh can
+// serve other shifts.
+template <int L> struct CrcLdsT {
+  static constexpr int kLevels = L;
+  uint32_t t8[8][256];
+  uint32_t tl[L][4][256];
+  uint32_t basis[L][32];
+};
+using CrcLds = CrcLdsT<kCrcLevels>;
+
+// a * b mod P with bit 31 - d of a word holding the coefficient of x^d
+__device__ __forceinline__ uint32_t gf2_mulmod(uint32_t a, uint32_t b) {
+  uint32_t r = 0;
+  for (int i = 0; i < 32; ++i) {
+    if (a & (0x80000000u >> i)) r ^= b;
+    b = (b >> 1) ^ (kPoly & (0u - (b & 1u)));
+  }
+  return r;
+}
+
+// x^(8n) mod P (square and multiply)
+__device__ __forceinline__ uint32_t gf2_xpow8(uint64_t n) {
+  uint32_t r = 0x80000000u, sq = 0x00800000u;  // 1 and x^8
+  while (n) {
+    if (n & 1) r = gf2_mulmod(r, sq);
+    sq = gf2_mulmod(sq, sq);
+    n >>= 1;
+  }
+  return r;
+}
+
+// Fills the tables; lvl[l] is multiplication constant l.  Every thread of
+// the workgroup calls it; it ends with a workgroup barrier.
+template <int L>
+__device__ __forceinline__ void crc_build_tables(CrcLdsT<L>& s, const uint32_t* lvl, uint32_t tid,
+                                                 uint32_t nthreads) {
+  for (uint32_t b = tid; b < 256; b += nthreads) {
+    // t8[m][b] = register after byte b followed by m zero bytes
+    uint32_t c = b;
+    for (int m = 0; m < 8; ++m) {
+      for (int k = 0; k < 8; ++k) c = (c >> 1) ^ (kPoly & (0u - (c & 1u)));
+      s.t8[m][b] = c;
+    }
+  }
+  // images of the 32 single-bit words under each level's multiplication
+  for (uint32_t i = tid; i < L * 32; i += nthreads)
+    s.basis[i / 32][i % 32] = gf2_mulmod(1u << (i % 32), lvl[i / 32]);
+  __syncthreads();
+  for (uint32_t idx = tid; idx < L * 4 * 256; idx += nthreads) {
+    const uint32_t l = idx / 1024, p = (idx / 256) & 3, b = idx & 255;
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (b & (1u << i)) v ^= s.basis[l][8 * p + i];
+    s.tl[l][p][b] = v;
+  }
+  __syncthreads();
+}
+
+// register c advanced over the 16 bytes of q (little-endian words)
+template <int L>
+__device__ __forceinline__ uint32_t crc_step16(const CrcLdsT<L>& s, uint32_t c, const uint4 q) {
+  c ^= q.x;
+  c = s.t8[7][c & 0xFFu] ^ s.t8[6][(c >> 8) & 0xFFu] ^ s.t8[5][(c >> 16) & 0xFFu] ^
+      s.t8[4][c >> 24] ^ s.t8[3][q.y & 0xFFu] ^ s.t8[2][(q.y >> 8) & 0xFFu] ^
+      s.t8[1][(q.y >> 16) & 0xFFu] ^ s.t8[0][q.y >> 24];
+  c ^= q.z;
+  c = s.t8[7][c & 0xFFu] ^ s.t8[6][(c >> 8) & 0xFFu] ^ s.t8[5][(c >> 16) & 0xFFu] ^
+      s.t8[4][c >> 24] ^ s.t8[3][q.w & 0xFFu] ^ s.t8[2][(q.w >> 8) & 0xFFu] ^
+      s.t8[1][(q.w >> 16) & 0xFFu] ^ s.t8[0][q.w >> 24];
+  return c;
+}
+
+template <int L>
+__device__ __forceinline__ uint32_t crc_step1(const CrcLdsT<L>& s, uint32_t c, uint32_t byte) {
+  return s.t8[0][(c ^ byte) & 0xFFu] ^ (c >> 8);
+}
+
+// c * lvl[l] mod P
+template <int L>
+__device__ __forceinline__ uint32_t crc_mul_level(const CrcLdsT<L>& s, int l, uint32_t c) {
+  return s.tl[l][0][c & 0xFFu] ^ s.tl[l][1][(c >> 8) & 0xFFu] ^ s.tl[l][2][(c >> 16) & 0xFFu] ^
+         s.tl[l][3][c >> 24];
+}
+
+// Lane i holds the remainder of segment i of 64 equal consecutive segments
+// (level l's constant shifts by 2^l segments).  Returns, in lane 0, the
+// remainder of the concatenation; every lane of the wave must call it.
+template <int L>
+__device__ __forceinline__ uint32_t crc_tree64(const CrcLdsT<L>& s, uint32_t c, uint32_t lane) {
+#pragma unroll
+  for (int l = 0; l < kCrcLevels; ++l) {
+    const uint32_t right = __shfl_down(c, 1u << l, 64);
+    if ((lane & ((2u << l) - 1u)) == 0) c = crc_mul_level(s, l, c) ^ right;
+  }
+  return c;
+}
+
+// the same for two independent sets of segments at once
+template <int L>
+__device__ __forceinline__ void crc_tree64x2(const CrcLdsT<L>& s, uint32_t& a, uint32_t& b,
+                                             uint32_t lane) {
+#pragma unroll
+  for (int l = 0; l < kCrcLevels; ++l) {
+    const uint32_t ra = __shfl_down(a, 1u << l, 64);
+    const uint32_t rb = __shfl_down(b, 1u << l, 64);
+    if ((lane & ((2u << l) - 1u)) == 0) {
+      a = crc_mul_level(s, l, a) ^ ra;
+      b = crc_mul_level(s, l, b) ^ rb;
+    }
+  }
+}
+
+}  // namespace ltc

@@ -70,6 +70,7 @@ struct CJob {
   uint32_t n_tail;            // elements in the last chunk
   uint32_t pmax_full;         // P_max for a full chunk's stream
   uint32_t pmax_tail;         // P_max for the last chunk's stream
+  uint32_t* frames;           // with CTable::crc: remainders of the blob's 1 KiB frames
 };
 
 struct CTable {
@@ -84,6 +85,12 @@ struct CTable {
   // the launch covers global chunks [c_begin, c_end) (a group of a pipelined
   // call, or all of them)
   uint64_t c_begin, c_end;
+  // compress_with_crc32: k_pack accumulates the remainder of every 1 KiB
+  // frame of payload it writes into CJob::frames, combining runs of frames
+  // that lie in one checksum chunk of crc_frames frames
+  uint32_t crc;
+  uint32_t crc_frames;
+  uint32_t crc_lvl[7];   // x^(8*16*2^l) mod P: shifts by 16 * 2^l bytes (l = 6: 1 KiB)
 };
 
 struct CWork {

@@ -106,3 +106,17 @@ def test_argument_errors_before_any_launch():
     assert L.ltc_compress(fake, 16, 1, 131072, 0.95, fake, 1 << 20, fake, fake, 16, null) == -7
     assert L.ltc_crc32_chunks(fake, 100, 0, fake, null) == -1
     assert L.ltc_crc32_chunks(fake, 0, 16384, fake, null) == 0
+    # compress_with_crc32: checksum chunk 0, short or misaligned checksum array
+    cwc = L.ltc_compress_with_crc32
+    cwc.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32, ctypes.c_double,
+                    ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p,
+                    ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    bound = L.ltc_compress_bound(4096, 1, 131072)
+    need = (bound + 1023) // 1024
+    assert cwc(fake, 4096, 1, 131072, 0.95, fake, bound, fake, 0, fake, 99, fake, 1 << 30, null) == -1
+    assert cwc(fake, 4096, 1, 131072, 0.95, fake, bound, fake, 1024, fake, need - 1, fake, 1 << 30,
+               null) == -6
+    assert cwc(fake, 4096, 1, 131072, 0.95, fake, bound, fake, 1024, ctypes.c_void_p((1 << 20) + 2),
+               need, fake, 1 << 30, null) == -1
+    assert cwc(fake, 4096, 9, 131072, 0.95, fake, bound, fake, 1024, fake, need, fake, 1 << 30, null) == -2
+    assert cwc(fake, 4096, 1, 131072, 0.95, fake, bound, fake, 1024, fake, need, fake, 16, null) == -7

@@ -1,0 +1,197 @@
+"""GPU parity of compress_with_crc32 (cuZipNN 0.1.0, "API",
+compress_tensor_with_crc32): the blob must equal the oracle's blob byte for
+byte, and the checksums must equal the oracle's CRC-32 (zlib's) of every
+checksum_chunk_bytes-byte chunk of that blob.
+
+Checksum chunk sizes cover both ways the library computes them: multiples of
+1 KiB up to 1 MiB (the payload is checksummed while k_pack writes it, in
+1 KiB frames) and all other sizes (the blob is read back).  Inputs put payload borders inside frames, several RAW streams at
+different positions within their frames, frames shared by the chunk groups
+of a pipelined call, empty and one-element tensors, and blobs whose last
+checksum chunk is short.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import banner, to_gpu, to_np_bytes
+
+pytestmark = pytest.mark.gpu
+
+FUSED_K = [1024, 3072, 4096, 16384, 65536, 131072, 196608, 1 << 20]  # frames combined
+READBACK_K = [7, 1000, 16385, 2 << 20]                                # blob read back
+
+
+@pytest.fixture(scope="module")
+def ltc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import lossless_tensor_compression_amd as m
+    m.lib()
+    return m
+
+
+def _u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def check_crc_case(ltc, arr, dtype, chunk, ks, thr=0.95, label=""):
+    src = np.ascontiguousarray(arr).reshape(-1).view(np.uint8)
+    want_blob = oracle.compress(src, dtype, chunk, thr)
+    t = to_gpu(src, dtype)
+    for k in ks:
+        banner(f"crc case {label} dtype={dtype} chunk={chunk} K={k} bytes={src.size}")
+        blob, crc = ltc.compress_with_crc32(t, chunk, thr, k)
+        got = to_np_bytes(blob)
+        assert got.size == want_blob.size and np.array_equal(got, want_blob)
+        want = np.array(oracle.crc32_chunks(want_blob, k), dtype=np.uint32)
+        assert np.array_equal(_u32(crc), want), (label, k)
+    return want_blob
+
+
+def _fp32_split_streams(rng, nelem):
+    """FP32 words whose byte 0 and byte 2 are random (RAW) and byte 1 takes
+    three values (a short RANS payload of odd size), so the two RAW payloads
+    of a chunk sit at different positions within their 1 KiB frames."""
+    b0 = rng.integers(0, 256, nelem, dtype=np.uint32)
+    b1 = rng.choice(np.array([3, 77, 200], dtype=np.uint32), nelem, p=[0.6, 0.3, 0.1])
+    b2 = rng.integers(0, 256, nelem, dtype=np.uint32)
+    b3 = rng.choice(np.array([0x3C, 0x3D, 0xBC, 0xBD], dtype=np.uint32), nelem)
+    return (b0 | (b1 << 8) | (b2 << 16) | (b3 << 24)).astype(np.uint32)
+
+
+def test_c1_bf16_all_checksum_sizes(ltc):
+    check_crc_case(ltc, workloads.c1(), 1, 131072, FUSED_K + READBACK_K, label="C1")
+
+
+def test_fp32_raw_streams_at_different_frame_positions(ltc):
+    rng = np.random.default_rng(21)
+    x = _fp32_split_streams(rng, 200003)
+    blob = check_crc_case(ltc, x, 3, 65536, [1024, 16384, 65536, 1000], label="split streams")
+    e, k = 4, int.from_bytes(blob[20:24].tobytes(), "little")
+    d = blob[64:64 + 16 * k * e].reshape(-1, 16)
+    modes = d[:, 12].reshape(k, e)
+    offs = d[:, :8].copy().view(np.uint64).reshape(k, e)
+    assert (modes[:, 0] == 0).all() and (modes[:, 2] == 0).all() and (modes[:, 1] == 1).all()
+    # the case the test is for: RAW payloads of one chunk at different positions
+    assert any(int(offs[c, 0]) % 1024 != int(offs[c, 2]) % 1024 for c in range(k))
+
+
+def test_fp32_three_raw_streams_and_fp16(ltc):
+    check_crc_case(ltc, workloads.c2().reshape(-1)[: 1 << 20], 3, 131072, [16384, 4096],
+                   label="C2 slice")
+    clean, h = workloads.c4()
+    check_crc_case(ltc, clean.reshape(-1)[: 1 << 20], 3, 131072, [16384], label="C4 clean slice")
+    check_crc_case(ltc, h.reshape(-1)[: 1 << 21], 2, 131072, [16384, 65536], label="C4 fp16 slice")
+
+
+@pytest.mark.parametrize("dtype,nelem,chunk", [(0, 0, 4096), (0, 1, 4096), (1, 1, 8), (2, 63, 24),
+                                               (3, 129, 4096), (1, 5003, 8), (0, 70001, 4096),
+                                               (3, 70001, 131072), (1, 8192, 16384)])
+def test_small_and_ragged(ltc, dtype, nelem, chunk):
+    rng = np.random.default_rng(nelem + dtype)
+    x = rng.standard_normal(nelem) * 0.02
+    if dtype == 0:
+        arr = np.clip(np.rint(x * 2000) + 128, 0, 255).astype(np.uint8)
+    elif dtype == 1:
+        arr = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    else:
+        arr = x.astype(np.float16 if dtype == 2 else np.float32)
+    check_crc_case(ltc, arr, dtype, chunk, [1024, 16384, 1000], label=f"small n={nelem}")
+
+
+@pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (0, 2048)])
+def test_grouped_call(ltc, dtype, chunk):
+    """Over 512 chunks: four chunk groups on several streams add into frames
+    that straddle the group borders; every 5th chunk is random bytes."""
+    rng = np.random.default_rng(300 + dtype)
+    nbytes = 700 * chunk + 24
+    if dtype == 0:
+        data = rng.integers(0, 6, nbytes, dtype=np.uint8)
+    else:
+        x = (rng.standard_normal(nbytes // 4) * 0.02).astype(np.float32)
+        if dtype == 1:
+            data = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint8)
+            data = np.concatenate([data, data])[:nbytes]
+        else:
+            data = x.view(np.uint8)[:nbytes]
+    for c in range(0, nbytes // chunk, 5):
+        data[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
+    e = oracle.ELEM_BYTES[dtype]
+    data = data[: nbytes // e * e]
+    check_crc_case(ltc, data, dtype, chunk, [1024, 16384, 131072, 5000], label=f"grouped {dtype}")
+
+
+def test_batch_with_empty_and_tiny(ltc):
+    rng = np.random.default_rng(78)
+    chunk = 1024
+    sizes = (90000, 0, 1, 123457, 2, 40000, 250001, 17, 60000)
+    arrs = [(rng.standard_normal(n) * rng.choice([0.02, 1.0, 1e-4])).astype(np.float32) for n in sizes]
+    ts = [to_gpu(a, 3) for a in arrs]
+    for k in (16384, 2048, 999):
+        banner(f"crc batch K={k}")
+        blobs, crcs = ltc.compress_batch_with_crc32(ts, chunk, 0.95, k)
+        for a, b, c in zip(arrs, blobs, crcs):
+            want = oracle.compress(a, 3, chunk)
+            assert np.array_equal(to_np_bytes(b), want)
+            assert np.array_equal(_u32(c), np.array(oracle.crc32_chunks(want, k), dtype=np.uint32))
+        plain = ltc.compress_batch(ts, chunk)
+        for b1, b2 in zip(blobs, plain):
+            assert torch.equal(b1, b2)
+
+
+def test_repeat_calls_and_untouched_tail(ltc):
+    """Frames are cleared at every call: a second call gives the same
+    checksums; entries past ceil(blob / K) keep what the caller put there."""
+    x = workloads.c1()[:300000]
+    t = to_gpu(x, 1)
+    code, chunk, k = 1, 131072, 16384
+    nbytes = x.nbytes
+    cap = ltc.compress_bound(nbytes, code, chunk)
+    blob = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    ncap = (cap + k - 1) // k
+    crc = torch.full((ncap,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws_n = ltc.workspace_size([nbytes], code, chunk)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        ltc.compress_crc32_raw([t.data_ptr()], [nbytes], code, chunk, 0.95, [blob.data_ptr()], [cap],
+                               size.data_ptr(), k, [crc.data_ptr()], [ncap], ws.data_ptr(), ws_n)
+        torch.cuda.synchronize()
+        outs.append(_u32(crc).copy())
+    assert np.array_equal(outs[0], outs[1])
+    b = int(size.item())
+    n = (b + k - 1) // k
+    want = oracle.compress(x, 1, chunk)
+    assert b == want.size
+    assert outs[0][:n].tolist() == [zlib.crc32(want[i:i + k].tobytes()) for i in range(0, b, k)]
+    assert (outs[0][n:] == 0x5A5A5A5A).all()
+
+
+def test_argument_errors(ltc):
+    x = to_gpu(workloads.c1()[:1000], 1)
+    nbytes = 2000
+    cap = ltc.compress_bound(nbytes, 1, 131072)
+    blob = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    crc = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws_n = ltc.workspace_size([nbytes], 1, 131072)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    args = dict(src_ptrs=[x.data_ptr()], nbytes=[nbytes], dtype_code=1, chunk_bytes=131072,
+                threshold=0.95, blob_ptrs=[blob.data_ptr()], caps=[cap], nbytes_out_ptr=size.data_ptr(),
+                ws_ptr=ws.data_ptr(), ws_nbytes=ws_n)
+    with pytest.raises(ltc.LTCError) as e:
+        ltc.compress_crc32_raw(**args, crc_chunk_bytes=0, crc_ptrs=[crc.data_ptr()], crc_caps=[4])
+    assert e.value.code == -1
+    with pytest.raises(ltc.LTCError) as e:  # ceil(cap / 64) entries are needed
+        ltc.compress_crc32_raw(**args, crc_chunk_bytes=64, crc_ptrs=[crc.data_ptr()], crc_caps=[4])
+    assert e.value.code == -6
+    with pytest.raises(ltc.LTCError) as e:
+        ltc.compress_crc32_raw(**args, crc_chunk_bytes=16384, crc_ptrs=[crc.data_ptr() + 2],
+                               crc_caps=[1])
+    assert e.value.code == -1

@@ -74,6 +74,27 @@ def test_c3_batch_full_size(ltc):
         assert np.array_equal(blobs[i].cpu().numpy(), want)
 
 
+def test_c3_compress_with_crc32_full_size(ltc):
+    """compress_with_crc32 over the C3 batch, in bench.py's launch
+    configuration: blobs identical to compress_batch, checksums identical to
+    the CRC kernel's over the finished blobs, sampled chunks equal to zlib."""
+    banner("C3 generate")
+    ts = workloads.c3_gpu()
+    banner("C3 compress_batch_with_crc32 (K = 16 KiB)")
+    blobs, crcs = ltc.compress_batch_with_crc32(ts, CHUNK, 0.95, 16384)
+    plain = ltc.compress_batch(ts)
+    rng = np.random.default_rng(5)
+    for i, (b, p, c) in enumerate(zip(blobs, plain, crcs)):
+        assert torch.equal(b, p), i
+        ref = ltc.crc32_chunks(b, 16384)
+        assert torch.equal(c, ref), i
+        nb = b.numel()
+        n = c.numel()
+        for w in sorted(set([0, 1, n - 2, n - 1] + rng.integers(0, n, 20).tolist())):
+            seg = b[w * 16384:min(nb, (w + 1) * 16384)].cpu().numpy()
+            assert int(c[w].item()) & 0xFFFFFFFF == zlib.crc32(seg.tobytes()), (i, w)
+
+
 def test_c5_full_size_with_crc(ltc):
     banner("C5 generate (8 GiB)")
     buf = workloads.c5_gpu()
