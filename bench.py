@@ -251,6 +251,8 @@ def main():
     fused = args.crc == "fused"
 
     def compress_crc(events=None):
+        if events is None and args.isolated:
+            events = ev_f  # kernel by kernel
         ltc.compress_crc32_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, blob_ptrs, caps,
                                sizes.data_ptr(), CRC_CHUNK, fcrc_ptrs, fcap, ws.data_ptr(), ws_n,
                                events=events)

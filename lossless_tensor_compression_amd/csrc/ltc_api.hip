@@ -91,6 +91,28 @@ uint32_t gf2_mulmod_host(uint32_t a, uint32_t b) {
   return r;
 }
 
+// v * x^-1 mod P (undoes one step of v * x = (v >> 1) ^ (P if v & 1): the
+// reflected polynomial has its top bit set, so that bit of the product is
+// the bit v lost)
+uint32_t div_x(uint32_t d) {
+  const uint32_t low = d >> 31;
+  return ((d ^ (0xEDB88320u & (0u - low))) << 1) | low;
+}
+
+// x^(-8*16*j) mod P for j = 0..63
+const uint32_t* xinv_table() {
+  static const std::vector<uint32_t> tab = [] {
+    std::vector<uint32_t> v(64);
+    uint32_t r = 0x80000000u;  // 1
+    for (int j = 0; j < 64; ++j) {
+      v[j] = r;
+      for (int k = 0; k < 128; ++k) r = div_x(r);
+    }
+    return v;
+  }();
+  return tab.data();
+}
+
 // x^(8n) mod P in the reflected representation (bit 31 - d = x^d)
 uint32_t xpow8(uint64_t n) {
   uint32_t r = 0x80000000u, sq = 0x00800000u;
@@ -258,57 +280,45 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   w.words = reinterpret_cast<uint16_t*>(ws + l.words);
   if (!crc.chunk_bytes) return run_compress(t, w, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 
-  // compress_with_crc32: when checksum chunks are whole 1 KiB frames, k_pack
-  // accumulates the payload's frame remainders, k_crc_frames combines the
-  // full payload chunks from them, and k_crc32 reads back the leading chunks
-  // (header and directory) and each blob's last chunk; otherwise k_crc32
-  // reads back every chunk of the finished blobs.
+  // compress_with_crc32: when checksum chunks are whole 1 KiB frames, k_scan
+  // and k_pack accumulate the remainders of the blob's frames as they write
+  // it and k_crc_frames chains them per chunk; otherwise k_crc32 reads the
+  // finished blobs back.
   const uint64_t K = crc.chunk_bytes;
   const bool fused = crc_frames_usable(K);
   uint32_t* frames = reinterpret_cast<uint32_t*>(ws + l.frames);
-  CrcArgs a;  // k_crc32
+  CrcArgs a;
   memset(&a, 0, sizeof(a));
   a.count = (uint32_t)count;
   a.chunk_bytes = K;
   a.seg = round_up(K, 256) / 64;
   for (int lv = 0; lv < 6; ++lv) a.lvl[lv] = xpow8(a.seg << lv);
-  a.init_full = gf2_mulmod_host(0xFFFFFFFFu, xpow8(K));
   a.x1k = xpow8(1024);
-  a.tail_slot = fused ? 1u : 0u;
-  CrcArgs af = a;  // k_crc_frames
+  memcpy(a.xinv, xinv_table(), sizeof(a.xinv));
   if (fused) {
     t.crc = 1;
     t.crc_frames = (uint32_t)(K / 1024);
-    for (int lv = 0; lv < 7; ++lv) t.crc_lvl[lv] = xpow8(16ull << lv);
+    t.crc_x1k = xpow8(1024);
+    for (int k = 0; k < 64; ++k) t.crc_pos[k] = xpow8(16ull * (63 - k));
   }
-  uint64_t fcur = 0, scur = 0, ccur = 0;
+  uint64_t fcur = 0, ccur = 0;
   for (int i = 0; i < count; ++i) {
     const uint64_t bound = bound_of(nbytes[i], e, chunk_bytes);
-    const uint64_t chunks = (bound + K - 1) / K;
     t.jobs[i].frames = frames + fcur;
     CrcJob& jb = a.jobs[i];
     jb.src = t.jobs[i].blob;
     jb.out = crc.outs[i];
     jb.len = d_blob_nbytes + i;
     jb.frames = fused ? frames + fcur : nullptr;
-    jb.frames_from = kHeader + kDirEntry * (uint64_t)t.jobs[i].nchunks * e;
-    jb.lead = (jb.frames_from + K - 1) / K;
-    if (jb.lead > chunks) jb.lead = chunks;
-    af.jobs[i] = jb;
-    af.jobs[i].chunk0 = ccur;
-    af.jobs[i].nchunks = chunks;
-    jb.chunk0 = scur;
-    jb.nchunks = fused ? jb.lead + 1 : chunks;
+    jb.chunk0 = ccur;
+    jb.nchunks = (bound + K - 1) / K;
     fcur += (bound + 1023) / 1024;
-    scur += jb.nchunks;
-    ccur += chunks;
+    ccur += jb.nchunks;
   }
-  a.total_chunks = scur;
-  af.total_chunks = ccur;
+  a.total_chunks = ccur;
   hipError_t err = fused ? launch_zero_u32(frames, fcur, stream) : hipSuccess;
   if (err == hipSuccess) err = run_compress(t, w, stream, ev);
-  if (err == hipSuccess && fused) err = launch_crc32_frames(af, stream);
-  if (err == hipSuccess) err = launch_crc32(a, stream);
+  if (err == hipSuccess) err = fused ? launch_crc32_frames(a, stream) : launch_crc32(a, stream);
   if (ev) record(ev, 5, stream);
   return err == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 }
@@ -537,7 +547,6 @@ int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint6
   a.chunk_bytes = chunk_bytes;
   a.seg = round_up(chunk_bytes, 256) / 64;
   for (int l = 0; l < 6; ++l) a.lvl[l] = xpow8(a.seg << l);
-  a.init_full = gf2_mulmod_host(0xFFFFFFFFu, xpow8(chunk_bytes));
   uint64_t total = 0;
   for (int i = 0; i < count; ++i) {
     CrcJob& jb = a.jobs[i];
@@ -547,7 +556,6 @@ int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint6
     jb.nchunks = (h_nbytes[i] + chunk_bytes - 1) / chunk_bytes;
     if (jb.nchunks && (!jb.src || !jb.out)) return LTC_ERR_INVALID_ARGUMENT;
     jb.tail_len = jb.nchunks ? h_nbytes[i] - (jb.nchunks - 1) * (uint64_t)chunk_bytes : 0;
-    jb.init_tail = gf2_mulmod_host(0xFFFFFFFFu, xpow8(jb.tail_len));
     total += jb.nchunks;
   }
   a.total_chunks = total;

@@ -31,10 +31,10 @@ constexpr int kHistThreads = 256;
 constexpr int kHistCopies = 32;  // sub-histograms, picked by lane & 31
 constexpr uint32_t kHistSeg = 1u << 20;  // elements between sub-histogram flushes
 constexpr int kPackThreads = 256;
-// CRC variant: larger workgroups share one copy of the 37 KiB of tables, two
-// per CU, so that LDS stays free for the encoder of a concurrent chunk group
-constexpr int kPackCrcThreads = 512;
-constexpr uint64_t kPackCrcGrid = 512;
+// CRC variant: a grid of 4 workgroups per CU (13 KiB of tables each, up to
+// 128 VGPRs), which build their tables once
+constexpr int kPackCrcThreads = 256;
+constexpr uint64_t kPackCrcGrid = 1024;
 constexpr int kScanThreads = 1024;
 constexpr uint32_t kRingWords = 512;    // encoder word ring per stream (LDS)
 constexpr uint32_t kFlushWords = 256;   // one drain = 64 lanes x 8 bytes
@@ -651,6 +651,20 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
     else
       v = make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(job.blob + 16 * tid) = v;
+    if (t.crc) {
+      // header unit tid sits at position tid of frame 0: its remainder
+      // (bit by bit) times x^(8*16*(63 - tid)) is its share of the frame's
+      uint32_t r = 0;
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      for (int q = 0; q < 4; ++q) {
+        for (int b = 0; b < 4; ++b) {
+          r ^= (wv[q] >> (8 * b)) & 0xFFu;
+          for (int k = 0; k < 8; ++k) r = (r >> 1) ^ (kPoly & (0u - (r & 1u)));
+        }
+      }
+      r = gf2_mulmod(r, t.crc_pos[tid]);
+      if (r) atomicXor(job.frames, r);
+    }
   }
 }
 
@@ -695,19 +709,26 @@ __device__ __forceinline__ uint32_t pack4(const uint32_t* y, int k) {
 __device__ __forceinline__ uint32_t pack_u16x2(uint32_t a, uint32_t b) { return a | (b << 16); }
 
 // ---- CRC-32 of the blob as it is written (compress_with_crc32)
-// Payload bytes are checksummed in 16-byte units: a unit's remainder comes
-// from slicing-by-8 tables, the 64 units of a 1 KiB frame sit in the 64 lanes
-// of a wave (lane = position in the frame), and a 6-level tree combines them
-// (ltc_crc.h).  A wave walks consecutive frames, so each lane first chains
-// its units across frames (multiply by x^(8*1024), then add) and the tree
-// runs once per run of frames; a run ends at the last frame of a checksum
-// chunk or of the wave's share, and its remainder, relative to the end of its
-// last frame, is XORed into frames[last frame].  Several workgroups can add
-// to one frame where payloads meet; CRC linearity makes the XOR of the parts
-// the remainder of the whole.
+// Blob bytes are checksummed in 16-byte units: a unit's remainder comes from
+// slicing-by-8 tables, and the 64 units of a 1 KiB frame sit in the 64 lanes
+// of a wave (lane = position in the frame).  A wave walks consecutive frames,
+// so each lane first chains its units across frames (multiply by x^(8*1024)
+// from byte tables, then add).  A run of frames ends at the last frame of a
+// checksum chunk or of the wave's share; then each lane moves its chain to
+// the end of the frame (times x^(8*16*(63 - lane)), bit by bit), the wave
+// XORs the 64 values together, and lane 0 XORs the result, the run's
+// remainder relative to the end of its last frame, into frames[last frame].
+// Several workgroups can add to one frame where payloads meet; CRC linearity
+// makes the XOR of the parts the remainder of the whole.
 
 template <bool CRC> struct PackLds {};
-template <> struct PackLds<true> { CrcLdsT<7> c; };
+template <> struct PackLds<true> { CrcLdsT<1> c; };  // t8 and x^(8*1024)
+
+__device__ __forceinline__ uint32_t wave_xor(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v ^= __shfl_xor(v, o, 64);
+  return v;
+}
 
 struct FrameRun {
   uint32_t acc;    // per lane
@@ -716,20 +737,35 @@ struct FrameRun {
   bool open;
 };
 
-__device__ __forceinline__ void run_flush(FrameRun& r, const CrcLdsT<7>& s, uint32_t* frames,
+// pos: this lane's x^(8*16*(63 - lane)) mod P
+__device__ __forceinline__ void run_flush(FrameRun& r, uint32_t pos, uint32_t* frames,
                                           uint32_t lane) {
   if (!r.open) return;
-  const uint32_t v = crc_tree64(s, r.acc, lane);
+  const uint32_t v = wave_xor(gf2_mulmod(r.acc, pos));
   if (lane == 0 && v) atomicXor(frames + r.last, v);
   r.open = false;
 }
 
+// lanes hold unit remainders of 64 consecutive units starting at position
+// rot of frame f: lanes below 64 - rot in frame f, the rest in frame f + 1
+__device__ __forceinline__ void split_frames(uint32_t c, uint32_t rot, uint64_t f, uint32_t* frames,
+                                             uint32_t pos, uint32_t lane) {
+  const uint32_t v = __shfl(c, (lane - rot) & 63u, 64);  // lane = position in its frame
+  const uint32_t m = gf2_mulmod(v, pos);
+  const uint32_t lo = wave_xor(lane >= rot ? m : 0u), hi = wave_xor(lane < rot ? m : 0u);
+  if (lane == 0) {
+    if (lo) atomicXor(frames + f, lo);
+    if (hi) atomicXor(frames + f + 1, hi);
+  }
+}
+
 // lane l's unit remainder c at position l of frame f
-__device__ __forceinline__ void run_add(FrameRun& r, const CrcLdsT<7>& s, uint32_t* frames,
-                                        uint64_t f, uint32_t c, uint32_t per_chunk, uint32_t lane) {
-  if (r.open && (f != r.last + 1 || r.wpos + 1 == per_chunk)) run_flush(r, s, frames, lane);
+__device__ __forceinline__ void run_add(FrameRun& r, const CrcLdsT<1>& s, uint32_t* frames,
+                                        uint64_t f, uint32_t c, uint32_t per_chunk, uint32_t pos,
+                                        uint32_t lane) {
+  if (r.open && (f != r.last + 1 || r.wpos + 1 == per_chunk)) run_flush(r, pos, frames, lane);
   if (r.open) {
-    r.acc = crc_mul_level(s, 6, r.acc) ^ c;
+    r.acc = crc_mul_level(s, 0, r.acc) ^ c;
     r.wpos += 1;
   } else {
     r.acc = c;
@@ -773,7 +809,7 @@ __device__ __forceinline__ uint4 rans_unit(uint32_t u, uint64_t s, uint32_t lo, 
 template <bool CRC>
 __device__ void write_rans(uint8_t* blob, uint64_t off, uint64_t s, uint32_t info, uint32_t size,
                            uint32_t nw, const CTable& t, const CWork& w, uint32_t* frames,
-                           const PackLds<CRC>& L) {
+                           const PackLds<CRC>& L, uint32_t pos) {
   const uint32_t lo = (info >> 16) & 0xFFu, hi = info >> 24;
   const uint32_t tcount = hi - lo + 1u;
   const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * tcount);
@@ -799,15 +835,15 @@ __device__ void write_rans(uint8_t* blob, uint64_t off, uint64_t s, uint32_t inf
         *reinterpret_cast<uint4*>(dst + 16 * u) = v;
         c = crc_step16(L.c, 0u, v);
       }
-      run_add(r, L.c, frames, f, c, t.crc_frames, lane);
+      run_add(r, L.c, frames, f, c, t.crc_frames, pos, lane);
     }
-    run_flush(r, L.c, frames, lane);
+    run_flush(r, pos, frames, lane);
   }
 }
 
 template <int DT, bool CRC>
 __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint64_t g,
-                                           const PackLds<CRC>& L) {
+                                           const PackLds<CRC>& L, uint32_t pos) {
   constexpr int E = Dt<DT>::E;
   const int j = find_job(t, g);
   const CJob& job = t.jobs[j];
@@ -819,14 +855,25 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
   const uint64_t s0 = g * E;
   const uint32_t tid = threadIdx.x;
 
+  uint4 dir = make_uint4(0, 0, 0, 0);
   if (tid < (uint32_t)E) {
     const uint64_t s = s0 + tid;
     const uint4 si = *reinterpret_cast<const uint4*>(w.sinfo + 4 * s);
     const uint32_t mode = si.y & 0xFFu;
     const uint32_t cval = mode == LTC_MODE_CONST ? (si.y >> 8) & 0xFFu : 0u;
     const uint64_t off = w.offsets[s];
-    *reinterpret_cast<uint4*>(blob + kHeader + kDirEntry * (c * E + tid)) =
-        make_uint4((uint32_t)off, (uint32_t)(off >> 32), si.x, mode | (cval << 8));
+    dir = make_uint4((uint32_t)off, (uint32_t)(off >> 32), si.x, mode | (cval << 8));
+    *reinterpret_cast<uint4*>(blob + kHeader + kDirEntry * (c * E + tid)) = dir;
+  }
+  if constexpr (CRC) {
+    // the chunk's E directory entries: units 4 + c*E + k of the blob, in
+    // lanes 0..E-1 of wave 0, rotated to their positions in their frame(s)
+    if (tid < 64) {
+      const uint32_t lane = tid;
+      const uint32_t cr = lane < (uint32_t)E ? crc_step16(L.c, 0u, dir) : 0u;
+      const uint64_t a = kHeader / 16 + c * E;
+      split_frames(cr, (uint32_t)(a & 63), a >> 6, job.frames, pos, lane);
+    }
   }
   uint32_t rawmask = 0;
   uint64_t raw_off[E];
@@ -838,7 +885,7 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
     raw_off[k] = w.offsets[s];
     if (mode == LTC_MODE_RAW) rawmask |= 1u << k;
     else if (mode == LTC_MODE_RANS)
-      write_rans<CRC>(blob, raw_off[k], s, si.y, si.x, si.z, t, w, job.frames, L);
+      write_rans<CRC>(blob, raw_off[k], s, si.y, si.x, si.z, t, w, job.frames, L, pos);
   }
   if (!rawmask) return;
   const uint32_t units = (n + 15) / 16;
@@ -883,21 +930,12 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
         const uint64_t d = raw_off[k] / 16 - a0;  // >= 0: streams are laid out in order
         const uint32_t rot = (uint32_t)(d & 63);
         const uint64_t fk = f + (d >> 6);
-        if (rot == 0) {
-          run_add(r[k], L.c, job.frames, fk, cr, t.crc_frames, lane);
-        } else {
-          const uint32_t v = __shfl(cr, (lane - rot) & 63u, 64);
-          uint32_t lo = lane >= rot ? v : 0u, hi = lane < rot ? v : 0u;
-          crc_tree64x2(L.c, lo, hi, lane);
-          if (lane == 0) {
-            if (lo) atomicXor(job.frames + fk, lo);
-            if (hi) atomicXor(job.frames + fk + 1, hi);
-          }
-        }
+        if (rot == 0) run_add(r[k], L.c, job.frames, fk, cr, t.crc_frames, pos, lane);
+        else split_frames(cr, rot, fk, job.frames, pos, lane);
       }
     }
 #pragma unroll
-    for (int k = 0; k < E; ++k) run_flush(r[k], L.c, job.frames, lane);
+    for (int k = 0; k < E; ++k) run_flush(r[k], pos, job.frames, lane);
   }
 }
 
@@ -906,8 +944,12 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
 template <int DT, bool CRC>
 __global__ __launch_bounds__(CRC ? kPackCrcThreads : kPackThreads) void k_pack(CTable t, CWork w) {
   __shared__ PackLds<CRC> lds;
-  if constexpr (CRC) crc_build_tables(lds.c, t.crc_lvl, threadIdx.x, kPackCrcThreads);
-  for (uint64_t g = t.c_begin + blockIdx.x; g < t.c_end; g += gridDim.x) pack_chunk<DT, CRC>(t, w, g, lds);
+  uint32_t pos = 0;
+  if constexpr (CRC) {
+    crc_build_tables(lds.c, &t.crc_x1k, threadIdx.x, kPackCrcThreads);
+    pos = t.crc_pos[threadIdx.x & 63];
+  }
+  for (uint64_t g = t.c_begin + blockIdx.x; g < t.c_end; g += gridDim.x) pack_chunk<DT, CRC>(t, w, g, lds, pos);
 }
 
 // ------------------------------------------------------------------ launch

@@ -6,9 +6,9 @@
 // CRC is linear over GF(2).  With crc_raw(M) the remainder of a register that
 // starts at zero,
 //   crc_raw(A || B) = crc_raw(A) * x^(8|B|) mod P  xor  crc_raw(B),
-// and leading zero bytes leave crc_raw unchanged.  zlib's preset adds
-// 0xFFFFFFFF * x^(8L) mod P for a message of L bytes, and the result is
-// complemented.  Multiplication by a constant power of x is itself a linear
+// and leading zero bytes leave crc_raw unchanged.  zlib's register is preset
+// to 0xFFFFFFFF at the first byte (which adds 0xFFFFFFFF * x^(8L) mod P for a
+// message of L bytes), and the result is complemented.  Multiplication by a constant power of x is itself a linear
 // map of the 32-bit remainder, tabulated per operand byte (four 256-entry
 // tables); remainders of 16-byte units come from slicing-by-8 tables
 // (Kounavis & Berry, "A Systematic Approach to Building High Performance
@@ -39,17 +39,6 @@ __device__ __forceinline__ uint32_t gf2_mulmod(uint32_t a, uint32_t b) {
   for (int i = 0; i < 32; ++i) {
     if (a & (0x80000000u >> i)) r ^= b;
     b = (b >> 1) ^ (kPoly & (0u - (b & 1u)));
-  }
-  return r;
-}
-
-// x^(8n) mod P (square and multiply)
-__device__ __forceinline__ uint32_t gf2_xpow8(uint64_t n) {
-  uint32_t r = 0x80000000u, sq = 0x00800000u;  // 1 and x^8
-  while (n) {
-    if (n & 1) r = gf2_mulmod(r, sq);
-    sq = gf2_mulmod(sq, sq);
-    n >>= 1;
   }
   return r;
 }

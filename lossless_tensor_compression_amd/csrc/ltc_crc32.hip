@@ -11,15 +11,13 @@
 // x^(8 * seg * 2^l) mod P (the linearity rules are in ltc_crc.h).  A short
 // chunk is aligned to the END of its 64-segment frame (leading zero bytes do
 // not change a register that starts at zero), so every chunk uses the same
-// constants.  zlib's preset contributes 0xFFFFFFFF * x^(8L) mod P, for the
-// full and the last chunk length, and the result is complemented.
+// constants.  zlib's preset is the register value at the chunk's first
+// byte, so the lane whose segment holds that byte starts its register at
+// 0xFFFFFFFF; the combined register is complemented.
 //
-// compress_with_crc32 finishes with two launches.  k_crc_frames combines
-// every full chunk of the payload region from the 1 KiB frame remainders
-// k_pack accumulated while writing it, one lane per chunk (x^(8*1024)
-// multiplications from byte tables in LDS).  k_crc32 then reads back only
-// the chunks that also hold header or directory bytes and the blob's last
-// chunk, whose length is known on the device only.
+// compress_with_crc32 finishes with k_crc_frames: one lane per chunk chains
+// the 1 KiB frame remainders that k_scan and k_pack accumulated while they
+// wrote the blob (x^(8*1024) multiplications from byte tables in LDS).
 #include "ltc_crc.h"
 #include "ltc_internal.h"
 #include "ltc_launch.h"
@@ -28,6 +26,8 @@ namespace ltc {
 
 constexpr int kCrcThreads = 256;
 
+// DEVLEN: buffer lengths are read on the device (compress_with_crc32)
+template <bool DEVLEN>
 __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
   __shared__ CrcLds s;
   const uint32_t tid = threadIdx.x;
@@ -40,22 +40,15 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
     int jb = 0;
     while (jb + 1 < (int)a.count && gi >= a.jobs[jb + 1].chunk0) ++jb;
     const CrcJob& job = a.jobs[jb];
-    uint64_t i = gi - job.chunk0;
+    const uint64_t i = gi - job.chunk0;
     uint64_t len;
-    bool last;
-    if (job.len) {  // length known on the device only
+    if constexpr (DEVLEN) {  // length known on the device only
       const uint64_t total = *job.len;
       const uint64_t n = (total + a.chunk_bytes - 1) / a.chunk_bytes;
-      if (a.tail_slot && i == job.lead) {  // the last chunk, unless a leading one
-        if (n == 0 || n - 1 < job.lead) continue;
-        i = n - 1;
-      }
       if (i >= n) continue;
-      last = i + 1 == n;
-      len = last ? total - i * a.chunk_bytes : a.chunk_bytes;
+      len = i + 1 == n ? total - i * a.chunk_bytes : a.chunk_bytes;
     } else {
-      last = i + 1 == job.nchunks;
-      len = last ? job.tail_len : a.chunk_bytes;
+      len = i + 1 == job.nchunks ? job.tail_len : a.chunk_bytes;
     }
     const uint64_t pad = frame - len;  // leading virtual zero bytes
     const uint64_t vs = lane * a.seg, ve = vs + a.seg;
@@ -66,7 +59,7 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
       p = base + (vs > pad ? vs - pad : 0);
       end = base + (ve - pad);
     }
-    uint32_t crc = 0;
+    uint32_t crc = vs <= pad && pad < ve ? 0xFFFFFFFFu : 0u;  // zlib's preset at the first byte
     while (p < end && (reinterpret_cast<uintptr_t>(p) & 15)) crc = crc_step1(s, crc, *p++);
     // all sixteen 16-byte loads of a 256-byte segment are in flight together
     for (; p + 256 <= end; p += 256) {
@@ -79,19 +72,15 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
     for (; p + 16 <= end; p += 16) crc = crc_step16(s, crc, *reinterpret_cast<const uint4*>(p));
     for (; p < end; ++p) crc = crc_step1(s, crc, *p);
     crc = crc_tree64(s, crc, lane);
-    if (lane == 0) {
-      uint32_t init;
-      if (!last) init = a.init_full;
-      else if (job.len) init = gf2_mulmod(0xFFFFFFFFu, gf2_xpow8(len));
-      else init = job.init_tail;
-      job.out[i] = crc ^ init ^ 0xFFFFFFFFu;
-    }
+    if (lane == 0) job.out[i] = crc ^ 0xFFFFFFFFu;
   }
 }
 
-// One lane per chunk of the blobs' bound: a full chunk at or past the job's
-// lead that is not the blob's last is the chain of its K/1024 frame
-// remainders, each step multiplying by x^(8*1024) (one 1 KiB frame).
+// One lane per chunk of the blobs' bound.  The register starts at zlib's
+// preset at the chunk's first byte and takes in the chunk's frames one by
+// one (multiply by x^(8*1024), add the frame's remainder).  The last frame
+// of a blob can end past the blob, with zero bytes that no kernel wrote; the
+// result is then moved back by those bytes (a multiple of 16).
 __global__ __launch_bounds__(256) void k_crc_frames(CrcArgs a) {
   __shared__ uint32_t t1k[4][256];
   __shared__ uint32_t basis[32];
@@ -113,15 +102,17 @@ __global__ __launch_bounds__(256) void k_crc_frames(CrcArgs a) {
   while (jb + 1 < (int)a.count && gi >= a.jobs[jb + 1].chunk0) ++jb;
   const CrcJob& job = a.jobs[jb];
   const uint64_t i = gi - job.chunk0;
-  const uint64_t n = (*job.len + a.chunk_bytes - 1) / a.chunk_bytes;
-  if (i < job.lead || i + 1 >= n) return;
-  const uint32_t per = (uint32_t)(a.chunk_bytes / 1024);
-  const uint32_t* fr = job.frames + i * per;
+  const uint64_t total = *job.len;
+  const uint64_t lo = i * a.chunk_bytes;
+  if (lo >= total) return;
+  const uint64_t len = min(a.chunk_bytes, total - lo);
+  const uint32_t per = (uint32_t)((len + 1023) / 1024);
+  const uint32_t* fr = job.frames + lo / 1024;
   auto step = [&](uint32_t c, uint32_t v) {
     return t1k[0][c & 0xFFu] ^ t1k[1][(c >> 8) & 0xFFu] ^ t1k[2][(c >> 16) & 0xFFu] ^
            t1k[3][c >> 24] ^ v;
   };
-  uint32_t c = 0, q = 0;
+  uint32_t c = 0xFFFFFFFFu, q = 0;
   for (; q + 8 <= per; q += 8) {  // eight loads in flight
     uint32_t v[8];
 #pragma unroll
@@ -130,7 +121,9 @@ __global__ __launch_bounds__(256) void k_crc_frames(CrcArgs a) {
     for (int k = 0; k < 8; ++k) c = step(c, v[k]);
   }
   for (; q < per; ++q) c = step(c, fr[q]);
-  job.out[i] = c ^ a.init_full ^ 0xFFFFFFFFu;
+  const uint32_t z = (uint32_t)(1024ull * per - len);
+  if (z) c = gf2_mulmod(c, a.xinv[z / 16]);
+  job.out[i] = c ^ 0xFFFFFFFFu;
 }
 
 hipError_t launch_crc32_frames(const CrcArgs& a, hipStream_t st) {
@@ -156,7 +149,10 @@ hipError_t launch_crc32(const CrcArgs& a, hipStream_t st) {
   if (a.total_chunks == 0) return hipSuccess;
   const uint64_t want = (a.total_chunks + 3) / 4;
   const uint32_t grid = (uint32_t)(want < 1280 ? want : 1280);
-  hipLaunchKernelGGL(k_crc32, dim3(grid), dim3(kCrcThreads), 0, st, a);
+  if (a.jobs[0].len)
+    hipLaunchKernelGGL(k_crc32<true>, dim3(grid), dim3(kCrcThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_crc32<false>, dim3(grid), dim3(kCrcThreads), 0, st, a);
   return hipGetLastError();
 }
 

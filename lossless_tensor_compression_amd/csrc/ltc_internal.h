@@ -85,12 +85,14 @@ struct CTable {
   // the launch covers global chunks [c_begin, c_end) (a group of a pipelined
   // call, or all of them)
   uint64_t c_begin, c_end;
-  // compress_with_crc32: k_pack accumulates the remainder of every 1 KiB
-  // frame of payload it writes into CJob::frames, combining runs of frames
-  // that lie in one checksum chunk of crc_frames frames
+  // compress_with_crc32: k_scan (header) and k_pack (directory, payloads)
+  // accumulate the remainder of every 1 KiB frame of the blob into
+  // CJob::frames; k_pack combines runs of frames that lie in one checksum
+  // chunk of crc_frames frames
   uint32_t crc;
   uint32_t crc_frames;
-  uint32_t crc_lvl[7];   // x^(8*16*2^l) mod P: shifts by 16 * 2^l bytes (l = 6: 1 KiB)
+  uint32_t crc_x1k;      // x^(8*1024) mod P: one frame on
+  uint32_t crc_pos[64];  // x^(8*16*(63-k)) mod P: unit k of a frame to the frame's end
 };
 
 struct CWork {

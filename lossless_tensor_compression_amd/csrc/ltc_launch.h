@@ -24,42 +24,35 @@ hipError_t launch_decompress(int dtype, const DTable& t, hipStream_t st, const h
 struct CrcJob {
   const uint8_t* src;
   uint32_t* out;
-  uint64_t chunk0;       // first global slot of this buffer
-  uint64_t nchunks;      // slots of the buffer (see CrcArgs::tail_slot)
+  uint64_t chunk0;       // first global chunk index of this buffer
+  uint64_t nchunks;      // chunks of the buffer; with len, an upper bound
   uint64_t tail_len;     // length of the buffer's last chunk (without len)
-  uint32_t init_tail;    // 0xFFFFFFFF * x^(8*tail_len) mod P (without len)
-  // optional: the buffer is its first *len bytes, a length known only on the
-  // device (a blob being written); chunks at or past ceil(*len / K) are skipped
+  // optional (all jobs or none): the buffer is its first *len bytes, a length
+  // known only on the device (a blob being written); chunks at or past
+  // ceil(*len / K) are skipped
   const uint64_t* len;
-  // compress_with_crc32: remainders of the buffer's 1 KiB frames that k_pack
-  // accumulated for every byte at or past frames_from, and the number of
-  // leading chunks (lead = ceil(frames_from / K)) that hold other bytes too
+  // compress_with_crc32: remainders of the buffer's 1 KiB frames, accumulated
+  // by k_scan and k_pack while they wrote the blob (k_crc_frames)
   const uint32_t* frames;
-  uint64_t frames_from;
-  uint64_t lead;
 };
 
 struct CrcArgs {
   CrcJob jobs[kMaxJobs];
   uint32_t count;
-  uint64_t total_chunks;  // slots over all jobs
+  uint64_t total_chunks;
   uint64_t chunk_bytes;   // K
   uint64_t seg;           // bytes per lane segment (K rounded up to 256, / 64)
   uint32_t lvl[6];        // x^(8*seg*2^l) mod P, reflected
-  uint32_t init_full;     // 0xFFFFFFFF * x^(8K) mod P
   uint32_t x1k;           // x^(8*1024) mod P
-  // k_crc32 slots: 0 -- slot i is chunk i; 1 -- a job's slots are its `lead`
-  // leading chunks and then its last chunk (the chunks k_crc_frames leaves)
-  uint32_t tail_slot;
+  uint32_t xinv[64];      // x^(-8*16*j) mod P: moves a remainder back by 16*j bytes
 };
 
-// whether compress_with_crc32 can combine a K-byte chunk from k_pack's 1 KiB
-// frame remainders (at most 1024 frames per chunk, combined by one lane)
+// whether compress_with_crc32 can combine a K-byte chunk from the 1 KiB
+// frame remainders (at most 1024 frames per chunk, chained by one lane)
 inline bool crc_frames_usable(uint64_t K) { return K % 1024 == 0 && K <= (1u << 20); }
 
-// k_crc_frames: every full chunk at or past a job's lead, except its last,
-// combined from the frame remainders (one lane per chunk); a.total_chunks
-// then counts chunks of the bound (job.nchunks, job.chunk0 in chunks)
+// k_crc_frames: every chunk of the blobs, one lane per chunk, from the frame
+// remainders (jobs need len and frames)
 hipError_t launch_crc32_frames(const CrcArgs& a, hipStream_t st);
 
 hipError_t launch_crc32(const CrcArgs& a, hipStream_t st);
