@@ -33,11 +33,14 @@
  * enqueued after the call, so the call still behaves as work on `stream`.
  * One group's compute-bound encoding then overlaps another's memory-bound
  * passes.  The groups' offset scans run in chunk order, so blobs are the same
- * as from one group.  The internal streams (default priority) and events
- * are the library's only state: created once per device on first use, kept
- * until the process ends, and used under a lock while a call enqueues.  A
- * stream of another device than the current one, or the *_prof variants,
- * run all chunks on `stream` alone.
+ * as from one group.  Decoding blobs held in host memory
+ * (ltc_decompress_from_host) likewise copies them on an internal stream
+ * forked from and joined to `stream`.  The internal streams (default
+ * priority) and events are the library's only state: created once per device
+ * on first use, kept until the process ends, and used under a lock while a
+ * call enqueues.  For compression, a stream of another device than the
+ * current one, or the *_prof variants, run all chunks on `stream` alone; the
+ * host-blob decode needs the stream to belong to the current device.
  *
  * BLOB FORMAT v1 (byte exact; all integers little-endian).
  *   dtype codes: LTC_U8 (element 1 byte), LTC_BF16, LTC_FP16 (2 bytes),
@@ -183,6 +186,29 @@ int ltc_decompress_batch(int count, const void* const* h_headers,
                          const void* const* h_blob_ptrs, const uint64_t* h_blob_nbytes,
                          void* const* h_dst_ptrs, const uint64_t* h_dst_capacity,
                          int32_t* d_status, hipStream_t stream);
+
+/* Decode a blob held in host memory (cuZipNN 0.1.0 "API": decompress_tensor
+ * takes a blob on the CPU and decodes on the GPU; lmz README, "On a GPU":
+ * once decoding outruns the host link, the ratio becomes load bandwidth).
+ * h_blob is the whole blob (blob_nbytes bytes) in host memory, pinned
+ * (hipHostMalloc) for the copies to overlap; d_stage is a device buffer of
+ * stage_capacity >= blob_nbytes bytes, 16-byte aligned, that receives it.
+ * The blob is copied in chunk-ordered groups on a library-internal stream
+ * (forked from and joined to `stream`), and each group is decoded on
+ * `stream` as soon as its bytes have arrived.  The host reads the header and
+ * the directory from h_blob to size the copies; h_blob must stay unchanged
+ * until the call's work on `stream` has finished.  Output, status and errors
+ * as ltc_decompress, plus CAPACITY for a short staging buffer. */
+int ltc_decompress_from_host(const void* h_blob, uint64_t blob_nbytes, void* d_dst,
+                             uint64_t dst_capacity, int32_t* d_status, void* d_stage,
+                             uint64_t stage_capacity, hipStream_t stream);
+
+/* Batch form: `count` (1..LTC_BATCH_MAX) host blobs of one dtype and chunk
+ * size, each with its own staging buffer; d_status holds `count` i32. */
+int ltc_decompress_batch_from_host(int count, const void* const* h_blobs, const uint64_t* h_blob_nbytes,
+                                   void* const* h_dst_ptrs, const uint64_t* h_dst_capacity,
+                                   int32_t* d_status, void* const* h_stage_ptrs,
+                                   const uint64_t* h_stage_capacity, hipStream_t stream);
 
 /* CRC-32 (zlib's: reflected 0xEDB88320, init and final xor 0xFFFFFFFF) of
  * every chunk_bytes-byte chunk of d_src, the last one possibly shorter

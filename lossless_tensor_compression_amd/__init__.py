@@ -12,6 +12,8 @@ API (names as in cuZipNN 0.1.0, "API", and the C ABI):
   crc32_chunks(t, chunk_bytes=16384) -> int32 tensor holding CRC-32 bits
   compress_with_crc32(t, ..., checksum_chunk_bytes=16384) -> (blob, CRC-32 of
       the blob's chunks), the checksums computed while the blob is written
+  compress_to_host(t) -> pinned CPU blob; decompress_from_host(cpu_blob) ->
+      GPU tensor (copies of chunk groups overlapped with their decoding)
   compress_batch / decompress_batch for many tensors in one launch sequence
   blob_info / blob_stats for host-side inspection of a blob's header
 """
@@ -91,6 +93,8 @@ def lib():
         L.ltc_decompress.argtypes = [ctypes.c_char_p, vp, u64, vp, u64, vp, vp]
         L.ltc_decompress_batch.argtypes = [i32, pvp, pvp, pu64, pvp, pu64, vp, vp]
         L.ltc_decompress_batch_prof.argtypes = [i32, pvp, pvp, pu64, pvp, pu64, vp, vp, pvp]
+        L.ltc_decompress_from_host.argtypes = [vp, u64, vp, u64, vp, vp, u64, vp]
+        L.ltc_decompress_batch_from_host.argtypes = [i32, pvp, pu64, pvp, pu64, vp, pvp, pu64, vp]
         L.ltc_crc32_chunks.argtypes = [vp, u64, u32, vp, vp]
         L.ltc_crc32_chunks_batch.argtypes = [i32, pvp, pu64, u32, pvp, vp]
         L.ltc_blob_stats.argtypes = [ctypes.c_char_p, u64, ctypes.POINTER(Stats)]
@@ -99,7 +103,8 @@ def lib():
                      "ltc_compress_with_crc32", "ltc_compress_batch_with_crc32",
                      "ltc_compress_batch_with_crc32_prof",
                      "ltc_blob_info", "ltc_decompress", "ltc_decompress_batch",
-                     "ltc_decompress_batch_prof", "ltc_crc32_chunks", "ltc_crc32_chunks_batch",
+                     "ltc_decompress_batch_prof", "ltc_decompress_from_host",
+                     "ltc_decompress_batch_from_host", "ltc_crc32_chunks", "ltc_crc32_chunks_batch",
                      "ltc_blob_stats"):
             getattr(L, name).restype = i32
         _lib = L
@@ -294,6 +299,63 @@ def decompress_batch(blobs, shapes=None, check=True):
 
 def decompress(blob, shape=None):
     return decompress_batch([blob], [shape])[0]
+
+
+def decompress_from_host_raw(h_blob_ptrs, blob_nbytes, dst_ptrs, caps, status_ptr, stage_ptrs,
+                             stage_caps, stream=None):
+    """Pointer-level batch decode of blobs in host memory through device
+    staging buffers, on `stream` (no allocation, no sync)."""
+    count = len(h_blob_ptrs)
+    _check(lib().ltc_decompress_batch_from_host(count, _ptrs(h_blob_ptrs), _u64s(blob_nbytes),
+                                                _ptrs(dst_ptrs), _u64s(caps),
+                                                ctypes.c_void_p(status_ptr), _ptrs(stage_ptrs),
+                                                _u64s(stage_caps), _stream(stream)),
+           "decompress_from_host")
+
+
+def decompress_batch_from_host(blobs, shapes=None, device=None, check=True):
+    """Decoded GPU tensors of up to 32 blobs held in CPU memory (uint8 CPU
+    tensors, pinned for the copies to overlap the decoding)."""
+    if not 1 <= len(blobs) <= BATCH_MAX:
+        raise ValueError(f"1..{BATCH_MAX} blobs per batch")
+    if any(b.is_cuda or b.dtype != torch.uint8 or not b.is_contiguous() for b in blobs):
+        raise ValueError("blobs must be contiguous uint8 CPU tensors")
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    infos = [blob_info(_header_bytes(b)) for b in blobs]
+    outs = [torch.empty(i["nbytes"], dtype=torch.uint8, device=dev) for i in infos]
+    stages = [torch.empty(max(b.numel(), 16), dtype=torch.uint8, device=dev) for b in blobs]
+    status = torch.full((len(blobs),), -99, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        decompress_from_host_raw([b.data_ptr() for b in blobs], [b.numel() for b in blobs],
+                                 [o.data_ptr() for o in outs], [o.numel() for o in outs],
+                                 status.data_ptr(), [st.data_ptr() for st in stages],
+                                 [st.numel() for st in stages])
+        st = status.cpu().tolist()  # synchronises: the host blobs are free again
+    if check:
+        for v in st:
+            _check(v, "decompress_from_host (device status)")
+    res = []
+    for k, (o, i) in enumerate(zip(outs, infos)):
+        t = o.view(CODE_DTYPE[i["dtype"]])
+        if shapes is not None and shapes[k] is not None:
+            t = t.view(shapes[k])
+        res.append(t)
+    return res
+
+
+def decompress_from_host(blob, shape=None, device=None):
+    """cuZipNN's decompress_tensor for a CPU blob: decoded on the GPU."""
+    return decompress_batch_from_host([blob], [shape], device)[0]
+
+
+def compress_to_host(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
+                     pin_memory=True):
+    """cuZipNN's compress_tensor: the blob of a GPU tensor as a 1-D uint8 CPU
+    tensor (pinned by default, ready for decompress_from_host)."""
+    blob = compress(t, chunk_bytes, passthrough_threshold)
+    out = torch.empty(blob.numel(), dtype=torch.uint8, pin_memory=pin_memory)
+    out.copy_(blob)
+    return out
 
 
 def crc32_chunks(t, chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):

@@ -28,9 +28,18 @@ constexpr uint32_t kWordsGranule = 1024;
 constexpr int kPipeGroups = 4;
 constexpr uint64_t kPipeMinChunks = 512;
 
+// ---- decoding blobs held in host memory
+// The blobs are copied into device staging buffers in chunk-ordered groups
+// on an internal stream (the DMA engines), and each group is decoded on the
+// caller's stream as soon as its bytes have arrived, so decoding overlaps the
+// transfer of the following groups.
+constexpr int kCopyGroupsMax = 64;
+constexpr uint64_t kCopyGroupBytes = 4ull << 20;  // at least this much per group
+
 struct PipeRes {
   hipStream_t s[kPipeGroups] = {};
   hipEvent_t fork = nullptr, scan[kPipeGroups] = {}, done[kPipeGroups] = {};
+  hipEvent_t copied[kCopyGroupsMax] = {};
   bool ok = false;
 };
 std::mutex g_pipe_mu;
@@ -51,6 +60,8 @@ PipeRes* pipe_res(hipStream_t stream) {
       ok = ok && hipEventCreateWithFlags(&r->scan[g], hipEventDisableTiming) == hipSuccess;
       ok = ok && hipEventCreateWithFlags(&r->done[g], hipEventDisableTiming) == hipSuccess;
     }
+    for (int g = 0; g < kCopyGroupsMax; ++g)
+      ok = ok && hipEventCreateWithFlags(&r->copied[g], hipEventDisableTiming) == hipSuccess;
     r->ok = ok;
     g_pipe[dev] = r;
   }
@@ -339,11 +350,64 @@ uint16_t rd16(const uint8_t* p) {
   return v;
 }
 
+// byte offset of stream s in a blob's directory, read from host memory
+uint64_t dir_offset(const uint8_t* h_blob, uint64_t s) { return rd64(h_blob + kHeader + kDirEntry * s); }
+
+// Copies and decodes blobs held in host memory (t's blobs are the staging
+// buffers; every header was checked).  Group g holds global chunks
+// [T*g/G, T*(g+1)/G); its bytes of blob j are that tensor's directory (first
+// group of the tensor) and the payloads from the first stream of its first
+// chunk to the first stream of the next group's (or the blob's end), clamped
+// to the blob.  The decoder validates every offset it uses, so a corrupt
+// directory can only leave bytes of the staging buffer stale, never lead to
+// an access outside it.
+hipError_t decode_from_host(int dtype, const DTable& t, uint32_t e, const void* const* host_blobs,
+                            hipStream_t stream) {
+  const uint64_t T = t.total_chunks;
+  if (T == 0) return launch_decompress_range(dtype, t, stream, nullptr, 0, 0, true);
+  uint64_t total = 0;
+  for (uint32_t j = 0; j < t.count; ++j) total += t.jobs[j].blob_nbytes;
+  uint64_t G = total / kCopyGroupBytes;
+  G = G < 1 ? 1 : (G > (uint64_t)kCopyGroupsMax ? kCopyGroupsMax : G);
+  if (G > T) G = T;
+  std::lock_guard<std::mutex> lock(g_pipe_mu);
+  PipeRes* r = pipe_res(stream);
+  if (!r) return hipErrorInvalidValue;
+  hipStream_t cs = r->s[1];
+  hipError_t err = hipEventRecord(r->fork, stream);
+  if (err == hipSuccess) err = hipStreamWaitEvent(cs, r->fork, 0);
+  for (uint64_t g = 0; g < G && err == hipSuccess; ++g) {
+    const uint64_t c0 = T * g / G, c1 = T * (g + 1) / G;
+    for (uint32_t j = 0; j < t.count && err == hipSuccess; ++j) {
+      const DJob& jb = t.jobs[j];
+      if (c1 <= jb.chunk0 || c0 >= jb.chunk0 + jb.nchunks) continue;  // no chunk of blob j here
+      const uint64_t lo_c = c0 > jb.chunk0 ? c0 - jb.chunk0 : 0;
+      const uint64_t hi_c = c1 - jb.chunk0 < jb.nchunks ? c1 - jb.chunk0 : jb.nchunks;
+      const uint8_t* hb = static_cast<const uint8_t*>(host_blobs[j]);
+      const uint64_t B = jb.blob_nbytes;
+      uint64_t lo = lo_c == 0 ? 0 : dir_offset(hb, lo_c * e);
+      uint64_t hi = hi_c == jb.nchunks ? B : dir_offset(hb, hi_c * e);
+      lo = lo < B ? lo : B;
+      hi = hi < lo ? lo : (hi < B ? hi : B);
+      if (hi > lo)
+        err = hipMemcpyAsync(const_cast<uint8_t*>(jb.blob) + lo, hb + lo, hi - lo, hipMemcpyHostToDevice, cs);
+    }
+    if (err == hipSuccess) err = hipEventRecord(r->copied[g], cs);
+    if (err == hipSuccess) err = hipStreamWaitEvent(stream, r->copied[g], 0);
+    if (err == hipSuccess) err = launch_decompress_range(dtype, t, stream, nullptr, c0, c1, g == 0);
+  }
+  return err;
+}
+
+// host_blobs (optional): the whole blobs in host memory; blobs are then the
+// device staging buffers they are copied into (stage_caps bytes each)
 int decompress_impl(int count, const void* const* headers, const void* const* blobs,
                     const uint64_t* blob_nbytes, void* const* dsts, const uint64_t* caps,
-                    int32_t* d_status, hipStream_t stream, const hipEvent_t* ev) {
+                    int32_t* d_status, hipStream_t stream, const hipEvent_t* ev,
+                    const void* const* host_blobs = nullptr, const uint64_t* stage_caps = nullptr) {
   if (count < 1 || count > kMaxJobs || !headers || !blobs || !blob_nbytes || !dsts || !caps || !d_status)
     return LTC_ERR_INVALID_ARGUMENT;
+  if (host_blobs && !stage_caps) return LTC_ERR_INVALID_ARGUMENT;
   DTable t;
   memset(&t, 0, sizeof(t));
   t.count = (uint32_t)count;
@@ -366,6 +430,7 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
     if (caps[i] < info.nbytes) return LTC_ERR_CAPACITY;
     if (!blobs[i] || (info.nbytes && !dsts[i])) return LTC_ERR_INVALID_ARGUMENT;
     if (reinterpret_cast<uintptr_t>(blobs[i]) % 16) return LTC_ERR_INVALID_ARGUMENT;
+    if (host_blobs && stage_caps[i] < info.blob_nbytes) return LTC_ERR_CAPACITY;
     DJob& jb = t.jobs[i];
     jb.blob = static_cast<const uint8_t*>(blobs[i]);
     jb.dst = static_cast<uint8_t*>(dsts[i]);
@@ -384,7 +449,8 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
   t.n_full = chunk_bytes / e;
   t.vec16 = (vec && chunk_bytes % 16 == 0) ? 1u : 0u;
   t.total_chunks = chunk0;
-  return launch_decompress(dtype, t, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+  if (!host_blobs) return launch_decompress(dtype, t, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+  return decode_from_host(dtype, t, e, host_blobs, stream) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 }
 
 }  // namespace
@@ -535,6 +601,29 @@ int ltc_decompress_batch_prof(int count, const void* const* h_headers, const voi
                               const hipEvent_t* h_events) {
   return decompress_impl(count, h_headers, h_blob_ptrs, h_blob_nbytes, h_dst_ptrs, h_dst_capacity,
                          d_status, stream, h_events);
+}
+
+int ltc_decompress_from_host(const void* h_blob, uint64_t blob_nbytes, void* d_dst,
+                             uint64_t dst_capacity, int32_t* d_status, void* d_stage,
+                             uint64_t stage_capacity, hipStream_t stream) {
+  return ltc_decompress_batch_from_host(1, &h_blob, &blob_nbytes, &d_dst, &dst_capacity, d_status,
+                                        &d_stage, &stage_capacity, stream);
+}
+
+int ltc_decompress_batch_from_host(int count, const void* const* h_blobs, const uint64_t* h_blob_nbytes,
+                                   void* const* h_dst_ptrs, const uint64_t* h_dst_capacity,
+                                   int32_t* d_status, void* const* h_stage_ptrs,
+                                   const uint64_t* h_stage_capacity, hipStream_t stream) {
+  if (count < 1 || count > kMaxJobs || !h_blobs || !h_blob_nbytes || !h_stage_ptrs || !h_stage_capacity)
+    return LTC_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < count; ++i) {
+    if (!h_blobs[i]) return LTC_ERR_INVALID_ARGUMENT;
+    if (h_blob_nbytes[i] < kHeader) return LTC_ERR_CORRUPT;
+  }
+  // the headers are the first bytes of the host blobs
+  return decompress_impl(count, h_blobs, const_cast<const void* const*>(h_stage_ptrs), h_blob_nbytes,
+                         h_dst_ptrs, h_dst_capacity, d_status, stream, nullptr, h_blobs,
+                         h_stage_capacity);
 }
 
 int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,

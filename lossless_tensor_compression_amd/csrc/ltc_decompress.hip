@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   // decoded symbols of a block: dword 64*(q/4) + l holds steps q..q+3 of lane l
   __shared__ __attribute__((aligned(16))) uint32_t stage[MAXR][128];
 
-  const uint64_t g = blockIdx.x;
+  const uint64_t g = t.c_begin + blockIdx.x;
   const int j = find_job(t, g);
   const DJob& job = t.jobs[j];
   const uint64_t c = g - job.chunk0;
@@ -448,27 +448,35 @@ __global__ void k_status_init(DTable t) {
 }
 
 template <int DT>
-static hipError_t launch_decompress_t(const DTable& t, hipStream_t st, const hipEvent_t* ev) {
+static hipError_t launch_decompress_t(DTable t, hipStream_t st, const hipEvent_t* ev, uint64_t c_begin,
+                                      uint64_t c_end, bool init_status) {
   constexpr int E = Dt<DT>::E;
-  hipLaunchKernelGGL(k_status_init, dim3(1), dim3(64), 0, st, t);
+  t.c_begin = c_begin;
+  const uint64_t n = c_end - c_begin;
+  if (init_status) hipLaunchKernelGGL(k_status_init, dim3(1), dim3(64), 0, st, t);
   record(ev, 0, st);
-  if (t.total_chunks) hipLaunchKernelGGL((k_decode<DT, 1>), dim3((uint32_t)t.total_chunks), dim3(64), 0, st, t);
+  if (n) hipLaunchKernelGGL((k_decode<DT, 1>), dim3((uint32_t)n), dim3(64), 0, st, t);
   record(ev, 1, st);
   if constexpr (E > 1) {
-    if (t.total_chunks) hipLaunchKernelGGL((k_decode<DT, E>), dim3((uint32_t)t.total_chunks), dim3(64), 0, st, t);
+    if (n) hipLaunchKernelGGL((k_decode<DT, E>), dim3((uint32_t)n), dim3(64), 0, st, t);
   }
   record(ev, 2, st);
   return hipGetLastError();
 }
 
-hipError_t launch_decompress(int dtype, const DTable& t, hipStream_t st, const hipEvent_t* ev) {
+hipError_t launch_decompress_range(int dtype, const DTable& t, hipStream_t st, const hipEvent_t* ev,
+                                   uint64_t c_begin, uint64_t c_end, bool init_status) {
   switch (dtype) {
-    case LTC_U8: return launch_decompress_t<LTC_U8>(t, st, ev);
-    case LTC_BF16: return launch_decompress_t<LTC_BF16>(t, st, ev);
-    case LTC_FP16: return launch_decompress_t<LTC_FP16>(t, st, ev);
-    case LTC_FP32: return launch_decompress_t<LTC_FP32>(t, st, ev);
+    case LTC_U8: return launch_decompress_t<LTC_U8>(t, st, ev, c_begin, c_end, init_status);
+    case LTC_BF16: return launch_decompress_t<LTC_BF16>(t, st, ev, c_begin, c_end, init_status);
+    case LTC_FP16: return launch_decompress_t<LTC_FP16>(t, st, ev, c_begin, c_end, init_status);
+    case LTC_FP32: return launch_decompress_t<LTC_FP32>(t, st, ev, c_begin, c_end, init_status);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decompress(int dtype, const DTable& t, hipStream_t st, const hipEvent_t* ev) {
+  return launch_decompress_range(dtype, t, st, ev, 0, t.total_chunks, true);
 }
 
 }  // namespace ltc

@@ -122,6 +122,7 @@ struct DTable {
   uint32_t n_full;
   uint32_t vec16;       // every dst 16-byte aligned and chunk_bytes % 16 == 0
   uint64_t total_chunks;
+  uint64_t c_begin;     // a launch decodes global chunks [c_begin, c_begin + grid)
 };
 
 template <class T>

@@ -21,6 +21,11 @@ hipError_t launch_zero_u32(uint32_t* p, uint64_t n, hipStream_t st);
 // multi-table decode kernels
 hipError_t launch_decompress(int dtype, const DTable& t, hipStream_t st, const hipEvent_t* ev);
 
+// the same for global chunks [c_begin, c_end) only; init_status: also set
+// every job's status to OK first (the first range of a call)
+hipError_t launch_decompress_range(int dtype, const DTable& t, hipStream_t st, const hipEvent_t* ev,
+                                   uint64_t c_begin, uint64_t c_end, bool init_status);
+
 struct CrcJob {
   const uint8_t* src;
   uint32_t* out;
