@@ -47,7 +47,7 @@ def test_c1_one_group(ltc):
 
 
 def test_c2_many_groups(ltc):
-    # a ~50 MB blob: a dozen copy groups, each decoded as it lands
+    # a ~50 MB blob: three copy groups, each decoded as it lands
     _check_host_decode(ltc, workloads.c2(), 3, label="C2")
 
 
@@ -74,7 +74,7 @@ def test_small_and_ragged(ltc, dtype, nelem, chunk):
 def test_batch_groups_split_tensors(ltc):
     """A batch whose copy groups start and end inside different tensors."""
     rng = np.random.default_rng(12)
-    sizes = (3_000_001, 0, 1, 2_500_000, 17, 4_000_000, 1_000)
+    sizes = (9_000_001, 0, 1, 7_500_000, 17, 12_000_000, 1_000)  # ~90 MB of blobs: 5 groups
     arrs = [(rng.standard_normal(n) * rng.choice([0.02, 1.0, 1e-3])).astype(np.float32) for n in sizes]
     blobs = [oracle.compress(a, 3, 65536) for a in arrs]
     banner(f"host batch: {len(arrs)} blobs, {sum(b.size for b in blobs)} bytes")
