@@ -17,6 +17,7 @@ from . import build as _build
 DTYPES = {"u8": 0, "bf16": 1, "fp16": 2, "fp32": 3}
 ELEM_BYTES = {0: 1, 1: 2, 2: 2, 3: 4}
 MODE_RAW, MODE_RANS, MODE_CONST = 0, 1, 2
+FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
 
 OK = 0
 ERR_INVALID_ARGUMENT = -1
@@ -64,6 +65,10 @@ def lib():
         L.ltco_compress_bound.restype = c.c_uint64
         L.ltco_compress.argtypes = [u8p, c.c_uint64, c.c_int, c.c_uint32,
                                     c.c_double, u8p, c.c_uint64, u64p, c.c_int]
+        L.ltco_compress_bound_ex.argtypes = [c.c_uint64, c.c_int, c.c_uint32, c.c_uint32]
+        L.ltco_compress_bound_ex.restype = c.c_uint64
+        L.ltco_compress_ex.argtypes = [u8p, c.c_uint64, c.c_int, c.c_uint32, c.c_double,
+                                       c.c_uint32, u8p, c.c_uint64, u64p, c.c_int]
         L.ltco_encode_chunk.argtypes = [u8p, c.c_uint64, c.c_int, c.c_uint32,
                                         c.c_double, c.c_uint64, u8p, u8p, u32p,
                                         u8p, c.c_uint64, u64p]
@@ -145,20 +150,23 @@ def rans_decode(words, states, f, n):
     return rc, out[:n].copy()
 
 
-def compress_bound(nbytes, dtype, chunk_bytes=131072):
-    return lib().ltco_compress_bound(nbytes, dtype, chunk_bytes)
+def compress_bound(nbytes, dtype, chunk_bytes=131072, shared_tables=False):
+    return lib().ltco_compress_bound_ex(nbytes, dtype, chunk_bytes,
+                                        FLAG_SHARED_TABLES if shared_tables else 0)
 
 
-def compress(src, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None):
-    """Blob (np.uint8) of the bytes of `src` read as `dtype` (a code)."""
+def compress(src, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None, shared_tables=False):
+    """Blob (np.uint8) of the bytes of `src` read as `dtype` (a code);
+    shared_tables: format v2 (one frequency table per stream index)."""
     b = _as_bytes(src)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
-    cap = max(64, compress_bound(b.size, dtype, chunk_bytes))
+    cap = max(64, compress_bound(b.size, dtype, chunk_bytes, shared_tables))
     blob = np.zeros(cap, dtype=np.uint8)
     nb = ctypes.c_uint64(0)
-    rc = lib().ltco_compress(_u8p(b), b.size, dtype, chunk_bytes, threshold,
-                             _u8p(blob), blob.size, ctypes.byref(nb), int(nthreads))
+    rc = lib().ltco_compress_ex(_u8p(b), b.size, dtype, chunk_bytes, threshold,
+                                FLAG_SHARED_TABLES if shared_tables else 0,
+                                _u8p(blob), blob.size, ctypes.byref(nb), int(nthreads))
     if rc:
         raise ValueError(f"oracle compress: status {rc}")
     return blob[: nb.value].copy()

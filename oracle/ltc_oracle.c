@@ -460,12 +460,207 @@ int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
   return rc;
 }
 
+/* ---- format v2: one frequency table per stream index (shared tables) ---- */
+
+/* bytes of a table record: 16-byte head plus f[lo..hi], padded to 16 */
+static uint64_t record_bytes(int lo, int hi) {
+  return lo > hi ? 16u : align16(16u + 2u * (uint64_t)(hi - lo + 1));
+}
+
+/* v2 stream: CONST as in v1; otherwise coded with the plane's table f (which
+ * covers every value of the stream) and kept if the payload (272 + 2W bytes)
+ * is at most P_max, else RAW. */
+static int encode_stream_shared(const uint8_t* sym, uint64_t n, double theta,
+                                const uint16_t f[256], stream_result* r) {
+  uint64_t h[256];
+  ltco_histogram(sym, n, h);
+  int nonzero = 0, only = 0;
+  for (int v = 0; v < 256; v++)
+    if (h[v]) {
+      nonzero++;
+      only = v;
+    }
+  r->payload = NULL;
+  r->cval = 0;
+  if (nonzero == 1) {
+    r->mode = LTCO_MODE_CONST;
+    r->cval = (uint8_t)only;
+    r->size = 0;
+    return LTCO_OK;
+  }
+  uint32_t states[64];
+  uint16_t* words = (uint16_t*)malloc(n * sizeof(uint16_t));
+  if (!words) return LTCO_ERR_INVALID_ARGUMENT;
+  uint64_t nw = 0;
+  int rc = ltco_rans_encode(sym, n, f, states, words, n, &nw);
+  if (rc) {
+    free(words);
+    return rc;
+  }
+  uint64_t p = RANS_FIXED + 2 * nw;
+  if (p <= ltco_p_max(n, theta)) {
+    uint8_t* pl = (uint8_t*)calloc(p, 1);
+    if (!pl) {
+      free(words);
+      return LTCO_ERR_INVALID_ARGUMENT;
+    }
+    put_u32(pl + 0, (uint32_t)nw);
+    for (int l = 0; l < LANES; l++) put_u32(pl + 16 + 4 * l, states[l]);
+    for (uint64_t i = 0; i < nw; i++) put_u16(pl + RANS_FIXED + 2 * i, words[i]);
+    r->mode = LTCO_MODE_RANS;
+    r->size = (uint32_t)p;
+    r->payload = pl;
+  } else {
+    uint8_t* pl = (uint8_t*)malloc(n);
+    if (!pl) {
+      free(words);
+      return LTCO_ERR_INVALID_ARGUMENT;
+    }
+    memcpy(pl, sym, n);
+    r->mode = LTCO_MODE_RAW;
+    r->size = (uint32_t)n;
+    r->payload = pl;
+  }
+  free(words);
+  return LTCO_OK;
+}
+
+uint64_t ltco_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                                uint32_t flags) {
+  uint64_t b = ltco_compress_bound(nbytes, dtype, chunk_bytes);
+  if (b && (flags & LTCO_FLAG_SHARED_TABLES))
+    b += (uint64_t)ltco_elem_bytes(dtype) * record_bytes(0, 255);
+  return b;
+}
+
+static int compress_shared(const uint8_t* src, uint64_t nbytes, int dtype,
+                           uint32_t chunk_bytes, double theta, uint8_t* blob,
+                           uint64_t blob_capacity, uint64_t* blob_nbytes,
+                           int nthreads) {
+  int e = ltco_elem_bytes(dtype);
+  uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
+  uint64_t s = k * (uint64_t)e;
+  if (nthreads < 1) nthreads = 1;
+  /* plane k's histogram: the sum of stream k's histograms over all chunks */
+  uint64_t plane[4][256];
+  memset(plane, 0, sizeof(plane));
+  uint8_t* sym = (uint8_t*)malloc(chunk_bytes / (uint32_t)e + 1);
+  if (!sym) return LTCO_ERR_INVALID_ARGUMENT;
+  for (uint64_t c = 0; c < k; c++)
+    for (int q = 0; q < e; q++) {
+      uint64_t n = ltco_chunk_stream(src, nbytes, dtype, chunk_bytes, c, q, sym);
+      uint64_t h[256];
+      ltco_histogram(sym, n, h);
+      for (int v = 0; v < 256; v++) plane[q][v] += h[v];
+    }
+  free(sym);
+  uint16_t f[4][256];
+  int lo[4], hi[4];
+  for (int q = 0; q < e; q++) {
+    lo[q] = 0;
+    hi[q] = 255;
+    while (lo[q] < 256 && plane[q][lo[q]] == 0) lo[q]++;
+    while (hi[q] >= 0 && plane[q][hi[q]] == 0) hi[q]--;
+    memset(f[q], 0, sizeof(f[q]));
+    if (lo[q] < hi[q]) {
+      int rc = ltco_normalize(plane[q], f[q]);
+      if (rc) return rc;
+    } else {  /* at most one value in the whole plane: no table */
+      lo[q] = 1;
+      hi[q] = 0;
+    }
+  }
+  stream_result* res = (stream_result*)calloc(s ? s : 1, sizeof(stream_result));
+  if (!res) return LTCO_ERR_INVALID_ARGUMENT;
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (long long c = 0; c < (long long)k; c++) {
+    uint8_t* cs = (uint8_t*)malloc(chunk_bytes / (uint32_t)e + 1);
+    int r = cs ? LTCO_OK : LTCO_ERR_INVALID_ARGUMENT;
+    for (int q = 0; q < e && r == LTCO_OK; q++) {
+      uint64_t n = ltco_chunk_stream(src, nbytes, dtype, chunk_bytes, (uint64_t)c, q, cs);
+      r = encode_stream_shared(cs, n, theta, f[q], res + (uint64_t)c * e + q);
+    }
+    free(cs);
+    if (r) {
+#pragma omp atomic write
+      failed = r;
+    }
+  }
+  uint64_t tables = 0;
+  for (int q = 0; q < e; q++) tables += record_bytes(lo[q], hi[q]);
+  uint64_t base = HDR_BYTES + DIR_BYTES * s + tables;
+  uint64_t cursor = base;
+  for (uint64_t i = 0; i < s; i++) cursor = align16(cursor + res[i].size);
+  int rc = LTCO_OK;
+  if (failed) {
+    rc = failed;
+  } else if (cursor > blob_capacity) {
+    rc = LTCO_ERR_CAPACITY;
+  } else {
+    memset(blob, 0, cursor);
+    memcpy(blob, "LTCB", 4);
+    put_u16(blob + 4, 2);
+    blob[6] = (uint8_t)dtype;
+    blob[7] = (uint8_t)e;
+    put_u64(blob + 8, nbytes);
+    put_u32(blob + 16, chunk_bytes);
+    put_u32(blob + 20, (uint32_t)k);
+    put_u16(blob + 24, LANES);
+    blob[26] = 12;
+    blob[27] = (uint8_t)LTCO_FLAG_SHARED_TABLES;
+    put_u64(blob + 32, cursor);
+    put_u64(blob + 40, base);
+    uint64_t t = HDR_BYTES + DIR_BYTES * s;
+    for (int q = 0; q < e; q++) {
+      put_u16(blob + t, (uint32_t)lo[q]);
+      put_u16(blob + t + 2, (uint32_t)hi[q]);
+      for (int v = lo[q]; v <= hi[q]; v++) put_u16(blob + t + 16 + 2 * (uint64_t)(v - lo[q]), f[q][v]);
+      t += record_bytes(lo[q], hi[q]);
+    }
+    uint64_t cur = base;
+    for (uint64_t i = 0; i < s; i++) {
+      uint8_t* d = blob + HDR_BYTES + DIR_BYTES * i;
+      put_u64(d, cur);
+      put_u32(d + 8, res[i].size);
+      d[12] = res[i].mode;
+      d[13] = res[i].cval;
+      if (res[i].size) memcpy(blob + cur, res[i].payload, res[i].size);
+      cur = align16(cur + res[i].size);
+    }
+    *blob_nbytes = cursor;
+  }
+  for (uint64_t i = 0; i < s; i++) free(res[i].payload);
+  free(res);
+  return rc;
+}
+
+int ltco_compress_ex(const uint8_t* src, uint64_t nbytes, int dtype,
+                     uint32_t chunk_bytes, double theta, uint32_t flags,
+                     uint8_t* blob, uint64_t blob_capacity, uint64_t* blob_nbytes,
+                     int nthreads) {
+  if (flags & ~(uint32_t)LTCO_FLAG_SHARED_TABLES) return LTCO_ERR_INVALID_ARGUMENT;
+  if (!(flags & LTCO_FLAG_SHARED_TABLES))
+    return ltco_compress(src, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity,
+                         blob_nbytes, nthreads);
+  int rc = check_args(nbytes, dtype, chunk_bytes, theta);
+  if (rc) return rc;
+  return compress_shared(src, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity,
+                         blob_nbytes, nthreads);
+}
+
 typedef struct {
   uint64_t off;
   uint32_t size;
   uint8_t mode;
   uint8_t cval;
 } dir_entry;
+
+/* a v2 blob's tables, one per stream index (present = 0: no table) */
+typedef struct {
+  int present[4];
+  uint16_t f[4][256];
+} shared_tables;
 
 /* Structural checks of one RANS payload (lo, hi, zeros, table, states). */
 static int check_rans_payload(const uint8_t* pl, uint32_t size, uint16_t f[256],
@@ -499,8 +694,24 @@ static int check_rans_payload(const uint8_t* pl, uint32_t size, uint16_t f[256],
   return LTCO_OK;
 }
 
+/* Structural checks of one v2 RANS payload (zeros, word count, states). */
+static int check_shared_payload(const uint8_t* pl, uint32_t size, uint32_t states[64],
+                                uint64_t* nwords) {
+  if (size < RANS_FIXED) return LTCO_ERR_CORRUPT;
+  uint32_t nw = get_u32(pl);
+  for (int i = 4; i < 16; i++)
+    if (pl[i]) return LTCO_ERR_CORRUPT;
+  if ((uint64_t)size - RANS_FIXED != 2 * (uint64_t)nw) return LTCO_ERR_CORRUPT;
+  for (int l = 0; l < LANES; l++) {
+    states[l] = get_u32(pl + 16 + 4 * l);
+    if (states[l] < RANS_LOW) return LTCO_ERR_CORRUPT;
+  }
+  *nwords = nw;
+  return LTCO_OK;
+}
+
 static int decode_chunk(const uint8_t* blob, const dir_entry* ent, int dtype,
-                        int e, uint64_t n, uint8_t* dst) {
+                        int e, uint64_t n, uint8_t* dst, const shared_tables* st) {
   uint8_t* planes = (uint8_t*)malloc((uint64_t)e * (n ? n : 1));
   if (!planes) return LTCO_ERR_INVALID_ARGUMENT;
   int rc = LTCO_OK;
@@ -515,7 +726,17 @@ static int decode_chunk(const uint8_t* blob, const dir_entry* ent, int dtype,
       uint16_t f[256];
       uint32_t states[64];
       uint64_t nw = 0, wo = 0;
-      rc = check_rans_payload(pl, ent[k].size, f, states, &nw, &wo);
+      if (st) {  /* v2: the plane's table */
+        if (!st->present[k]) {
+          rc = LTCO_ERR_CORRUPT;
+          break;
+        }
+        memcpy(f, st->f[k], sizeof(f));
+        wo = RANS_FIXED;
+        rc = check_shared_payload(pl, ent[k].size, states, &nw);
+      } else {
+        rc = check_rans_payload(pl, ent[k].size, f, states, &nw, &wo);
+      }
       if (rc) break;
       uint16_t* words = (uint16_t*)malloc((nw ? nw : 1) * sizeof(uint16_t));
       if (!words) {
@@ -542,7 +763,8 @@ int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
                     uint64_t dst_capacity, uint64_t* out_nbytes, int nthreads) {
   if (blob_nbytes < HDR_BYTES) return LTCO_ERR_CORRUPT;
   if (memcmp(blob, "LTCB", 4) != 0) return LTCO_ERR_BAD_MAGIC;
-  if (get_u16(blob + 4) != 1) return LTCO_ERR_BAD_VERSION;
+  const int version = (int)get_u16(blob + 4);
+  if (version != 1 && version != 2) return LTCO_ERR_BAD_VERSION;
   int dtype = blob[6];
   int e = ltco_elem_bytes(dtype);
   if (e == 0) return LTCO_ERR_UNSUPPORTED_DTYPE;
@@ -550,8 +772,8 @@ int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
   uint64_t nbytes = get_u64(blob + 8);
   uint32_t chunk_bytes = get_u32(blob + 16);
   uint64_t k = get_u32(blob + 20);
-  if (get_u16(blob + 24) != LANES || blob[26] != 12 || blob[27] != 0 ||
-      get_u32(blob + 28) != 0)
+  if (get_u16(blob + 24) != LANES || blob[26] != 12 ||
+      blob[27] != (version == 2 ? LTCO_FLAG_SHARED_TABLES : 0) || get_u32(blob + 28) != 0)
     return LTCO_ERR_CORRUPT;
   for (int i = 48; i < 64; i++)
     if (blob[i]) return LTCO_ERR_CORRUPT;
@@ -561,9 +783,40 @@ int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
   if (k != (nbytes + chunk_bytes - 1) / chunk_bytes) return LTCO_ERR_CORRUPT;
   uint64_t s = k * (uint64_t)e;
   uint64_t base = HDR_BYTES + DIR_BYTES * s;
-  if (get_u64(blob + 40) != base) return LTCO_ERR_CORRUPT;
   if (get_u64(blob + 32) != blob_nbytes) return LTCO_ERR_CORRUPT;
   if (base > blob_nbytes) return LTCO_ERR_CORRUPT;
+  shared_tables st;
+  if (version == 2) {
+    /* table records follow the directory, one per stream index */
+    uint64_t t = base;
+    for (int q = 0; q < e; q++) {
+      if (t + 16 > blob_nbytes) return LTCO_ERR_CORRUPT;
+      int lo = (int)get_u16(blob + t), hi = (int)get_u16(blob + t + 2);
+      for (int i = 4; i < 16; i++)
+        if (blob[t + i]) return LTCO_ERR_CORRUPT;
+      if (lo == 1 && hi == 0) {
+        st.present[q] = 0;
+        t += 16;
+        continue;
+      }
+      if (lo >= hi || hi > 255) return LTCO_ERR_CORRUPT;
+      uint64_t rb = record_bytes(lo, hi);
+      if (t + rb > blob_nbytes) return LTCO_ERR_CORRUPT;
+      memset(st.f[q], 0, sizeof(st.f[q]));
+      uint32_t total = 0;
+      for (int v = lo; v <= hi; v++) {
+        st.f[q][v] = (uint16_t)get_u16(blob + t + 16 + 2 * (uint64_t)(v - lo));
+        total += st.f[q][v];
+      }
+      for (uint64_t i = 16 + 2 * (uint64_t)(hi - lo + 1); i < rb; i++)
+        if (blob[t + i]) return LTCO_ERR_CORRUPT;
+      if (st.f[q][lo] == 0 || st.f[q][hi] == 0 || total != M_TOTAL) return LTCO_ERR_CORRUPT;
+      st.present[q] = 1;
+      t += rb;
+    }
+    base = t;
+  }
+  if (get_u64(blob + 40) != base) return LTCO_ERR_CORRUPT;
   if (dst_capacity < nbytes) return LTCO_ERR_CAPACITY;
 
   dir_entry* ent = (dir_entry*)malloc((s ? s : 1) * sizeof(dir_entry));
@@ -602,7 +855,7 @@ int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
     uint64_t len = nbytes - start;
     if (len > chunk_bytes) len = chunk_bytes;
     int r = decode_chunk(blob, ent + (uint64_t)c * e, dtype, e, len / (uint64_t)e,
-                         dst + start);
+                         dst + start, version == 2 ? &st : NULL);
     if (r) {
 #pragma omp atomic write
       failed = r;

@@ -62,6 +62,21 @@
  *    cursor, cursor = align16(cursor + size); blob_nbytes = final cursor.
  *  CRC-32: reflected polynomial 0xEDB88320, init and final xor 0xFFFFFFFF
  *    (the zlib / ISO-HDLC CRC), computed afresh per chunk.
+ *
+ * Format v2, shared tables (lmz README, "One format choice worth knowing
+ * about": one frequency table per plane kind instead of one per rANS stream;
+ * READING: a plane is a stream index k of one blob, and sharing is the
+ * caller's choice, not decided per plane):
+ *  header as v1 but version = 2 and flags (byte 27) = 1.
+ *  After the directory come E table records, k = 0..E-1:
+ *    u16 lo | u16 hi | 12 zero bytes | u16 f[lo..hi] | zero pad to 16;
+ *    a plane without a table (at most one value over the whole blob):
+ *    lo = 1, hi = 0, 16 bytes.
+ *  payload_base = end of the records.  Table of plane k: normalise (as v1)
+ *    the sum over all chunks of stream k's histograms.
+ *  Per stream: one value -> CONST; else rANS with the plane's table, payload
+ *    u32 W | 12 zero bytes | u32 states[64] | u16 words[W], P = 272 + 2W;
+ *    P <= P_max(n) -> RANS, else RAW.  Offsets and gaps as v1.
  */
 #ifndef LTC_ORACLE_H
 #define LTC_ORACLE_H
@@ -81,6 +96,8 @@ extern "C" {
 #define LTCO_ERR_BAD_VERSION (-4)
 #define LTCO_ERR_CORRUPT (-5)
 #define LTCO_ERR_CAPACITY (-6)
+
+#define LTCO_FLAG_SHARED_TABLES 1u /* compress_ex: format v2 */
 
 #define LTCO_MODE_RAW 0
 #define LTCO_MODE_RANS 1
@@ -108,6 +125,13 @@ uint64_t ltco_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes);
 int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
                   uint32_t chunk_bytes, double theta, uint8_t* blob,
                   uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads);
+/* flags 0: ltco_compress (v1); LTCO_FLAG_SHARED_TABLES: format v2 */
+uint64_t ltco_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                                uint32_t flags);
+int ltco_compress_ex(const uint8_t* src, uint64_t nbytes, int dtype,
+                     uint32_t chunk_bytes, double theta, uint32_t flags,
+                     uint8_t* blob, uint64_t blob_capacity, uint64_t* blob_nbytes,
+                     int nthreads);
 /* the E payloads of one chunk, each zero-padded to a multiple of 16 and
  * concatenated; modes/cvals/sizes get one entry per stream; *nout = bytes */
 int ltco_encode_chunk(const uint8_t* src, uint64_t nbytes, int dtype,
