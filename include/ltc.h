@@ -80,6 +80,21 @@
  *     payload bytes = WO + 2W.
  *   Decoding reverses this; a RANS stream must consume exactly W words and
  *   end with every state at 65536.
+ *
+ * BLOB FORMAT v2, SHARED TABLES (flag LTC_FLAG_SHARED_TABLES; lmz README,
+ * "One format choice worth knowing about": one frequency table per plane
+ * kind instead of one per rANS stream -- here a plane is a stream index k of
+ * one blob, and sharing is the caller's choice):
+ *   Header as v1 with version = 2 and flags (byte 27) = 1.
+ *   After the directory, E table records, k = 0..E-1: 0 u16 lo | 2 u16 hi |
+ *     4 twelve zero bytes | 16 u16 f[lo..hi] | zero pad to a multiple of 16;
+ *     a plane with at most one distinct value in the whole blob has no table
+ *     (lo = 1, hi = 0, 16 bytes).  payload_base = end of the records.
+ *   Plane k's table: the v1 normalisation of the sum over all chunks of
+ *     stream k's histograms.  A stream with one value is CONST; otherwise it
+ *     is coded with its plane's table, payload 0 u32 W | 4 twelve zero bytes
+ *     | 16 u32 states[64] | 272 u16 words[W] (272 + 2W bytes), RANS if that
+ *     is at most P_max(n), else RAW.  Offsets and gaps as v1.
  */
 #ifndef LTC_H
 #define LTC_H
@@ -108,6 +123,8 @@ enum {
 
 enum { LTC_MODE_RAW = 0, LTC_MODE_RANS = 1, LTC_MODE_CONST = 2 };
 
+#define LTC_FLAG_SHARED_TABLES 1u /* compress flags: format v2 */
+
 #define LTC_HEADER_BYTES 64
 #define LTC_DEFAULT_CHUNK_BYTES 131072u
 #define LTC_DEFAULT_THRESHOLD 0.95
@@ -123,6 +140,7 @@ typedef struct {
   uint32_t nchunks;      /* K */
   uint64_t blob_nbytes;
   uint64_t payload_base;
+  uint32_t version;      /* 1, or 2 (shared tables) */
 } ltc_info;
 
 /* Element size of a dtype code, 0 if unknown. */
@@ -221,6 +239,28 @@ int ltc_crc32_chunks(const void* d_src, uint64_t nbytes, uint32_t chunk_bytes,
  * checksums go to h_crc_ptrs[i] (a device pointer held in a host array). */
 int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
                            uint32_t chunk_bytes, uint32_t* const* h_crc_ptrs, hipStream_t stream);
+
+/* Upper bound of the blob size with compress flags (0: ltc_compress_bound;
+ * LTC_FLAG_SHARED_TABLES adds E table records of at most 528 bytes).  0 on
+ * bad arguments. */
+uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes, uint32_t flags);
+
+/* The general compress call: ltc_compress_batch plus
+ *   flags: 0 (format v1) or LTC_FLAG_SHARED_TABLES (format v2); capacities
+ *     are checked against ltc_compress_bound_ex;
+ *   checksum_chunk_bytes: 0, or the CRC-32 of the blobs as in
+ *     ltc_compress_batch_with_crc32 (h_crc_ptrs / h_crc_capacity);
+ *   h_events: NULL, or the events of the *_prof variants (5, or 6 with
+ *     checksums), and then every kernel runs on `stream` one after another.
+ * v2 first builds every plane's table from the histograms of all chunks,
+ * then codes the chunks (in groups on several streams, as v1). */
+int ltc_compress_batch_ex(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                          int dtype, uint32_t chunk_bytes, double passthrough_threshold,
+                          uint32_t flags, void* const* h_blob_ptrs,
+                          const uint64_t* h_blob_capacity, uint64_t* d_blob_nbytes,
+                          uint32_t checksum_chunk_bytes, uint32_t* const* h_crc_ptrs,
+                          const uint64_t* h_crc_capacity, void* d_ws, uint64_t ws_nbytes,
+                          hipStream_t stream, const hipEvent_t* h_events);
 
 /* Compress and checksum the blob in one call (cuZipNN 0.1.0 "API",
  * compress_tensor_with_crc32): the same blob as ltc_compress, and in d_crc

@@ -46,7 +46,7 @@ class Info(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("elem_bytes", ctypes.c_uint32),
                 ("nbytes", ctypes.c_uint64), ("chunk_bytes", ctypes.c_uint32),
                 ("nchunks", ctypes.c_uint32), ("blob_nbytes", ctypes.c_uint64),
-                ("payload_base", ctypes.c_uint64)]
+                ("payload_base", ctypes.c_uint64), ("version", ctypes.c_uint32)]
 
 
 class Stats(ctypes.Structure):
@@ -85,6 +85,10 @@ def lib():
                                               u64, vp, pvp]
         L.ltc_compress_with_crc32.argtypes = [vp, u64, i32, u32, dbl, vp, u64, vp, u32, vp, u64,
                                               vp, u64, vp]
+        L.ltc_compress_bound_ex.argtypes = [u64, i32, u32, u32]
+        L.ltc_compress_bound_ex.restype = u64
+        L.ltc_compress_batch_ex.argtypes = [i32, pvp, pu64, i32, u32, dbl, u32, pvp, pu64, vp, u32,
+                                            pvp, pu64, vp, u64, vp, pvp]
         L.ltc_compress_batch_with_crc32.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp,
                                                     u32, pvp, pu64, vp, u64, vp]
         L.ltc_compress_batch_with_crc32_prof.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64,
@@ -100,7 +104,7 @@ def lib():
         L.ltc_blob_stats.argtypes = [ctypes.c_char_p, u64, ctypes.POINTER(Stats)]
         for name in ("ltc_compress_workspace_size", "ltc_compress_batch_workspace_size",
                      "ltc_compress", "ltc_compress_batch", "ltc_compress_batch_prof",
-                     "ltc_compress_with_crc32", "ltc_compress_batch_with_crc32",
+                     "ltc_compress_with_crc32", "ltc_compress_batch_with_crc32", "ltc_compress_batch_ex",
                      "ltc_compress_batch_with_crc32_prof",
                      "ltc_blob_info", "ltc_decompress", "ltc_decompress_batch",
                      "ltc_decompress_batch_prof", "ltc_decompress_from_host",
@@ -137,8 +141,12 @@ def _flat_bytes(t):
     return t.contiguous()
 
 
-def compress_bound(nbytes, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES):
-    return int(lib().ltc_compress_bound(nbytes, dtype_code, chunk_bytes))
+FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
+
+
+def compress_bound(nbytes, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES, shared_tables=False):
+    return int(lib().ltc_compress_bound_ex(nbytes, dtype_code, chunk_bytes,
+                                           FLAG_SHARED_TABLES if shared_tables else 0))
 
 
 def workspace_size(nbytes_list, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES):
@@ -159,6 +167,22 @@ def compress_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blob_ptrs
         _check(lib().ltc_compress_batch(*args), "compress")
     else:
         _check(lib().ltc_compress_batch_prof(*args, _ptrs(events)), "compress")
+
+
+def compress_ex_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, flags, blob_ptrs, caps,
+                    nbytes_out_ptr, ws_ptr, ws_nbytes, crc_chunk_bytes=0, crc_ptrs=None,
+                    crc_caps=None, stream=None, events=None):
+    """Pointer-level ltc_compress_batch_ex: format flags, optional checksums
+    (crc_chunk_bytes > 0) and optional events (5, or 6 with checksums)."""
+    count = len(src_ptrs)
+    crc_ptrs = crc_ptrs or [0] * count
+    crc_caps = crc_caps or [0] * count
+    ev = _ptrs(events) if events is not None else None
+    _check(lib().ltc_compress_batch_ex(count, _ptrs(src_ptrs), _u64s(nbytes), dtype_code, chunk_bytes,
+                                       threshold, flags, _ptrs(blob_ptrs), _u64s(caps),
+                                       ctypes.c_void_p(nbytes_out_ptr), crc_chunk_bytes, _ptrs(crc_ptrs),
+                                       _u64s(crc_caps), ctypes.c_void_p(ws_ptr), ws_nbytes,
+                                       _stream(stream), ev), "compress")
 
 
 def compress_crc32_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blob_ptrs, caps,
@@ -190,8 +214,9 @@ def decompress_raw(headers, blob_ptrs, blob_nbytes, dst_ptrs, caps, status_ptr, 
 
 
 def compress_batch(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
-                   passthrough_threshold=DEFAULT_THRESHOLD):
-    """Blobs (uint8 GPU tensors) for up to 32 tensors of one dtype."""
+                   passthrough_threshold=DEFAULT_THRESHOLD, shared_tables=False):
+    """Blobs (uint8 GPU tensors) for up to 32 tensors of one dtype;
+    shared_tables: format v2 (one frequency table per stream index)."""
     if not 1 <= len(tensors) <= BATCH_MAX:
         raise ValueError(f"1..{BATCH_MAX} tensors per batch")
     ts = [_flat_bytes(t) for t in tensors]
@@ -200,22 +225,23 @@ def compress_batch(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
         raise ValueError("one dtype per batch")
     dev = ts[0].device
     nbytes = [t.numel() * t.element_size() for t in ts]
-    caps = [compress_bound(n, code, chunk_bytes) for n in nbytes]
+    caps = [compress_bound(n, code, chunk_bytes, shared_tables) for n in nbytes]
     if any(c == 0 for c in caps):
         raise LTCError(-1, "compress_bound")
     blobs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
     ws_n = workspace_size(nbytes, code, chunk_bytes)
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
     sizes = torch.zeros(len(ts), dtype=torch.int64, device=dev)
-    compress_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
-                 [b.data_ptr() for b in blobs], caps, sizes.data_ptr(), ws.data_ptr(), ws.numel())
+    compress_ex_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
+                    FLAG_SHARED_TABLES if shared_tables else 0, [b.data_ptr() for b in blobs], caps,
+                    sizes.data_ptr(), ws.data_ptr(), ws.numel())
     host_sizes = sizes.cpu().tolist()
     return [b[:s] for b, s in zip(blobs, host_sizes)]
 
 
 def compress_batch_with_crc32(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
                               passthrough_threshold=DEFAULT_THRESHOLD,
-                              checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):
+                              checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES, shared_tables=False):
     """(blobs, checksums): the blobs of compress_batch and, per blob, the
     CRC-32 of each checksum_chunk_bytes-byte chunk (int32 GPU tensors holding
     the CRC bits)."""
@@ -229,7 +255,7 @@ def compress_batch_with_crc32(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
         raise LTCError(-1, "checksum_chunk_bytes")
     dev = ts[0].device
     nbytes = [t.numel() * t.element_size() for t in ts]
-    caps = [compress_bound(n, code, chunk_bytes) for n in nbytes]
+    caps = [compress_bound(n, code, chunk_bytes, shared_tables) for n in nbytes]
     if any(c == 0 for c in caps):
         raise LTCError(-1, "compress_bound")
     blobs = [torch.empty(c, dtype=torch.uint8, device=dev) for c in caps]
@@ -238,25 +264,27 @@ def compress_batch_with_crc32(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
     ws_n = workspace_size(nbytes, code, chunk_bytes)
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
     sizes = torch.zeros(len(ts), dtype=torch.int64, device=dev)
-    compress_crc32_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
-                       [b.data_ptr() for b in blobs], caps, sizes.data_ptr(), checksum_chunk_bytes,
-                       [c.data_ptr() for c in crcs], ccaps, ws.data_ptr(), ws.numel())
+    compress_ex_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
+                    FLAG_SHARED_TABLES if shared_tables else 0, [b.data_ptr() for b in blobs], caps,
+                    sizes.data_ptr(), ws.data_ptr(), ws.numel(), checksum_chunk_bytes,
+                    [c.data_ptr() for c in crcs], ccaps)
     host_sizes = sizes.cpu().tolist()
     return ([b[:s] for b, s in zip(blobs, host_sizes)],
             [c[:(s + checksum_chunk_bytes - 1) // checksum_chunk_bytes] for c, s in zip(crcs, host_sizes)])
 
 
 def compress_with_crc32(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
-                        checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):
+                        checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES, shared_tables=False):
     """(blob, checksums) of one GPU tensor (cuZipNN's compress_tensor_with_crc32)."""
     blobs, crcs = compress_batch_with_crc32([t], chunk_bytes, passthrough_threshold,
-                                            checksum_chunk_bytes)
+                                            checksum_chunk_bytes, shared_tables)
     return blobs[0], crcs[0]
 
 
-def compress(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD):
+def compress(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
+             shared_tables=False):
     """Blob (1-D uint8 tensor on t's device) of a GPU tensor's bytes."""
-    return compress_batch([t], chunk_bytes, passthrough_threshold)[0]
+    return compress_batch([t], chunk_bytes, passthrough_threshold, shared_tables)[0]
 
 
 def blob_info(blob_or_header):
@@ -349,10 +377,10 @@ def decompress_from_host(blob, shape=None, device=None):
 
 
 def compress_to_host(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
-                     pin_memory=True):
+                     pin_memory=True, shared_tables=False):
     """cuZipNN's compress_tensor: the blob of a GPU tensor as a 1-D uint8 CPU
     tensor (pinned by default, ready for decompress_from_host)."""
-    blob = compress(t, chunk_bytes, passthrough_threshold)
+    blob = compress(t, chunk_bytes, passthrough_threshold, shared_tables)
     out = torch.empty(blob.numel(), dtype=torch.uint8, pin_memory=pin_memory)
     out.copy_(blob)
     return out

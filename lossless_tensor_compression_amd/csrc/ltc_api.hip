@@ -76,10 +76,17 @@ hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipE
   const uint64_t total = t.total_chunks;
   t.c_begin = 0;
   t.c_end = total;
-  if (ev || total < kPipeMinChunks) return launch_compress(t, w, stream, ev);
+  // v2: every plane's table needs the histograms of all chunks, so they come
+  // first, on the caller's stream, before the chunks are coded
+  const bool staged = t.v2 != 0;
+  if (staged) {
+    const hipError_t err = launch_v2_tables(t, w, stream, ev);
+    if (err != hipSuccess) return err;
+  }
+  if (ev || total < kPipeMinChunks) return launch_compress(t, w, stream, ev, nullptr, nullptr, staged);
   std::lock_guard<std::mutex> lock(g_pipe_mu);
   PipeRes* r = pipe_res(stream);
-  if (!r) return launch_compress(t, w, stream, nullptr);
+  if (!r) return launch_compress(t, w, stream, nullptr, nullptr, nullptr, staged);
   hipError_t err = hipEventRecord(r->fork, stream);
   for (int g = 1; g < kPipeGroups && err == hipSuccess; ++g) err = hipStreamWaitEvent(r->s[g], r->fork, 0);
   for (int g = 0; g < kPipeGroups && err == hipSuccess; ++g) {
@@ -87,7 +94,7 @@ hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipE
     tg.c_begin = total * g / kPipeGroups;
     tg.c_end = total * (g + 1) / kPipeGroups;
     hipStream_t st = g == 0 ? stream : r->s[g];
-    err = launch_compress(tg, w, st, nullptr, g > 0 ? r->scan[g - 1] : nullptr, r->scan[g]);
+    err = launch_compress(tg, w, st, nullptr, g > 0 ? r->scan[g - 1] : nullptr, r->scan[g], staged);
     if (err == hipSuccess && g > 0) err = hipEventRecord(r->done[g], st);
   }
   for (int g = 1; g < kPipeGroups && err == hipSuccess; ++g) err = hipStreamWaitEvent(stream, r->done[g], 0);
@@ -178,15 +185,20 @@ uint32_t words_capacity(uint32_t chunk_bytes, uint32_t e) {
 }
 
 struct Layout {
-  uint64_t sinfo, freq, states, offsets, blobn, frames, words, total;
+  uint64_t sinfo, freq, hist, plane, ptab, pbase, states, offsets, blobn, frames, words, total;
 };
 
-// frames: one u32 per KiB of every blob's bound (compress_with_crc32)
-Layout layout(uint64_t streams, int count, uint32_t wcap, uint64_t frames) {
+// frames: one u32 per KiB of every blob's bound (compress_with_crc32);
+// hist, plane, ptab, pbase: format v2
+Layout layout(uint64_t streams, int count, uint32_t wcap, uint64_t frames, uint32_t e) {
   Layout l;
   uint64_t cur = 0;
   l.sinfo = cur;   cur = round_up(cur + 16 * streams, kAlign);
   l.freq = cur;    cur = round_up(cur + 512 * streams, kAlign);
+  l.hist = cur;    cur = round_up(cur + 1024 * streams, kAlign);
+  l.plane = cur;   cur = round_up(cur + 2048ull * e * (uint64_t)count, kAlign);
+  l.ptab = cur;    cur = round_up(cur + 512ull * e * (uint64_t)count, kAlign);
+  l.pbase = cur;   cur = round_up(cur + 8 * (uint64_t)count, kAlign);
   l.states = cur;  cur = round_up(cur + 256 * streams, kAlign);
   l.offsets = cur; cur = round_up(cur + 8 * streams, kAlign);
   l.blobn = cur;   cur = round_up(cur + 8 * (uint64_t)count, kAlign);
@@ -206,9 +218,16 @@ uint64_t bound_of(uint64_t nbytes, uint32_t e, uint32_t chunk_bytes) {
   return b;
 }
 
+// v2 adds E table records of at most 16 + 2*256 bytes
+uint64_t bound_flags(uint64_t nbytes, uint32_t e, uint32_t chunk_bytes, uint32_t flags) {
+  return bound_of(nbytes, e, chunk_bytes) + ((flags & LTC_FLAG_SHARED_TABLES) ? 528ull * e : 0);
+}
+
+// frame slots for compress_with_crc32: enough for either format
 uint64_t batch_frames(int count, const uint64_t* nbytes, uint32_t e, uint32_t chunk_bytes) {
   uint64_t f = 0;
-  for (int i = 0; i < count; ++i) f += (bound_of(nbytes[i], e, chunk_bytes) + 1023) / 1024;
+  for (int i = 0; i < count; ++i)
+    f += (bound_flags(nbytes[i], e, chunk_bytes, LTC_FLAG_SHARED_TABLES) + 1023) / 1024;
   return f;
 }
 
@@ -230,9 +249,11 @@ struct CrcReq {
 int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, int dtype,
                   uint32_t chunk_bytes, double theta, void* const* blobs, const uint64_t* caps,
                   uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes, hipStream_t stream,
-                  const hipEvent_t* ev, const CrcReq& crc = CrcReq{0, nullptr, nullptr}) {
+                  const hipEvent_t* ev, const CrcReq& crc = CrcReq{0, nullptr, nullptr},
+                  uint32_t flags = 0) {
   if (count < 1 || count > kMaxJobs || !srcs || !nbytes || !blobs || !caps || !d_blob_nbytes)
     return LTC_ERR_INVALID_ARGUMENT;
+  if (flags & ~LTC_FLAG_SHARED_TABLES) return LTC_ERR_INVALID_ARGUMENT;
   if (!(theta > 0.0 && theta <= 1.0)) return LTC_ERR_INVALID_ARGUMENT;
   const uint32_t e = elem_bytes(dtype);
   for (int i = 0; i < count; ++i) {
@@ -241,20 +262,21 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
     if (!blobs[i] || (nbytes[i] && !srcs[i])) return LTC_ERR_INVALID_ARGUMENT;
     if (reinterpret_cast<uintptr_t>(srcs[i]) % e) return LTC_ERR_INVALID_ARGUMENT;
     if (reinterpret_cast<uintptr_t>(blobs[i]) % 16) return LTC_ERR_INVALID_ARGUMENT;
-    if (caps[i] < bound_of(nbytes[i], e, chunk_bytes)) return LTC_ERR_CAPACITY;
+    if (caps[i] < bound_flags(nbytes[i], e, chunk_bytes, flags)) return LTC_ERR_CAPACITY;
   }
   if (crc.chunk_bytes) {
     if (!crc.outs || !crc.caps) return LTC_ERR_INVALID_ARGUMENT;
     for (int i = 0; i < count; ++i) {
       if (!crc.outs[i] || reinterpret_cast<uintptr_t>(crc.outs[i]) % 4) return LTC_ERR_INVALID_ARGUMENT;
-      const uint64_t need = (bound_of(nbytes[i], e, chunk_bytes) + crc.chunk_bytes - 1) / crc.chunk_bytes;
+      const uint64_t need =
+          (bound_flags(nbytes[i], e, chunk_bytes, flags) + crc.chunk_bytes - 1) / crc.chunk_bytes;
       if (crc.caps[i] < need) return LTC_ERR_CAPACITY;
     }
   }
   const int64_t streams = batch_streams(count, nbytes, e, chunk_bytes);
   if (streams < 0) return LTC_ERR_INVALID_ARGUMENT;
   const uint32_t wcap = words_capacity(chunk_bytes, e);
-  const Layout l = layout((uint64_t)streams, count, wcap, batch_frames(count, nbytes, e, chunk_bytes));
+  const Layout l = layout((uint64_t)streams, count, wcap, batch_frames(count, nbytes, e, chunk_bytes), e);
   if (!d_ws || ws_nbytes < l.total || reinterpret_cast<uintptr_t>(d_ws) % kAlign)
     return LTC_ERR_WORKSPACE;
 
@@ -265,6 +287,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   t.n_full = chunk_bytes / e;
   t.wcap = wcap;
   t.dtype = (uint32_t)dtype;
+  t.v2 = (flags & LTC_FLAG_SHARED_TABLES) ? 1u : 0u;
   bool vec = chunk_bytes % 16 == 0;
   uint64_t chunk0 = 0;
   for (int i = 0; i < count; ++i) {
@@ -288,6 +311,10 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   CWork w;
   w.sinfo = reinterpret_cast<uint32_t*>(ws + l.sinfo);
   w.freq = reinterpret_cast<uint16_t*>(ws + l.freq);
+  w.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+  w.plane = reinterpret_cast<uint64_t*>(ws + l.plane);
+  w.ptab = reinterpret_cast<uint16_t*>(ws + l.ptab);
+  w.pbase = reinterpret_cast<uint64_t*>(ws + l.pbase);
   w.states = reinterpret_cast<uint32_t*>(ws + l.states);
   w.offsets = reinterpret_cast<uint64_t*>(ws + l.offsets);
   w.blob_nbytes = reinterpret_cast<uint64_t*>(ws + l.blobn);
@@ -317,7 +344,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   }
   uint64_t fcur = 0, ccur = 0;
   for (int i = 0; i < count; ++i) {
-    const uint64_t bound = bound_of(nbytes[i], e, chunk_bytes);
+    const uint64_t bound = bound_flags(nbytes[i], e, chunk_bytes, flags);
     t.jobs[i].frames = frames + fcur;
     CrcJob& jb = a.jobs[i];
     jb.src = t.jobs[i].blob;
@@ -438,6 +465,8 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
     jb.blob = static_cast<const uint8_t*>(blobs[i]);
     jb.dst = static_cast<uint8_t*>(dsts[i]);
     jb.status = d_status + i;
+    jb.payload_base = info.payload_base;
+    jb.v2 = info.version == 2 ? 1u : 0u;
     jb.blob_nbytes = info.blob_nbytes;
     jb.nbytes = info.nbytes;
     jb.chunk0 = chunk0;
@@ -470,6 +499,24 @@ uint64_t ltc_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
   return bound_of(nbytes, elem_bytes(dtype), chunk_bytes);
 }
 
+uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes, uint32_t flags) {
+  if (check_shape(nbytes, dtype, chunk_bytes) || (flags & ~LTC_FLAG_SHARED_TABLES)) return 0;
+  return bound_flags(nbytes, elem_bytes(dtype), chunk_bytes, flags);
+}
+
+int ltc_compress_batch_ex(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
+                          int dtype, uint32_t chunk_bytes, double passthrough_threshold,
+                          uint32_t flags, void* const* h_blob_ptrs,
+                          const uint64_t* h_blob_capacity, uint64_t* d_blob_nbytes,
+                          uint32_t checksum_chunk_bytes, uint32_t* const* h_crc_ptrs,
+                          const uint64_t* h_crc_capacity, void* d_ws, uint64_t ws_nbytes,
+                          hipStream_t stream, const hipEvent_t* h_events) {
+  const CrcReq crc{checksum_chunk_bytes, h_crc_ptrs, h_crc_capacity};
+  return compress_impl(count, h_src_ptrs, h_nbytes, dtype, chunk_bytes, passthrough_threshold,
+                       h_blob_ptrs, h_blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, h_events,
+                       crc, flags);
+}
+
 int ltc_compress_workspace_size(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
                                 uint64_t* ws_nbytes) {
   return ltc_compress_batch_workspace_size(1, &nbytes, dtype, chunk_bytes, ws_nbytes);
@@ -486,7 +533,7 @@ int ltc_compress_batch_workspace_size(int count, const uint64_t* h_nbytes, int d
   const int64_t streams = batch_streams(count, h_nbytes, e, chunk_bytes);
   if (streams < 0) return LTC_ERR_INVALID_ARGUMENT;
   *ws_nbytes = layout((uint64_t)streams, count, words_capacity(chunk_bytes, e),
-                      batch_frames(count, h_nbytes, e, chunk_bytes)).total;
+                      batch_frames(count, h_nbytes, e, chunk_bytes), e).total;
   return LTC_OK;
 }
 
@@ -558,7 +605,8 @@ int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {
   if (h_nbytes < kHeader) return LTC_ERR_CORRUPT;
   const uint8_t* h = static_cast<const uint8_t*>(h_header);
   if (memcmp(h, "LTCB", 4) != 0) return LTC_ERR_BAD_MAGIC;
-  if (rd16(h + 4) != 1) return LTC_ERR_BAD_VERSION;
+  const uint32_t version = rd16(h + 4);
+  if (version != 1 && version != 2) return LTC_ERR_BAD_VERSION;
   const int dtype = h[6];
   const uint32_t e = elem_bytes(dtype);
   if (!e) return LTC_ERR_UNSUPPORTED_DTYPE;
@@ -566,15 +614,22 @@ int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {
   const uint64_t nbytes = rd64(h + 8);
   const uint32_t chunk_bytes = rd32(h + 16);
   const uint64_t k = rd32(h + 20);
-  if (rd16(h + 24) != kLanes || h[26] != 12 || h[27] != 0 || rd32(h + 28) != 0) return LTC_ERR_CORRUPT;
+  if (rd16(h + 24) != kLanes || h[26] != 12 || h[27] != (version == 2 ? LTC_FLAG_SHARED_TABLES : 0u) ||
+      rd32(h + 28) != 0)
+    return LTC_ERR_CORRUPT;
   for (int i = 48; i < 64; ++i)
     if (h[i]) return LTC_ERR_CORRUPT;
   if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8) return LTC_ERR_CORRUPT;
   if (nbytes % e) return LTC_ERR_CORRUPT;
   if (k != (nbytes + chunk_bytes - 1) / chunk_bytes) return LTC_ERR_CORRUPT;
-  const uint64_t base = kHeader + kDirEntry * k * e;
+  // v2: E table records of 16 to 528 bytes between the directory and the payloads
+  const uint64_t dir_end = kHeader + kDirEntry * k * e;
+  const uint64_t base = rd64(h + 40);
   const uint64_t blob_nbytes = rd64(h + 32);
-  if (rd64(h + 40) != base || blob_nbytes < base || blob_nbytes % 16) return LTC_ERR_CORRUPT;
+  if (version == 1 ? base != dir_end
+                   : (base < dir_end + 16ull * e || base > dir_end + 528ull * e || base % 16))
+    return LTC_ERR_CORRUPT;
+  if (blob_nbytes < base || blob_nbytes % 16) return LTC_ERR_CORRUPT;
   out->dtype = dtype;
   out->elem_bytes = e;
   out->nbytes = nbytes;
@@ -582,6 +637,7 @@ int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {
   out->nchunks = (uint32_t)k;
   out->blob_nbytes = blob_nbytes;
   out->payload_base = base;
+  out->version = version;
   return LTC_OK;
 }
 

@@ -94,34 +94,28 @@ __device__ __forceinline__ void hist_vec(uint32_t* hs, const uint4 q, uint32_t c
   hist_word<DT>(hs, q.w, copy);
 }
 
-// Normalise one stream's histogram (one wave; lane l owns symbols 4l..4l+3),
-// pick CONST / RAW / encode, write the frequency table and the stream info.
-__device__ void normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, uint64_t s,
-                                 const CWork& w) {
-  const uint32_t lane = lane_id();
-  uint32_t hv[4], f[4];
-  uint32_t nz = 0, lo = 0xFFFFu, hi = 0;
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hv[i] = h[4 * lane + i];
-    if (hv[i]) {
-      ++nz;
-      lo = min(lo, 4 * lane + i);
-      hi = max(hi, 4 * lane + i);
-    }
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    const uint64_t u = ((uint64_t)hi << 32) | lo;
+    v = u > v ? u : v;
   }
-  nz = wave_sum_u32(nz);
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if (nz == 1) {  // a single value: the stream is a header ("NOTE-241", Method item 3)
-    if (lane == 0)
-      *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(LTC_MODE_CONST, lo, 0, 0), 0, 0);
-    return;
-  }
+  return v;
+}
+
+// Frequencies summing to 4096 from counts hv (lane l owns symbols 4l..4l+3,
+// n = sum of all counts, at least two nonzero): f = max(1, floor(h*4096/n))
+// for h > 0; while the sum exceeds 4096 the largest f > 1 loses one (ties:
+// smaller symbol); a shortfall goes to the largest count (ties: smaller
+// symbol).  One wave.
+template <class T>
+__device__ __forceinline__ void normalize_wave(const T hv[4], uint64_t n, uint32_t f[4]) {
+  const uint32_t lane = lane_id();
   uint32_t fsum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[i] = hv[i] ? max(1u, (uint32_t)(((uint64_t)hv[i] << 12) / n)) : 0u;
+    f[i] = hv[i] ? (uint32_t)max((uint64_t)1, ((uint64_t)hv[i] << 12) / n) : 0u;
     fsum += f[i];
   }
   uint32_t total = wave_sum_u32(fsum);
@@ -138,31 +132,76 @@ __device__ void normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, u
     --total;
   }
   if (total < kTotal) {  // shortfall to the largest count, ties to the smaller symbol
-    uint32_t key = 0;
+    uint64_t key = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (hv[i]) key = max(key, (hv[i] << 8) | (255u - (4 * lane + i)));
-    key = wave_max_u32(key);
-    const uint32_t v = 255u - (key & 255u);
+      if (hv[i]) key = max(key, ((uint64_t)hv[i] << 8) | (255u - (4 * lane + i)));
+    key = wave_max_u64(key);
+    const uint32_t v = 255u - (uint32_t)(key & 255u);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (4 * lane + i == v) f[i] += kTotal - total;
   }
-  // Lower bound on the rANS word count: each coding step gains at least
-  // log2(4096/f) - log2(16/15) bits of state information (x >= 16 f there),
-  // each renormalisation loses at most log2(16/15) (x >= 2^20 there), and the
-  // 64 final states can hold at most 1024 bits more than the initial ones.
-  // If even that bound exceeds P_max the stream is RAW whatever the encoder
-  // would do, so it is not encoded.  64 bits of slack absorb rounding.
+}
+
+// Lower bound on the rANS word count: each coding step gains at least
+// log2(4096/f) - log2(16/15) bits of state information (x >= 16 f there),
+// each renormalisation loses at most log2(16/15) (x >= 2^20 there), and the
+// 64 final states can hold at most 1024 bits more than the initial ones.  If
+// even that bound puts the payload (wo + 2 words) above P_max the stream is
+// RAW whatever the encoder would do, so it is not encoded.  64 bits of slack
+// absorb rounding.
+__device__ __forceinline__ bool raw_by_bound(const uint32_t hv[4], const uint32_t f[4], uint32_t n,
+                                             uint32_t wo, uint32_t pmax) {
   double bits = 0.0;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (hv[i]) bits += (double)hv[i] * (12.0 - log2((double)f[i]));
   bits = wave_sum_f64(bits);
-  const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * (hi - lo + 1u));
   const double wlb = (bits - 0.1862 * (double)n - 1024.0 - 64.0) / 16.0;
   const double plb = (double)wo + 2.0 * (wlb > 0.0 ? ceil(wlb) : 0.0);
-  const bool raw = wo > pmax || plb > (double)pmax;
+  return wo > pmax || plb > (double)pmax;
+}
+
+// Normalise one stream's histogram (one wave; lane l owns symbols 4l..4l+3),
+// pick CONST / RAW / encode, write the frequency table and the stream info.
+// v2: keep the histogram for k_decide and add it to the plane's instead.
+__device__ void normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, uint64_t s,
+                                 const CWork& w, uint64_t* plane) {
+  const uint32_t lane = lane_id();
+  uint32_t hv[4], f[4];
+  uint32_t nz = 0, lo = 0xFFFFu, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hv[i] = h[4 * lane + i];
+    if (hv[i]) {
+      ++nz;
+      lo = min(lo, 4 * lane + i);
+      hi = max(hi, 4 * lane + i);
+    }
+  }
+  nz = wave_sum_u32(nz);
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (plane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (hv[i]) atomicAdd(reinterpret_cast<unsigned long long*>(plane + 4 * lane + i), (unsigned long long)hv[i]);
+  }
+  if (nz == 1) {  // a single value: the stream is a header ("NOTE-241", Method item 3)
+    if (lane == 0)
+      *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(LTC_MODE_CONST, lo, 0, 0), 0, 0);
+    return;
+  }
+  if (plane) {  // v2: decided once the plane's table exists (k_decide)
+    *reinterpret_cast<uint4*>(w.hist + 256 * s + 4 * lane) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+    if (lane == 0)
+      *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(kModeCand, 0, 0, 0), 0, 0);
+    return;
+  }
+  normalize_wave(hv, n, f);
+  const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * (hi - lo + 1u));
+  const bool raw = raw_by_bound(hv, f, n, wo, pmax);
   const uint64_t packed = (uint64_t)f[0] | ((uint64_t)f[1] << 16) | ((uint64_t)f[2] << 32) |
                           ((uint64_t)f[3] << 48);
   *reinterpret_cast<uint64_t*>(w.freq + 256 * s + 4 * lane) = packed;
@@ -229,7 +268,129 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   }
   const uint32_t wave = tid / 64;
   if (wave < (uint32_t)E)
-    normalize_stream(hf + 256 * wave, n, last ? job.pmax_tail : job.pmax_full, g * E + wave, w);
+    normalize_stream(hf + 256 * wave, n, last ? job.pmax_tail : job.pmax_full, g * E + wave, w,
+                     t.v2 ? w.plane + ((uint64_t)j * E + wave) * 256 : nullptr);
+}
+
+// ---------------------------------------------------------------- v2 tables
+
+__device__ __forceinline__ uint32_t record_bytes(uint32_t lo, uint32_t hi) {
+  return lo > hi ? 16u : (uint32_t)align16(16u + 2u * (hi - lo + 1u));
+}
+
+// CRC-32 remainder (register from zero) of one 16-byte unit, bit by bit
+__device__ __forceinline__ uint32_t unit_remainder_bitwise(uint4 v) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r = 0;
+  for (int q = 0; q < 4; ++q)
+    for (int b = 0; b < 4; ++b) {
+      r ^= (wv[q] >> (8 * b)) & 0xFFu;
+      for (int k = 0; k < 8; ++k) r = (r >> 1) ^ (kPoly & (0u - (r & 1u)));
+    }
+  return r;
+}
+
+// One workgroup per tensor, wave k for stream index k: the plane's table
+// (the normalised sum of its streams' histograms) into the workspace and as
+// a table record into the blob after the directory; payload_base = the end
+// of the records.  A plane with at most one value has no table.
+template <int DT>
+__global__ __launch_bounds__(256) void k_share(CTable t, CWork w) {
+  constexpr int E = Dt<DT>::E;
+  __shared__ uint32_t rlo[4], rhi[4];
+  __shared__ uint16_t sf[4][256];
+  const int j = blockIdx.x;
+  const CJob& job = t.jobs[j];
+  const uint32_t wave = threadIdx.x / 64, lane = lane_id();
+  if (wave < (uint32_t)E) {
+    const uint64_t* H = w.plane + ((uint64_t)j * E + wave) * 256;
+    uint64_t hv[4];
+    uint32_t nz = 0, lo = 0xFFFFu, hi = 0;
+    uint64_t n = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hv[i] = H[4 * lane + i];
+      n += hv[i];
+      if (hv[i]) {
+        ++nz;
+        lo = min(lo, 4 * lane + i);
+        hi = max(hi, 4 * lane + i);
+      }
+    }
+    nz = wave_sum_u32(nz);
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += ((uint64_t)__shfl_xor((uint32_t)(n >> 32), o, 64) << 32) | __shfl_xor((uint32_t)n, o, 64);
+    uint32_t f[4] = {0, 0, 0, 0};
+    if (nz >= 2) normalize_wave(hv, n, f);
+    else lo = 1, hi = 0;
+    const uint64_t packed = (uint64_t)f[0] | ((uint64_t)f[1] << 16) | ((uint64_t)f[2] << 32) |
+                            ((uint64_t)f[3] << 48);
+    *reinterpret_cast<uint64_t*>(w.ptab + ((uint64_t)j * E + wave) * 256 + 4 * lane) = packed;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sf[wave][4 * lane + i] = (uint16_t)f[i];
+    if (lane == 0) {
+      rlo[wave] = lo;
+      rhi[wave] = hi;
+    }
+  }
+  __syncthreads();
+  const uint64_t dir_end = kHeader + kDirEntry * (uint64_t)job.nchunks * E;
+  uint64_t off = dir_end, end = dir_end;
+  for (int q = 0; q < E; ++q) {
+    if ((uint32_t)q < wave) off += record_bytes(rlo[q], rhi[q]);
+    end += record_bytes(rlo[q], rhi[q]);
+  }
+  if (threadIdx.x == 0) w.pbase[j] = end;
+  if (wave >= (uint32_t)E) return;
+  const uint32_t lo = rlo[wave], hi = rhi[wave];
+  const uint32_t units = record_bytes(lo, hi) / 16;
+  for (uint32_t u = lane; u < units; u += 64) {
+    uint4 v;
+    if (u == 0) {
+      v = make_uint4(lo | (hi << 16), 0, 0, 0);
+    } else {
+      uint32_t hw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sym = lo + 8 * (u - 1) + i;
+        hw[i] = sym <= hi ? sf[wave][sym] : 0u;
+      }
+      v = make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16));
+    }
+    *reinterpret_cast<uint4*>(job.blob + off + 16 * u) = v;
+    if (t.crc) {  // this unit's share of its 1 KiB frame (compress_with_crc32)
+      const uint64_t ua = (off >> 4) + u;
+      const uint32_t r = gf2_mulmod(unit_remainder_bitwise(v), t.crc_pos[ua & 63]);
+      if (r) atomicXor(job.frames + (ua >> 6), r);
+    }
+  }
+}
+
+// One wave per stream still to be decided (v2): the skip bound with the
+// plane's table; the encoder then codes the rest with that table.
+template <int DT>
+__global__ __launch_bounds__(256) void k_decide(CTable t, CWork w) {
+  constexpr int E = Dt<DT>::E;
+  const uint64_t s = (t.c_begin * E) + (uint64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  if (s >= t.c_end * E) return;
+  const uint32_t info = w.sinfo[4 * s + 1];
+  if ((info & 0xFFu) != kModeCand) return;
+  const uint64_t g = s / E;
+  const uint32_t k = (uint32_t)(s % E);
+  const int j = find_job(t, g);
+  const CJob& job = t.jobs[j];
+  const bool last = g - job.chunk0 + 1 == job.nchunks;
+  const uint32_t n = last ? job.n_tail : t.n_full;
+  const uint32_t lane = lane_id();
+  const uint4 hq = *reinterpret_cast<const uint4*>(w.hist + 256 * s + 4 * lane);
+  const uint64_t fq = *reinterpret_cast<const uint64_t*>(w.ptab + ((uint64_t)j * E + k) * 256 + 4 * lane);
+  const uint32_t hv[4] = {hq.x, hq.y, hq.z, hq.w};
+  const uint32_t f[4] = {(uint32_t)fq & 0xFFFFu, (uint32_t)(fq >> 16) & 0xFFFFu,
+                         (uint32_t)(fq >> 32) & 0xFFFFu, (uint32_t)(fq >> 48)};
+  if (raw_by_bound(hv, f, n, kRansFixed, last ? job.pmax_tail : job.pmax_full) && lane == 0)
+    *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(n, pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
 }
 
 // ---------------------------------------------------------------- k_encode
@@ -292,12 +453,14 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   uint64_t sid[U];
   uint32_t n[U], full[U], wlimit[U], wo[U], lo[U], hi[U];
   const uint8_t* src[U];
+  const uint16_t* ftab[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     on[u] = false;
     sid[u] = 0;
     n[u] = full[u] = wlimit[u] = wo[u] = lo[u] = hi[u] = 0;
     src[u] = nullptr;
+    ftab[u] = nullptr;
     const uint64_t g = g0 + u;
     if (g >= t.c_end) continue;
     const uint64_t s = g * E + k;
@@ -313,7 +476,9 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     full[u] = n[u] / 64;
     lo[u] = (info >> 16) & 0xFFu;
     hi[u] = info >> 24;
-    wo[u] = (uint32_t)align16(kRansFixed + 2u * (hi[u] - lo[u] + 1u));
+    // v2: the plane's table and no table in the payload
+    wo[u] = t.v2 ? kRansFixed : (uint32_t)align16(kRansFixed + 2u * (hi[u] - lo[u] + 1u));
+    ftab[u] = t.v2 ? w.ptab + ((uint64_t)j * E + k) * 256 : w.freq + 256 * s;
     wlimit[u] = ((last ? job.pmax_tail : job.pmax_full) - wo[u]) / 2;
     src[u] = job.src + c * t.chunk_bytes;
   }
@@ -322,7 +487,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!on[u]) continue;
-    const uint64_t fq = *reinterpret_cast<const uint64_t*>(w.freq + 256 * sid[u] + 4 * lane);
+    const uint64_t fq = *reinterpret_cast<const uint64_t*>(ftab[u] + 4 * lane);
     uint32_t f[4], cum[4], acc = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -601,7 +766,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
   const bool first = c_lo == job.chunk0, final = c_hi == job.chunk0 + job.nchunks;
   const uint64_t s0 = c_lo * E;
   const uint64_t S = (c_hi - c_lo) * E;
-  const uint64_t base = kHeader + kDirEntry * (uint64_t)job.nchunks * E;
+  const uint64_t base = t.v2 ? w.pbase[j] : kHeader + kDirEntry * (uint64_t)job.nchunks * E;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
   uint64_t running = first ? base : w.blob_nbytes[j];
   for (uint64_t tile = 0; tile < S; tile += 4 * kScanThreads) {
@@ -641,10 +806,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
   if (tid < 4) {  // header
     uint4 v;
     if (tid == 0)
-      v = make_uint4(0x4243544Cu /* "LTCB" */, 1u | (t.dtype << 16) | (E << 24),
+      v = make_uint4(0x4243544Cu /* "LTCB" */, (t.v2 ? 2u : 1u) | (t.dtype << 16) | (E << 24),
                      (uint32_t)job.nbytes, (uint32_t)(job.nbytes >> 32));
     else if (tid == 1)
-      v = make_uint4(t.chunk_bytes, job.nchunks, 64u | (12u << 16), 0u);
+      v = make_uint4(t.chunk_bytes, job.nchunks, 64u | (12u << 16) | ((t.v2 ? 1u : 0u) << 24), 0u);
     else if (tid == 2)
       v = make_uint4((uint32_t)running, (uint32_t)(running >> 32), (uint32_t)base,
                      (uint32_t)(base >> 32));
@@ -786,11 +951,13 @@ __device__ __forceinline__ void wave_frames(uint64_t a, uint32_t units, uint64_t
 }
 
 // unit u (16 bytes) of a RANS payload: prefix, states, frequencies, words
-__device__ __forceinline__ uint4 rans_unit(uint32_t u, uint64_t s, uint32_t lo, uint32_t tcount,
+// y1: the prefix's second word (v1: sym_lo | sym_hi << 8; v2: 0); v2 payloads
+// have no table (tcount 0, wo 272)
+__device__ __forceinline__ uint4 rans_unit(uint32_t u, uint64_t s, uint32_t y1, uint32_t tcount,
                                            uint32_t wo, uint32_t nw, const uint16_t* fr,
                                            const uint16_t* words, const CWork& w) {
   const uint32_t pos = 16 * u;
-  if (u == 0) return make_uint4(nw, lo | ((lo + tcount - 1) << 8), 0, 0);
+  if (u == 0) return make_uint4(nw, y1, 0, 0);
   if (pos < kRansFixed) return *reinterpret_cast<const uint4*>(w.states + 64 * s + (pos - 16) / 4);
   uint32_t h[8];
   if (pos < wo) {
@@ -811,15 +978,16 @@ __device__ void write_rans(uint8_t* blob, uint64_t off, uint64_t s, uint32_t inf
                            uint32_t nw, const CTable& t, const CWork& w, uint32_t* frames,
                            const PackLds<CRC>& L, uint32_t pos) {
   const uint32_t lo = (info >> 16) & 0xFFu, hi = info >> 24;
-  const uint32_t tcount = hi - lo + 1u;
+  const uint32_t tcount = t.v2 ? 0u : hi - lo + 1u;
   const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * tcount);
+  const uint32_t y1 = t.v2 ? 0u : lo | (hi << 8);
   const uint32_t units = (uint32_t)(align16(size) / 16);
   const uint16_t* fr = w.freq + 256 * s + lo;
   const uint16_t* words = w.words + s * t.wcap + (t.wcap - nw);
   uint8_t* dst = blob + off;
   if constexpr (!CRC) {
     for (uint32_t u = threadIdx.x; u < units; u += kPackThreads)
-      *reinterpret_cast<uint4*>(dst + 16 * u) = rans_unit(u, s, lo, tcount, wo, nw, fr, words, w);
+      *reinterpret_cast<uint4*>(dst + 16 * u) = rans_unit(u, s, y1, tcount, wo, nw, fr, words, w);
   } else {
     const uint32_t lane = threadIdx.x & 63;
     const uint64_t a = off / 16;
@@ -831,7 +999,7 @@ __device__ void write_rans(uint8_t* blob, uint64_t off, uint64_t s, uint32_t inf
       uint32_t c = 0;
       if (ua >= a && ua < a + units) {
         const uint32_t u = (uint32_t)(ua - a);
-        const uint4 v = rans_unit(u, s, lo, tcount, wo, nw, fr, words, w);
+        const uint4 v = rans_unit(u, s, y1, tcount, wo, nw, fr, words, w);
         *reinterpret_cast<uint4*>(dst + 16 * u) = v;
         c = crc_step16(L.c, 0u, v);
       }
@@ -957,12 +1125,14 @@ __global__ __launch_bounds__(CRC ? kPackCrcThreads : kPackThreads) void k_pack(C
 template <int DT>
 static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t st,
                                     const hipEvent_t* ev, hipEvent_t scan_after,
-                                    hipEvent_t scan_done) {
+                                    hipEvent_t scan_done, bool staged) {
   constexpr int E = Dt<DT>::E;
   const uint64_t chunks = t.c_end - t.c_begin;
-  record(ev, 0, st);
-  if (chunks) hipLaunchKernelGGL(k_hist<DT>, dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
-  record(ev, 1, st);
+  if (!staged) {
+    record(ev, 0, st);
+    if (chunks) hipLaunchKernelGGL(k_hist<DT>, dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
+    record(ev, 1, st);
+  }
   if (chunks)
     hipLaunchKernelGGL(k_encode<DT>, dim3((uint32_t)((chunks + kEncStreams - 1) / kEncStreams * E)), dim3(64), 0,
                        st, t, w);
@@ -980,13 +1150,39 @@ static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t
   return hipGetLastError();
 }
 
+// v2, all chunks of t: histograms (summed per plane), plane tables and
+// records, then the skip bound of every stream with its plane's table
+template <int DT>
+static hipError_t launch_v2_tables_t(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev) {
+  constexpr int E = Dt<DT>::E;
+  const uint64_t chunks = t.c_end - t.c_begin;
+  record(ev, 0, st);
+  hipError_t err = launch_zero_u32(reinterpret_cast<uint32_t*>(w.plane), 2ull * 256 * E * t.count, st);
+  if (err != hipSuccess) return err;
+  if (chunks) hipLaunchKernelGGL(k_hist<DT>, dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
+  hipLaunchKernelGGL(k_share<DT>, dim3(t.count), dim3(256), 0, st, t, w);
+  if (chunks) hipLaunchKernelGGL(k_decide<DT>, dim3((uint32_t)((chunks * E + 3) / 4)), dim3(256), 0, st, t, w);
+  record(ev, 1, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
-                           hipEvent_t scan_after, hipEvent_t scan_done) {
+                           hipEvent_t scan_after, hipEvent_t scan_done, bool staged) {
   switch (t.dtype) {
-    case LTC_U8: return launch_compress_t<LTC_U8>(t, w, st, ev, scan_after, scan_done);
-    case LTC_BF16: return launch_compress_t<LTC_BF16>(t, w, st, ev, scan_after, scan_done);
-    case LTC_FP16: return launch_compress_t<LTC_FP16>(t, w, st, ev, scan_after, scan_done);
-    case LTC_FP32: return launch_compress_t<LTC_FP32>(t, w, st, ev, scan_after, scan_done);
+    case LTC_U8: return launch_compress_t<LTC_U8>(t, w, st, ev, scan_after, scan_done, staged);
+    case LTC_BF16: return launch_compress_t<LTC_BF16>(t, w, st, ev, scan_after, scan_done, staged);
+    case LTC_FP16: return launch_compress_t<LTC_FP16>(t, w, st, ev, scan_after, scan_done, staged);
+    case LTC_FP32: return launch_compress_t<LTC_FP32>(t, w, st, ev, scan_after, scan_done, staged);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_v2_tables(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev) {
+  switch (t.dtype) {
+    case LTC_U8: return launch_v2_tables_t<LTC_U8>(t, w, st, ev);
+    case LTC_BF16: return launch_v2_tables_t<LTC_BF16>(t, w, st, ev);
+    case LTC_FP16: return launch_v2_tables_t<LTC_FP16>(t, w, st, ev);
+    case LTC_FP32: return launch_v2_tables_t<LTC_FP32>(t, w, st, ev);
     default: return hipErrorInvalidValue;
   }
 }

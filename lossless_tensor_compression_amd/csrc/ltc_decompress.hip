@@ -116,9 +116,9 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     cval[k] = (e.w >> 8) & 0xFFu;
     bad |= (e.w >> 16) != 0 || mode[k] > 2 || (mode[k] != LTC_MODE_CONST && cval[k] != 0) ||
            (mode[k] == LTC_MODE_RAW && size[k] != n) || (mode[k] == LTC_MODE_CONST && size[k] != 0) ||
-           (mode[k] == LTC_MODE_RANS && size[k] < kRansFixed + 16) || off[k] > B ||
+           (mode[k] == LTC_MODE_RANS && size[k] < kRansFixed + (job.v2 ? 0u : 16u)) || off[k] > B ||
            (uint64_t)size[k] > B - off[k];
-    if (k == 0 && c == 0) bad |= off[0] != kHeader + kDirEntry * S;
+    if (k == 0 && c == 0) bad |= off[0] != job.payload_base;
     if (k > 0) bad |= off[k] != align16(off[k - 1] + size[k - 1]);
     nr += mode[k] == LTC_MODE_RANS;
   }
@@ -141,8 +141,66 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     return;
   }
 
+  // ---- v2: the table records between the directory and payload_base (each
+  // chunk finds its planes' records; chunk 0 also checks every table, so the
+  // verdict on a blob does not depend on which planes are used)
+  const uint8_t* recs[E];
+  uint32_t rlo[E], rhi[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    recs[k] = nullptr;
+    rlo[k] = 1;
+    rhi[k] = 0;
+  }
+  if (job.v2) {
+    const uint8_t* cur = blob + kHeader + kDirEntry * S;
+    const uint8_t* end = blob + job.payload_base;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      if (bad || cur + 16 > end) {
+        bad = true;
+        break;
+      }
+      const uint4 h = *reinterpret_cast<const uint4*>(cur);
+      const uint32_t lo = h.x & 0xFFFFu, hi = h.x >> 16;
+      const bool absent = lo == 1 && hi == 0;
+      bad |= h.y != 0 || h.z != 0 || h.w != 0 || (!absent && (lo >= hi || hi > 255));
+      if (bad) break;
+      recs[k] = cur;
+      rlo[k] = lo;
+      rhi[k] = hi;
+      cur += absent ? 16u : (uint32_t)align16(16u + 2u * (hi - lo + 1u));
+    }
+    bad |= cur != end;
+    if (c == 0 && !bad) {
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        if (rlo[k] > rhi[k]) continue;
+        const uint32_t tcount = rhi[k] - rlo[k] + 1u;
+        const uint16_t* ft = reinterpret_cast<const uint16_t*>(recs[k] + 16);
+        uint32_t acc = 0, flast = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t i = 4 * lane + q;
+          const uint32_t fv = i < tcount ? ft[i] : 0u;
+          acc += fv;
+          if (i == tcount - 1) flast = fv;
+        }
+        const uint32_t pad = (uint32_t)align16(2u * tcount) - 2u * tcount;
+        const bool padbad = lane < pad && recs[k][16 + 2 * tcount + lane] != 0;
+        bad |= wave_sum_u32(acc) != kTotal || __shfl(ft[0], 0, 64) == 0 || wave_max_u32(flast) == 0 ||
+               ballot(padbad) != 0;
+      }
+    }
+    if (bad) {  // exactly one of the two instantiations gets here for a chunk
+      if (lane == 0) *job.status = LTC_ERR_CORRUPT;
+      return;
+    }
+  }
+
   // ---- coded-stream headers and tables
   int rstream[MAXR];
+  uint32_t tlo[MAXR], tcnt[MAXR];
   uint32_t x[MAXR], nwords[MAXR], pos[MAXR], hcur[MAXR];
   uint2 staged[MAXR];
   const uint16_t* wp[MAXR];
@@ -166,23 +224,41 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     pos[rr] = 0;
     hcur[rr] = 0;
     wp[rr] = nullptr;
+    tlo[rr] = 0;
+    tcnt[rr] = 0;
     if (rr >= nr) continue;
     const int k = rstream[rr];
     const uint8_t* p = blob + off[k];
     const uint4 h = *reinterpret_cast<const uint4*>(p);
-    const uint32_t lo = h.y & 0xFFu, hi = (h.y >> 8) & 0xFFu;
-    const uint32_t tcount = hi - lo + 1u;
-    const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * tcount);
-    bad |= lo >= hi || (h.y >> 16) != 0 || h.z != 0 || h.w != 0 || wo > size[k] ||
-           (uint64_t)(size[k] - wo) != 2ull * h.x;
+    // the table (u16 f[lo..hi] then zero pad to 16): v1 in the payload after
+    // the states, v2 in the plane's record
+    uint32_t lo, hi, wo;
+    const uint8_t* tb;
+    if (job.v2) {
+      lo = rlo[k];
+      hi = rhi[k];
+      wo = kRansFixed;
+      tb = recs[k] + 16;
+      bad |= lo >= hi || h.y != 0 || h.z != 0 || h.w != 0 || (uint64_t)(size[k] - wo) != 2ull * h.x;
+    } else {
+      lo = h.y & 0xFFu;
+      hi = (h.y >> 8) & 0xFFu;
+      wo = (uint32_t)align16(kRansFixed + 2u * (hi - lo + 1u));
+      tb = p + kRansFixed;
+      bad |= lo >= hi || (h.y >> 16) != 0 || h.z != 0 || h.w != 0 || wo > size[k] ||
+             (uint64_t)(size[k] - wo) != 2ull * h.x;
+    }
     if (bad) break;
+    const uint32_t tcount = hi - lo + 1u;
+    tlo[rr] = lo;
+    tcnt[rr] = tcount;
     nwords[rr] = h.x;
     // with no words, refills (reached only by a corrupt stream) read the
     // directory, which is always inside the blob
     wp[rr] = reinterpret_cast<const uint16_t*>(h.x ? p + wo : blob + kHeader);
     x[rr] = reinterpret_cast<const uint32_t*>(p + 16)[lane];
     bad |= ballot(x[rr] < kRansLow) != 0;
-    const uint16_t* ft = reinterpret_cast<const uint16_t*>(p + kRansFixed);
+    const uint16_t* ft = reinterpret_cast<const uint16_t*>(tb);
     uint32_t f[4], cum[4], acc = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -199,8 +275,8 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
       if (4 * lane + q == tcount - 1) flast = f[q];
     const uint32_t f_lo = __shfl(f[0], 0, 64);
     const uint32_t f_hi = wave_max_u32(flast);
-    const uint32_t pad = wo - (kRansFixed + 2 * tcount);
-    const bool padbad = lane < pad && p[kRansFixed + 2 * tcount + lane] != 0;
+    const uint32_t pad = (uint32_t)align16(2u * tcount) - 2u * tcount;
+    const bool padbad = lane < pad && tb[2 * tcount + lane] != 0;
     bad |= total != kTotal || f_lo == 0 || f_hi == 0 || ballot(padbad) != 0;
     if (bad) break;
     uint16_t* cumt = ring[rr];  // the ring doubles as the cum table while building
@@ -223,9 +299,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
 #pragma unroll
   for (int rr = 0; rr < MAXR; ++rr) {
     if (rr >= nr) continue;
-    const uint8_t* p = blob + off[rstream[rr]];
-    const uint32_t lo = p[4], hi = p[5];
-    const uint32_t tcount = hi - lo + 1u;
+    const uint32_t lo = tlo[rr], tcount = tcnt[rr];
     const uint16_t* cumt = ring[rr];
     const uint32_t slot0 = 64 * lane;
     uint32_t a = 0, z = tcount - 1;  // largest i with cumt[i] <= slot0

@@ -82,6 +82,7 @@ struct CTable {
   uint64_t total_chunks;
   uint32_t vec16;      // every src 16-byte aligned and chunk_bytes % 16 == 0
   uint32_t dtype;
+  uint32_t v2;         // format v2: one table per (tensor, stream index)
   // the launch covers global chunks [c_begin, c_end) (a group of a pipelined
   // call, or all of them)
   uint64_t c_begin, c_end;
@@ -98,6 +99,10 @@ struct CTable {
 struct CWork {
   uint32_t* sinfo;      // [S][4]: size, mode | cval<<8 | lo<<16 | hi<<24, W, 0
   uint16_t* freq;       // [S][256]
+  uint32_t* hist;       // v2: [S][256] histograms of the streams to code
+  uint64_t* plane;      // v2: [count][E][256] summed histograms (zeroed first)
+  uint16_t* ptab;       // v2: [count][E][256] the plane tables
+  uint64_t* pbase;      // v2: [count] payload_base (end of the table records)
   uint32_t* states;     // [S][64]
   uint16_t* words;      // [S][wcap]  (a stream's words end at its slot's end)
   uint64_t* offsets;    // [S]
@@ -108,6 +113,8 @@ struct DJob {
   const uint8_t* blob;
   uint8_t* dst;
   int32_t* status;
+  uint64_t payload_base;  // from the header (v1: the end of the directory)
+  uint32_t v2;            // table records between the directory and payload_base
   uint64_t blob_nbytes;
   uint64_t nbytes;
   uint64_t chunk0;

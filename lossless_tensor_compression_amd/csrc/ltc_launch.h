@@ -8,11 +8,19 @@ namespace ltc {
 // Launches k_hist, k_encode, k_scan and k_pack for chunks [t.c_begin,
 // t.c_end) on st.  ev (optional): 5 events recorded around the kernels.
 // scan_after (optional): the scan waits for it (the previous group's scan);
-// scan_done (optional): recorded right after the scan.
+// scan_done (optional): recorded right after the scan.  staged: the
+// histograms and decisions exist already (v2: launch_v2_tables), so k_hist
+// and the first two events are left out.
 // With t.crc set, k_pack also accumulates the blob's 1 KiB frame remainders
 // into each job's frames array (zeroed beforehand with launch_zero_u32).
 hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
-                           hipEvent_t scan_after = nullptr, hipEvent_t scan_done = nullptr);
+                           hipEvent_t scan_after = nullptr, hipEvent_t scan_done = nullptr,
+                           bool staged = false);
+
+// Format v2 for all chunks of t (c_begin = 0, c_end = total): k_hist (which
+// then sums each plane's histograms), k_share (tables, records, payload
+// base), k_decide (skip bound per stream).  ev (optional): events 0 and 1.
+hipError_t launch_v2_tables(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev);
 
 // p[0, n) = 0 (a kernel, so that the call can be captured in a graph)
 hipError_t launch_zero_u32(uint32_t* p, uint64_t n, hipStream_t st);

@@ -75,7 +75,7 @@ def test_blob_info_errors_match_oracle():
     blob = oracle.compress(workloads.c1()[:5000], 1, 1024)
     assert _info_rc(blob[:64]) == 0
     cases = []
-    for pos, val in ((0, 0x4D), (4, 2), (6, 7), (7, 4), (24, 32), (26, 11), (27, 1),
+    for pos, val in ((0, 0x4D), (4, 2), (4, 3), (6, 7), (7, 4), (24, 32), (26, 11), (27, 1),
                      (28, 1), (50, 1), (16, 0), (20, 99), (40, 0)):
         b = blob.copy()
         b[pos] = val

@@ -95,6 +95,24 @@ def test_c3_compress_with_crc32_full_size(ltc):
             assert int(c[w].item()) & 0xFFFFFFFF == zlib.crc32(seg.tobytes()), (i, w)
 
 
+def test_c3_shared_tables_full_size(ltc):
+    """Format v2 (one table per stream index) over the C3 batch: exact round
+    trip, and two tensors byte for byte against the oracle's v2 blobs."""
+    banner("C3 generate")
+    ts = workloads.c3_gpu()
+    banner("C3 compress_batch, shared tables")
+    blobs = ltc.compress_batch(ts, shared_tables=True)
+    outs = ltc.decompress_batch(blobs)
+    for t, o in zip(ts, outs):
+        assert torch.equal(t.view(-1).view(torch.int16), o.view(torch.int16))
+    del outs
+    for i in (1, 27):
+        banner(f"C3 v2 oracle parity tensor {i} {workloads.C3_SHAPES[i]}")
+        host = ts[i].view(torch.int16).cpu().numpy()
+        want = oracle.compress(host, 1, CHUNK, 0.95, nthreads=16, shared_tables=True)
+        assert np.array_equal(blobs[i].cpu().numpy(), want)
+
+
 def test_c5_full_size_with_crc(ltc):
     banner("C5 generate (8 GiB)")
     buf = workloads.c5_gpu()

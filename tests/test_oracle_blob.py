@@ -150,8 +150,10 @@ def test_corruption_is_detected():
     assert oracle.decompress(blob)[0] == 0
     b = blob.copy(); b[0] ^= 1
     assert oracle.decompress(b)[0] == oracle.ERR_BAD_MAGIC
-    b = blob.copy(); b[4] = 2
+    b = blob.copy(); b[4] = 3                 # no such version
     assert oracle.decompress(b)[0] == oracle.ERR_BAD_VERSION
+    b = blob.copy(); b[4] = 2                 # v2 needs the shared-table flag and records
+    assert oracle.decompress(b)[0] == oracle.ERR_CORRUPT
     b = blob.copy(); b[6] = 9
     assert oracle.decompress(b)[0] == oracle.ERR_UNSUPPORTED_DTYPE
     assert oracle.decompress(blob[:-16])[0] == oracle.ERR_CORRUPT
