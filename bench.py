@@ -59,6 +59,9 @@ def parse():
                     help="run every step kernel by kernel on one stream (for per-kernel profiles)")
     ap.add_argument("--crc", default="fused", choices=["fused", "beside"],
                     help="CRC-32 of the blobs computed while packing, or by its own kernel")
+    ap.add_argument("--tables", default="own", choices=["own", "shared"],
+                    help="blob format: v1 (a frequency table per coded stream) or v2 (one per "
+                         "stream index, shared by all chunks of a tensor)")
     ap.add_argument("--host-path", action="store_true",
                     help="also time decoding from pinned host blobs (copies over the host link "
                          "overlapped with decoding) against plain host-to-device copies of the "
@@ -268,7 +271,9 @@ def main():
     count = len(ts)
     nbytes = [t.numel() * t.element_size() for t in ts]
     N = sum(nbytes)
-    caps = [ltc.compress_bound(n, code, CHUNK) for n in nbytes]
+    shared = args.tables == "shared"
+    flags = ltc.FLAG_SHARED_TABLES if shared else 0
+    caps = [ltc.compress_bound(n, code, CHUNK, shared) for n in nbytes]
     blobs = [torch.empty(c, dtype=torch.uint8, device="cuda") for c in caps]
     ws_n = ltc.workspace_size(nbytes, code, CHUNK)
     ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
@@ -287,8 +292,11 @@ def main():
     ev_x = hip.events(2)
 
     # first pass: sizes and headers (host copies) for the decode and CRC launches
-    ltc.compress_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, blob_ptrs, caps, sizes.data_ptr(),
-                     ws.data_ptr(), ws_n, events=ev_c if args.isolated else None)
+    def compress_plain(events=None):
+        ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, flags, blob_ptrs, caps,
+                            sizes.data_ptr(), ws.data_ptr(), ws_n, events=events)
+
+    compress_plain(ev_c if args.isolated else None)
     bsz = sizes.cpu().tolist()
     headers = [bytes(b[:64].cpu().numpy().tobytes()) for b in blobs]
     B = sum(bsz)
@@ -305,9 +313,9 @@ def main():
     def compress_crc(events=None):
         if events is None and args.isolated:
             events = ev_f  # kernel by kernel
-        ltc.compress_crc32_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, blob_ptrs, caps,
-                               sizes.data_ptr(), CRC_CHUNK, fcrc_ptrs, fcap, ws.data_ptr(), ws_n,
-                               events=events)
+        ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, flags, blob_ptrs, caps,
+                            sizes.data_ptr(), ws.data_ptr(), ws_n, CRC_CHUNK, fcrc_ptrs, fcap,
+                            events=events)
 
     ev_p = hip.events(4)
     side = torch.cuda.Stream()  # default priority
@@ -330,8 +338,7 @@ def main():
         serial = prof or phases
         if phases:
             hip.record(ev_p[0], sptr)
-        ltc.compress_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, blob_ptrs, caps, sizes.data_ptr(),
-                         ws.data_ptr(), ws_n, events=ev_c if prof else None)
+        compress_plain(ev_c if prof else None)
         if phases:
             hip.record(ev_p[1], sptr)
         if not serial:
@@ -471,6 +478,7 @@ def main():
                    "crc_chunk_bytes": CRC_CHUNK, "parallelism": "single GPU",
                    "crc": "computed while packing (compress_with_crc32)" if fused
                           else "own kernel beside decompress",
+                   "format": "v2, one table per stream index" if shared else "v1, a table per coded stream",
                    "launch": "kernel by kernel, one stream" if args.isolated
                              else "compress in 4 chunk groups on 4 streams"},
         "decompress_gbs": round(N / (t_dec * 1e-3) / 1e9, 2),
