@@ -16,8 +16,9 @@ from . import build as _build
 
 DTYPES = {"u8": 0, "bf16": 1, "fp16": 2, "fp32": 3}
 ELEM_BYTES = {0: 1, 1: 2, 2: 2, 3: 4}
-MODE_RAW, MODE_RANS, MODE_CONST = 0, 1, 2
+MODE_RAW, MODE_RANS, MODE_CONST, MODE_ZRUN = 0, 1, 2, 3
 FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
+FLAG_DELTA = 2          # header flag: XOR delta against a base
 
 OK = 0
 ERR_INVALID_ARGUMENT = -1
@@ -69,6 +70,9 @@ def lib():
         L.ltco_compress_bound_ex.restype = c.c_uint64
         L.ltco_compress_ex.argtypes = [u8p, c.c_uint64, c.c_int, c.c_uint32, c.c_double,
                                        c.c_uint32, u8p, c.c_uint64, u64p, c.c_int]
+        L.ltco_compress_delta.argtypes = [u8p, u8p, c.c_uint64, c.c_int, c.c_uint32, c.c_double,
+                                          c.c_uint32, u8p, c.c_uint64, u64p, c.c_int]
+        L.ltco_decompress_delta.argtypes = [u8p, c.c_uint64, u8p, u8p, c.c_uint64, u64p, c.c_int]
         L.ltco_encode_chunk.argtypes = [u8p, c.c_uint64, c.c_int, c.c_uint32,
                                         c.c_double, c.c_uint64, u8p, u8p, u32p,
                                         u8p, c.c_uint64, u64p]
@@ -170,6 +174,44 @@ def compress(src, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None, shar
     if rc:
         raise ValueError(f"oracle compress: status {rc}")
     return blob[: nb.value].copy()
+
+
+def compress_delta(src, base, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None,
+                   shared_tables=False):
+    """Blob of src XOR base (same byte size), with ZipNN's zero-run rule."""
+    b = _as_bytes(src)
+    bb = _as_bytes(base)
+    if bb.size != b.size:
+        raise ValueError("base must have the input's size")
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    cap = max(64, compress_bound(b.size, dtype, chunk_bytes, shared_tables))
+    blob = np.zeros(cap, dtype=np.uint8)
+    nb = ctypes.c_uint64(0)
+    rc = lib().ltco_compress_delta(_u8p(b), _u8p(bb), b.size, dtype, chunk_bytes, threshold,
+                                   FLAG_SHARED_TABLES if shared_tables else 0,
+                                   _u8p(blob), blob.size, ctypes.byref(nb), int(nthreads))
+    if rc:
+        raise ValueError(f"oracle compress_delta: status {rc}")
+    return blob[: nb.value].copy()
+
+
+def decompress_delta(blob, base, nthreads=None):
+    """(status, decoded bytes) of a delta blob given its base."""
+    bl = np.ascontiguousarray(blob, dtype=np.uint8)
+    bb = _as_bytes(base)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    capacity = int.from_bytes(bytes(bl[8:16]), "little") if bl.size >= 16 else 0
+    dst = np.zeros(max(1, capacity), dtype=np.uint8)
+    if bb.size < capacity:
+        return ERR_INVALID_ARGUMENT, None
+    nout = ctypes.c_uint64(0)
+    rc = lib().ltco_decompress_delta(_u8p(bl), bl.size, _u8p(bb), _u8p(dst), capacity,
+                                     ctypes.byref(nout), int(nthreads))
+    if rc:
+        return rc, None
+    return rc, dst[: nout.value].copy()
 
 
 def encode_chunk(src, dtype, chunk_bytes, threshold, c):

@@ -274,9 +274,131 @@ typedef struct {
   uint8_t* payload; /* malloc'd, size bytes (NULL for CONST) */
 } stream_result;
 
+/* ---- deltas (NOTE-241: ZipNN, "Method" item 6 and "Key results", Deltas) --
+ * ZipNN's rule picks a coder for runs of zeros over its order-0 coder when
+ * more than 90% of a byte group is zero bytes or a zero run is longer than 3%
+ * of it.  READING: the byte group is the chunk's stream, the run coder is the
+ * ZRUN payload below, and the rule only admits ZRUN as a candidate: the
+ * stream takes the smaller of RANS and ZRUN (ties: RANS), RAW if neither is
+ * at most P_max. */
+static int zrun_rule(const uint8_t* sym, uint64_t n) {
+  uint64_t zeros = 0, run = 0, longest = 0;
+  for (uint64_t i = 0; i < n; i++) {
+    if (sym[i] == 0) {
+      zeros++;
+      run++;
+      if (run > longest) longest = run;
+    } else {
+      run = 0;
+    }
+  }
+  return 10 * zeros > 9 * n || 100 * longest > 3 * n;
+}
+
+/* ZRUN payload: u32 nnz | u32 nblk | 8 zero bytes | bitmap of the nonzero
+ * 64-byte blocks (bit b = block b, least significant bit first), zero-padded
+ * to 16 | one u64 per nonzero block (bit i = its byte i is nonzero), padded to
+ * 16 | the nnz nonzero bytes in order. */
+static uint64_t zrun_size(const uint8_t* sym, uint64_t n, uint64_t* nnz_out, uint64_t* nblk_out) {
+  uint64_t nb = (n + 63) / 64, nnz = 0, nblk = 0;
+  for (uint64_t b = 0; b < nb; b++) {
+    int any = 0;
+    for (uint64_t i = 64 * b; i < n && i < 64 * b + 64; i++)
+      if (sym[i]) {
+        any = 1;
+        nnz++;
+      }
+    nblk += (uint64_t)any;
+  }
+  *nnz_out = nnz;
+  *nblk_out = nblk;
+  return 16 + align16((nb + 7) / 8) + align16(8 * nblk) + nnz;
+}
+
+static uint8_t* zrun_payload(const uint8_t* sym, uint64_t n, uint64_t size) {
+  uint64_t nnz = 0, nblk = 0;
+  zrun_size(sym, n, &nnz, &nblk);
+  uint8_t* pl = (uint8_t*)calloc(size, 1);
+  if (!pl) return NULL;
+  uint64_t nb = (n + 63) / 64;
+  uint64_t l2 = 16 + align16((nb + 7) / 8), lit = l2 + align16(8 * nblk);
+  put_u32(pl, (uint32_t)nnz);
+  put_u32(pl + 4, (uint32_t)nblk);
+  uint64_t k = 0;
+  for (uint64_t b = 0; b < nb; b++) {
+    uint64_t mask = 0;
+    for (uint64_t i = 64 * b; i < n && i < 64 * b + 64; i++)
+      if (sym[i]) {
+        mask |= 1ull << (i - 64 * b);
+        pl[lit++] = sym[i];
+      }
+    if (mask) {
+      pl[16 + b / 8] |= (uint8_t)(1u << (b % 8));
+      put_u64(pl + l2 + 8 * k, mask);
+      k++;
+    }
+  }
+  return pl;
+}
+
+/* ZRUN payload -> the n stream bytes; checks every field */
+static int zrun_decode(const uint8_t* pl, uint32_t size, uint64_t n, uint8_t* out) {
+  if (size < 16) return LTCO_ERR_CORRUPT;
+  uint64_t nnz = get_u32(pl), nblk = get_u32(pl + 4);
+  for (int i = 8; i < 16; i++)
+    if (pl[i]) return LTCO_ERR_CORRUPT;
+  uint64_t nb = (n + 63) / 64;
+  uint64_t l2 = 16 + align16((nb + 7) / 8), lit = l2 + align16(8 * nblk);
+  if (nblk > nb || nnz > n || lit + nnz != size) return LTCO_ERR_CORRUPT;
+  for (uint64_t i = 16 + (nb + 7) / 8; i < l2; i++)
+    if (pl[i]) return LTCO_ERR_CORRUPT;
+  if (nb % 8 && (pl[16 + nb / 8] >> (nb % 8))) return LTCO_ERR_CORRUPT;
+  for (uint64_t i = l2 + 8 * nblk; i < lit; i++)
+    if (pl[i]) return LTCO_ERR_CORRUPT;
+  uint64_t k = 0, used = 0;
+  for (uint64_t b = 0; b < nb; b++) {
+    uint64_t mask = 0;
+    if ((pl[16 + b / 8] >> (b % 8)) & 1) {
+      if (k >= nblk) return LTCO_ERR_CORRUPT;
+      mask = get_u64(pl + l2 + 8 * k);
+      k++;
+      if (mask == 0) return LTCO_ERR_CORRUPT;
+    }
+    for (uint64_t i = 64 * b; i < 64 * b + 64; i++) {
+      const int nz = (int)((mask >> (i - 64 * b)) & 1);
+      if (i >= n) {
+        if (nz) return LTCO_ERR_CORRUPT;
+        continue;
+      }
+      if (nz) {
+        if (used >= nnz || pl[lit + used] == 0) return LTCO_ERR_CORRUPT;
+        out[i] = pl[lit + used++];
+      } else {
+        out[i] = 0;
+      }
+    }
+  }
+  if (k != nblk || used != nnz) return LTCO_ERR_CORRUPT;
+  return LTCO_OK;
+}
+
+/* a delta stream whose rule fires: ZRUN instead of RANS when strictly
+ * smaller and at most P_max (p = the RANS payload size) */
+static int maybe_zrun(const uint8_t* sym, uint64_t n, double theta, uint64_t p, stream_result* r) {
+  if (!zrun_rule(sym, n)) return 0;
+  uint64_t nnz = 0, nblk = 0;
+  uint64_t pz = zrun_size(sym, n, &nnz, &nblk);
+  if (pz >= p || pz > ltco_p_max(n, theta)) return 0;
+  r->payload = zrun_payload(sym, n, pz);
+  if (!r->payload) return -1;
+  r->mode = LTCO_MODE_ZRUN;
+  r->size = (uint32_t)pz;
+  return 1;
+}
+
 /* One stream: histogram, CONST / RANS / RAW decision, payload bytes. */
 static int encode_stream(const uint8_t* sym, uint64_t n, double theta,
-                         stream_result* r) {
+                         stream_result* r, int delta) {
   uint64_t h[256];
   ltco_histogram(sym, n, h);
   int nonzero = 0, only = 0;
@@ -312,6 +434,11 @@ static int encode_stream(const uint8_t* sym, uint64_t n, double theta,
   uint64_t tcount = (uint64_t)(hi - lo + 1);
   uint64_t wo = align16(RANS_FIXED + 2 * tcount);
   uint64_t p = wo + 2 * nw;
+  int z = delta ? maybe_zrun(sym, n, theta, p, r) : 0;
+  if (z) {
+    free(words);
+    return z < 0 ? LTCO_ERR_INVALID_ARGUMENT : LTCO_OK;
+  }
   if (p <= ltco_p_max(n, theta)) {
     uint8_t* pl = (uint8_t*)calloc(p, 1);
     if (!pl) {
@@ -345,14 +472,14 @@ static int encode_stream(const uint8_t* sym, uint64_t n, double theta,
 
 static int encode_chunk_streams(const uint8_t* src, uint64_t nbytes, int dtype,
                                 uint32_t chunk_bytes, double theta, uint64_t c,
-                                stream_result* out) {
+                                stream_result* out, int delta) {
   int e = ltco_elem_bytes(dtype);
   uint8_t* sym = (uint8_t*)malloc(chunk_bytes / (uint32_t)e + 1);
   if (!sym) return LTCO_ERR_INVALID_ARGUMENT;
   int rc = LTCO_OK;
   for (int k = 0; k < e && rc == LTCO_OK; k++) {
     uint64_t n = ltco_chunk_stream(src, nbytes, dtype, chunk_bytes, c, k, sym);
-    rc = encode_stream(sym, n, theta, &out[k]);
+    rc = encode_stream(sym, n, theta, &out[k], delta);
   }
   free(sym);
   return rc;
@@ -381,7 +508,7 @@ int ltco_encode_chunk(const uint8_t* src, uint64_t nbytes, int dtype,
   if (c * (uint64_t)chunk_bytes >= nbytes) return LTCO_ERR_INVALID_ARGUMENT;
   stream_result r[4];
   memset(r, 0, sizeof(r));
-  rc = encode_chunk_streams(src, nbytes, dtype, chunk_bytes, theta, c, r);
+  rc = encode_chunk_streams(src, nbytes, dtype, chunk_bytes, theta, c, r, 0);
   uint64_t cur = 0;
   for (int k = 0; k < e && rc == LTCO_OK; k++) {
     uint64_t next = align16(cur + r[k].size);
@@ -401,11 +528,11 @@ int ltco_encode_chunk(const uint8_t* src, uint64_t nbytes, int dtype,
   return rc;
 }
 
-int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
-                  uint32_t chunk_bytes, double theta, uint8_t* blob,
-                  uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads) {
-  int rc = check_args(nbytes, dtype, chunk_bytes, theta);
-  if (rc) return rc;
+static int compress_v1(const uint8_t* src, uint64_t nbytes, int dtype,
+                       uint32_t chunk_bytes, double theta, uint8_t* blob,
+                       uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads,
+                       int delta) {
+  int rc = LTCO_OK;
   int e = ltco_elem_bytes(dtype);
   uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
   uint64_t s = k * (uint64_t)e;
@@ -416,7 +543,7 @@ int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
   for (long long c = 0; c < (long long)k; c++) {
     int r = encode_chunk_streams(src, nbytes, dtype, chunk_bytes, theta,
-                                 (uint64_t)c, res + (uint64_t)c * e);
+                                 (uint64_t)c, res + (uint64_t)c * e, delta);
     if (r) {
 #pragma omp atomic write
       failed = r;
@@ -440,7 +567,7 @@ int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
     put_u32(blob + 20, (uint32_t)k);
     put_u16(blob + 24, LANES);
     blob[26] = 12;
-    blob[27] = 0;
+    blob[27] = (uint8_t)(delta ? LTCO_FLAG_DELTA : 0);
     put_u64(blob + 32, cursor);
     put_u64(blob + 40, base);
     uint64_t cur = base;
@@ -460,6 +587,15 @@ int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
   return rc;
 }
 
+int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
+                  uint32_t chunk_bytes, double theta, uint8_t* blob,
+                  uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads) {
+  int rc = check_args(nbytes, dtype, chunk_bytes, theta);
+  if (rc) return rc;
+  return compress_v1(src, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity, blob_nbytes,
+                     nthreads, 0);
+}
+
 /* ---- format v2: one frequency table per stream index (shared tables) ---- */
 
 /* bytes of a table record: 16-byte head plus f[lo..hi], padded to 16 */
@@ -471,7 +607,7 @@ static uint64_t record_bytes(int lo, int hi) {
  * covers every value of the stream) and kept if the payload (272 + 2W bytes)
  * is at most P_max, else RAW. */
 static int encode_stream_shared(const uint8_t* sym, uint64_t n, double theta,
-                                const uint16_t f[256], stream_result* r) {
+                                const uint16_t f[256], stream_result* r, int delta) {
   uint64_t h[256];
   ltco_histogram(sym, n, h);
   int nonzero = 0, only = 0;
@@ -498,6 +634,11 @@ static int encode_stream_shared(const uint8_t* sym, uint64_t n, double theta,
     return rc;
   }
   uint64_t p = RANS_FIXED + 2 * nw;
+  int z = delta ? maybe_zrun(sym, n, theta, p, r) : 0;
+  if (z) {
+    free(words);
+    return z < 0 ? LTCO_ERR_INVALID_ARGUMENT : LTCO_OK;
+  }
   if (p <= ltco_p_max(n, theta)) {
     uint8_t* pl = (uint8_t*)calloc(p, 1);
     if (!pl) {
@@ -536,7 +677,7 @@ uint64_t ltco_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes
 static int compress_shared(const uint8_t* src, uint64_t nbytes, int dtype,
                            uint32_t chunk_bytes, double theta, uint8_t* blob,
                            uint64_t blob_capacity, uint64_t* blob_nbytes,
-                           int nthreads) {
+                           int nthreads, int delta) {
   int e = ltco_elem_bytes(dtype);
   uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
   uint64_t s = k * (uint64_t)e;
@@ -579,7 +720,7 @@ static int compress_shared(const uint8_t* src, uint64_t nbytes, int dtype,
     int r = cs ? LTCO_OK : LTCO_ERR_INVALID_ARGUMENT;
     for (int q = 0; q < e && r == LTCO_OK; q++) {
       uint64_t n = ltco_chunk_stream(src, nbytes, dtype, chunk_bytes, (uint64_t)c, q, cs);
-      r = encode_stream_shared(cs, n, theta, f[q], res + (uint64_t)c * e + q);
+      r = encode_stream_shared(cs, n, theta, f[q], res + (uint64_t)c * e + q, delta);
     }
     free(cs);
     if (r) {
@@ -608,7 +749,7 @@ static int compress_shared(const uint8_t* src, uint64_t nbytes, int dtype,
     put_u32(blob + 20, (uint32_t)k);
     put_u16(blob + 24, LANES);
     blob[26] = 12;
-    blob[27] = (uint8_t)LTCO_FLAG_SHARED_TABLES;
+    blob[27] = (uint8_t)(LTCO_FLAG_SHARED_TABLES | (delta ? LTCO_FLAG_DELTA : 0));
     put_u64(blob + 32, cursor);
     put_u64(blob + 40, base);
     uint64_t t = HDR_BYTES + DIR_BYTES * s;
@@ -646,7 +787,27 @@ int ltco_compress_ex(const uint8_t* src, uint64_t nbytes, int dtype,
   int rc = check_args(nbytes, dtype, chunk_bytes, theta);
   if (rc) return rc;
   return compress_shared(src, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity,
-                         blob_nbytes, nthreads);
+                         blob_nbytes, nthreads, 0);
+}
+
+int ltco_compress_delta(const uint8_t* src, const uint8_t* base, uint64_t nbytes, int dtype,
+                        uint32_t chunk_bytes, double theta, uint32_t flags, uint8_t* blob,
+                        uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads) {
+  if (flags & ~(uint32_t)LTCO_FLAG_SHARED_TABLES) return LTCO_ERR_INVALID_ARGUMENT;
+  int rc = check_args(nbytes, dtype, chunk_bytes, theta);
+  if (rc) return rc;
+  /* NOTE-241: ZipNN, "Method" item 6: XOR against the base, then as usual */
+  uint8_t* x = (uint8_t*)malloc(nbytes ? nbytes : 1);
+  if (!x) return LTCO_ERR_INVALID_ARGUMENT;
+  for (uint64_t i = 0; i < nbytes; i++) x[i] = src[i] ^ base[i];
+  if (flags & LTCO_FLAG_SHARED_TABLES)
+    rc = compress_shared(x, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity, blob_nbytes,
+                         nthreads, 1);
+  else
+    rc = compress_v1(x, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity, blob_nbytes,
+                     nthreads, 1);
+  free(x);
+  return rc;
 }
 
 typedef struct {
@@ -722,6 +883,8 @@ static int decode_chunk(const uint8_t* blob, const dir_entry* ent, int dtype,
       memset(plane, ent[k].cval, n);
     } else if (ent[k].mode == LTCO_MODE_RAW) {
       memcpy(plane, pl, n);
+    } else if (ent[k].mode == LTCO_MODE_ZRUN) {
+      rc = zrun_decode(pl, ent[k].size, n, plane);
     } else {
       uint16_t f[256];
       uint32_t states[64];
@@ -759,8 +922,10 @@ static int decode_chunk(const uint8_t* blob, const dir_entry* ent, int dtype,
   return rc;
 }
 
-int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
-                    uint64_t dst_capacity, uint64_t* out_nbytes, int nthreads) {
+/* base: the delta base (delta blobs only; NULL otherwise) */
+static int decompress_impl(const uint8_t* blob, uint64_t blob_nbytes, const uint8_t* xbase,
+                           uint8_t* dst, uint64_t dst_capacity, uint64_t* out_nbytes,
+                           int nthreads) {
   if (blob_nbytes < HDR_BYTES) return LTCO_ERR_CORRUPT;
   if (memcmp(blob, "LTCB", 4) != 0) return LTCO_ERR_BAD_MAGIC;
   const int version = (int)get_u16(blob + 4);
@@ -772,9 +937,12 @@ int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
   uint64_t nbytes = get_u64(blob + 8);
   uint32_t chunk_bytes = get_u32(blob + 16);
   uint64_t k = get_u32(blob + 20);
+  const int delta = (blob[27] & LTCO_FLAG_DELTA) != 0;
   if (get_u16(blob + 24) != LANES || blob[26] != 12 ||
-      blob[27] != (version == 2 ? LTCO_FLAG_SHARED_TABLES : 0) || get_u32(blob + 28) != 0)
+      (blob[27] & ~LTCO_FLAG_DELTA) != (version == 2 ? LTCO_FLAG_SHARED_TABLES : 0) ||
+      get_u32(blob + 28) != 0)
     return LTCO_ERR_CORRUPT;
+  if (delta != (xbase != NULL)) return LTCO_ERR_INVALID_ARGUMENT; /* a delta blob needs its base */
   for (int i = 48; i < 64; i++)
     if (blob[i]) return LTCO_ERR_CORRUPT;
   if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8)
@@ -832,7 +1000,8 @@ int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
     uint64_t len = nbytes - c * (uint64_t)chunk_bytes;
     if (len > chunk_bytes) len = chunk_bytes;
     uint64_t n = len / (uint64_t)e;
-    int bad = ent[i].off != cursor || get_u16(d + 14) != 0 || ent[i].mode > 2 ||
+    int bad = ent[i].off != cursor || get_u16(d + 14) != 0 ||
+              ent[i].mode > (delta ? LTCO_MODE_ZRUN : LTCO_MODE_CONST) ||
               (ent[i].mode != LTCO_MODE_CONST && ent[i].cval != 0) ||
               (ent[i].mode == LTCO_MODE_RAW && ent[i].size != n) ||
               (ent[i].mode == LTCO_MODE_CONST && ent[i].size != 0) ||
@@ -863,8 +1032,22 @@ int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
   }
   free(ent);
   if (failed) return failed;
+  if (xbase)
+    for (uint64_t i = 0; i < nbytes; i++) dst[i] ^= xbase[i];
   *out_nbytes = nbytes;
   return LTCO_OK;
+}
+
+int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
+                    uint64_t dst_capacity, uint64_t* out_nbytes, int nthreads) {
+  return decompress_impl(blob, blob_nbytes, NULL, dst, dst_capacity, out_nbytes, nthreads);
+}
+
+int ltco_decompress_delta(const uint8_t* blob, uint64_t blob_nbytes, const uint8_t* base,
+                          uint8_t* dst, uint64_t dst_capacity, uint64_t* out_nbytes,
+                          int nthreads) {
+  if (!base) return LTCO_ERR_INVALID_ARGUMENT;
+  return decompress_impl(blob, blob_nbytes, base, dst, dst_capacity, out_nbytes, nthreads);
 }
 
 /* CRC-32 as zlib computes it (cuZipNN 0.1.0, "API": checksums match

@@ -77,6 +77,19 @@
  *  Per stream: one value -> CONST; else rANS with the plane's table, payload
  *    u32 W | 12 zero bytes | u32 states[64] | u16 words[W], P = 272 + 2W;
  *    P <= P_max(n) -> RANS, else RAW.  Offsets and gaps as v1.
+ *
+ * Deltas (NOTE-241: ZipNN, "Method" item 6; "Key results", Deltas): the
+ * input is src XOR base, byte for byte, before everything above; header
+ * flag bit 1 (value 2) marks a delta blob (flags 2 in v1, 3 in v2).  ZipNN
+ * picks a run coder over its order-0 coder for a byte group when more than
+ * 90% of it is zero bytes or a zero run exceeds 3% of it (READING: integers,
+ * 10*zeros > 9n or 100*longest_zero_run > 3n, per chunk stream).  Here the
+ * rule admits a ZRUN payload (mode 3) as a candidate; the stream takes the
+ * smaller of RANS and ZRUN (ties: RANS), RAW if neither is <= P_max(n).
+ *  ZRUN payload: u32 nnz | u32 nblk | 8 zero bytes | bitmap of the nonzero
+ *    64-byte blocks (ceil(n/64) bits, LSB first), zero pad to 16 | nblk u64
+ *    masks (bit i = byte i of the block is nonzero), zero pad to 16 | the
+ *    nnz nonzero bytes in order.
  */
 #ifndef LTC_ORACLE_H
 #define LTC_ORACLE_H
@@ -98,10 +111,12 @@ extern "C" {
 #define LTCO_ERR_CAPACITY (-6)
 
 #define LTCO_FLAG_SHARED_TABLES 1u /* compress_ex: format v2 */
+#define LTCO_FLAG_DELTA 2u         /* header flag: XOR delta against a base */
 
 #define LTCO_MODE_RAW 0
 #define LTCO_MODE_RANS 1
 #define LTCO_MODE_CONST 2
+#define LTCO_MODE_ZRUN 3 /* delta blobs only */
 
 int ltco_elem_bytes(int dtype);
 uint32_t ltco_reorder(int dtype, uint32_t x);
@@ -140,6 +155,14 @@ int ltco_encode_chunk(const uint8_t* src, uint64_t nbytes, int dtype,
                       uint8_t* out, uint64_t out_cap, uint64_t* nout);
 int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
                     uint64_t dst_capacity, uint64_t* out_nbytes, int nthreads);
+/* deltas: compress src XOR base (flags 0 or LTCO_FLAG_SHARED_TABLES); decode
+ * and XOR the base back in.  A delta blob needs its base and only then. */
+int ltco_compress_delta(const uint8_t* src, const uint8_t* base, uint64_t nbytes, int dtype,
+                        uint32_t chunk_bytes, double theta, uint32_t flags, uint8_t* blob,
+                        uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads);
+int ltco_decompress_delta(const uint8_t* blob, uint64_t blob_nbytes, const uint8_t* base,
+                          uint8_t* dst, uint64_t dst_capacity, uint64_t* out_nbytes,
+                          int nthreads);
 
 uint32_t ltco_crc32(const uint8_t* p, uint64_t n);
 int ltco_crc32_chunks(const uint8_t* p, uint64_t n, uint32_t chunk_bytes,
