@@ -95,6 +95,25 @@
  *     is coded with its plane's table, payload 0 u32 W | 4 twelve zero bytes
  *     | 16 u32 states[64] | 272 u16 words[W] (272 + 2W bytes), RANS if that
  *     is at most P_max(n), else RAW.  Offsets and gaps as v1.
+ *
+ * DELTAS (header flag LTC_FLAG_DELTA, in v1 or v2; "NOTE-241: ZipNN",
+ * section "Method" item 6 and the delta results: the XOR of two versions of
+ * a model's weights, coded with a run coder instead of the order-0 coder
+ * when a byte group is mostly zero bytes):
+ *   The coded input is d = src XOR base, byte for byte; the header, reorder,
+ *   streams and v1/v2 tables are those of the plain blob of d.  Directory
+ *   mode 3 (ZRUN) adds a zero-run payload for a stream of n bytes:
+ *     0 u32 nnz | 4 u32 nblk | 8 eight zero bytes | 16 bitmap of the
+ *     ceil(n/64) 64-byte blocks, bit b (LSB first) set when block b holds a
+ *     nonzero byte, zero pad to a multiple of 16 | nblk u64 masks, one per
+ *     set block in order, bit j set when byte j of the block is nonzero,
+ *     zero pad to a multiple of 16 | nnz nonzero bytes in stream order.
+ *   Choice per stream: CONST if one value occurs; otherwise ZRUN is a
+ *   candidate when 10*zeros > 9n or 100*(longest zero run) > 3n, and the
+ *   smaller of the RANS and ZRUN payloads that are at most P_max(n) is
+ *   stored (RANS on a tie); RAW if neither fits.  Decoding a delta blob
+ *   needs the same base; without it, or with a base for a plain blob, the
+ *   call returns INVALID_ARGUMENT.
  */
 #ifndef LTC_H
 #define LTC_H
@@ -121,9 +140,10 @@ enum {
   LTC_ERR_HIP = -8               /* a HIP call or launch failed */
 };
 
-enum { LTC_MODE_RAW = 0, LTC_MODE_RANS = 1, LTC_MODE_CONST = 2 };
+enum { LTC_MODE_RAW = 0, LTC_MODE_RANS = 1, LTC_MODE_CONST = 2, LTC_MODE_ZRUN = 3 /* deltas */ };
 
 #define LTC_FLAG_SHARED_TABLES 1u /* compress flags: format v2 */
+#define LTC_FLAG_DELTA 2u         /* header flag: XOR delta against a base */
 
 #define LTC_HEADER_BYTES 64
 #define LTC_DEFAULT_CHUNK_BYTES 131072u
@@ -141,6 +161,7 @@ typedef struct {
   uint64_t blob_nbytes;
   uint64_t payload_base;
   uint32_t version;      /* 1, or 2 (shared tables) */
+  uint32_t flags;        /* header byte 27: LTC_FLAG_SHARED_TABLES | LTC_FLAG_DELTA */
 } ltc_info;
 
 /* Element size of a dtype code, 0 if unknown. */
@@ -193,7 +214,9 @@ int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out);
  * or writing out of bounds, and write LTC_OK or LTC_ERR_CORRUPT to *d_status
  * (device i32).  After CORRUPT the contents of d_dst are unspecified.  A
  * checksum is still the way to detect a corrupted payload that happens to
- * decode (cuZipNN "API": verify untrusted blobs with CRC-32 first). */
+ * decode (cuZipNN "API": verify untrusted blobs with CRC-32 first).  A delta
+ * blob (LTC_FLAG_DELTA) is refused with INVALID_ARGUMENT here and in the
+ * other base-less decode calls: ltc_decompress_delta decodes it. */
 int ltc_decompress(const void* h_header, const void* d_blob, uint64_t blob_nbytes,
                    void* d_dst, uint64_t dst_capacity, int32_t* d_status,
                    hipStream_t stream);
@@ -248,6 +271,10 @@ uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
 /* The general compress call: ltc_compress_batch plus
  *   flags: 0 (format v1) or LTC_FLAG_SHARED_TABLES (format v2); capacities
  *     are checked against ltc_compress_bound_ex;
+ *   h_base_ptrs: NULL, or per tensor the device pointer of its delta base
+ *     (nbytes bytes, aligned like the source): the blobs are XOR deltas
+ *     (LTC_FLAG_DELTA set in the header; with checksums the CRC kernel reads
+ *     the finished blobs back);
  *   checksum_chunk_bytes: 0, or the CRC-32 of the blobs as in
  *     ltc_compress_batch_with_crc32 (h_crc_ptrs / h_crc_capacity);
  *   h_events: NULL, or the events of the *_prof variants (5, or 6 with
@@ -256,11 +283,41 @@ uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
  * then codes the chunks (in groups on several streams, as v1). */
 int ltc_compress_batch_ex(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
                           int dtype, uint32_t chunk_bytes, double passthrough_threshold,
-                          uint32_t flags, void* const* h_blob_ptrs,
+                          uint32_t flags, const void* const* h_base_ptrs, void* const* h_blob_ptrs,
                           const uint64_t* h_blob_capacity, uint64_t* d_blob_nbytes,
                           uint32_t checksum_chunk_bytes, uint32_t* const* h_crc_ptrs,
                           const uint64_t* h_crc_capacity, void* d_ws, uint64_t ws_nbytes,
                           hipStream_t stream, const hipEvent_t* h_events);
+
+/* XOR delta of d_src against d_base ("NOTE-241: ZipNN", "Method" item 6;
+ * format above, DELTAS): both nbytes bytes of `dtype`, aligned to the
+ * element size.  flags: 0 or LTC_FLAG_SHARED_TABLES.  Capacity, workspace
+ * (ltc_compress_workspace_size) and errors as ltc_compress, plus
+ * INVALID_ARGUMENT for a NULL or misaligned base. */
+int ltc_compress_delta(const void* d_src, const void* d_base, uint64_t nbytes, int dtype,
+                       uint32_t chunk_bytes, double passthrough_threshold, uint32_t flags, void* d_blob,
+                       uint64_t blob_capacity, uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
+                       hipStream_t stream);
+
+/* Device workspace for decoding these delta blobs: the sum over blobs of
+ * K * floor(C / E) * E bytes (each stream gets a slot its ZRUN payload is
+ * expanded into before the decode kernel reads it as a RAW stream). */
+int ltc_decompress_delta_workspace_size(int count, const void* const* h_headers, uint64_t* ws_nbytes);
+
+/* Decode delta blobs: output = decoded delta XOR base.  h_base_ptrs[i] is a
+ * device pointer to blob i's base (N bytes, aligned to the element size);
+ * d_ws/ws_nbytes at least ltc_decompress_delta_workspace_size().  Every ZRUN
+ * payload is checked (counts, block bitmap and masks agree, no zero
+ * literal, exact size) before use.  Status and errors as
+ * ltc_decompress_batch, plus INVALID_ARGUMENT for a plain blob, a NULL or
+ * misaligned base, and WORKSPACE. */
+int ltc_decompress_delta_batch(int count, const void* const* h_headers, const void* const* h_blob_ptrs,
+                               const uint64_t* h_blob_nbytes, const void* const* h_base_ptrs,
+                               void* const* h_dst_ptrs, const uint64_t* h_dst_capacity,
+                               int32_t* d_status, void* d_ws, uint64_t ws_nbytes, hipStream_t stream);
+int ltc_decompress_delta(const void* h_header, const void* d_blob, uint64_t blob_nbytes,
+                         const void* d_base, void* d_dst, uint64_t dst_capacity, int32_t* d_status,
+                         void* d_ws, uint64_t ws_nbytes, hipStream_t stream);
 
 /* Compress and checksum the blob in one call (cuZipNN 0.1.0 "API",
  * compress_tensor_with_crc32): the same blob as ltc_compress, and in d_crc
@@ -300,7 +357,7 @@ typedef struct {
   uint32_t elem_bytes;
   uint64_t nbytes;
   uint64_t blob_nbytes;
-  uint64_t mode_count[4][3];     /* [stream index k][mode] */
+  uint64_t mode_count[4][4];     /* [stream index k][mode]; mode 3 only in deltas */
   uint64_t payload_bytes[4];     /* sum of payload sizes per stream index */
   uint64_t stream_bytes[4];      /* sum of raw stream sizes per stream index */
 } ltc_stats;

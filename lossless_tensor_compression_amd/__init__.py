@@ -15,6 +15,8 @@ API (names as in cuZipNN 0.1.0, "API", and the C ABI):
   compress_to_host(t) -> pinned CPU blob; decompress_from_host(cpu_blob) ->
       GPU tensor (copies of chunk groups overlapped with their decoding)
   compress_batch / decompress_batch for many tensors in one launch sequence
+  compress_delta(t, base) / decompress_delta(blob, base): XOR deltas against
+      a base tensor, zero-run coded where the delta is mostly zero bytes
   blob_info / blob_stats for host-side inspection of a blob's header
 """
 import ctypes
@@ -46,13 +48,14 @@ class Info(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("elem_bytes", ctypes.c_uint32),
                 ("nbytes", ctypes.c_uint64), ("chunk_bytes", ctypes.c_uint32),
                 ("nchunks", ctypes.c_uint32), ("blob_nbytes", ctypes.c_uint64),
-                ("payload_base", ctypes.c_uint64), ("version", ctypes.c_uint32)]
+                ("payload_base", ctypes.c_uint64), ("version", ctypes.c_uint32),
+                ("flags", ctypes.c_uint32)]
 
 
 class Stats(ctypes.Structure):
     _fields_ = [("elem_bytes", ctypes.c_uint32), ("nbytes", ctypes.c_uint64),
                 ("blob_nbytes", ctypes.c_uint64),
-                ("mode_count", (ctypes.c_uint64 * 3) * 4),
+                ("mode_count", (ctypes.c_uint64 * 4) * 4),
                 ("payload_bytes", ctypes.c_uint64 * 4),
                 ("stream_bytes", ctypes.c_uint64 * 4)]
 
@@ -87,8 +90,12 @@ def lib():
                                               vp, u64, vp]
         L.ltc_compress_bound_ex.argtypes = [u64, i32, u32, u32]
         L.ltc_compress_bound_ex.restype = u64
-        L.ltc_compress_batch_ex.argtypes = [i32, pvp, pu64, i32, u32, dbl, u32, pvp, pu64, vp, u32,
-                                            pvp, pu64, vp, u64, vp, pvp]
+        L.ltc_compress_batch_ex.argtypes = [i32, pvp, pu64, i32, u32, dbl, u32, pvp, pvp, pu64, vp,
+                                            u32, pvp, pu64, vp, u64, vp, pvp]
+        L.ltc_compress_delta.argtypes = [vp, vp, u64, i32, u32, dbl, u32, vp, u64, vp, vp, u64, vp]
+        L.ltc_decompress_delta_workspace_size.argtypes = [i32, pvp, pu64]
+        L.ltc_decompress_delta_batch.argtypes = [i32, pvp, pvp, pu64, pvp, pvp, pu64, vp, vp, u64, vp]
+        L.ltc_decompress_delta.argtypes = [ctypes.c_char_p, vp, u64, vp, vp, u64, vp, vp, u64, vp]
         L.ltc_compress_batch_with_crc32.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp,
                                                     u32, pvp, pu64, vp, u64, vp]
         L.ltc_compress_batch_with_crc32_prof.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64,
@@ -109,7 +116,8 @@ def lib():
                      "ltc_blob_info", "ltc_decompress", "ltc_decompress_batch",
                      "ltc_decompress_batch_prof", "ltc_decompress_from_host",
                      "ltc_decompress_batch_from_host", "ltc_crc32_chunks", "ltc_crc32_chunks_batch",
-                     "ltc_blob_stats"):
+                     "ltc_blob_stats", "ltc_compress_delta", "ltc_decompress_delta_workspace_size",
+                     "ltc_decompress_delta_batch", "ltc_decompress_delta"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -142,6 +150,7 @@ def _flat_bytes(t):
 
 
 FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
+FLAG_DELTA = 2          # header flag: the blob codes src XOR base
 
 
 def compress_bound(nbytes, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES, shared_tables=False):
@@ -171,15 +180,17 @@ def compress_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blob_ptrs
 
 def compress_ex_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, flags, blob_ptrs, caps,
                     nbytes_out_ptr, ws_ptr, ws_nbytes, crc_chunk_bytes=0, crc_ptrs=None,
-                    crc_caps=None, stream=None, events=None):
+                    crc_caps=None, stream=None, events=None, base_ptrs=None):
     """Pointer-level ltc_compress_batch_ex: format flags, optional checksums
-    (crc_chunk_bytes > 0) and optional events (5, or 6 with checksums)."""
+    (crc_chunk_bytes > 0), optional events (5, or 6 with checksums) and
+    optional delta bases (XOR deltas)."""
     count = len(src_ptrs)
     crc_ptrs = crc_ptrs or [0] * count
     crc_caps = crc_caps or [0] * count
     ev = _ptrs(events) if events is not None else None
+    bases = _ptrs(base_ptrs) if base_ptrs is not None else None
     _check(lib().ltc_compress_batch_ex(count, _ptrs(src_ptrs), _u64s(nbytes), dtype_code, chunk_bytes,
-                                       threshold, flags, _ptrs(blob_ptrs), _u64s(caps),
+                                       threshold, flags, bases, _ptrs(blob_ptrs), _u64s(caps),
                                        ctypes.c_void_p(nbytes_out_ptr), crc_chunk_bytes, _ptrs(crc_ptrs),
                                        _u64s(crc_caps), ctypes.c_void_p(ws_ptr), ws_nbytes,
                                        _stream(stream), ev), "compress")
@@ -217,12 +228,38 @@ def compress_batch(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
                    passthrough_threshold=DEFAULT_THRESHOLD, shared_tables=False):
     """Blobs (uint8 GPU tensors) for up to 32 tensors of one dtype;
     shared_tables: format v2 (one frequency table per stream index)."""
+    return _compress_batch(tensors, None, chunk_bytes, passthrough_threshold, shared_tables)
+
+
+def compress_batch_delta(tensors, bases, chunk_bytes=DEFAULT_CHUNK_BYTES,
+                         passthrough_threshold=DEFAULT_THRESHOLD, shared_tables=False):
+    """XOR-delta blobs of up to 32 tensors against their bases (same dtype
+    and size each): ZipNN's delta compression of a fine-tuned model against
+    its base model."""
+    if len(bases) != len(tensors):
+        raise ValueError("one base per tensor")
+    return _compress_batch(tensors, bases, chunk_bytes, passthrough_threshold, shared_tables)
+
+
+def compress_delta(t, base, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
+                   shared_tables=False):
+    """XOR-delta blob of a GPU tensor against a base of the same dtype and size."""
+    return compress_batch_delta([t], [base], chunk_bytes, passthrough_threshold, shared_tables)[0]
+
+
+def _compress_batch(tensors, bases, chunk_bytes, passthrough_threshold, shared_tables):
     if not 1 <= len(tensors) <= BATCH_MAX:
         raise ValueError(f"1..{BATCH_MAX} tensors per batch")
     ts = [_flat_bytes(t) for t in tensors]
     code = DTYPE_CODE[ts[0].dtype]
     if any(DTYPE_CODE[t.dtype] != code for t in ts):
         raise ValueError("one dtype per batch")
+    bs = None
+    if bases is not None:
+        bs = [_flat_bytes(b) for b in bases]
+        if any(b.dtype != t.dtype or b.numel() != t.numel() or b.device != t.device
+               for b, t in zip(bs, ts)):
+            raise ValueError("a base must match its tensor's dtype, size and device")
     dev = ts[0].device
     nbytes = [t.numel() * t.element_size() for t in ts]
     caps = [compress_bound(n, code, chunk_bytes, shared_tables) for n in nbytes]
@@ -234,7 +271,8 @@ def compress_batch(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
     sizes = torch.zeros(len(ts), dtype=torch.int64, device=dev)
     compress_ex_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
                     FLAG_SHARED_TABLES if shared_tables else 0, [b.data_ptr() for b in blobs], caps,
-                    sizes.data_ptr(), ws.data_ptr(), ws.numel())
+                    sizes.data_ptr(), ws.data_ptr(), ws.numel(),
+                    base_ptrs=[b.data_ptr() for b in bs] if bs is not None else None)
     host_sizes = sizes.cpu().tolist()
     return [b[:s] for b, s in zip(blobs, host_sizes)]
 
@@ -327,6 +365,62 @@ def decompress_batch(blobs, shapes=None, check=True):
 
 def decompress(blob, shape=None):
     return decompress_batch([blob], [shape])[0]
+
+
+def delta_workspace_size(headers):
+    """Device workspace bytes for decoding these delta blobs (host headers)."""
+    hdr = (ctypes.c_void_p * len(headers))(*[ctypes.cast(ctypes.c_char_p(h), ctypes.c_void_p)
+                                             for h in headers])
+    out = ctypes.c_uint64(0)
+    _check(lib().ltc_decompress_delta_workspace_size(len(headers), hdr, ctypes.byref(out)),
+           "delta workspace size")
+    return out.value
+
+
+def decompress_delta_raw(headers, blob_ptrs, blob_nbytes, base_ptrs, dst_ptrs, caps, status_ptr,
+                         ws_ptr, ws_nbytes, stream=None):
+    """Pointer-level batch decode of delta blobs on `stream`."""
+    count = len(blob_ptrs)
+    hdr = (ctypes.c_void_p * count)(*[ctypes.cast(ctypes.c_char_p(h), ctypes.c_void_p) for h in headers])
+    _check(lib().ltc_decompress_delta_batch(count, hdr, _ptrs(blob_ptrs), _u64s(blob_nbytes),
+                                            _ptrs(base_ptrs), _ptrs(dst_ptrs), _u64s(caps),
+                                            ctypes.c_void_p(status_ptr), ctypes.c_void_p(ws_ptr),
+                                            ws_nbytes, _stream(stream)), "decompress_delta")
+
+
+def decompress_batch_delta(blobs, bases, shapes=None, check=True):
+    """Tensors rebuilt from delta blobs and their bases (GPU tensors)."""
+    if not 1 <= len(blobs) <= BATCH_MAX or len(bases) != len(blobs):
+        raise ValueError(f"1..{BATCH_MAX} blobs per batch, one base each")
+    headers = [_header_bytes(b) for b in blobs]
+    infos = [blob_info(h) for h in headers]
+    dev = blobs[0].device
+    bs = [b.contiguous() for b in bases]
+    for b, i in zip(bs, infos):
+        if not b.is_cuda or b.numel() * b.element_size() != i["nbytes"]:
+            raise ValueError("a base must be a GPU tensor of the blob's decoded size")
+    outs = [torch.empty(i["nbytes"], dtype=torch.uint8, device=dev) for i in infos]
+    ws_n = delta_workspace_size(headers)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+    status = torch.full((len(blobs),), -99, dtype=torch.int32, device=dev)
+    decompress_delta_raw(headers, [b.data_ptr() for b in blobs], [b.numel() for b in blobs],
+                         [b.data_ptr() for b in bs], [o.data_ptr() for o in outs],
+                         [o.numel() for o in outs], status.data_ptr(), ws.data_ptr(), ws.numel())
+    if check:
+        for s in status.cpu().tolist():
+            _check(s, "decompress_delta (device status)")
+    res = []
+    for k, (o, i) in enumerate(zip(outs, infos)):
+        t = o.view(CODE_DTYPE[i["dtype"]])
+        if shapes is not None and shapes[k] is not None:
+            t = t.view(shapes[k])
+        res.append(t)
+    return res
+
+
+def decompress_delta(blob, base, shape=None):
+    """The tensor a delta blob codes, given its base."""
+    return decompress_batch_delta([blob], [base], [shape])[0]
 
 
 def decompress_from_host_raw(h_blob_ptrs, blob_nbytes, dst_ptrs, caps, status_ptr, stage_ptrs,
@@ -428,7 +522,7 @@ def blob_stats(blob):
         "nbytes": st.nbytes, "blob_nbytes": st.blob_nbytes,
         "ratio": st.blob_nbytes / st.nbytes if st.nbytes else 0.0,
         "modes": [{"raw": st.mode_count[k][0], "rans": st.mode_count[k][1],
-                   "const": st.mode_count[k][2]} for k in range(e)],
+                   "const": st.mode_count[k][2], "zrun": st.mode_count[k][3]} for k in range(e)],
         "group_percent": [100.0 * st.payload_bytes[k] / st.stream_bytes[k]
                           if st.stream_bytes[k] else 0.0 for k in range(e)],
     }

@@ -185,7 +185,7 @@ uint32_t words_capacity(uint32_t chunk_bytes, uint32_t e) {
 }
 
 struct Layout {
-  uint64_t sinfo, freq, hist, plane, ptab, pbase, states, offsets, blobn, frames, words, total;
+  uint64_t sinfo, freq, hist, plane, ptab, pbase, zinfo, states, offsets, blobn, frames, words, total;
 };
 
 // frames: one u32 per KiB of every blob's bound (compress_with_crc32);
@@ -199,6 +199,7 @@ Layout layout(uint64_t streams, int count, uint32_t wcap, uint64_t frames, uint3
   l.plane = cur;   cur = round_up(cur + 2048ull * e * (uint64_t)count, kAlign);
   l.ptab = cur;    cur = round_up(cur + 512ull * e * (uint64_t)count, kAlign);
   l.pbase = cur;   cur = round_up(cur + 8 * (uint64_t)count, kAlign);
+  l.zinfo = cur;   cur = round_up(cur + 8 * streams, kAlign);
   l.states = cur;  cur = round_up(cur + 256 * streams, kAlign);
   l.offsets = cur; cur = round_up(cur + 8 * streams, kAlign);
   l.blobn = cur;   cur = round_up(cur + 8 * (uint64_t)count, kAlign);
@@ -250,7 +251,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
                   uint32_t chunk_bytes, double theta, void* const* blobs, const uint64_t* caps,
                   uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes, hipStream_t stream,
                   const hipEvent_t* ev, const CrcReq& crc = CrcReq{0, nullptr, nullptr},
-                  uint32_t flags = 0) {
+                  uint32_t flags = 0, const void* const* bases = nullptr) {
   if (count < 1 || count > kMaxJobs || !srcs || !nbytes || !blobs || !caps || !d_blob_nbytes)
     return LTC_ERR_INVALID_ARGUMENT;
   if (flags & ~LTC_FLAG_SHARED_TABLES) return LTC_ERR_INVALID_ARGUMENT;
@@ -263,6 +264,8 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
     if (reinterpret_cast<uintptr_t>(srcs[i]) % e) return LTC_ERR_INVALID_ARGUMENT;
     if (reinterpret_cast<uintptr_t>(blobs[i]) % 16) return LTC_ERR_INVALID_ARGUMENT;
     if (caps[i] < bound_flags(nbytes[i], e, chunk_bytes, flags)) return LTC_ERR_CAPACITY;
+    if (bases && nbytes[i] && (!bases[i] || reinterpret_cast<uintptr_t>(bases[i]) % e))
+      return LTC_ERR_INVALID_ARGUMENT;
   }
   if (crc.chunk_bytes) {
     if (!crc.outs || !crc.caps) return LTC_ERR_INVALID_ARGUMENT;
@@ -288,11 +291,13 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   t.wcap = wcap;
   t.dtype = (uint32_t)dtype;
   t.v2 = (flags & LTC_FLAG_SHARED_TABLES) ? 1u : 0u;
+  t.delta = bases ? 1u : 0u;
   bool vec = chunk_bytes % 16 == 0;
   uint64_t chunk0 = 0;
   for (int i = 0; i < count; ++i) {
     CJob& jb = t.jobs[i];
     jb.src = static_cast<const uint8_t*>(srcs[i]);
+    jb.base = bases ? static_cast<const uint8_t*>(bases[i]) : nullptr;
     jb.blob = static_cast<uint8_t*>(blobs[i]);
     jb.blob_nbytes_out = d_blob_nbytes + i;
     jb.nbytes = nbytes[i];
@@ -304,6 +309,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
     jb.pmax_tail = p_max(jb.n_tail, theta);
     chunk0 += jb.nchunks;
     if (nbytes[i] && reinterpret_cast<uintptr_t>(srcs[i]) % 16) vec = false;
+    if (bases && nbytes[i] && reinterpret_cast<uintptr_t>(bases[i]) % 16) vec = false;
   }
   t.total_chunks = chunk0;
   t.vec16 = vec ? 1u : 0u;
@@ -315,6 +321,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   w.plane = reinterpret_cast<uint64_t*>(ws + l.plane);
   w.ptab = reinterpret_cast<uint16_t*>(ws + l.ptab);
   w.pbase = reinterpret_cast<uint64_t*>(ws + l.pbase);
+  w.zinfo = reinterpret_cast<uint2*>(ws + l.zinfo);
   w.states = reinterpret_cast<uint32_t*>(ws + l.states);
   w.offsets = reinterpret_cast<uint64_t*>(ws + l.offsets);
   w.blob_nbytes = reinterpret_cast<uint64_t*>(ws + l.blobn);
@@ -326,7 +333,8 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   // it and k_crc_frames chains them per chunk; otherwise k_crc32 reads the
   // finished blobs back.
   const uint64_t K = crc.chunk_bytes;
-  const bool fused = crc_frames_usable(K);
+  // deltas write ZRUN payloads byte by byte: their blobs are read back
+  const bool fused = crc_frames_usable(K) && !bases;
   uint32_t* frames = reinterpret_cast<uint32_t*>(ws + l.frames);
   CrcArgs a;
   memset(&a, 0, sizeof(a));
@@ -363,6 +371,8 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   if (ev) record(ev, 5, stream);
   return err == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 }
+
+uint32_t rd_flags(const void* header) { return static_cast<const uint8_t*>(header)[27]; }
 
 uint64_t rd64(const uint8_t* p) {
   uint64_t v;
@@ -431,10 +441,13 @@ hipError_t decode_from_host(int dtype, const DTable& t, uint32_t e, const void* 
 
 // host_blobs (optional): the whole blobs in host memory; blobs are then the
 // device staging buffers they are copied into (stage_caps bytes each)
+// bases (optional): the delta bases; every blob must then be a delta blob,
+// and d_ws holds the expanded ZRUN streams (ltc_decompress_workspace_size)
 int decompress_impl(int count, const void* const* headers, const void* const* blobs,
                     const uint64_t* blob_nbytes, void* const* dsts, const uint64_t* caps,
                     int32_t* d_status, hipStream_t stream, const hipEvent_t* ev,
-                    const void* const* host_blobs = nullptr, const uint64_t* stage_caps = nullptr) {
+                    const void* const* host_blobs = nullptr, const uint64_t* stage_caps = nullptr,
+                    const void* const* bases = nullptr, void* d_ws = nullptr, uint64_t ws_nbytes = 0) {
   if (count < 1 || count > kMaxJobs || !headers || !blobs || !blob_nbytes || !dsts || !caps || !d_status)
     return LTC_ERR_INVALID_ARGUMENT;
   if (host_blobs && !stage_caps) return LTC_ERR_INVALID_ARGUMENT;
@@ -461,7 +474,14 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
     if (!blobs[i] || (info.nbytes && !dsts[i])) return LTC_ERR_INVALID_ARGUMENT;
     if (reinterpret_cast<uintptr_t>(blobs[i]) % 16) return LTC_ERR_INVALID_ARGUMENT;
     if (host_blobs && stage_caps[i] < info.blob_nbytes) return LTC_ERR_CAPACITY;
+    // a delta blob needs its base, and a base needs a delta blob
+    const bool delta = (rd_flags(headers[i]) & LTC_FLAG_DELTA) != 0;
+    if (delta != (bases != nullptr)) return LTC_ERR_INVALID_ARGUMENT;
+    if (delta && info.nbytes && (!bases[i] || reinterpret_cast<uintptr_t>(bases[i]) % e))
+      return LTC_ERR_INVALID_ARGUMENT;
     DJob& jb = t.jobs[i];
+    jb.base = delta ? static_cast<const uint8_t*>(bases[i]) : nullptr;
+    if (delta && info.nbytes && reinterpret_cast<uintptr_t>(bases[i]) % 16) vec = false;
     jb.blob = static_cast<const uint8_t*>(blobs[i]);
     jb.dst = static_cast<uint8_t*>(dsts[i]);
     jb.status = d_status + i;
@@ -481,6 +501,13 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
   t.n_full = chunk_bytes / e;
   t.vec16 = (vec && chunk_bytes % 16 == 0) ? 1u : 0u;
   t.total_chunks = chunk0;
+  if (bases) {
+    if (host_blobs) return LTC_ERR_INVALID_ARGUMENT;  // deltas are decoded from device blobs
+    const uint64_t need = chunk0 * e * (uint64_t)t.n_full;
+    if (need && (!d_ws || ws_nbytes < need)) return LTC_ERR_WORKSPACE;
+    t.delta = 1;
+    t.zbuf = static_cast<uint8_t*>(d_ws);
+  }
   if (!host_blobs) return launch_decompress(dtype, t, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
   return decode_from_host(dtype, t, e, host_blobs, stream) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 }
@@ -506,7 +533,7 @@ uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
 
 int ltc_compress_batch_ex(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
                           int dtype, uint32_t chunk_bytes, double passthrough_threshold,
-                          uint32_t flags, void* const* h_blob_ptrs,
+                          uint32_t flags, const void* const* h_base_ptrs, void* const* h_blob_ptrs,
                           const uint64_t* h_blob_capacity, uint64_t* d_blob_nbytes,
                           uint32_t checksum_chunk_bytes, uint32_t* const* h_crc_ptrs,
                           const uint64_t* h_crc_capacity, void* d_ws, uint64_t ws_nbytes,
@@ -514,7 +541,17 @@ int ltc_compress_batch_ex(int count, const void* const* h_src_ptrs, const uint64
   const CrcReq crc{checksum_chunk_bytes, h_crc_ptrs, h_crc_capacity};
   return compress_impl(count, h_src_ptrs, h_nbytes, dtype, chunk_bytes, passthrough_threshold,
                        h_blob_ptrs, h_blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, h_events,
-                       crc, flags);
+                       crc, flags, h_base_ptrs);
+}
+
+int ltc_compress_delta(const void* d_src, const void* d_base, uint64_t nbytes, int dtype,
+                       uint32_t chunk_bytes, double passthrough_threshold, uint32_t flags, void* d_blob,
+                       uint64_t blob_capacity, uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
+                       hipStream_t stream) {
+  if (!d_base) return LTC_ERR_INVALID_ARGUMENT;
+  return ltc_compress_batch_ex(1, &d_src, &nbytes, dtype, chunk_bytes, passthrough_threshold, flags,
+                               &d_base, &d_blob, &blob_capacity, d_blob_nbytes, 0, nullptr, nullptr,
+                               d_ws, ws_nbytes, stream, nullptr);
 }
 
 int ltc_compress_workspace_size(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
@@ -614,8 +651,8 @@ int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {
   const uint64_t nbytes = rd64(h + 8);
   const uint32_t chunk_bytes = rd32(h + 16);
   const uint64_t k = rd32(h + 20);
-  if (rd16(h + 24) != kLanes || h[26] != 12 || h[27] != (version == 2 ? LTC_FLAG_SHARED_TABLES : 0u) ||
-      rd32(h + 28) != 0)
+  if (rd16(h + 24) != kLanes || h[26] != 12 ||
+      (h[27] & ~LTC_FLAG_DELTA) != (version == 2 ? LTC_FLAG_SHARED_TABLES : 0u) || rd32(h + 28) != 0)
     return LTC_ERR_CORRUPT;
   for (int i = 48; i < 64; ++i)
     if (h[i]) return LTC_ERR_CORRUPT;
@@ -638,6 +675,7 @@ int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {
   out->blob_nbytes = blob_nbytes;
   out->payload_base = base;
   out->version = version;
+  out->flags = h[27];
   return LTC_OK;
 }
 
@@ -652,6 +690,35 @@ int ltc_decompress_batch(int count, const void* const* h_headers, const void* co
                          const uint64_t* h_dst_capacity, int32_t* d_status, hipStream_t stream) {
   return decompress_impl(count, h_headers, h_blob_ptrs, h_blob_nbytes, h_dst_ptrs, h_dst_capacity,
                          d_status, stream, nullptr);
+}
+
+int ltc_decompress_delta_workspace_size(int count, const void* const* h_headers, uint64_t* ws_nbytes) {
+  if (count < 1 || count > kMaxJobs || !h_headers || !ws_nbytes) return LTC_ERR_INVALID_ARGUMENT;
+  uint64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    ltc_info info;
+    const int rc = ltc_blob_info(h_headers[i], kHeader, &info);
+    if (rc) return rc;
+    total += (uint64_t)info.nchunks * (info.chunk_bytes / info.elem_bytes) * info.elem_bytes;
+  }
+  *ws_nbytes = total;
+  return LTC_OK;
+}
+
+int ltc_decompress_delta_batch(int count, const void* const* h_headers, const void* const* h_blob_ptrs,
+                               const uint64_t* h_blob_nbytes, const void* const* h_base_ptrs,
+                               void* const* h_dst_ptrs, const uint64_t* h_dst_capacity,
+                               int32_t* d_status, void* d_ws, uint64_t ws_nbytes, hipStream_t stream) {
+  if (!h_base_ptrs) return LTC_ERR_INVALID_ARGUMENT;
+  return decompress_impl(count, h_headers, h_blob_ptrs, h_blob_nbytes, h_dst_ptrs, h_dst_capacity,
+                         d_status, stream, nullptr, nullptr, nullptr, h_base_ptrs, d_ws, ws_nbytes);
+}
+
+int ltc_decompress_delta(const void* h_header, const void* d_blob, uint64_t blob_nbytes,
+                         const void* d_base, void* d_dst, uint64_t dst_capacity, int32_t* d_status,
+                         void* d_ws, uint64_t ws_nbytes, hipStream_t stream) {
+  return ltc_decompress_delta_batch(1, &h_header, &d_blob, &blob_nbytes, &d_base, &d_dst, &dst_capacity,
+                                    d_status, d_ws, ws_nbytes, stream);
 }
 
 int ltc_decompress_batch_prof(int count, const void* const* h_headers, const void* const* h_blob_ptrs,
@@ -734,7 +801,8 @@ int ltc_blob_stats(const void* h_prefix, uint64_t h_nbytes, ltc_stats* out) {
     for (uint32_t k = 0; k < e; ++k) {
       const uint8_t* ent = d + kDirEntry * (c * e + k);
       const uint32_t mode = ent[12];
-      if (mode > 2) return LTC_ERR_CORRUPT;
+      if (mode > ((static_cast<const uint8_t*>(h_prefix)[27] & LTC_FLAG_DELTA) ? 3u : 2u))
+        return LTC_ERR_CORRUPT;
       out->mode_count[k][mode] += 1;
       out->payload_bytes[k] += rd32(ent + 8);
       out->stream_bytes[k] += len / e;

@@ -46,11 +46,40 @@ __device__ __forceinline__ uint32_t pack_info(uint32_t mode, uint32_t cval, uint
   return mode | (cval << 8) | (lo << 16) | (hi << 24);
 }
 
+// ZRUN payload bytes: 16-byte head, the block bitmap padded to 16, a u64 per
+// nonzero 64-byte block padded to 16, the nonzero bytes
+__device__ __forceinline__ uint32_t zrun_bytes(uint32_t n, uint32_t nblk, uint32_t nnz) {
+  const uint32_t nb = (n + 63) / 64;
+  return 16u + (uint32_t)align16((nb + 7) / 8) + (uint32_t)align16(8ull * nblk) + nnz;
+}
+
 template <int DT> __device__ __forceinline__ uint32_t load_elem(const uint8_t* p) {
   constexpr int E = Dt<DT>::E;
   if constexpr (E == 1) return *p;
   else if constexpr (E == 2) return *reinterpret_cast<const uint16_t*>(p);
   else return *reinterpret_cast<const uint32_t*>(p);
+}
+
+// Deltas ("NOTE-241: ZipNN", Method item 6): the coded element is src XOR
+// base, taken at every load so the XOR never touches HBM by itself.
+template <int DT, bool DELTA>
+__device__ __forceinline__ uint32_t load_x(const uint8_t* src, const uint8_t* base, uint64_t off) {
+  uint32_t v = load_elem<DT>(src + off);
+  if constexpr (DELTA) v ^= load_elem<DT>(base + off);
+  return v;
+}
+
+template <bool DELTA>
+__device__ __forceinline__ uint4 load_x16(const uint8_t* src, const uint8_t* base, uint64_t off) {
+  uint4 v = *reinterpret_cast<const uint4*>(src + off);
+  if constexpr (DELTA) {
+    const uint4 b = *reinterpret_cast<const uint4*>(base + off);
+    v.x ^= b.x;
+    v.y ^= b.y;
+    v.z ^= b.z;
+    v.w ^= b.w;
+  }
+  return v;
 }
 
 // ------------------------------------------------------------------ k_hist
@@ -210,7 +239,7 @@ __device__ void normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, u
         make_uint4(raw ? n : 0u, pack_info(raw ? LTC_MODE_RAW : kModeCand, 0, lo, hi), 0, 0);
 }
 
-template <int DT>
+template <int DT, bool DELTA>
 __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
   constexpr uint32_t kWords = E * 128 * kHistCopies;
@@ -223,6 +252,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   const bool last = c + 1 == job.nchunks;
   const uint32_t n = last ? job.n_tail : t.n_full;
   const uint8_t* chunk = job.src + c * t.chunk_bytes;
+  const uint8_t* bchunk = DELTA ? job.base + c * t.chunk_bytes : nullptr;
   const uint32_t tid = threadIdx.x;
   const uint32_t copy = tid & (kHistCopies - 1);
 
@@ -231,18 +261,19 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
     const uint32_t sn = n - seg < kHistSeg ? n - seg : kHistSeg;
     const uint32_t len = sn * E;
     const uint8_t* src = chunk + (uint64_t)seg * E;
+    const uint8_t* bsrc = DELTA ? bchunk + (uint64_t)seg * E : nullptr;
     for (uint32_t i = tid; i < kWords; i += kHistThreads) hs[i] = 0;
     __syncthreads();
     uint32_t done = 0;
     if (t.vec16 && len >= 32) {
       const uint32_t nvec = len / 16, lastv = nvec - 1;
-      const uint4* v = reinterpret_cast<const uint4*>(src);
+      auto v = [&](uint32_t i) { return load_x16<DELTA>(src, bsrc, 16ull * i); };
       // two 16-byte loads in flight ahead of the two being counted; indices
       // are clamped instead of branched so the waits land at the uses
-      uint4 q0 = v[min(tid, lastv)], q1 = v[min(tid + kHistThreads, lastv)];
+      uint4 q0 = v(min(tid, lastv)), q1 = v(min(tid + kHistThreads, lastv));
       for (uint32_t i = tid; i < nvec; i += 2 * kHistThreads) {
-        const uint4 n0 = v[min(i + 2 * kHistThreads, lastv)];
-        const uint4 n1 = v[min(i + 3 * kHistThreads, lastv)];
+        const uint4 n0 = v(min(i + 2 * kHistThreads, lastv));
+        const uint4 n1 = v(min(i + 3 * kHistThreads, lastv));
         hist_vec<DT>(hs, q0, copy);
         if (i + kHistThreads < nvec) hist_vec<DT>(hs, q1, copy);
         q0 = n0;
@@ -251,7 +282,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
       done = nvec * 16;
     }
     for (uint32_t e = done / E + tid; e < sn; e += kHistThreads)
-      hist_elem<DT>(hs, reorder<DT>(load_elem<DT>(src + (uint64_t)e * E)), copy);
+      hist_elem<DT>(hs, reorder<DT>(load_x<DT, DELTA>(src, bsrc, (uint64_t)e * E)), copy);
     __syncthreads();
     // fold the 32 copies; the copy index rotates with the thread so the 32
     // reads of a half-wave hit 32 different banks
@@ -408,7 +439,7 @@ __device__ __forceinline__ uint32_t mul_u24(uint32_t a, uint32_t b) {
 // biased exponent field itself, one bit-field extract.
 template <int DT, bool TOP>
 __device__ __forceinline__ uint32_t stream_byte(uint32_t x, uint32_t k) {
-  if constexpr (TOP) return (x >> Dt<DT>::WM) & 0xFFu;
+  if constexpr (TOP && Dt<DT>::WM >= 0) return (x >> Dt<DT>::WM) & 0xFFu;
   else return (reorder<DT>(x) >> (8 * k)) & 0xFFu;
 }
 
@@ -437,7 +468,7 @@ __device__ __forceinline__ uint32_t stream_byte(uint32_t x, uint32_t k) {
 // Abort and drain checks run every 4 steps: 4 steps emit at most 256 words,
 // so a block is never overwritten before it drains, and an abort is seen
 // before any word past the stream's limit reaches the workspace.
-template <int DT>
+template <int DT, bool DELTA>
 __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
   constexpr int U = kEncStreams;
@@ -453,14 +484,18 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   uint64_t sid[U];
   uint32_t n[U], full[U], wlimit[U], wo[U], lo[U], hi[U];
   const uint8_t* src[U];
+  const uint8_t* bsrc[U];
   const uint16_t* ftab[U];
+  uint4 fallback[U];  // the stream's directory info if coding it does not pay
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     on[u] = false;
     sid[u] = 0;
     n[u] = full[u] = wlimit[u] = wo[u] = lo[u] = hi[u] = 0;
     src[u] = nullptr;
+    bsrc[u] = nullptr;
     ftab[u] = nullptr;
+    fallback[u] = make_uint4(0, 0, 0, 0);
     const uint64_t g = g0 + u;
     if (g >= t.c_end) continue;
     const uint64_t s = g * E + k;
@@ -479,7 +514,28 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     // v2: the plane's table and no table in the payload
     wo[u] = t.v2 ? kRansFixed : (uint32_t)align16(kRansFixed + 2u * (hi[u] - lo[u] + 1u));
     ftab[u] = t.v2 ? w.ptab + ((uint64_t)j * E + k) * 256 : w.freq + 256 * s;
-    wlimit[u] = ((last ? job.pmax_tail : job.pmax_full) - wo[u]) / 2;
+    const uint32_t pmax = last ? job.pmax_tail : job.pmax_full;
+    uint32_t limit = pmax;
+    fallback[u] = make_uint4(n[u], pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
+    if constexpr (DELTA) {
+      // a ZRUN candidate (the zero-run rule fired): RANS must also be no
+      // larger than it; otherwise ZRUN if within P_max, else RAW
+      const uint2 zi = w.zinfo[s];
+      if (zi.y >> 31) {
+        const uint32_t pz = zrun_bytes(n[u], zi.x, zi.y & 0x7FFFFFFFu);
+        if (pz <= pmax) {
+          limit = pz;
+          fallback[u] = make_uint4(pz, pack_info(LTC_MODE_ZRUN, 0, 0, 0), zi.x, zi.y & 0x7FFFFFFFu);
+        }
+      }
+      if (limit < wo[u]) {  // no RANS payload fits
+        on[u] = false;
+        if (lane == 0) *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = fallback[u];
+        continue;
+      }
+      bsrc[u] = job.base + c * t.chunk_bytes;
+    }
+    wlimit[u] = (limit - wo[u]) / 2;
     src[u] = job.src + c * t.chunk_bytes;
   }
   if (!on[0] && !on[1]) return;
@@ -534,9 +590,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   auto check = [&](int u) {
     if (top[u] < atop[u]) {
       on[u] = false;
-      if (lane == 0)
-        *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =
-            make_uint4(n[u], pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
+      if (lane == 0) *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) = fallback[u];
     } else if (top[u] <= ftop[u]) {
       flush(u);
       ftop[u] = uniform(ftop[u] - kFlushWords);
@@ -565,7 +619,8 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     constexpr bool TOP = decltype(topexp)::value;
     auto sym_at = [&](int u, uint32_t step) -> uint32_t {  // direct load, index clamped
       const uint32_t e = 64 * step + lane;
-      return stream_byte<DT, TOP>(load_elem<DT>(src[u] + (uint64_t)(e < n[u] ? e : n[u] - 1) * E), k);
+      return stream_byte<DT, TOP>(
+          load_x<DT, DELTA>(src[u], bsrc[u], (uint64_t)(e < n[u] ? e : n[u] - 1) * E), k);
     };
     // the partial step (the last one) is coded first
 #pragma unroll
@@ -587,14 +642,18 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     auto fetch = [&](int u, uint32_t bi) {  // block bi: elements 64*(full - 8(bi+1)) + 8 lane ...
       const uint32_t e0 = 64u * (full[u] - kEncBlock * (bi + 1)) + 8u * lane;
       if constexpr (E == 1) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src[u] + e0);
+        uint2 v = *reinterpret_cast<const uint2*>(src[u] + e0);
+        if constexpr (DELTA) {
+          const uint2 b = *reinterpret_cast<const uint2*>(bsrc[u] + e0);
+          v.x ^= b.x;
+          v.y ^= b.y;
+        }
         pf[u][0] = v.x;
         pf[u][1] = v.y;
       } else {
-        const uint4* p = reinterpret_cast<const uint4*>(src[u] + (uint64_t)e0 * E);
 #pragma unroll
         for (int h = 0; h < E / 2; ++h) {
-          const uint4 v = p[h];
+          const uint4 v = load_x16<DELTA>(src[u], bsrc[u], (uint64_t)e0 * E + 16 * h);
           pf[u][4 * h] = v.x;
           pf[u][4 * h + 1] = v.y;
           pf[u][4 * h + 2] = v.z;
@@ -809,7 +868,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
       v = make_uint4(0x4243544Cu /* "LTCB" */, (t.v2 ? 2u : 1u) | (t.dtype << 16) | (E << 24),
                      (uint32_t)job.nbytes, (uint32_t)(job.nbytes >> 32));
     else if (tid == 1)
-      v = make_uint4(t.chunk_bytes, job.nchunks, 64u | (12u << 16) | ((t.v2 ? 1u : 0u) << 24), 0u);
+      v = make_uint4(t.chunk_bytes, job.nchunks,
+                     64u | (12u << 16) | ((t.v2 ? LTC_FLAG_SHARED_TABLES : 0u) << 24) |
+                         ((t.delta ? LTC_FLAG_DELTA : 0u) << 24),
+                     0u);
     else if (tid == 2)
       v = make_uint4((uint32_t)running, (uint32_t)(running >> 32), (uint32_t)base,
                      (uint32_t)(base >> 32));
@@ -835,17 +897,17 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
 
 // ------------------------------------------------------------------ k_pack
 
-// 16 consecutive elements of a chunk starting at element e0 (zeros past n)
-template <int DT>
+// 16 consecutive (reordered) elements of a chunk starting at element e0
+// (zeros past n); deltas XOR the base in
+template <int DT, bool DELTA = false>
 __device__ __forceinline__ void load16(const uint8_t* src, uint32_t e0, uint32_t n, bool vec,
-                                       uint32_t y[16]) {
+                                       uint32_t y[16], const uint8_t* bsrc = nullptr) {
   constexpr int E = Dt<DT>::E;
   if (vec && e0 + 16 <= n) {
-    const uint4* p = reinterpret_cast<const uint4*>(src + (uint64_t)e0 * E);
     uint32_t wv[4 * E];
 #pragma unroll
     for (int q = 0; q < E; ++q) {
-      const uint4 v = p[q];
+      const uint4 v = load_x16<DELTA>(src, bsrc, (uint64_t)e0 * E + 16 * q);
       wv[4 * q] = v.x;
       wv[4 * q + 1] = v.y;
       wv[4 * q + 2] = v.z;
@@ -862,7 +924,157 @@ __device__ __forceinline__ void load16(const uint8_t* src, uint32_t e0, uint32_t
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      y[i] = e0 + i < n ? reorder<DT>(load_elem<DT>(src + (uint64_t)(e0 + i) * E)) : 0u;
+      y[i] = e0 + i < n ? reorder<DT>(load_x<DT, DELTA>(src, bsrc, (uint64_t)(e0 + i) * E)) : 0u;
+  }
+}
+
+// ---- deltas: the zero-run coder's statistics and payload
+
+// Zero-run statistics of a byte range: length, leading and trailing zero
+// runs, longest zero run, all zero.  Ranges in order combine associatively.
+struct ZRun {
+  uint32_t len, pre, suf, mx;
+};
+__device__ __forceinline__ ZRun zrun_join(ZRun a, ZRun b) {
+  ZRun r;
+  r.len = a.len + b.len;
+  r.pre = a.pre == a.len ? a.len + b.pre : a.pre;
+  r.suf = b.suf == b.len ? b.len + a.suf : b.suf;
+  r.mx = max(max(a.mx, b.mx), a.suf + b.pre);
+  return r;
+}
+
+// One wave per stream of a delta batch that is not CONST: zero bytes,
+// nonzero 64-byte blocks and the longest zero run.  ZipNN's rule ("NOTE-241",
+// Deltas: more than 90% zero bytes, or a zero run over 3% of the group)
+// makes ZRUN a candidate; a stream the skip bound already made RAW becomes
+// ZRUN when that fits under P_max.
+template <int DT>
+__global__ __launch_bounds__(256) void k_zrun_stats(CTable t, CWork w) {
+  constexpr int E = Dt<DT>::E;
+  const uint64_t s = t.c_begin * E + (uint64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  if (s >= t.c_end * E) return;
+  const uint32_t mode = w.sinfo[4 * s + 1] & 0xFFu;
+  if (mode == LTC_MODE_CONST) return;
+  const uint64_t g = s / E;
+  const int k = (int)(s % E);
+  const int j = find_job(t, g);
+  const CJob& job = t.jobs[j];
+  const uint64_t c = g - job.chunk0;
+  const bool last = c + 1 == job.nchunks;
+  const uint32_t n = last ? job.n_tail : t.n_full;
+  const uint8_t* src = job.src + c * t.chunk_bytes;
+  const uint8_t* bsrc = job.base + c * t.chunk_bytes;
+  const uint32_t lane = lane_id();
+  const uint32_t nb = (n + 63) / 64, per = (nb + 63) / 64;
+  ZRun z{0, 0, 0, 0};
+  uint32_t zeros = 0, nzb = 0;
+  for (uint32_t b = lane * per; b < nb && b < (lane + 1) * per; ++b) {
+    bool any = false;
+    for (uint32_t q = 0; q < 4; ++q) {
+      uint32_t y[16];
+      load16<DT, true>(src, 64 * b + 16 * q, n, t.vec16 != 0, y, bsrc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (64 * b + 16 * q + i < n) {
+          const bool zb = ((y[i] >> (8 * k)) & 0xFFu) == 0;
+          zeros += zb;
+          any |= !zb;
+          z = zrun_join(z, ZRun{1u, zb ? 1u : 0u, zb ? 1u : 0u, zb ? 1u : 0u});
+        }
+      }
+    }
+    nzb += any;
+  }
+  // combine the lanes' ranges in lane order
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    ZRun r;
+    r.len = __shfl_down(z.len, o, 64);
+    r.pre = __shfl_down(z.pre, o, 64);
+    r.suf = __shfl_down(z.suf, o, 64);
+    r.mx = __shfl_down(z.mx, o, 64);
+    if ((lane & (2 * o - 1)) == 0 && lane + o < 64) z = zrun_join(z, r);
+  }
+  zeros = wave_sum_u32(zeros);
+  nzb = wave_sum_u32(nzb);
+  if (lane != 0) return;
+  const bool rule = 10ull * zeros > 9ull * n || 100ull * z.mx > 3ull * n;
+  const uint32_t nnz = n - zeros;
+  w.zinfo[s] = make_uint2(nzb, nnz | (rule ? 0x80000000u : 0u));
+  if (mode == LTC_MODE_RAW && rule) {
+    const uint32_t pz = zrun_bytes(n, nzb, nnz);
+    if (pz <= (last ? job.pmax_tail : job.pmax_full))
+      *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(pz, pack_info(LTC_MODE_ZRUN, 0, 0, 0), nzb, nnz);
+  }
+}
+
+// ZRUN payload of stream k of a chunk at dst (all threads of the workgroup;
+// every byte of the payload and of its gap to 16 is written): 16-byte head,
+// block bitmap (one ballot per 64 blocks), per nonzero block its byte mask at
+// its rank, and the nonzero bytes at their rank.
+template <int DT, bool DELTA>
+__device__ void write_zrun(uint8_t* dst, const uint8_t* src, const uint8_t* bsrc, uint32_t n, int k,
+                           uint32_t nblk, uint32_t nnz, uint32_t size, bool vec, uint32_t* red) {
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
+  const uint32_t nb = (n + 63) / 64;
+  const uint32_t l1 = 16, l2 = l1 + (uint32_t)align16((nb + 7) / 8);
+  const uint32_t lit = l2 + (uint32_t)align16(8ull * nblk);
+  if (tid == 0) *reinterpret_cast<uint4*>(dst) = make_uint4(nnz, nblk, 0, 0);
+  for (uint32_t i = l1 + 8 * ((nb + 63) / 64) + tid; i < l2; i += kPackThreads) dst[i] = 0;
+  for (uint32_t i = l2 + 8 * nblk + tid; i < lit; i += kPackThreads) dst[i] = 0;
+  for (uint32_t i = size + tid; i < align16(size); i += kPackThreads) dst[i] = 0;
+  uint32_t run_blk = 0, run_lit = 0;
+  for (uint32_t r0 = 0; r0 < nb; r0 += kPackThreads) {
+    const uint32_t b = r0 + tid;
+    uint64_t mask = 0;
+    uint32_t by[16];  // the block's 64 stream bytes, 4 per word
+#pragma unroll
+    for (int i = 0; i < 16; ++i) by[i] = 0;
+    if (b < nb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t y[16];
+        load16<DT, DELTA>(src, 64 * b + 16 * q, n, vec, y, bsrc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t v = (y[i] >> (8 * k)) & 0xFFu;
+          by[4 * q + i / 4] |= v << (8 * (i & 3));
+          if (v) mask |= 1ull << (16 * q + i);
+        }
+      }
+    }
+    const uint64_t bal = ballot(mask != 0);
+    if (lane == 0 && r0 + 64 * wave < nb)
+      *reinterpret_cast<uint64_t*>(dst + l1 + (r0 + 64 * wave) / 8) = bal;
+    const uint32_t pc = (uint32_t)__popcll(mask);
+    const uint32_t lit_below = wave_exclusive_scan_u32(pc);
+    if (lane == 63) {
+      red[wave] = (uint32_t)__popcll(bal);
+      red[4 + wave] = lit_below + pc;
+    }
+    __syncthreads();
+    uint32_t blk_before = run_blk, lit_before = run_lit, blk_round = 0, lit_round = 0;
+    for (uint32_t q = 0; q < kPackThreads / 64; ++q) {
+      if (q < wave) {
+        blk_before += red[q];
+        lit_before += red[4 + q];
+      }
+      blk_round += red[q];
+      lit_round += red[4 + q];
+    }
+    __syncthreads();
+    if (mask) {
+      const uint32_t rank = blk_before + lanes_below(bal);
+      if (rank < nblk) *reinterpret_cast<uint64_t*>(dst + l2 + 8 * rank) = mask;
+      uint32_t o = lit_before + lit_below;
+      for (int i = 0; i < 64; ++i) {
+        const uint32_t v = (by[i / 4] >> (8 * (i & 3))) & 0xFFu;
+        if (v && o < nnz) dst[lit + o++] = (uint8_t)v;
+      }
+    }
+    run_blk += blk_round;
+    run_lit += lit_round;
   }
 }
 
@@ -1009,9 +1221,9 @@ __device__ void write_rans(uint8_t* blob, uint64_t off, uint64_t s, uint32_t inf
   }
 }
 
-template <int DT, bool CRC>
+template <int DT, bool CRC, bool DELTA>
 __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint64_t g,
-                                           const PackLds<CRC>& L, uint32_t pos) {
+                                           const PackLds<CRC>& L, uint32_t pos, uint32_t* red) {
   constexpr int E = Dt<DT>::E;
   const int j = find_job(t, g);
   const CJob& job = t.jobs[j];
@@ -1054,13 +1266,16 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
     if (mode == LTC_MODE_RAW) rawmask |= 1u << k;
     else if (mode == LTC_MODE_RANS)
       write_rans<CRC>(blob, raw_off[k], s, si.y, si.x, si.z, t, w, job.frames, L, pos);
+    else if (DELTA && mode == LTC_MODE_ZRUN)
+      write_zrun<DT, DELTA>(blob + raw_off[k], src, job.base + c * t.chunk_bytes, n, k, si.z, si.w, si.x,
+                            t.vec16 != 0, red);
   }
   if (!rawmask) return;
   const uint32_t units = (n + 15) / 16;
   if constexpr (!CRC) {
     for (uint32_t u = tid; u < units; u += kPackThreads) {
       uint32_t y[16];
-      load16<DT>(src, 16 * u, n, t.vec16 != 0, y);
+      load16<DT, DELTA>(src, 16 * u, n, t.vec16 != 0, y, DELTA ? job.base + c * t.chunk_bytes : nullptr);
 #pragma unroll
       for (int k = 0; k < E; ++k) {
         if (!(rawmask & (1u << k))) continue;
@@ -1109,49 +1324,66 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
 
 // One workgroup per chunk (a grid-stride loop; the CRC variant runs a grid
 // of at most kPackCrcGrid workgroups, which build their tables once).
-template <int DT, bool CRC>
+template <int DT, bool CRC, bool DELTA>
 __global__ __launch_bounds__(CRC ? kPackCrcThreads : kPackThreads) void k_pack(CTable t, CWork w) {
+  __shared__ uint32_t red[8];  // ZRUN: per-wave counts
   __shared__ PackLds<CRC> lds;
   uint32_t pos = 0;
   if constexpr (CRC) {
     crc_build_tables(lds.c, &t.crc_x1k, threadIdx.x, kPackCrcThreads);
     pos = t.crc_pos[threadIdx.x & 63];
   }
-  for (uint64_t g = t.c_begin + blockIdx.x; g < t.c_end; g += gridDim.x) pack_chunk<DT, CRC>(t, w, g, lds, pos);
+  for (uint64_t g = t.c_begin + blockIdx.x; g < t.c_end; g += gridDim.x)
+    pack_chunk<DT, CRC, DELTA>(t, w, g, lds, pos, red);
 }
 
 // ------------------------------------------------------------------ launch
 
-template <int DT>
-static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t st,
+template <int DT, bool DELTA>
+static hipError_t launch_compress_d(const CTable& t, const CWork& w, hipStream_t st,
                                     const hipEvent_t* ev, hipEvent_t scan_after,
                                     hipEvent_t scan_done, bool staged) {
   constexpr int E = Dt<DT>::E;
   const uint64_t chunks = t.c_end - t.c_begin;
   if (!staged) {
     record(ev, 0, st);
-    if (chunks) hipLaunchKernelGGL(k_hist<DT>, dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
+    if (chunks) hipLaunchKernelGGL((k_hist<DT, DELTA>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
+    if (DELTA && chunks)
+      hipLaunchKernelGGL(k_zrun_stats<DT>, dim3((uint32_t)((chunks * E + 3) / 4)), dim3(256), 0, st, t, w);
     record(ev, 1, st);
   }
   if (chunks)
-    hipLaunchKernelGGL(k_encode<DT>, dim3((uint32_t)((chunks + kEncStreams - 1) / kEncStreams * E)), dim3(64), 0,
-                       st, t, w);
+    hipLaunchKernelGGL((k_encode<DT, DELTA>), dim3((uint32_t)((chunks + kEncStreams - 1) / kEncStreams * E)),
+                       dim3(64), 0, st, t, w);
   record(ev, 2, st);
   if (scan_after) (void)hipStreamWaitEvent(st, scan_after, 0);
   hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E);
   if (scan_done) (void)hipEventRecord(scan_done, st);
   record(ev, 3, st);
-  if (chunks && t.crc)
-    hipLaunchKernelGGL((k_pack<DT, true>), dim3((uint32_t)(chunks < kPackCrcGrid ? chunks : kPackCrcGrid)),
-                       dim3(kPackCrcThreads), 0, st, t, w);
-  else if (chunks)
-    hipLaunchKernelGGL((k_pack<DT, false>), dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
+  if constexpr (DELTA) {  // the blob is read back for checksums (no CRC variant)
+    if (chunks) hipLaunchKernelGGL((k_pack<DT, false, true>), dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
+  } else {
+    if (chunks && t.crc)
+      hipLaunchKernelGGL((k_pack<DT, true, false>), dim3((uint32_t)(chunks < kPackCrcGrid ? chunks : kPackCrcGrid)),
+                         dim3(kPackCrcThreads), 0, st, t, w);
+    else if (chunks)
+      hipLaunchKernelGGL((k_pack<DT, false, false>), dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
+  }
   record(ev, 4, st);
   return hipGetLastError();
 }
 
+template <int DT>
+static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t st,
+                                    const hipEvent_t* ev, hipEvent_t scan_after,
+                                    hipEvent_t scan_done, bool staged) {
+  return t.delta ? launch_compress_d<DT, true>(t, w, st, ev, scan_after, scan_done, staged)
+                 : launch_compress_d<DT, false>(t, w, st, ev, scan_after, scan_done, staged);
+}
+
 // v2, all chunks of t: histograms (summed per plane), plane tables and
-// records, then the skip bound of every stream with its plane's table
+// records, then the skip bound of every stream with its plane's table (and,
+// for deltas, the zero-run statistics)
 template <int DT>
 static hipError_t launch_v2_tables_t(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev) {
   constexpr int E = Dt<DT>::E;
@@ -1159,9 +1391,14 @@ static hipError_t launch_v2_tables_t(const CTable& t, const CWork& w, hipStream_
   record(ev, 0, st);
   hipError_t err = launch_zero_u32(reinterpret_cast<uint32_t*>(w.plane), 2ull * 256 * E * t.count, st);
   if (err != hipSuccess) return err;
-  if (chunks) hipLaunchKernelGGL(k_hist<DT>, dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
+  if (chunks && t.delta)
+    hipLaunchKernelGGL((k_hist<DT, true>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
+  else if (chunks)
+    hipLaunchKernelGGL((k_hist<DT, false>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
   hipLaunchKernelGGL(k_share<DT>, dim3(t.count), dim3(256), 0, st, t, w);
   if (chunks) hipLaunchKernelGGL(k_decide<DT>, dim3((uint32_t)((chunks * E + 3) / 4)), dim3(256), 0, st, t, w);
+  if (chunks && t.delta)
+    hipLaunchKernelGGL(k_zrun_stats<DT>, dim3((uint32_t)((chunks * E + 3) / 4)), dim3(256), 0, st, t, w);
   record(ev, 1, st);
   return hipGetLastError();
 }

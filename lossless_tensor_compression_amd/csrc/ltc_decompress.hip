@@ -80,7 +80,7 @@ template <int DT> __device__ __forceinline__ void planes_to_words(const uint32_t
   }
 }
 
-template <int DT, int MAXR>
+template <int DT, int MAXR, bool DELTA>
 __global__ __launch_bounds__(64) void k_decode(DTable t) {
   constexpr int E = Dt<DT>::E;
   __shared__ uint8_t lut[MAXR][4096];
@@ -114,7 +114,8 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     size[k] = e.z;
     mode[k] = e.w & 0xFFu;
     cval[k] = (e.w >> 8) & 0xFFu;
-    bad |= (e.w >> 16) != 0 || mode[k] > 2 || (mode[k] != LTC_MODE_CONST && cval[k] != 0) ||
+    bad |= (e.w >> 16) != 0 || mode[k] > (DELTA ? 3u : 2u) || (mode[k] != LTC_MODE_CONST && cval[k] != 0) ||
+           (mode[k] == LTC_MODE_ZRUN && size[k] < 16) ||
            (mode[k] == LTC_MODE_RAW && size[k] != n) || (mode[k] == LTC_MODE_CONST && size[k] != 0) ||
            (mode[k] == LTC_MODE_RANS && size[k] < kRansFixed + (job.v2 ? 0u : 16u)) || off[k] > B ||
            (uint64_t)size[k] > B - off[k];
@@ -345,12 +346,15 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   // RAW bytes for block b are loaded while block b-1 decodes.  Non-RAW
   // streams read 8 bytes of the directory (always inside the blob) and never
   // use them, so the loads carry no branch.
+  // Deltas: a ZRUN stream was expanded by k_zrun_expand into its slot of
+  // zbuf and is read like a RAW one.
   const uint8_t* rbase[E];
   uint32_t rlim[E];
 #pragma unroll
   for (int k = 0; k < E; ++k) {
-    const bool raw = mode[k] == LTC_MODE_RAW;
-    rbase[k] = raw ? blob + off[k] : blob + kHeader;
+    const bool zr = DELTA && mode[k] == LTC_MODE_ZRUN;
+    const bool raw = mode[k] == LTC_MODE_RAW || zr;
+    rbase[k] = zr ? t.zbuf + (g * E + k) * (uint64_t)t.n_full : raw ? blob + off[k] : blob + kHeader;
     rlim[k] = raw ? n : 0u;
   }
   uint64_t rawv[E];
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
       for (int k = 0; k < E; ++k) {
         uint64_t v;
         if (mode[k] == LTC_MODE_RANS) v = stage_bytes(slot_of[k]);
-        else if (mode[k] == LTC_MODE_RAW) v = rawv[k];
+        else if (mode[k] == LTC_MODE_RAW || (DELTA && mode[k] == LTC_MODE_ZRUN)) v = rawv[k];
         else v = 0x0101010101010101ull * cval[k];
         pl[0][k] = (uint32_t)v;
         pl[1][k] = (uint32_t)(v >> 32);
@@ -471,6 +475,20 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
       uint32_t* ow = obuf[SUB];
       planes_to_words<DT>(pl[0], ow);
       planes_to_words<DT>(pl[1], ow + E);
+      if constexpr (DELTA) {  // the decoded bytes are the delta: XOR the base back in
+        const uint8_t* bp = job.base + c * t.chunk_bytes + (uint64_t)e0 * E;
+        if (vec && e0 + 8 <= n) {
+#pragma unroll
+          for (int q = 0; q < 2 * E; q += 2) {
+            const uint2 bv = *reinterpret_cast<const uint2*>(bp + 4 * q);
+            ow[q] ^= bv.x;
+            ow[q + 1] ^= bv.y;
+          }
+        } else {
+          const uint32_t nb = (n - e0 < 8 ? n - e0 : 8) * E;
+          for (uint32_t i = 0; i < nb; ++i) ow[i / 4] ^= (uint32_t)bp[i] << (8 * (i & 3));
+        }
+      }
       if (!(vec && e0 + 8 <= n)) {  // a ragged or unaligned block: bytes, now
         uint8_t* op = dst + (uint64_t)e0 * E;
         const uint32_t nb = (n - e0 < 8 ? n - e0 : 8) * E;
@@ -516,26 +534,131 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   if (ballot(endbad) != 0 && lane == 0) *job.status = LTC_ERR_CORRUPT;
 }
 
+// Deltas: one workgroup per stream of the launch's chunks; a ZRUN payload is
+// checked field by field and expanded into the stream's zbuf slot (the
+// decoder then reads it like a RAW stream).  Any inconsistency is CORRUPT.
+template <int DT>
+__global__ __launch_bounds__(256) void k_zrun_expand(DTable t) {
+  constexpr int E = Dt<DT>::E;
+  __shared__ uint32_t red[8];
+  const uint64_t s = t.c_begin * E + blockIdx.x;
+  const uint64_t g = s / E;
+  const int k = (int)(s % E);
+  const int j = find_job(t, g);
+  const DJob& job = t.jobs[j];
+  const uint64_t c = g - job.chunk0;
+  const uint32_t n = c + 1 == job.nchunks ? job.n_tail : t.n_full;
+  const uint4 e = reinterpret_cast<const uint4*>(job.blob + kHeader)[c * E + k];
+  if ((e.w & 0xFFu) != LTC_MODE_ZRUN) return;
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
+  const uint64_t B = job.blob_nbytes;
+  const uint64_t off = (uint64_t)e.x | ((uint64_t)e.y << 32);
+  const uint32_t size = e.z;
+  const uint32_t nb = (n + 63) / 64;
+  bool bad = size < 16 || off > B || size > B - off || (off & 15);
+  const uint8_t* pl = job.blob + off;
+  uint32_t nnz = 0, nblk = 0, l2 = 0, lit = 0;
+  if (!bad) {
+    const uint4 h = *reinterpret_cast<const uint4*>(pl);
+    nnz = h.x;
+    nblk = h.y;
+    l2 = 16u + (uint32_t)align16((nb + 7) / 8);
+    lit = l2 + (uint32_t)align16(8ull * min(nblk, nb));
+    bad = h.z != 0 || h.w != 0 || nblk > nb || nnz > n || (uint64_t)lit + nnz != size;
+  }
+  if (!bad) {  // pads: bitmap bits past the last block, bitmap pad, mask pad
+    bool pb = false;
+    for (uint32_t i = 16 + nb / 8 + tid; i < l2; i += 256) {
+      const uint32_t v = pl[i];
+      pb |= (i == 16 + nb / 8 && (nb & 7)) ? (v >> (nb & 7)) != 0 : v != 0;
+    }
+    for (uint32_t i = l2 + 8 * nblk + tid; i < lit; i += 256) pb |= pl[i] != 0;
+    bad = __syncthreads_or(pb) != 0;
+  }
+  if (bad) {
+    if (tid == 0) *job.status = LTC_ERR_CORRUPT;
+    return;
+  }
+  uint8_t* out = t.zbuf + s * (uint64_t)t.n_full;
+  const uint8_t* l2p = pl + l2;
+  const uint8_t* lp = pl + lit;
+  uint32_t run_blk = 0, run_lit = 0;
+  bool err = false;
+  for (uint32_t r0 = 0; r0 < nb; r0 += 256) {
+    const uint32_t b = r0 + tid;
+    const bool set = b < nb && ((pl[16 + b / 8] >> (b & 7)) & 1u);
+    const uint64_t bal = ballot(set);
+    if (lane == 63) red[wave] = (uint32_t)__popcll(bal);
+    __syncthreads();
+    uint32_t blk_before = run_blk, blk_round = 0;
+    for (uint32_t q = 0; q < 4; ++q) {
+      if (q < wave) blk_before += red[q];
+      blk_round += red[q];
+    }
+    const uint32_t rank = blk_before + lanes_below(bal);
+    uint64_t mask = 0;
+    if (set) {
+      if (rank < nblk) mask = *reinterpret_cast<const uint64_t*>(l2p + 8 * rank);
+      err |= mask == 0 || (64 * b + 64 > n && (mask >> (n - 64 * b)) != 0);
+    }
+    const uint32_t pc = (uint32_t)__popcll(mask);
+    const uint32_t lit_below = wave_exclusive_scan_u32(pc);
+    __syncthreads();
+    if (lane == 63) red[4 + wave] = lit_below + pc;
+    __syncthreads();
+    uint32_t lit_before = run_lit, lit_round = 0;
+    for (uint32_t q = 0; q < 4; ++q) {
+      if (q < wave) lit_before += red[4 + q];
+      lit_round += red[4 + q];
+    }
+    if (b < nb) {
+      uint32_t o = lit_before + lit_below;
+      for (uint32_t i = 0; i < 64 && 64 * b + i < n; ++i) {
+        uint8_t v = 0;
+        if ((mask >> i) & 1u) {
+          if (o < nnz) v = lp[o];
+          ++o;
+          err |= v == 0;
+        }
+        out[64 * b + i] = v;
+      }
+    }
+    run_blk += blk_round;
+    run_lit += lit_round;
+    __syncthreads();
+  }
+  err |= run_blk != nblk || run_lit != nnz;
+  if (__syncthreads_or(err) && tid == 0) *job.status = LTC_ERR_CORRUPT;
+}
+
 __global__ void k_status_init(DTable t) {
   const uint32_t j = threadIdx.x;
   if (j < t.count) *t.jobs[j].status = LTC_OK;
 }
 
-template <int DT>
-static hipError_t launch_decompress_t(DTable t, hipStream_t st, const hipEvent_t* ev, uint64_t c_begin,
+template <int DT, bool DELTA>
+static hipError_t launch_decompress_d(DTable t, hipStream_t st, const hipEvent_t* ev, uint64_t c_begin,
                                       uint64_t c_end, bool init_status) {
   constexpr int E = Dt<DT>::E;
   t.c_begin = c_begin;
   const uint64_t n = c_end - c_begin;
   if (init_status) hipLaunchKernelGGL(k_status_init, dim3(1), dim3(64), 0, st, t);
+  if (DELTA && n) hipLaunchKernelGGL(k_zrun_expand<DT>, dim3((uint32_t)(n * E)), dim3(256), 0, st, t);
   record(ev, 0, st);
-  if (n) hipLaunchKernelGGL((k_decode<DT, 1>), dim3((uint32_t)n), dim3(64), 0, st, t);
+  if (n) hipLaunchKernelGGL((k_decode<DT, 1, DELTA>), dim3((uint32_t)n), dim3(64), 0, st, t);
   record(ev, 1, st);
   if constexpr (E > 1) {
-    if (n) hipLaunchKernelGGL((k_decode<DT, E>), dim3((uint32_t)n), dim3(64), 0, st, t);
+    if (n) hipLaunchKernelGGL((k_decode<DT, E, DELTA>), dim3((uint32_t)n), dim3(64), 0, st, t);
   }
   record(ev, 2, st);
   return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_decompress_t(DTable t, hipStream_t st, const hipEvent_t* ev, uint64_t c_begin,
+                                      uint64_t c_end, bool init_status) {
+  return t.delta ? launch_decompress_d<DT, true>(t, st, ev, c_begin, c_end, init_status)
+                 : launch_decompress_d<DT, false>(t, st, ev, c_begin, c_end, init_status);
 }
 
 hipError_t launch_decompress_range(int dtype, const DTable& t, hipStream_t st, const hipEvent_t* ev,

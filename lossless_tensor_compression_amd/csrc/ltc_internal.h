@@ -62,6 +62,7 @@ template <int DT> __device__ __forceinline__ uint32_t unreorder(uint32_t y) {
 
 struct CJob {
   const uint8_t* src;
+  const uint8_t* base;        // deltas: XOR base (src's layout), else null
   uint8_t* blob;
   uint64_t* blob_nbytes_out;  // device u64
   uint64_t nbytes;
@@ -83,6 +84,7 @@ struct CTable {
   uint32_t vec16;      // every src 16-byte aligned and chunk_bytes % 16 == 0
   uint32_t dtype;
   uint32_t v2;         // format v2: one table per (tensor, stream index)
+  uint32_t delta;      // XOR deltas: every job has a base; ZRUN candidates
   // the launch covers global chunks [c_begin, c_end) (a group of a pipelined
   // call, or all of them)
   uint64_t c_begin, c_end;
@@ -103,6 +105,7 @@ struct CWork {
   uint64_t* plane;      // v2: [count][E][256] summed histograms (zeroed first)
   uint16_t* ptab;       // v2: [count][E][256] the plane tables
   uint64_t* pbase;      // v2: [count] payload_base (end of the table records)
+  uint2* zinfo;         // deltas: [S] nonzero 64-byte blocks, nonzero bytes | rule << 31
   uint32_t* states;     // [S][64]
   uint16_t* words;      // [S][wcap]  (a stream's words end at its slot's end)
   uint64_t* offsets;    // [S]
@@ -112,6 +115,7 @@ struct CWork {
 struct DJob {
   const uint8_t* blob;
   uint8_t* dst;
+  const uint8_t* base;    // deltas: XOR base (dst's layout), else null
   int32_t* status;
   uint64_t payload_base;  // from the header (v1: the end of the directory)
   uint32_t v2;            // table records between the directory and payload_base
@@ -130,6 +134,8 @@ struct DTable {
   uint32_t vec16;       // every dst 16-byte aligned and chunk_bytes % 16 == 0
   uint64_t total_chunks;
   uint64_t c_begin;     // a launch decodes global chunks [c_begin, c_begin + grid)
+  uint32_t delta;       // every job is a delta blob with its base
+  uint8_t* zbuf;        // deltas: n_full bytes per global stream, ZRUN streams expanded
 };
 
 template <class T>

@@ -22,6 +22,12 @@ here.  Seeded normal tensors with per-tensor scales stand in for them:
       log-uniform in [1e-3, 1e-1] from numpy seed 5, values from torch Philox
       on the GPU (seed 5); tensors with index % 8 == 7 are uniform random
       bytes instead (incompressible).
+  C3D a checkpoint pair over C3 for XOR deltas ("NOTE-241: ZipNN", Deltas:
+      every parameter moves a little each epoch, the exponent least): the
+      base is C3; the later checkpoint is bfloat16(float32(base) + sigma *
+      lr * N(0,1)) per tensor, lr log-uniform in [5e-4, 5e-3] from numpy
+      seed 6, the noise from torch Philox on the GPU (seed 6); tensor 0
+      (a frozen layer) is left unchanged.
 The numpy recipes are reproducible on any host; the torch-on-GPU recipes are
 reproducible for a given torch build and device type, and every consumer
 records the SHA-256 of what it used.
@@ -92,6 +98,27 @@ def c3_gpu(device="cuda", count=None) -> list:
         out.append(t.mul_(sigma).to(torch.bfloat16))
         del t
     return out
+
+
+def c3_delta_lrs() -> list:
+    rng = np.random.default_rng(6)
+    return [float(np.exp(rng.uniform(np.log(5e-4), np.log(5e-3)))) for _ in C3_SHAPES]
+
+
+def c3_delta_gpu(device="cuda", count=None) -> tuple:
+    """(later checkpoint, base) lists of the C3D pair, bfloat16 on `device`."""
+    torch = _torch()
+    base = c3_gpu(device, count)
+    g = torch.Generator(device=device).manual_seed(6)
+    fine = []
+    for i, (b, sigma, lr) in enumerate(zip(base, c3_sigmas(), c3_delta_lrs())):
+        if i == 0:
+            fine.append(b.clone())
+            continue
+        t = torch.randn(b.shape, generator=g, device=device, dtype=torch.float32)
+        fine.append(t.mul_(sigma * lr).add_(b.float()).to(torch.bfloat16))
+        del t
+    return fine, base
 
 
 def c5_sigmas() -> list:
