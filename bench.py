@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--tables", default="own", choices=["own", "shared"],
                     help="blob format: v1 (a frequency table per coded stream) or v2 (one per "
                          "stream index, shared by all chunks of a tensor)")
+    ap.add_argument("--delta", action="store_true",
+                    help="also time XOR-delta compress and decompress of the C3D checkpoint pair "
+                         "(C3 and a slightly trained copy); reported beside value, never as value")
     ap.add_argument("--host-path", action="store_true",
                     help="also time decoding from pinned host blobs (copies over the host link "
                          "overlapped with decoding) against plain host-to-device copies of the "
@@ -215,6 +218,79 @@ def host_path(ts, blobs, bsz, outs, nbytes, N, B, hip, sptr, torch):
             "raw_h2d_ms": round(res["raw"], 3), "raw_h2d_gbs": round(N / (res["raw"] * 1e-3) / 1e9, 2),
             "speedup_vs_raw_copy": round(res["raw"] / res["load"], 3),
             "note": "PCIe-inclusive; original bytes per second"}
+
+
+def delta_bench(args, hip, sptr, torch):
+    """C3D: the later checkpoint of a pair coded as its XOR with the base
+    (ltc_compress_batch_ex with bases, ltc_decompress_delta_batch), against the
+    same tensors compressed on their own.  Algorithmic bytes: compress reads
+    source and base and writes the blob (2N + B); decompress reads blob and
+    base and writes the output (2N + B)."""
+    import lossless_tensor_compression_amd as ltc
+    import workloads
+    fine, base = workloads.c3_delta_gpu("cuda")
+    count = len(fine)
+    nbytes = [t.numel() * 2 for t in fine]
+    N = sum(nbytes)
+    caps = [ltc.compress_bound(n, 1, CHUNK) for n in nbytes]
+    blobs = [torch.empty(c, dtype=torch.uint8, device="cuda") for c in caps]
+    ws_n = ltc.workspace_size(nbytes, 1, CHUNK)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    sizes = torch.zeros(count, dtype=torch.int64, device="cuda")
+    src_ptrs = [t.data_ptr() for t in fine]
+    base_ptrs = [t.data_ptr() for t in base]
+    blob_ptrs = [b.data_ptr() for b in blobs]
+
+    def comp():
+        ltc.compress_ex_raw(src_ptrs, nbytes, 1, CHUNK, THRESHOLD, 0, blob_ptrs, caps, sizes.data_ptr(),
+                            ws.data_ptr(), ws_n, base_ptrs=base_ptrs)
+
+    comp()
+    bsz = sizes.cpu().tolist()
+    B = sum(bsz)
+    headers = [bytes(b[:64].cpu().numpy().tobytes()) for b in blobs]
+    dws_n = ltc.delta_workspace_size(headers)
+    dws = torch.empty(max(dws_n, 256), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty(n, dtype=torch.uint8, device="cuda") for n in nbytes]
+    status = torch.zeros(count, dtype=torch.int32, device="cuda")
+
+    def dec():
+        ltc.decompress_delta_raw(headers, blob_ptrs, bsz, base_ptrs, [o.data_ptr() for o in outs], nbytes,
+                                 status.data_ptr(), dws.data_ptr(), dws_n)
+
+    for _ in range(max(1, args.warmup)):
+        comp()
+        dec()
+    torch.cuda.synchronize()
+    assert sizes.cpu().tolist() == bsz and status.cpu().tolist() == [0] * count, "delta status"
+    for t, o in zip(fine, outs):
+        assert torch.equal(t.view(-1).view(torch.uint8), o), "delta round trip"
+    ev = hip.events(2)
+    reps = max(3, min(args.steps, 10))
+    res = {}
+    for name, fn in (("compress", comp), ("decompress", dec)):
+        hip.record(ev[0], sptr)
+        for _ in range(reps):
+            fn()
+        hip.record(ev[1], sptr)
+        torch.cuda.synchronize()
+        res[name] = hip.ms(ev[0], ev[1]) / reps
+    modes = {"raw": 0, "rans": 0, "const": 0, "zrun": 0}
+    for b, s in zip(blobs, bsz):
+        for m in ltc.blob_stats(b[:s])["modes"]:
+            for kk in modes:
+                modes[kk] += m[kk]
+    alone = sum(b.numel() for b in ltc.compress_batch(fine))
+    algo = 2 * N + B
+    return {"workload": "C3D: C3 and a copy moved by sigma*lr*N(0,1), lr log-uniform [5e-4, 5e-3], "
+                        "tensor 0 unchanged", "orig_bytes": N, "blob_bytes": B,
+            "ratio": round(B / N, 5), "standalone_ratio": round(alone / N, 5),
+            "compress_ms": round(res["compress"], 4), "decompress_ms": round(res["decompress"], 4),
+            "compress_gbs": round(N / (res["compress"] * 1e-3) / 1e9, 2),
+            "decompress_gbs": round(N / (res["decompress"] * 1e-3) / 1e9, 2),
+            "compress_roofline_frac": round(algo / (res["compress"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decompress_roofline_frac": round(algo / (res["decompress"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stream_modes": modes}
 
 
 def cpu_baseline(args, ts, torch):
@@ -497,6 +573,8 @@ def main():
     }
     if args.host_path:
         rec["host_path"] = host_path(ts, blobs, bsz, outs, nbytes, N, B, hip, sptr, torch)
+    if args.delta:
+        rec["delta"] = delta_bench(args, hip, sptr, torch)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args, ts, torch)
     print(json.dumps(rec), flush=True)

@@ -30,6 +30,7 @@ namespace ltc {
 constexpr int kHistThreads = 256;
 constexpr int kHistCopies = 32;  // sub-histograms, picked by lane & 31
 constexpr uint32_t kHistSeg = 1u << 20;  // elements between sub-histogram flushes
+constexpr uint32_t kZSeg = 16384;         // elements per zero bitmap (deltas)
 constexpr int kPackThreads = 256;
 // CRC variant: a grid of 4 workgroups per CU (13 KiB of tables each, up to
 // 128 VGPRs), which build their tables once
@@ -195,8 +196,8 @@ __device__ __forceinline__ bool raw_by_bound(const uint32_t hv[4], const uint32_
 // Normalise one stream's histogram (one wave; lane l owns symbols 4l..4l+3),
 // pick CONST / RAW / encode, write the frequency table and the stream info.
 // v2: keep the histogram for k_decide and add it to the plane's instead.
-__device__ void normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, uint64_t s,
-                                 const CWork& w, uint64_t* plane) {
+__device__ uint32_t normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, uint64_t s,
+                                     const CWork& w, uint64_t* plane) {
   const uint32_t lane = lane_id();
   uint32_t hv[4], f[4];
   uint32_t nz = 0, lo = 0xFFFFu, hi = 0;
@@ -220,13 +221,13 @@ __device__ void normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, u
   if (nz == 1) {  // a single value: the stream is a header ("NOTE-241", Method item 3)
     if (lane == 0)
       *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(LTC_MODE_CONST, lo, 0, 0), 0, 0);
-    return;
+    return LTC_MODE_CONST;
   }
   if (plane) {  // v2: decided once the plane's table exists (k_decide)
     *reinterpret_cast<uint4*>(w.hist + 256 * s + 4 * lane) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     if (lane == 0)
       *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(kModeCand, 0, 0, 0), 0, 0);
-    return;
+    return kModeCand;
   }
   normalize_wave(hv, n, f);
   const uint32_t wo = (uint32_t)align16(kRansFixed + 2u * (hi - lo + 1u));
@@ -237,14 +238,90 @@ __device__ void normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, u
   if (lane == 0)
     *reinterpret_cast<uint4*>(w.sinfo + 4 * s) =
         make_uint4(raw ? n : 0u, pack_info(raw ? LTC_MODE_RAW : kModeCand, 0, lo, hi), 0, 0);
+  return raw ? LTC_MODE_RAW : kModeCand;
+}
+
+// Zero-run statistics of a delta stream (ZipNN's rule, "NOTE-241", Deltas:
+// more than 90% zero bytes, or a zero run over 3% of the byte group).  A run
+// summary of a range: its length, the zero run at its start and at its end,
+// and its longest zero run; summaries of neighbouring ranges join in order.
+struct ZRun {
+  uint32_t len, pre, suf, mx;
+};
+__device__ __forceinline__ ZRun zrun_join(ZRun a, ZRun b) {
+  ZRun r;
+  r.len = a.len + b.len;
+  r.pre = a.pre == a.len ? a.len + b.pre : a.pre;
+  r.suf = b.suf == b.len ? b.len + a.suf : b.suf;
+  r.mx = max(max(a.mx, b.mx), a.suf + b.pre);
+  return r;
+}
+
+// Run summary of the first L (1..32) flags of x (bit i set: byte i is zero).
+__device__ __forceinline__ ZRun zrun_word(uint32_t x, uint32_t L) {
+  const uint32_t full = L == 32 ? ~0u : (1u << L) - 1u;
+  x &= full;
+  if (x == full) return ZRun{L, L, L, L};
+  if (x == 0) return ZRun{L, 0, 0, 0};
+  uint32_t m = 0;
+  for (uint32_t y = x; y; y &= y >> 1) ++m;
+  return ZRun{L, (uint32_t)__builtin_ctz(~x), (uint32_t)__builtin_clz(~(x << (32 - L))), m};
+}
+
+// Join the lanes' summaries in lane order; lane 0 gets the wave's.
+__device__ __forceinline__ ZRun zrun_wave(ZRun z) {
+  const uint32_t lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    ZRun r;
+    r.len = __shfl_down(z.len, o, 64);
+    r.pre = __shfl_down(z.pre, o, 64);
+    r.suf = __shfl_down(z.suf, o, 64);
+    r.mx = __shfl_down(z.mx, o, 64);
+    if ((lane & (2 * o - 1)) == 0 && lane + o < 64) z = zrun_join(z, r);
+  }
+  return z;
+}
+
+// Bits of an element x that land in byte k of the reordered element: byte k
+// of the reordered element is zero exactly when x & byte_src_mask(k) is.
+template <int DT>
+__host__ __device__ constexpr uint32_t byte_src_mask(int k) {
+  constexpr int E = Dt<DT>::E, WM = Dt<DT>::WM, W = 8 * E;
+  uint32_t m = 0;
+  for (int b = 0; b < W; ++b) {
+    const int to = WM < 0 ? b : (b < WM ? b : (b == W - 1 ? WM : b + 1));
+    if (to / 8 == k) m |= 1u << b;
+  }
+  return m;
+}
+
+// Zero flags of stream k for the 16/E elements of a 16-byte vector (bit i:
+// element i of the vector).
+template <int DT, int K>
+__device__ __forceinline__ uint32_t zero_flags(const uint4 q) {
+  constexpr int E = Dt<DT>::E, PER = 4 / E;
+  const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+      bits |= (uint32_t)((wv[i] & (byte_src_mask<DT>(K) << (8 * E * m))) == 0) << (i * PER + m);
+  return bits;
 }
 
 template <int DT, bool DELTA>
 __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
   constexpr uint32_t kWords = E * 128 * kHistCopies;
+  // deltas: a zero bitmap per stream for kZSeg elements at a time, whose run
+  // summary wave k folds into the stream's before the next slice
+  constexpr uint32_t kSub = DELTA ? kZSeg : kHistSeg;
+  constexpr uint32_t kZWords = kZSeg / 32;
   __shared__ uint32_t hs[kWords];
   __shared__ uint32_t hf[E * 256];
+  __shared__ uint32_t zb[DELTA ? E * kZWords : 1];
   const uint64_t g = t.c_begin + blockIdx.x;
   const int j = find_job(t, g);
   const CJob& job = t.jobs[j];
@@ -253,36 +330,107 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   const uint32_t n = last ? job.n_tail : t.n_full;
   const uint8_t* chunk = job.src + c * t.chunk_bytes;
   const uint8_t* bchunk = DELTA ? job.base + c * t.chunk_bytes : nullptr;
-  const uint32_t tid = threadIdx.x;
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
   const uint32_t copy = tid & (kHistCopies - 1);
+  ZRun zacc{0, 0, 0, 0};  // wave k < E, lane 0: stream k so far
+  uint32_t nzb = 0;       // nonzero 64-byte blocks of stream k so far
 
   for (uint32_t i = tid; i < E * 256; i += kHistThreads) hf[i] = 0;
   for (uint32_t seg = 0; seg < n; seg += kHistSeg) {
     const uint32_t sn = n - seg < kHistSeg ? n - seg : kHistSeg;
-    const uint32_t len = sn * E;
-    const uint8_t* src = chunk + (uint64_t)seg * E;
-    const uint8_t* bsrc = DELTA ? bchunk + (uint64_t)seg * E : nullptr;
     for (uint32_t i = tid; i < kWords; i += kHistThreads) hs[i] = 0;
-    __syncthreads();
-    uint32_t done = 0;
-    if (t.vec16 && len >= 32) {
-      const uint32_t nvec = len / 16, lastv = nvec - 1;
-      auto v = [&](uint32_t i) { return load_x16<DELTA>(src, bsrc, 16ull * i); };
-      // two 16-byte loads in flight ahead of the two being counted; indices
-      // are clamped instead of branched so the waits land at the uses
-      uint4 q0 = v(min(tid, lastv)), q1 = v(min(tid + kHistThreads, lastv));
-      for (uint32_t i = tid; i < nvec; i += 2 * kHistThreads) {
-        const uint4 n0 = v(min(i + 2 * kHistThreads, lastv));
-        const uint4 n1 = v(min(i + 3 * kHistThreads, lastv));
-        hist_vec<DT>(hs, q0, copy);
-        if (i + kHistThreads < nvec) hist_vec<DT>(hs, q1, copy);
-        q0 = n0;
-        q1 = n1;
+    for (uint32_t sub = 0; sub < sn; sub += kSub) {
+      const uint32_t zn = sn - sub < kSub ? sn - sub : kSub;
+      const uint32_t len = zn * E;
+      const uint8_t* src = chunk + (uint64_t)(seg + sub) * E;
+      const uint8_t* bsrc = DELTA ? bchunk + (uint64_t)(seg + sub) * E : nullptr;
+      if constexpr (DELTA)
+        for (uint32_t i = tid; i < E * kZWords; i += kHistThreads) zb[i] = 0;
+      __syncthreads();
+      // vector i holds elements [i*16/E, (i+1)*16/E): its zero flags go to
+      // bit i*16/E of each stream's bitmap
+      auto zvec = [&](const uint4 q, uint32_t i) {
+        if constexpr (DELTA) {
+          if constexpr (E == 1) {
+            reinterpret_cast<uint16_t*>(zb)[i] = (uint16_t)zero_flags<DT, 0>(q);
+          } else if constexpr (E == 2) {
+            reinterpret_cast<uint8_t*>(zb)[i] = (uint8_t)zero_flags<DT, 0>(q);
+            reinterpret_cast<uint8_t*>(zb + kZWords)[i] = (uint8_t)zero_flags<DT, 1>(q);
+          } else {
+            const uint32_t sh = 4 * (i & 7u);
+            atomicOr(&zb[i / 8], zero_flags<DT, 0>(q) << sh);
+            atomicOr(&zb[kZWords + i / 8], zero_flags<DT, 1>(q) << sh);
+            atomicOr(&zb[2 * kZWords + i / 8], zero_flags<DT, 2>(q) << sh);
+            atomicOr(&zb[3 * kZWords + i / 8], zero_flags<DT, 3>(q) << sh);
+          }
+        }
+      };
+      uint32_t done = 0;
+      if (t.vec16 && len >= 32) {
+        const uint32_t nvec = len / 16, lastv = nvec - 1;
+        auto v = [&](uint32_t i) { return load_x16<DELTA>(src, bsrc, 16ull * i); };
+        // two 16-byte loads in flight ahead of the two being counted; indices
+        // are clamped instead of branched so the waits land at the uses
+        uint4 q0 = v(min(tid, lastv)), q1 = v(min(tid + kHistThreads, lastv));
+        for (uint32_t i = tid; i < nvec; i += 2 * kHistThreads) {
+          const uint4 n0 = v(min(i + 2 * kHistThreads, lastv));
+          const uint4 n1 = v(min(i + 3 * kHistThreads, lastv));
+          hist_vec<DT>(hs, q0, copy);
+          zvec(q0, i);
+          if (i + kHistThreads < nvec) {
+            hist_vec<DT>(hs, q1, copy);
+            zvec(q1, i + kHistThreads);
+          }
+          q0 = n0;
+          q1 = n1;
+        }
+        done = nvec * 16;
       }
-      done = nvec * 16;
+      for (uint32_t e = done / E + tid; e < zn; e += kHistThreads) {
+        const uint32_t x = load_x<DT, DELTA>(src, bsrc, (uint64_t)e * E);
+        hist_elem<DT>(hs, reorder<DT>(x), copy);
+        if constexpr (DELTA) {
+#pragma unroll
+          for (int k = 0; k < E; ++k)
+            if ((x & byte_src_mask<DT>(k)) == 0) atomicOr(&zb[k * kZWords + e / 32], 1u << (e & 31u));
+        }
+      }
+      if constexpr (DELTA) {
+        __syncthreads();
+        if (wave < (uint32_t)E) {  // lane l: words 8l..8l+7 of stream `wave`, four 64-byte blocks
+          const uint32_t* zw = zb + wave * kZWords;
+          const uint32_t nw = (zn + 31) / 32;
+          ZRun z{0, 0, 0, 0};
+          uint32_t blocks = 0;
+#pragma unroll
+          for (uint32_t q = 0; q < kZWords / 64; q += 2) {
+            const uint32_t w0 = 8 * lane + q, w1 = w0 + 1;
+            if (w0 < nw) {
+              const uint32_t l0 = min(32u, zn - 32 * w0);
+              const uint32_t m0 = l0 == 32 ? ~0u : (1u << l0) - 1u;
+              const uint32_t x0 = zw[w0];
+              z = zrun_join(z, zrun_word(x0, l0));
+              uint32_t nonzero = ~x0 & m0;
+              if (w1 < nw) {
+                const uint32_t l1 = min(32u, zn - 32 * w1);
+                const uint32_t m1 = l1 == 32 ? ~0u : (1u << l1) - 1u;
+                const uint32_t x1 = zw[w1];
+                z = zrun_join(z, zrun_word(x1, l1));
+                nonzero |= ~x1 & m1;
+              }
+              blocks += nonzero != 0;
+            }
+          }
+          z = zrun_wave(z);
+          blocks = wave_sum_u32(blocks);
+          if (lane == 0) {
+            zacc = zrun_join(zacc, z);
+            nzb += blocks;
+          }
+        }
+        __syncthreads();  // the bitmap is cleared for the next slice
+      }
     }
-    for (uint32_t e = done / E + tid; e < sn; e += kHistThreads)
-      hist_elem<DT>(hs, reorder<DT>(load_x<DT, DELTA>(src, bsrc, (uint64_t)e * E)), copy);
     __syncthreads();
     // fold the 32 copies; the copy index rotates with the thread so the 32
     // reads of a half-wave hit 32 different banks
@@ -297,10 +445,27 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
     }
     __syncthreads();
   }
-  const uint32_t wave = tid / 64;
-  if (wave < (uint32_t)E)
-    normalize_stream(hf + 256 * wave, n, last ? job.pmax_tail : job.pmax_full, g * E + wave, w,
-                     t.v2 ? w.plane + ((uint64_t)j * E + wave) * 256 : nullptr);
+  if (wave < (uint32_t)E) {
+    const uint64_t s = g * E + wave;
+    const uint32_t pmax = last ? job.pmax_tail : job.pmax_full;
+    const uint32_t mode = normalize_stream(hf + 256 * wave, n, pmax, s, w,
+                                           t.v2 ? w.plane + ((uint64_t)j * E + wave) * 256 : nullptr);
+    if constexpr (DELTA) {
+      if (lane == 0) {
+        // ZipNN's rule makes ZRUN a candidate; k_encode weighs it against
+        // RANS, and a stream the size bound made RAW takes it if it fits
+        const uint32_t zeros = hf[256 * wave];
+        const bool rule = 10ull * zeros > 9ull * n || 100ull * zacc.mx > 3ull * n;
+        const uint32_t nnz = n - zeros;
+        w.zinfo[s] = make_uint2(nzb, nnz | (rule ? 0x80000000u : 0u));
+        if (mode == LTC_MODE_RAW && rule) {
+          const uint32_t pz = zrun_bytes(n, nzb, nnz);
+          if (pz <= pmax)
+            *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(pz, pack_info(LTC_MODE_ZRUN, 0, 0, 0), nzb, nnz);
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- v2 tables
@@ -420,8 +585,16 @@ __global__ __launch_bounds__(256) void k_decide(CTable t, CWork w) {
   const uint32_t hv[4] = {hq.x, hq.y, hq.z, hq.w};
   const uint32_t f[4] = {(uint32_t)fq & 0xFFFFu, (uint32_t)(fq >> 16) & 0xFFFFu,
                          (uint32_t)(fq >> 32) & 0xFFFFu, (uint32_t)(fq >> 48)};
-  if (raw_by_bound(hv, f, n, kRansFixed, last ? job.pmax_tail : job.pmax_full) && lane == 0)
-    *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(n, pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
+  const uint32_t pmax = last ? job.pmax_tail : job.pmax_full;
+  if (raw_by_bound(hv, f, n, kRansFixed, pmax) && lane == 0) {
+    uint4 v = make_uint4(n, pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
+    if (t.delta) {  // a delta stream ZipNN's rule fired for: ZRUN if it fits
+      const uint2 zi = w.zinfo[s];
+      const uint32_t pz = zrun_bytes(n, zi.x, zi.y & 0x7FFFFFFFu);
+      if ((zi.y >> 31) && pz <= pmax) v = make_uint4(pz, pack_info(LTC_MODE_ZRUN, 0, 0, 0), zi.x, zi.y & 0x7FFFFFFFu);
+    }
+    *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = v;
+  }
 }
 
 // ---------------------------------------------------------------- k_encode
@@ -932,82 +1105,6 @@ __device__ __forceinline__ void load16(const uint8_t* src, uint32_t e0, uint32_t
 
 // Zero-run statistics of a byte range: length, leading and trailing zero
 // runs, longest zero run, all zero.  Ranges in order combine associatively.
-struct ZRun {
-  uint32_t len, pre, suf, mx;
-};
-__device__ __forceinline__ ZRun zrun_join(ZRun a, ZRun b) {
-  ZRun r;
-  r.len = a.len + b.len;
-  r.pre = a.pre == a.len ? a.len + b.pre : a.pre;
-  r.suf = b.suf == b.len ? b.len + a.suf : b.suf;
-  r.mx = max(max(a.mx, b.mx), a.suf + b.pre);
-  return r;
-}
-
-// One wave per stream of a delta batch that is not CONST: zero bytes,
-// nonzero 64-byte blocks and the longest zero run.  ZipNN's rule ("NOTE-241",
-// Deltas: more than 90% zero bytes, or a zero run over 3% of the group)
-// makes ZRUN a candidate; a stream the skip bound already made RAW becomes
-// ZRUN when that fits under P_max.
-template <int DT>
-__global__ __launch_bounds__(256) void k_zrun_stats(CTable t, CWork w) {
-  constexpr int E = Dt<DT>::E;
-  const uint64_t s = t.c_begin * E + (uint64_t)blockIdx.x * 4 + threadIdx.x / 64;
-  if (s >= t.c_end * E) return;
-  const uint32_t mode = w.sinfo[4 * s + 1] & 0xFFu;
-  if (mode == LTC_MODE_CONST) return;
-  const uint64_t g = s / E;
-  const int k = (int)(s % E);
-  const int j = find_job(t, g);
-  const CJob& job = t.jobs[j];
-  const uint64_t c = g - job.chunk0;
-  const bool last = c + 1 == job.nchunks;
-  const uint32_t n = last ? job.n_tail : t.n_full;
-  const uint8_t* src = job.src + c * t.chunk_bytes;
-  const uint8_t* bsrc = job.base + c * t.chunk_bytes;
-  const uint32_t lane = lane_id();
-  const uint32_t nb = (n + 63) / 64, per = (nb + 63) / 64;
-  ZRun z{0, 0, 0, 0};
-  uint32_t zeros = 0, nzb = 0;
-  for (uint32_t b = lane * per; b < nb && b < (lane + 1) * per; ++b) {
-    bool any = false;
-    for (uint32_t q = 0; q < 4; ++q) {
-      uint32_t y[16];
-      load16<DT, true>(src, 64 * b + 16 * q, n, t.vec16 != 0, y, bsrc);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (64 * b + 16 * q + i < n) {
-          const bool zb = ((y[i] >> (8 * k)) & 0xFFu) == 0;
-          zeros += zb;
-          any |= !zb;
-          z = zrun_join(z, ZRun{1u, zb ? 1u : 0u, zb ? 1u : 0u, zb ? 1u : 0u});
-        }
-      }
-    }
-    nzb += any;
-  }
-  // combine the lanes' ranges in lane order
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    ZRun r;
-    r.len = __shfl_down(z.len, o, 64);
-    r.pre = __shfl_down(z.pre, o, 64);
-    r.suf = __shfl_down(z.suf, o, 64);
-    r.mx = __shfl_down(z.mx, o, 64);
-    if ((lane & (2 * o - 1)) == 0 && lane + o < 64) z = zrun_join(z, r);
-  }
-  zeros = wave_sum_u32(zeros);
-  nzb = wave_sum_u32(nzb);
-  if (lane != 0) return;
-  const bool rule = 10ull * zeros > 9ull * n || 100ull * z.mx > 3ull * n;
-  const uint32_t nnz = n - zeros;
-  w.zinfo[s] = make_uint2(nzb, nnz | (rule ? 0x80000000u : 0u));
-  if (mode == LTC_MODE_RAW && rule) {
-    const uint32_t pz = zrun_bytes(n, nzb, nnz);
-    if (pz <= (last ? job.pmax_tail : job.pmax_full))
-      *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(pz, pack_info(LTC_MODE_ZRUN, 0, 0, 0), nzb, nnz);
-  }
-}
 
 // ZRUN payload of stream k of a chunk at dst (all threads of the workgroup;
 // every byte of the payload and of its gap to 16 is written): 16-byte head,
@@ -1348,8 +1445,6 @@ static hipError_t launch_compress_d(const CTable& t, const CWork& w, hipStream_t
   if (!staged) {
     record(ev, 0, st);
     if (chunks) hipLaunchKernelGGL((k_hist<DT, DELTA>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
-    if (DELTA && chunks)
-      hipLaunchKernelGGL(k_zrun_stats<DT>, dim3((uint32_t)((chunks * E + 3) / 4)), dim3(256), 0, st, t, w);
     record(ev, 1, st);
   }
   if (chunks)
@@ -1397,8 +1492,6 @@ static hipError_t launch_v2_tables_t(const CTable& t, const CWork& w, hipStream_
     hipLaunchKernelGGL((k_hist<DT, false>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
   hipLaunchKernelGGL(k_share<DT>, dim3(t.count), dim3(256), 0, st, t, w);
   if (chunks) hipLaunchKernelGGL(k_decide<DT>, dim3((uint32_t)((chunks * E + 3) / 4)), dim3(256), 0, st, t, w);
-  if (chunks && t.delta)
-    hipLaunchKernelGGL(k_zrun_stats<DT>, dim3((uint32_t)((chunks * E + 3) / 4)), dim3(256), 0, st, t, w);
   record(ev, 1, st);
   return hipGetLastError();
 }

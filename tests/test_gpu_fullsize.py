@@ -113,6 +113,33 @@ def test_c3_shared_tables_full_size(ltc):
         assert np.array_equal(blobs[i].cpu().numpy(), want)
 
 
+def test_c3d_delta_full_size(ltc):
+    """XOR deltas over the C3D checkpoint pair, as bench.py --delta runs them:
+    exact round trip with the bases, ZRUN streams present, and three tensors
+    byte for byte against the oracle's delta blobs (tensor 0 is unchanged:
+    CONST streams only)."""
+    banner("C3D generate")
+    fine, base = workloads.c3_delta_gpu()
+    banner("C3D compress_batch_delta")
+    blobs = ltc.compress_batch_delta(fine, base)
+    outs = ltc.decompress_batch_delta(blobs, base)
+    for t, o in zip(fine, outs):
+        assert torch.equal(t.view(-1).view(torch.int16), o.view(torch.int16))
+    del outs
+    b0 = blobs[0].cpu().numpy()
+    k = int.from_bytes(b0[20:24].tobytes(), "little")
+    assert b0.size == 64 + 16 * 2 * k and (b0[64 + 12::16] == oracle.MODE_CONST).all()
+    zr = sum(sum(m["zrun"] for m in ltc.blob_stats(b)["modes"]) for b in blobs)
+    banner(f"C3D ratio {sum(b.numel() for b in blobs) / sum(t.numel() * 2 for t in fine):.4f}, "
+           f"{zr} ZRUN streams")
+    for i in (1, 6, 27):
+        banner(f"C3D oracle parity tensor {i} {workloads.C3_SHAPES[i]}")
+        src = fine[i].view(torch.int16).cpu().numpy()
+        bs = base[i].view(torch.int16).cpu().numpy()
+        want = oracle.compress_delta(src, bs, 1, CHUNK, 0.95, nthreads=16)
+        assert np.array_equal(blobs[i].cpu().numpy(), want)
+
+
 def test_c5_full_size_with_crc(ltc):
     banner("C5 generate (8 GiB)")
     buf = workloads.c5_gpu()
