@@ -649,8 +649,14 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   __shared__ __attribute__((aligned(16))) uint32_t stg[U][256];  // 512 u16 entry offsets
   __shared__ __attribute__((aligned(16))) uint16_t ring[U][kRingWords + 64];
   const uint32_t lane = lane_id();
-  const uint32_t k = blockIdx.x % E;
-  const uint64_t g0 = t.c_begin + (uint64_t)(blockIdx.x / E) * U;
+  // Stream-index-major order, the top byte (usually the only coded stream)
+  // first: consecutive workgroups go to different XCDs in turn, so
+  // interleaving the stream indices would hand every coded stream of a
+  // BF16 tensor to half of the XCDs (of an FP32 tensor, to a quarter) while
+  // the rest only receive streams that exit at once.
+  const uint32_t pairs = gridDim.x / E;
+  const uint32_t k = (uint32_t)(E - 1) - blockIdx.x / pairs;
+  const uint64_t g0 = t.c_begin + (uint64_t)(blockIdx.x % pairs) * U;
   const uint32_t wcap = t.wcap;
 
   bool on[U];
