@@ -499,7 +499,8 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     for (int k = 0; k < E; ++k) rawv[k] = rawn[k];
     wave_sync();
   };
-  // vector stores of block b's elements 8 lane .. 8 lane + 7
+  // vector stores of block b's elements 8 lane .. 8 lane + 7 (streaming:
+  // nothing reads them back, measured about 1% faster than plain stores)
   auto store_block = [&](uint32_t b, auto subc) {
     constexpr int SUB = decltype(subc)::value;
     const uint32_t e0 = 512 * b + 8 * lane;
@@ -507,12 +508,12 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     const uint32_t* ow = obuf[SUB];
     uint8_t* op = dst + (uint64_t)e0 * E;
     if constexpr (E == 1) {
-      *reinterpret_cast<uint2*>(op) = make_uint2(ow[0], ow[1]);
+      store_nt8(op, ow[0], ow[1]);
     } else if constexpr (E == 2) {
-      *reinterpret_cast<uint4*>(op) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      store_nt16(op, ow[0], ow[1], ow[2], ow[3]);
     } else {
-      reinterpret_cast<uint4*>(op)[0] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      reinterpret_cast<uint4*>(op)[1] = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+      store_nt16(op, ow[0], ow[1], ow[2], ow[3]);
+      store_nt16(op + 16, ow[4], ow[5], ow[6], ow[7]);
     }
   };
   for (uint32_t b = 0; b < nblk; b += NB) {

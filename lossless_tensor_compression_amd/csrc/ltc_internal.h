@@ -149,6 +149,19 @@ __device__ __forceinline__ int find_job(const T& t, uint64_t g) {
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+// Streaming (nontemporal) vector stores, for output no kernel of the call
+// reads back.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4_t v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_nt8(void* p, uint32_t a, uint32_t b) {
+  const u32x2_t v = {a, b};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+}
+
 // lane mask of a predicate (the builtin avoids a round trip through a VGPR)
 __device__ __forceinline__ uint64_t ballot(bool b) { return __builtin_amdgcn_ballot_w64(b); }
 

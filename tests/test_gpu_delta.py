@@ -145,7 +145,7 @@ def test_oracle_cases_both_coders(ltc):
 @pytest.mark.parametrize("dtype,chunk,shared", [(1, 4096, False), (1, 4096, True), (3, 1024, False),
                                                 (0, 2048, True)])
 def test_grouped(ltc, dtype, chunk, shared):
-    """Over 512 chunks: four chunk groups on several streams (v2: after the
+    """Over 512 chunks: two chunk groups on two streams (v2: after the
     tables), ZRUN chunks in every group."""
     rng = np.random.default_rng(500 + dtype)
     e = oracle.ELEM_BYTES[dtype]

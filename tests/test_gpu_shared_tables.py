@@ -87,7 +87,7 @@ def test_thresholds(ltc, thr):
 
 @pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (0, 2048)])
 def test_grouped_with_random_chunks(ltc, dtype, chunk):
-    """Over 512 chunks: the tables come first, then four chunk groups."""
+    """Over 512 chunks: the tables come first, then two chunk groups."""
     rng = np.random.default_rng(400 + dtype)
     nbytes = 700 * chunk + 24
     if dtype == 0:
