@@ -309,3 +309,23 @@ def test_grouped_batch_with_empty_and_tiny(ltc):
     again = ltc.compress_batch(ts, chunk)
     for b1, b2 in zip(blobs, again):
         assert torch.equal(b1, b2)
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_largest_chunk_many_histogram_segments(ltc, dtype):
+    """chunk_bytes = 16 MiB (the largest): a U8 chunk holds 16 Mi elements and
+    a BF16 chunk 8 Mi, so the histogram pass flushes its 16-bit sub-histograms
+    many times per chunk; one value dominates (the largest per-copy counts
+    a flush allows), and a ragged second chunk follows."""
+    rng = np.random.default_rng(900 + dtype)
+    chunk = 16 << 20
+    nbytes = chunk + 3 * (1 << 20) + 8
+    if dtype == 0:
+        arr = np.full(nbytes, 7, dtype=np.uint8)
+        idx = rng.choice(nbytes, nbytes // 1000, replace=False)
+        arr[idx] = rng.integers(0, 256, idx.size, dtype=np.uint8)
+    else:
+        x = rng.standard_normal(nbytes // 2) * 0.02
+        x[: nbytes // 4] = 0.015625  # one bit pattern over half of the first chunk
+        arr = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    check_case(ltc, arr, dtype, chunk, label="16 MiB chunks")
