@@ -301,8 +301,9 @@ int ltc_compress_delta(const void* d_src, const void* d_base, uint64_t nbytes, i
                        hipStream_t stream);
 
 /* Device workspace for decoding these delta blobs: the sum over blobs of
- * K * floor(C / E) * E bytes (each stream gets a slot its ZRUN payload is
- * expanded into before the decode kernel reads it as a RAW stream). */
+ * K * E * align16(floor(C / E)) bytes (each stream gets a 16-byte aligned
+ * slot its ZRUN payload is expanded into before the decode kernel reads it as
+ * a RAW stream, 8 bytes at a time). */
 int ltc_decompress_delta_workspace_size(int count, const void* const* h_headers, uint64_t* ws_nbytes);
 
 /* Decode delta blobs: output = decoded delta XOR base.  h_base_ptrs[i] is a

@@ -508,7 +508,8 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
   t.total_chunks = chunk0;
   if (bases) {
     if (host_blobs) return LTC_ERR_INVALID_ARGUMENT;  // deltas are decoded from device blobs
-    const uint64_t need = chunk0 * e * (uint64_t)t.n_full;
+    t.zstride = (uint32_t)align16(t.n_full);
+    const uint64_t need = chunk0 * e * (uint64_t)t.zstride;
     if (need && (!d_ws || ws_nbytes < need)) return LTC_ERR_WORKSPACE;
     t.delta = 1;
     t.zbuf = static_cast<uint8_t*>(d_ws);
@@ -704,7 +705,7 @@ int ltc_decompress_delta_workspace_size(int count, const void* const* h_headers,
     ltc_info info;
     const int rc = ltc_blob_info(h_headers[i], kHeader, &info);
     if (rc) return rc;
-    total += (uint64_t)info.nchunks * (info.chunk_bytes / info.elem_bytes) * info.elem_bytes;
+    total += (uint64_t)info.nchunks * info.elem_bytes * align16(info.chunk_bytes / info.elem_bytes);
   }
   *ws_nbytes = total;
   return LTC_OK;

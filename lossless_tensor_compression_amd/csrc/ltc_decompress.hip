@@ -343,7 +343,8 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   const uint32_t steps = (n + 63) / 64;
   const uint32_t full = n / 64;  // steps in which every lane decodes a symbol
   const uint32_t nblk = (steps + 7) / 8;
-  // RAW bytes for block b are loaded while block b-1 decodes.  Non-RAW
+  // RAW bytes for block b are loaded while block b-2 decodes (two blocks
+  // ahead: more loads in flight per wave, about 1% faster than one).  Non-RAW
   // streams read 8 bytes of the directory (always inside the blob) and never
   // use them, so the loads carry no branch.
   // Deltas: a ZRUN stream was expanded by k_zrun_expand into its slot of
@@ -354,12 +355,15 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
   for (int k = 0; k < E; ++k) {
     const bool zr = DELTA && mode[k] == LTC_MODE_ZRUN;
     const bool raw = mode[k] == LTC_MODE_RAW || zr;
-    rbase[k] = zr ? t.zbuf + (g * E + k) * (uint64_t)t.n_full : raw ? blob + off[k] : blob + kHeader;
+    rbase[k] = zr ? t.zbuf + (g * E + k) * (uint64_t)t.zstride : raw ? blob + off[k] : blob + kHeader;
     rlim[k] = raw ? n : 0u;
   }
   uint64_t rawv[E];
 #pragma unroll
   for (int k = 0; k < E; ++k) rawv[k] = load_raw8(rbase[k], 8 * lane, rlim[k]);
+  uint64_t rawm[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) rawm[k] = load_raw8(rbase[k], 512 + 8 * lane, rlim[k]);
 
   // Output lane l writes elements 8l .. 8l+7 of the block: step l / 8, lanes
   // 8(l % 8) .. 8(l % 8)+7, i.e. byte (l / 8) % 4 of 8 consecutive stage
@@ -435,7 +439,7 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
     const uint32_t e0 = 512 * b + 8 * lane;
     uint64_t rawn[E];
 #pragma unroll
-    for (int k = 0; k < E; ++k) rawn[k] = load_raw8(rbase[k], e0 + 512, rlim[k]);
+    for (int k = 0; k < E; ++k) rawn[k] = load_raw8(rbase[k], e0 + 1024, rlim[k]);
 #pragma unroll
     for (int rr = 0; rr < MAXR; ++rr) {
       if (rr >= nr) continue;
@@ -496,7 +500,10 @@ __global__ __launch_bounds__(64) void k_decode(DTable t) {
       }
     }
 #pragma unroll
-    for (int k = 0; k < E; ++k) rawv[k] = rawn[k];
+    for (int k = 0; k < E; ++k) {
+      rawv[k] = rawm[k];
+      rawm[k] = rawn[k];
+    }
     wave_sync();
   };
   // vector stores of block b's elements 8 lane .. 8 lane + 7 (streaming:
@@ -580,7 +587,7 @@ __global__ __launch_bounds__(256) void k_zrun_expand(DTable t) {
     if (tid == 0) *job.status = LTC_ERR_CORRUPT;
     return;
   }
-  uint8_t* out = t.zbuf + s * (uint64_t)t.n_full;
+  uint8_t* out = t.zbuf + s * (uint64_t)t.zstride;
   const uint8_t* l2p = pl + l2;
   const uint8_t* lp = pl + lit;
   uint32_t run_blk = 0, run_lit = 0;

@@ -135,7 +135,8 @@ struct DTable {
   uint64_t total_chunks;
   uint64_t c_begin;     // a launch decodes global chunks [c_begin, c_begin + grid)
   uint32_t delta;       // every job is a delta blob with its base
-  uint8_t* zbuf;        // deltas: n_full bytes per global stream, ZRUN streams expanded
+  uint8_t* zbuf;        // deltas: zstride bytes per global stream, ZRUN streams expanded
+  uint32_t zstride;     // align16(n_full): a stream's 8-byte reads stay in its slot
 };
 
 template <class T>

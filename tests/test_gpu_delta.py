@@ -240,6 +240,9 @@ def test_base_rules_and_errors(ltc):
     hdr = bytes(dblob[:64].cpu().numpy().tobytes())
     need = ltc.delta_workspace_size([hdr])
     assert need == x.size * 2 // 131072 * 131072 + (131072 if x.size * 2 % 131072 else 0)
+    # slots are 16-byte aligned: C = 24 bytes of FP32 holds 6 elements, slot 16
+    h24 = bytes(oracle.compress_delta(x[:1000], x[:1000], 3, 24)[:64])
+    assert ltc.delta_workspace_size([h24]) == (2000 + 23) // 24 * 4 * 16
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     dst = torch.empty(x.size * 2, dtype=torch.uint8, device="cuda")
     status = torch.full((1,), -99, dtype=torch.int32, device="cuda")
