@@ -11,8 +11,8 @@ checksums the payload as it writes it) then decompress.  --crc beside: plain
 compress, then the CRC kernel over the blobs on a second stream beside the
 decompression.
 
-compress/decompress/CRC throughputs come from HIP events between the calls,
-run one after another; per-kernel times (kernel_ms, roofline) come from a
+compress/decompress/CRC throughputs come from HIP events around each call
+repeated back to back; per-kernel times (kernel_ms, roofline) come from a
 separate pass that launches the kernels one by one on one stream.  With
 --isolated the timed steps run that way too (the mode the committed
 rocprofv3 kernel summary is taken in).
@@ -393,31 +393,25 @@ def main():
                             sizes.data_ptr(), ws.data_ptr(), ws_n, CRC_CHUNK, fcrc_ptrs, fcap,
                             events=events)
 
-    ev_p = hip.events(4)
+    ev_p = hip.events(2)
     side = torch.cuda.Stream()  # default priority
     ev_fork, ev_join = hip.events(2)
 
-    def step(prof, phases=False, plain=False):
-        """One pass of the hot path.  Fused CRC (unless phases or plain):
+    def step(prof, plain=False):
+        """One pass of the hot path.  Fused CRC (unless plain):
         compress_with_crc32 then decompress.  Otherwise compress, decompress
-        and the CRC kernel: with prof or phases one after another on one
-        stream (prof: kernel by kernel, with events between the kernels),
-        else the CRC-32 of the blobs runs on a second stream beside the
-        decompression, which does not depend on it.  A compress call over
-        many chunks runs its chunk groups on several streams
-        (library-internal) unless prof."""
-        if fused and not phases and not plain:
+        and the CRC kernel: with prof one after another on one stream, kernel
+        by kernel with events between the kernels, else the CRC-32 of the
+        blobs runs on a second stream beside the decompression, which does not
+        depend on it.  A plain compress call over many chunks runs its chunk
+        groups on two streams (library-internal) unless prof."""
+        if fused and not plain:
             compress_crc(ev_f if prof else None)
             ltc.decompress_raw(headers, blob_ptrs, bsz, out_ptrs, nbytes, status.data_ptr(),
                                events=ev_d if prof else None)
             return
-        serial = prof or phases
-        if phases:
-            hip.record(ev_p[0], sptr)
         compress_plain(ev_c if prof else None)
-        if phases:
-            hip.record(ev_p[1], sptr)
-        if not serial:
+        if not prof:
             hip.record(ev_fork, sptr)
             hip.wait(side.cuda_stream, ev_fork)
             ltc.crc32_raw(blob_ptrs, bsz, CRC_CHUNK, crc_ptrs, stream=side)
@@ -426,16 +420,10 @@ def main():
                            events=ev_d if prof else None)
         if prof:
             hip.record(ev_x[0], sptr)
-        if phases:
-            hip.record(ev_p[2], sptr)
-        if serial:
             ltc.crc32_raw(blob_ptrs, bsz, CRC_CHUNK, crc_ptrs)
+            hip.record(ev_x[1], sptr)
         else:
             hip.wait(sptr, ev_join)
-        if prof:
-            hip.record(ev_x[1], sptr)
-        if phases:
-            hip.record(ev_p[3], sptr)
 
     for _ in range(max(1, args.warmup)):
         step(args.isolated)
@@ -466,23 +454,24 @@ def main():
     wall = time.time() - t_wall
     ms_step = hip.ms(start_ev[0], start_ev[1]) / args.steps
 
-    # phase times of the same steps, with events between the three calls
+    # phase times: each call repeated back to back between two events, as
+    # the timed steps run (so the host's enqueue time stays hidden)
     reps = max(3, min(args.steps, 10))
-    ph = [0.0, 0.0, 0.0]
-    for _ in range(reps):
-        step(args.isolated, phases=True)
-        torch.cuda.synchronize()
-        for i in range(3):
-            ph[i] += hip.ms(ev_p[i], ev_p[i + 1]) / reps
-    t_comp, t_dec, t_crc = ph
-    # compress_with_crc32 alone (the fused path's first call)
-    t_fused = 0.0
-    for _ in range(reps):
+
+    def timed(fn):
         hip.record(ev_p[0], sptr)
-        compress_crc()
+        for _ in range(reps):
+            fn()
         hip.record(ev_p[1], sptr)
         torch.cuda.synchronize()
-        t_fused += hip.ms(ev_p[0], ev_p[1]) / reps
+        return hip.ms(ev_p[0], ev_p[1]) / reps
+
+    t_comp = timed(lambda: compress_plain(ev_c if args.isolated else None))
+    t_dec = timed(lambda: ltc.decompress_raw(headers, blob_ptrs, bsz, out_ptrs, nbytes, status.data_ptr(),
+                                             events=ev_d if args.isolated else None))
+    t_crc = timed(lambda: ltc.crc32_raw(blob_ptrs, bsz, CRC_CHUNK, crc_ptrs))
+    # compress_with_crc32 alone (the fused path's first call)
+    t_fused = timed(lambda: compress_crc())
 
     # per-kernel durations (same work, events between the kernels)
     k = {"k_hist": 0.0, "k_encode": 0.0, "k_scan": 0.0, "k_pack": 0.0, "k_decode": 0.0,
