@@ -133,7 +133,8 @@ struct DTable {
   uint32_t n_full;
   uint32_t vec16;       // every dst 16-byte aligned and chunk_bytes % 16 == 0
   uint64_t total_chunks;
-  uint64_t c_begin;     // a launch decodes global chunks [c_begin, c_begin + grid)
+  uint64_t c_begin;     // a launch decodes global chunks [c_begin, c_end)
+  uint64_t c_end;
   uint32_t delta;       // every job is a delta blob with its base
   uint8_t* zbuf;        // deltas: zstride bytes per global stream, ZRUN streams expanded
   uint32_t zstride;     // align16(n_full): a stream's 8-byte reads stay in its slot
