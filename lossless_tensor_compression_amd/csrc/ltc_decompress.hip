@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
   __shared__ __attribute__((aligned(16))) uint16_t ring_w[kDecWaves][MAXR][kDecRing];
   // decoded symbols of a block: dword 64*(q/4) + l holds steps q..q+3 of lane l
   __shared__ __attribute__((aligned(16))) uint32_t stage_w[kDecWaves][MAXR][128];
-  const uint32_t wslot = threadIdx.x / 64;
+  const uint32_t wslot = kDecWaves > 1 ? threadIdx.x / 64 : 0u;
   auto& lut = lut_w[wslot];
   auto& symt = symt_w[wslot];
   auto& ring = ring_w[wslot];
