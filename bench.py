@@ -545,8 +545,7 @@ def main():
                           else "own kernel beside decompress",
                    "format": "v2, one table per stream index" if shared else "v1, a table per coded stream",
                    "launch": "kernel by kernel, one stream" if args.isolated
-                             else ("compress_with_crc32 on one stream" if fused else
-                                   "compress in 2 chunk groups on 2 streams")},
+                             else "compress in 2 chunk groups on 2 streams"},
         "decompress_gbs": round(N / (t_dec * 1e-3) / 1e9, 2),
         "compress_gbs": round(N / (t_comp * 1e-3) / 1e9, 2),
         "crc32_blob_gbs": round(B / (t_crc * 1e-3) / 1e9, 2),

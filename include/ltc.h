@@ -26,8 +26,8 @@
  * launch failure returns LTC_ERR_HIP.  Calls on different streams are
  * independent.
  *
- * PIPELINED COMPRESSION.  A compress call without checksums over 512 chunks
- * or more (all tensors of a batch together) splits its chunks into two
+ * PIPELINED COMPRESSION.  A compress call over 512 chunks or more (all
+ * tensors of a batch together) splits its chunks into two
  * chunk-ordered groups: the first runs on `stream`, the second on an internal
  * stream that waits for `stream` at the call and that `stream` waits for
  * before anything enqueued after the call, so the call still behaves as work

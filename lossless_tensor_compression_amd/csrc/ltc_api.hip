@@ -26,9 +26,8 @@ constexpr uint32_t kWordsGranule = 1024;
 // (default priority, non-blocking) and events are created once per device on
 // first use and kept until the process ends; the enqueue is serialised.
 // Measured on 28 BF16 tensors (13,312 chunks): 2 groups 1.50 ms, 4 groups
-// 1.56 ms, one stream 1.60 ms.  With the checksums computed in k_pack the
-// call runs on one stream (1.63 ms, against 1.67 with 4 groups and 1.69 with
-// 2): the groups' persistent pack grids then compete.
+// 1.56 ms, one stream 1.60 ms; with the checksums computed in k_pack, 2
+// groups 1.60 ms against 1.66 on one stream.
 constexpr int kPipeGroups = 2;
 constexpr uint64_t kPipeMinChunks = 512;
 
@@ -75,9 +74,8 @@ PipeRes* pipe_res(hipStream_t stream) {
   return g_pipe[dev]->ok ? g_pipe[dev] : nullptr;
 }
 
-// all chunks on one stream, or groups as above (pipeline = false: one stream)
-hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipEvent_t* ev,
-                        bool pipeline = true) {
+// all chunks on one stream, or groups as above
+hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipEvent_t* ev) {
   const uint64_t total = t.total_chunks;
   t.c_begin = 0;
   t.c_end = total;
@@ -88,7 +86,7 @@ hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipE
     const hipError_t err = launch_v2_tables(t, w, stream, ev);
     if (err != hipSuccess) return err;
   }
-  if (ev || !pipeline || total < kPipeMinChunks) return launch_compress(t, w, stream, ev, nullptr, nullptr, staged);
+  if (ev || total < kPipeMinChunks) return launch_compress(t, w, stream, ev, nullptr, nullptr, staged);
   std::lock_guard<std::mutex> lock(g_pipe_mu);
   PipeRes* r = pipe_res(stream);
   if (!r) return launch_compress(t, w, stream, nullptr, nullptr, nullptr, staged);
@@ -371,7 +369,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   }
   a.total_chunks = ccur;
   hipError_t err = fused ? launch_zero_u32(frames, fcur, stream) : hipSuccess;
-  if (err == hipSuccess) err = run_compress(t, w, stream, ev, !fused);
+  if (err == hipSuccess) err = run_compress(t, w, stream, ev);
   if (err == hipSuccess) err = fused ? launch_crc32_frames(a, stream) : launch_crc32(a, stream);
   if (ev) record(ev, 5, stream);
   return err == hipSuccess ? LTC_OK : LTC_ERR_HIP;

@@ -7,8 +7,8 @@ Checksum chunk sizes cover both ways the library computes them: multiples of
 1 KiB up to 1 MiB (the payload is checksummed while k_pack writes it, in
 1 KiB frames) and all other sizes (the blob is read back).  Inputs put
 payload borders inside frames, several RAW streams at different positions
-within their frames, frames shared by many chunks of a large call, empty and
-one-element tensors, and blobs whose last checksum chunk is short.
+within their frames, frames shared by the chunk groups of a pipelined call,
+empty and one-element tensors, and blobs whose last checksum chunk is short.
 """
 import zlib
 
@@ -106,9 +106,8 @@ def test_small_and_ragged(ltc, dtype, nelem, chunk):
 
 @pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (0, 2048)])
 def test_grouped_call(ltc, dtype, chunk):
-    """Over 512 chunks (where plain compression splits into chunk groups on
-    two streams; a checksummed call stays on one): frames shared by
-    neighbouring chunks' payloads; every 5th chunk is random bytes."""
+    """Over 512 chunks: two chunk groups on two streams add into frames that
+    straddle the group border; every 5th chunk is random bytes."""
     rng = np.random.default_rng(300 + dtype)
     nbytes = 700 * chunk + 24
     if dtype == 0:
