@@ -791,7 +791,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     const uint32_t xn = mul_u24(q1 >> sh, e.z) + (xo >> sh) + e.w;
     x[u] = active ? xn : xo;
     top[u] = uniform(top[u] - (uint32_t)__popcll(mask));
-    const uint32_t slot = (top[u] + lanes_below(mask)) & (kRingWords - 1);
+    const uint32_t slot = lanes_below_plus(mask, top[u]) & (kRingWords - 1);
     ring[u][need ? slot : kRingWords + lane] = (uint16_t)xo;
   };
 
@@ -1169,7 +1169,7 @@ __device__ void write_zrun(uint8_t* dst, const uint8_t* src, const uint8_t* bsrc
     }
     __syncthreads();
     if (mask) {
-      const uint32_t rank = blk_before + lanes_below(bal);
+      const uint32_t rank = lanes_below_plus(bal, blk_before);
       if (rank < nblk) *reinterpret_cast<uint64_t*>(dst + l2 + 8 * rank) = mask;
       uint32_t o = lit_before + lit_below;
       for (int i = 0; i < 64; ++i) {

@@ -410,7 +410,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
     const uint32_t xd = __umul24(e & 0xFFFFu, xs >> 12) + sl - (e >> 16);
     const bool need = active && xd < kRansLow;
     const uint64_t mask = ballot(need);
-    uint32_t wv = ring[rr][(pos[rr] + lanes_below(mask)) & (kDecRing - 1)];
+    uint32_t wv = ring[rr][lanes_below_plus(mask, pos[rr]) & (kDecRing - 1)];
     asm volatile("" : "+v"(wv));  // keep the read unconditional (no exec branch)
     const uint32_t xn = need ? (xd << 16) | wv : xd;
     x[rr] = active ? xn : xs;
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(256) void k_zrun_expand(DTable t) {
       if (q < wave) blk_before += red[q];
       blk_round += red[q];
     }
-    const uint32_t rank = blk_before + lanes_below(bal);
+    const uint32_t rank = lanes_below_plus(bal, blk_before);
     uint64_t mask = 0;
     if (set) {
       if (rank < nblk) mask = *reinterpret_cast<const uint64_t*>(l2p + 8 * rank);
