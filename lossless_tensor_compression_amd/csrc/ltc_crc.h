@@ -85,6 +85,34 @@ __device__ __forceinline__ uint32_t crc_step16(const CrcLdsT<L>& s, uint32_t c, 
   return c;
 }
 
+// Slicing-by-16: th[m][b] is the register after byte b and 8 + m zero
+// bytes, so with t8 a 16-byte unit takes one round of 16 independent
+// lookups instead of two rounds of 8.  Every thread of the workgroup calls
+// the builder (after crc_build_tables); it ends with a workgroup barrier.
+template <int L>
+__device__ __forceinline__ void crc_build_th(const CrcLdsT<L>& s, uint32_t (*th)[256], uint32_t tid,
+                                             uint32_t nthreads) {
+  for (uint32_t b = tid; b < 256; b += nthreads) {
+    uint32_t c = s.t8[7][b];
+    for (int m = 0; m < 8; ++m) {
+      for (int k = 0; k < 8; ++k) c = (c >> 1) ^ (kPoly & (0u - (c & 1u)));
+      th[m][b] = c;
+    }
+  }
+  __syncthreads();
+}
+
+template <int L>
+__device__ __forceinline__ uint32_t crc_step16x(const CrcLdsT<L>& s, const uint32_t (*th)[256], uint32_t c,
+                                                const uint4 q) {
+  c ^= q.x;
+  return th[7][c & 0xFFu] ^ th[6][(c >> 8) & 0xFFu] ^ th[5][(c >> 16) & 0xFFu] ^ th[4][c >> 24] ^
+         th[3][q.y & 0xFFu] ^ th[2][(q.y >> 8) & 0xFFu] ^ th[1][(q.y >> 16) & 0xFFu] ^ th[0][q.y >> 24] ^
+         s.t8[7][q.z & 0xFFu] ^ s.t8[6][(q.z >> 8) & 0xFFu] ^ s.t8[5][(q.z >> 16) & 0xFFu] ^
+         s.t8[4][q.z >> 24] ^ s.t8[3][q.w & 0xFFu] ^ s.t8[2][(q.w >> 8) & 0xFFu] ^
+         s.t8[1][(q.w >> 16) & 0xFFu] ^ s.t8[0][q.w >> 24];
+}
+
 template <int L>
 __device__ __forceinline__ uint32_t crc_step1(const CrcLdsT<L>& s, uint32_t c, uint32_t byte) {
   return s.t8[0][(c ^ byte) & 0xFFu] ^ (c >> 8);

@@ -4,7 +4,7 @@
 // zlib CRC-32 of every checksum_chunk_bytes-byte chunk, the last one
 // possibly shorter.  One wave per chunk: the chunk is split into 64 lane
 // segments, each lane runs a table-driven CRC over its segment with the
-// register starting at zero (slicing-by-8 with eight 256-entry tables in LDS;
+// register starting at zero (slicing-by-16 with sixteen 256-entry tables in LDS;
 // Kounavis & Berry, "A Systematic Approach to Building High Performance
 // Software-based CRC Generators", 2005), and the 64 partial remainders are
 // combined in a 6-level tree whose level l multiplies the left partial by
@@ -30,8 +30,10 @@ constexpr int kCrcThreads = 256;
 template <bool DEVLEN>
 __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
   __shared__ CrcLds s;
+  __shared__ uint32_t th[8][256];
   const uint32_t tid = threadIdx.x;
   crc_build_tables(s, a.lvl, tid, kCrcThreads);
+  crc_build_th(s, th, tid, kCrcThreads);
 
   const uint32_t lane = lane_id(), wave = tid / 64;
   const uint64_t frame = 64 * a.seg;
@@ -67,9 +69,9 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) q[u] = reinterpret_cast<const uint4*>(p)[u];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) crc = crc_step16(s, crc, q[u]);
+      for (int u = 0; u < 16; ++u) crc = crc_step16x(s, th, crc, q[u]);
     }
-    for (; p + 16 <= end; p += 16) crc = crc_step16(s, crc, *reinterpret_cast<const uint4*>(p));
+    for (; p + 16 <= end; p += 16) crc = crc_step16x(s, th, crc, *reinterpret_cast<const uint4*>(p));
     for (; p < end; ++p) crc = crc_step1(s, crc, *p);
     crc = crc_tree64(s, crc, lane);
     if (lane == 0) job.out[i] = crc ^ 0xFFFFFFFFu;

@@ -152,6 +152,20 @@ def test_crc32_matches_zlib(ltc, n, k):
         assert got == want
 
 
+def test_crc32_frame_edges(ltc):
+    """Chunks whose first bytes sit at the end of a 1 KiB frame of memory (the
+    preset's four bytes then cross into the next frame), chunks of 4..17
+    bytes, and buffers ending anywhere in a frame."""
+    rng = np.random.default_rng(17)
+    data = rng.integers(0, 256, 70000, dtype=np.uint8)
+    d = torch.from_numpy(data).cuda()
+    for start in (509, 510, 511, 1021, 1022, 1023, 1024, 2045):
+        for n, k in ((40000, 16384), (3000, 1024), (5000, 1021), (200, 4), (300, 17), (1030, 1027)):
+            got = ltc.crc32_chunks(d[start:start + n], k).cpu().numpy().view(np.uint32).tolist()
+            seg = data[start:start + n]
+            assert got == [zlib.crc32(seg[i:i + k].tobytes()) for i in range(0, n, k)], (start, n, k)
+
+
 def test_crc32_check_value(ltc):
     d = torch.frombuffer(bytearray(b"123456789"), dtype=torch.uint8).cuda()
     assert ltc.crc32_chunks(d, 16384).cpu().numpy().view(np.uint32).tolist() == [0xCBF43926]
