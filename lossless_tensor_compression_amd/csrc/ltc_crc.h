@@ -138,19 +138,4 @@ __device__ __forceinline__ uint32_t crc_tree64(const CrcLdsT<L>& s, uint32_t c, 
   return c;
 }
 
-// the same for two independent sets of segments at once
-template <int L>
-__device__ __forceinline__ void crc_tree64x2(const CrcLdsT<L>& s, uint32_t& a, uint32_t& b,
-                                             uint32_t lane) {
-#pragma unroll
-  for (int l = 0; l < kCrcLevels; ++l) {
-    const uint32_t ra = __shfl_down(a, 1u << l, 64);
-    const uint32_t rb = __shfl_down(b, 1u << l, 64);
-    if ((lane & ((2u << l) - 1u)) == 0) {
-      a = crc_mul_level(s, l, a) ^ ra;
-      b = crc_mul_level(s, l, b) ^ rb;
-    }
-  }
-}
-
 }  // namespace ltc

@@ -44,18 +44,6 @@ template <int DT> __device__ __forceinline__ uint32_t reorder(uint32_t x) {
   }
 }
 
-template <int DT> __device__ __forceinline__ uint32_t unreorder(uint32_t y) {
-  constexpr int E = Dt<DT>::E, WM = Dt<DT>::WM;
-  if constexpr (WM < 0) {
-    return y;
-  } else {
-    constexpr int W = 8 * E, WE = W - 1 - WM;
-    const uint32_t e = (y >> (WM + 1)) & ((1u << WE) - 1u);
-    const uint32_t s = (y >> WM) & 1u;
-    return (s << (W - 1)) | (e << WM) | (y & ((1u << WM) - 1u));
-  }
-}
-
 // ---------------------------------------------------------------- jobs
 // A launch covers up to kMaxJobs tensors of one dtype and chunk size; the
 // table travels as a kernel argument.
