@@ -446,11 +446,12 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
     }
     __syncthreads();
   }
+  __shared__ uint32_t modes[E];
   if (wave < (uint32_t)E) {
     const uint64_t s = g * E + wave;
     const uint32_t pmax = last ? job.pmax_tail : job.pmax_full;
-    const uint32_t mode = normalize_stream(hf + 256 * wave, n, pmax, s, w,
-                                           t.v2 ? w.plane + ((uint64_t)j * E + wave) * 256 : nullptr);
+    uint32_t mode = normalize_stream(hf + 256 * wave, n, pmax, s, w,
+                                     t.v2 ? w.plane + ((uint64_t)j * E + wave) * 256 : nullptr);
     if constexpr (DELTA) {
       if (lane == 0) {
         // ZipNN's rule makes ZRUN a candidate; k_encode weighs it against
@@ -461,10 +462,26 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
         w.zinfo[s] = make_uint2(nzb, nnz | (rule ? 0x80000000u : 0u));
         if (mode == LTC_MODE_RAW && rule) {
           const uint32_t pz = zrun_bytes(n, nzb, nnz);
-          if (pz <= pmax)
+          if (pz <= pmax) {
             *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(pz, pack_info(LTC_MODE_ZRUN, 0, 0, 0), nzb, nnz);
+            mode = LTC_MODE_ZRUN;
+          }
         }
       }
+    }
+    if (lane == 0) modes[wave] = mode;
+  }
+  // A coded top byte stages the chunk's RAW streams (see k_encode): its
+  // record's third word carries their mask.  The wave that wrote the record
+  // adds it, so the two stores keep their order.
+  if constexpr (E > 1) {
+    __syncthreads();
+    if (!t.v2 && wave == (uint32_t)(E - 1) && lane == 0 && modes[E - 1] == kModeCand) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int k = 0; k < E - 1; ++k)
+        if (modes[k] == LTC_MODE_RAW) m |= 1u << k;
+      if (m) w.sinfo[4 * (g * E + E - 1) + 2] = m;
     }
   }
 }
@@ -617,6 +634,35 @@ __device__ __forceinline__ uint32_t stream_byte(uint32_t x, uint32_t k) {
   else return (reorder<DT>(x) >> (8 * k)) & 0xFFu;
 }
 
+// Byte j of the reordered form of 8 consecutive elements held as loaded (8*E
+// bytes, little-endian), packed in element order.  BF16's byte 0 is the low 7
+// mantissa bits under the sign: two byte gathers and one bit-field select
+// per 4 elements.
+template <int DT> __device__ __forceinline__ uint2 stream_bytes8(const uint32_t* pf, int j) {
+  constexpr int E = Dt<DT>::E;
+  if constexpr (DT == LTC_BF16) {
+    // v_perm_b32 selector bytes 0-3 pick bytes of the second operand, 4-7
+    // of the first: low and high bytes of the four half-words
+    auto four = [](uint32_t w0, uint32_t w1) {
+      const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x06040200u);
+      const uint32_t b = __builtin_amdgcn_perm(w1, w0, 0x07050301u);
+      return (a & 0x7F7F7F7Fu) | (b & 0x80808080u);
+    };
+    return make_uint2(four(pf[0], pf[1]), four(pf[2], pf[3]));
+  } else {
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t x;
+      if constexpr (E == 4) x = pf[i];
+      else if constexpr (E == 2) x = (pf[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+      else x = (pf[i / 4] >> (8 * (i & 3))) & 0xFFu;
+      o[i / 4] |= ((reorder<DT>(x) >> (8 * j)) & 0xFFu) << (8 * (i & 3));
+    }
+    return make_uint2(o[0], o[1]);
+  }
+}
+
 // One wave codes stream k of two neighbouring chunks, interleaving their
 // independent state chains (instruction-level parallelism for a loop whose
 // every step is a dependent chain).
@@ -642,6 +688,15 @@ __device__ __forceinline__ uint32_t stream_byte(uint32_t x, uint32_t k) {
 // Abort and drain checks run every 4 steps: 4 steps emit at most 256 words,
 // so a block is never overwritten before it drains, and an abort is seen
 // before any word past the stream's limit reaches the workspace.
+//
+// Staging.  The wave coding a chunk's top byte loads every byte of its
+// elements, so it also writes the chunk's RAW streams (those k_hist decided,
+// named in its record's third word), in blob order, into their own
+// workspace slots, which nothing else uses; k_pack then copies them instead
+// of regrouping the input again.  Only whole chunks of full 8-step blocks
+// coded in lock step are staged, and a stream is marked staged (fourth word
+// of its record) once every block is written and the top stream was not
+// abandoned.
 template <int DT, bool DELTA>
 __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
@@ -662,7 +717,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
 
   bool on[U];
   uint64_t sid[U];
-  uint32_t n[U], full[U], wlimit[U], wo[U], lo[U], hi[U];
+  uint32_t n[U], full[U], wlimit[U], wo[U], lo[U], hi[U], smask[U];
   const uint8_t* src[U];
   const uint8_t* bsrc[U];
   const uint16_t* ftab[U];
@@ -671,7 +726,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   for (int u = 0; u < U; ++u) {
     on[u] = false;
     sid[u] = 0;
-    n[u] = full[u] = wlimit[u] = wo[u] = lo[u] = hi[u] = 0;
+    n[u] = full[u] = wlimit[u] = wo[u] = lo[u] = hi[u] = smask[u] = 0;
     src[u] = nullptr;
     bsrc[u] = nullptr;
     ftab[u] = nullptr;
@@ -691,6 +746,8 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     full[u] = n[u] / 64;
     lo[u] = (info >> 16) & 0xFFu;
     hi[u] = info >> 24;
+    if (E > 1 && k == (uint32_t)(E - 1) && n[u] % (64u * kEncBlock) == 0 && n[u] <= 2u * wcap)
+      smask[u] = w.sinfo[4 * s + 2];
     // v2: the plane's table and no table in the payload
     wo[u] = t.v2 ? kRansFixed : (uint32_t)align16(kRansFixed + 2u * (hi[u] - lo[u] + 1u));
     ftab[u] = t.v2 ? w.ptab + ((uint64_t)j * E + k) * 256 : w.freq + 256 * s;
@@ -891,15 +948,38 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     auto entry_at = [&](int u, uint32_t off) {
       return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(tab[u]) + off);
     };
+    // RAW stream bytes of the block in pf, taken when it is staged and
+    // stored after the next block's loads are issued
+    uint2 rw[U][E > 1 ? E - 1 : 1];
+    auto raw_take = [&]() {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < E - 1; ++j)
+          if (smask[u] & (1u << j)) rw[u][j] = stream_bytes8<DT>(pf[u], j);
+    };
+    auto raw_put = [&](uint32_t bi) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < E - 1; ++j)
+          if (smask[u] & (1u << j)) {  // a uniform block address and a lane offset
+            uint8_t* blk = reinterpret_cast<uint8_t*>(w.words + (sid[u] - k + j) * wcap) +
+                           64u * (full[u] - kEncBlock * (bi + 1));
+            *reinterpret_cast<uint2*>(blk + 8u * lane) = rw[u][j];
+          }
+    };
     if (nfb > 0) {
       uint32_t sy[U][kEncBlock], sn[U][kEncBlock];
       uint4 ta[U][4], tb[U][4];
 #pragma unroll
       for (int u = 0; u < U; ++u) fetch(u, 0);
       stage();
+      raw_take();
       read_offsets(sy);
 #pragma unroll
       for (int u = 0; u < U; ++u) fetch(u, nfb > 1 ? 1u : 0u);
+      raw_put(0);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -918,10 +998,12 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
         // drain check comes after, so its stores are a half-block old by the
         // time the next staging waits on the loads (one counter covers both)
         stage();
+        raw_take();
         read_offsets(sn);
         const uint32_t nxt = bi + 2 < nfb ? bi + 2 : nfb - 1;
 #pragma unroll
         for (int u = 0; u < U; ++u) fetch(u, nxt);
+        if (bi + 1 < nfb) raw_put(bi + 1);
 #pragma unroll
         for (int u = 0; u < U; ++u)
           if (on[u]) check(u);
@@ -966,6 +1048,8 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
       if (!on[u]) continue;
       const uint32_t nw = wcap - top[u];
       if (top[u] < ftop[u] + kFlushWords) flush(u);  // the last, partial block
+      if (smask[u] && done == full[u] && lane < (uint32_t)(E - 1) && (smask[u] & (1u << lane)))
+        w.sinfo[4 * (sid[u] - k + lane) + 3] = kRawStaged;
       w.states[64 * sid[u] + lane] = x[u];
       if (lane == 0)
         *reinterpret_cast<uint4*>(w.sinfo + 4 * sid[u]) =
@@ -1359,7 +1443,9 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
       split_frames(cr, (uint32_t)(a & 63), a >> 6, job.frames, pos, lane);
     }
   }
-  uint32_t rawmask = 0;
+  // RAW streams: copied from their workspace slots when k_encode staged
+  // them (stmask), else regrouped from the input
+  uint32_t rawmask = 0, stmask = 0;
   uint64_t raw_off[E];
 #pragma unroll
   for (int k = 0; k < E; ++k) {
@@ -1367,7 +1453,10 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
     const uint4 si = *reinterpret_cast<const uint4*>(w.sinfo + 4 * s);
     const uint32_t mode = si.y & 0xFFu;
     raw_off[k] = w.offsets[s];
-    if (mode == LTC_MODE_RAW) rawmask |= 1u << k;
+    if (mode == LTC_MODE_RAW) {
+      rawmask |= 1u << k;
+      if (si.w == kRawStaged) stmask |= 1u << k;
+    }
     else if (mode == LTC_MODE_RANS)
       write_rans<CRC>(blob, raw_off[k], s, si.y, si.x, si.z, t, w, job.frames, L, pos);
     else if (DELTA && mode == LTC_MODE_ZRUN)
@@ -1376,15 +1465,22 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
   }
   if (!rawmask) return;
   const uint32_t units = (n + 15) / 16;
+  const bool regroup = (rawmask & ~stmask) != 0;
+  // unit u of RAW stream k; y: the regrouped elements when not staged
+  auto raw_unit = [&](int k, uint32_t u, const uint32_t* y) -> uint4 {
+    if (stmask & (1u << k))
+      return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(w.words + (s0 + k) * t.wcap) + 16 * u);
+    return make_uint4(pack4(y, k), pack4(y + 4, k), pack4(y + 8, k), pack4(y + 12, k));
+  };
   if constexpr (!CRC) {
     for (uint32_t u = tid; u < units; u += kPackThreads) {
       uint32_t y[16];
-      load16<DT, DELTA>(src, 16 * u, n, t.vec16 != 0, y, DELTA ? job.base + c * t.chunk_bytes : nullptr);
+      if (regroup)
+        load16<DT, DELTA>(src, 16 * u, n, t.vec16 != 0, y, DELTA ? job.base + c * t.chunk_bytes : nullptr);
 #pragma unroll
       for (int k = 0; k < E; ++k) {
         if (!(rawmask & (1u << k))) continue;
-        const uint4 v = make_uint4(pack4(y, k), pack4(y + 4, k), pack4(y + 8, k), pack4(y + 12, k));
-        *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = v;
+        *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = raw_unit(k, u, y);
       }
     }
   } else {
@@ -1399,18 +1495,37 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
     FrameRun r[E];
 #pragma unroll
     for (int k = 0; k < E; ++k) r[k] = FrameRun{0, 0, 0, false};
+    // With one or two streams, staged units load a frame ahead, so a load
+    // is in flight while the current frame is checksummed (FP32's three
+    // would not fit the 128 registers of 4 workgroups per CU).
+    constexpr bool kAhead = E <= 2;
+    uint4 nv[E];
+    auto load_staged = [&](uint64_t f) {
+      const uint64_t ua = 64 * f + lane;
+      const bool have = ua >= a0 && ua < a0 + units;
+#pragma unroll
+      for (int k = 0; k < E; ++k)
+        if (stmask & (1u << k)) nv[k] = have ? raw_unit(k, (uint32_t)(ua - a0), nullptr) : make_uint4(0, 0, 0, 0);
+    };
+    if (kAhead && fb < fe) load_staged(fb);
     for (uint64_t f = fb; f < fe; ++f) {
       const uint64_t ua = 64 * f + lane;
       const bool have = ua >= a0 && ua < a0 + units;
       const uint32_t u = (uint32_t)(ua - a0);
+      uint4 cv[E];
+      if constexpr (kAhead) {
+#pragma unroll
+        for (int k = 0; k < E; ++k) cv[k] = nv[k];
+        if (f + 1 < fe) load_staged(f + 1);
+      }
       uint32_t y[16];
-      if (have) load16<DT>(src, 16 * u, n, t.vec16 != 0, y);
+      if (have && regroup) load16<DT>(src, 16 * u, n, t.vec16 != 0, y);
 #pragma unroll
       for (int k = 0; k < E; ++k) {
         if (!(rawmask & (1u << k))) continue;
         uint32_t cr = 0;
         if (have) {
-          const uint4 v = make_uint4(pack4(y, k), pack4(y + 4, k), pack4(y + 8, k), pack4(y + 12, k));
+          const uint4 v = (kAhead && (stmask & (1u << k))) ? cv[k] : raw_unit(k, u, y);
           *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = v;
           cr = crc_step16(L.c, 0u, v);
         }
@@ -1431,7 +1546,8 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
 // 1024 workgroups that builds them once each, and it lets checksummed calls
 // use the pipelined groups.
 template <int DT, bool CRC, bool DELTA>
-__global__ __launch_bounds__(CRC ? kPackCrcThreads : kPackThreads) void k_pack(CTable t, CWork w) {
+__global__ __launch_bounds__(CRC ? kPackCrcThreads : kPackThreads)
+__attribute__((amdgpu_waves_per_eu(CRC ? 4 : 1))) void k_pack(CTable t, CWork w) {
   __shared__ uint32_t red[8];  // ZRUN: per-wave counts
   __shared__ PackLds<CRC> lds;
   uint32_t pos = 0;

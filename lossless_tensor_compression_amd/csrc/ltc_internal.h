@@ -19,6 +19,7 @@ constexpr uint32_t kHeader = 64;
 constexpr uint32_t kDirEntry = 16;
 constexpr uint32_t kRansFixed = 272;    // 16-byte prefix + 64 u32 states
 constexpr uint32_t kModeCand = 0xFF;    // internal: histogram done, encode pending (no blob mode)
+constexpr uint32_t kRawStaged = 1;      // internal: a RAW stream's bytes wait in its workspace slot
 constexpr int kMaxJobs = LTC_BATCH_MAX;
 
 __host__ __device__ constexpr uint64_t align16(uint64_t v) { return (v + 15) & ~uint64_t(15); }

@@ -273,6 +273,47 @@ def test_mixed_stream_pairs(ltc, nchunks):
     check_case(ltc, data[: data.size // 4 * 4], 3, chunk, label=f"mixed pairs fp32 {nchunks}")
 
 
+
+def _abandon_mix(dtype, bits, chunk, rng):
+    """Chunks whose sign/mantissa bytes are uniform (RAW by the size bound)
+    and whose exponent bytes are uniform over 2**bits values: 5 bits code
+    well, 7 bits pass the bound but code above P_max, so the encoder
+    abandons the exponent stream part way."""
+    e_bytes = oracle.ELEM_BYTES[dtype]
+    n = chunk // e_bytes
+    parts = []
+    for b in bits:
+        e = rng.integers(0, 1 << b, n) + 40
+        if dtype == 1:
+            low = rng.integers(0, 256, n)
+            parts.append((((low >> 7) << 15) | (e << 7) | (low & 0x7F)).astype(np.uint16))
+        else:
+            m = rng.integers(0, 1 << 24, n)
+            parts.append((((m >> 23) << 31) | (e << 23) | (m & 0x7FFFFF)).astype(np.uint32))
+    return np.concatenate(parts)
+
+
+@pytest.mark.parametrize("dtype", [1, 3])
+@pytest.mark.parametrize("thr", [0.88, 0.95])
+def test_staged_raw_streams_with_abandoned_neighbours(ltc, dtype, thr):
+    """The wave coding a chunk's exponent stream also writes the chunk's RAW
+    streams to the workspace for packing; a chunk whose exponent stream is
+    abandoned part way, or whose partner's is, packs its RAW streams from
+    the input instead.  At threshold 0.88 the 7-bit chunks are abandoned, so
+    the chunk pairs cover both abandoned, both coded, and one of each in
+    either order (the odd last chunk has no partner); at 0.95 every exponent
+    stream is coded.  Blobs must equal the oracle's."""
+    rng = np.random.default_rng(31 + dtype)
+    x = _abandon_mix(dtype, [7, 7, 5, 5, 7, 5, 5, 7, 5], 131072, rng)
+    want = check_case(ltc, x, dtype, 131072, thr, label="abandoned exponent streams")
+    e = oracle.ELEM_BYTES[dtype]
+    nch = int(want[20:24].view(np.uint32)[0])
+    modes = want[64:64 + 16 * nch * e].reshape(nch, e, 16)[:, :, 12]
+    assert (modes[:, : e - 1] == 0).all()  # RAW
+    top = [0, 0, 1, 1, 0, 1, 1, 0, 1] if thr < 0.9 else [1] * 9  # RAW after abandoning, or RANS
+    assert modes[:, e - 1].tolist() == top
+
+
 # ---- pipelined compression: calls over 512 chunks or more run in four
 # chunk-ordered groups on several streams; blobs must not change.
 
