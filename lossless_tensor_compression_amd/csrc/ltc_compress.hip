@@ -11,11 +11,14 @@
 //             double multiply, words staged in an LDS ring and drained 512
 //             bytes at a time to the workspace in decoder order; aborts to
 //             RAW as soon as the payload can no longer beat the threshold.
+//             The wave coding a top byte also copies the chunk's RAW streams
+//             into their workspace slots.
 //   k_scan    one workgroup per tensor: exclusive scan of the 16-byte-aligned
 //             payload sizes into offsets; writes the 64-byte header.
-//   k_pack    one workgroup per chunk: directory entries, RANS payloads from
-//             the workspace, RAW streams regrouped from the input; every byte
-//             of the blob, padding included, is written exactly once.
+//   k_pack    one workgroup per chunk: directory entries, RANS payloads and
+//             staged RAW streams from the workspace, other RAW streams
+//             regrouped from the input; every byte of the blob, padding
+//             included, is written exactly once.
 // Method: "NOTE-241: ZipNN", Method items 1-3 and 5; chunk size and
 // passthrough rule: cuZipNN 0.1.0, API; interleaved rANS lanes and a table per
 // stream: lmz README, "On a GPU" and "Building on lmz".
