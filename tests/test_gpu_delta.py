@@ -142,6 +142,29 @@ def test_oracle_cases_both_coders(ltc):
         assert set(_modes(blob).tolist()) == {oracle.MODE_ZRUN, oracle.MODE_CONST, oracle.MODE_RANS}
 
 
+@pytest.mark.parametrize("dtype", [1, 3])
+def test_staged_raw_xor_streams(ltc, dtype):
+    """Every mantissa bit changes at random while 30% of the exponents move by
+    one: the XOR's mantissa streams are RAW and its exponent stream is coded,
+    so the encoder stages the RAW XOR bytes for packing (all chunk pairs but
+    the odd last chunk).  Blobs must equal the oracle's."""
+    rng = np.random.default_rng(40 + dtype)
+    e = oracle.ELEM_BYTES[dtype]
+    n = 9 * 131072 // e
+    _, base = _pair(dtype, n, "identical", rng)
+    wm = 7 if dtype == 1 else 23  # mantissa width
+    mant = rng.integers(0, 1 << wm, n, dtype=np.uint64)
+    sign = rng.integers(0, 2, n, dtype=np.uint64) << (8 * e - 1)
+    bump = (rng.random(n) < 0.3).astype(np.uint64) << wm  # exponent +1 (a carry into it)
+    b64 = base.astype(np.uint64)
+    src = (((b64 & ~np.uint64((1 << wm) - 1)) + bump) ^ sign | mant) & np.uint64((1 << (8 * e)) - 1)
+    src = src.astype(base.dtype)
+    blob = check_delta(ltc, src, base, dtype, label="staged RAW XOR streams")
+    modes = _modes(blob).reshape(-1, e)
+    assert (modes[:, : e - 1] == oracle.MODE_RAW).all()
+    assert (modes[:, e - 1] == oracle.MODE_RANS).all()
+
+
 @pytest.mark.parametrize("dtype,chunk,shared", [(1, 4096, False), (1, 4096, True), (3, 1024, False),
                                                 (0, 2048, True)])
 def test_grouped(ltc, dtype, chunk, shared):
