@@ -1051,6 +1051,8 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
       if (!on[u]) continue;
       const uint32_t nw = wcap - top[u];
       if (top[u] < ftop[u] + kFlushWords) flush(u);  // the last, partial block
+      // the fast loop staged every block and the stream was kept: lane j
+      // marks RAW stream j of the chunk staged
       if (smask[u] && done == full[u] && lane < (uint32_t)(E - 1) && (smask[u] & (1u << lane)))
         w.sinfo[4 * (sid[u] - k + lane) + 3] = kRawStaged;
       w.states[64 * sid[u] + lane] = x[u];
