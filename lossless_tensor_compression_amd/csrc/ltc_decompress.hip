@@ -418,6 +418,48 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
     sacc[rr] = __builtin_amdgcn_alignbit(v, sacc[rr], 8);  // step q in byte q % 4
     if ((q & 3) == 3) stage[rr][64 * (q >> 2) + lane] = sacc[rr];
   };
+  // the multi-table instantiations run only chunks with 2 or more coded
+  // streams; with two table slots that is exactly 2
+  const int nrun = MAXR == 2 ? 2 : nr;
+  // Step q of every coded stream of a multi-stream chunk (full steps only),
+  // phase by phase: the slot-table reads of all streams, then their symbol
+  // reads, then their state updates and ring reads, so the streams' LDS
+  // latencies overlap instead of adding up.  Same arithmetic as dstep.
+  auto dstep_all = [&](int q) {
+    static_assert(MAXR == 1 || MAXR == 2 || MAXR == 4, "table slots");
+    uint32_t xs[MAXR], sl[MAXR], v[MAXR], e[MAXR], xd[MAXR], wv[MAXR];
+    uint64_t mask[MAXR];
+#pragma unroll
+    for (int rr = 0; rr < MAXR; ++rr) wv[rr] = 0;
+#pragma unroll
+    for (int rr = 0; rr < MAXR; ++rr) {
+      if (rr >= nrun) continue;
+      xs[rr] = x[rr];
+      sl[rr] = xs[rr] & (kTotal - 1);
+      v[rr] = lut[rr][sl[rr]];
+    }
+#pragma unroll
+    for (int rr = 0; rr < MAXR; ++rr)
+      if (rr < nrun) e[rr] = symt[rr][v[rr]];
+#pragma unroll
+    for (int rr = 0; rr < MAXR; ++rr) {
+      if (rr >= nrun) continue;
+      xd[rr] = __umul24(e[rr] & 0xFFFFu, xs[rr] >> 12) + sl[rr] - (e[rr] >> 16);
+      mask[rr] = ballot(xd[rr] < kRansLow);
+      wv[rr] = ring[rr][lanes_below_plus(mask[rr], pos[rr]) & (kDecRing - 1)];
+    }
+    // keep the reads unconditional (one barrier for all streams)
+    if constexpr (MAXR == 2) asm volatile("" : "+v"(wv[0]), "+v"(wv[1]));
+    if constexpr (MAXR == 4) asm volatile("" : "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]));
+#pragma unroll
+    for (int rr = 0; rr < MAXR; ++rr) {
+      if (rr >= nrun) continue;
+      x[rr] = xd[rr] < kRansLow ? (xd[rr] << 16) | wv[rr] : xd[rr];
+      pos[rr] += (uint32_t)__popcll(mask[rr]);
+      sacc[rr] = __builtin_amdgcn_alignbit(v[rr], sacc[rr], 8);
+      if ((q & 3) == 3) stage[rr][64 * (q >> 2) + lane] = sacc[rr];
+    }
+  };
   // a step past the stream's end keeps the byte positions aligned
   auto dskip = [&](int rr, int q) {
     sacc[rr] = sacc[rr] >> 8;
@@ -451,27 +493,38 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
     uint64_t rawn[E];
 #pragma unroll
     for (int k = 0; k < E; ++k) rawn[k] = load_raw8(rbase[k], e0 + 1024, rlim[k]);
+    if (MAXR > 1 && 8 * (b + 1) <= full) {  // several streams, every step full
 #pragma unroll
-    for (int rr = 0; rr < MAXR; ++rr) {
-      if (rr >= nr) continue;
-      if (8 * (b + 1) <= full) {  // every step of the block is full
+      for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+        for (int q = 4 * sb; q < 4 * sb + 4; ++q) dstep_all(q);
 #pragma unroll
-          for (int q = 4 * sb; q < 4 * sb + 4; ++q) dstep(std::false_type{}, rr, q);
-          refill(rr);
-        }
-      } else {
+        for (int rr = 0; rr < MAXR; ++rr)
+          if (rr < nrun) refill(rr);
+      }
+    } else {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+      for (int rr = 0; rr < MAXR; ++rr) {
+        if (rr >= nr) continue;
+        if (8 * (b + 1) <= full) {  // every step of the block is full
 #pragma unroll
-          for (int q = 4 * sb; q < 4 * sb + 4; ++q) {
-            const uint32_t step = 8 * b + q;
-            if (step >= steps) dskip(rr, q);
-            else if (step < full) dstep(std::false_type{}, rr, q);
-            else dstep(std::true_type{}, rr, q);
+          for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int q = 4 * sb; q < 4 * sb + 4; ++q) dstep(std::false_type{}, rr, q);
+            refill(rr);
           }
-          refill(rr);
+        } else {
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int q = 4 * sb; q < 4 * sb + 4; ++q) {
+              const uint32_t step = 8 * b + q;
+              if (step >= steps) dskip(rr, q);
+              else if (step < full) dstep(std::false_type{}, rr, q);
+              else dstep(std::true_type{}, rr, q);
+            }
+            refill(rr);
+          }
         }
       }
     }
