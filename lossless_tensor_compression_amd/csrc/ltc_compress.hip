@@ -713,9 +713,23 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   // interleaving the stream indices would hand every coded stream of a
   // BF16 tensor to half of the XCDs (of an FP32 tensor, to a quarter) while
   // the rest only receive streams that exit at once.
-  const uint32_t pairs = gridDim.x / E;
-  const uint32_t k = (uint32_t)(E - 1) - blockIdx.x / pairs;
-  const uint64_t g0 = t.c_begin + (uint64_t)(blockIdx.x % pairs) * U;
+  // Deltas usually code every stream of a chunk, and each wave reads whole
+  // elements of source and base: there the E workgroups of a chunk pair sit
+  // 8 apart (blocks of 8 pairs), so they reach the same XCD together and walk
+  // the same elements in the same order, and the later reads hit its L2.
+  // The launch rounds the grid up to whole blocks; the spare workgroups find
+  // no chunk and exit.
+  uint32_t k;
+  uint64_t g0;
+  if constexpr (DELTA) {
+    const uint32_t grp = blockIdx.x / (8u * E), r = blockIdx.x % (8u * E);
+    k = (uint32_t)(E - 1) - r / 8u;
+    g0 = t.c_begin + (uint64_t)(grp * 8u + r % 8u) * U;
+  } else {
+    const uint32_t pairs = gridDim.x / E;
+    k = (uint32_t)(E - 1) - blockIdx.x / pairs;
+    g0 = t.c_begin + (uint64_t)(blockIdx.x % pairs) * U;
+  }
   const uint32_t wcap = t.wcap;
 
   bool on[U];
@@ -1578,7 +1592,9 @@ static hipError_t launch_compress_d(const CTable& t, const CWork& w, hipStream_t
     record(ev, 1, st);
   }
   if (chunks)
-    hipLaunchKernelGGL((k_encode<DT, DELTA>), dim3((uint32_t)((chunks + kEncStreams - 1) / kEncStreams * E)),
+    hipLaunchKernelGGL((k_encode<DT, DELTA>),
+                       dim3(DELTA ? (uint32_t)((chunks + 8 * kEncStreams - 1) / (8 * kEncStreams) * 8 * E)
+                                  : (uint32_t)((chunks + kEncStreams - 1) / kEncStreams * E)),
                        dim3(64), 0, st, t, w);
   record(ev, 2, st);
   if (scan_after) (void)hipStreamWaitEvent(st, scan_after, 0);
