@@ -151,6 +151,7 @@ def _flat_bytes(t):
 
 FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
 FLAG_DELTA = 2          # header flag: the blob codes src XOR base
+FLAG_CALLER_STREAM_ONLY = 4  # compress flag: every kernel on the caller's stream
 
 
 def compress_bound(nbytes, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES, shared_tables=False):

@@ -74,8 +74,10 @@ PipeRes* pipe_res(hipStream_t stream) {
   return g_pipe[dev]->ok ? g_pipe[dev] : nullptr;
 }
 
-// all chunks on one stream, or groups as above
-hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipEvent_t* ev) {
+// all chunks on one stream (one_stream, events, or a small call), or groups
+// as above
+hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipEvent_t* ev,
+                        bool one_stream) {
   const uint64_t total = t.total_chunks;
   t.c_begin = 0;
   t.c_end = total;
@@ -86,7 +88,8 @@ hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipE
     const hipError_t err = launch_v2_tables(t, w, stream, ev);
     if (err != hipSuccess) return err;
   }
-  if (ev || total < kPipeMinChunks) return launch_compress(t, w, stream, ev, nullptr, nullptr, staged);
+  if (ev || one_stream || total < kPipeMinChunks)
+    return launch_compress(t, w, stream, ev, nullptr, nullptr, staged);
   std::lock_guard<std::mutex> lock(g_pipe_mu);
   PipeRes* r = pipe_res(stream);
   if (!r) return launch_compress(t, w, stream, nullptr, nullptr, nullptr, staged);
@@ -257,8 +260,9 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
                   uint32_t flags = 0, const void* const* bases = nullptr) {
   if (count < 1 || count > kMaxJobs || !srcs || !nbytes || !blobs || !caps || !d_blob_nbytes)
     return LTC_ERR_INVALID_ARGUMENT;
-  if (flags & ~LTC_FLAG_SHARED_TABLES) return LTC_ERR_INVALID_ARGUMENT;
+  if (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY)) return LTC_ERR_INVALID_ARGUMENT;
   if (!(theta > 0.0 && theta <= 1.0)) return LTC_ERR_INVALID_ARGUMENT;
+  const bool one_stream = (flags & LTC_FLAG_CALLER_STREAM_ONLY) != 0;
   const uint32_t e = elem_bytes(dtype);
   for (int i = 0; i < count; ++i) {
     const int rc = check_shape(nbytes[i], dtype, chunk_bytes);
@@ -329,7 +333,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   w.offsets = reinterpret_cast<uint64_t*>(ws + l.offsets);
   w.blob_nbytes = reinterpret_cast<uint64_t*>(ws + l.blobn);
   w.words = reinterpret_cast<uint16_t*>(ws + l.words);
-  if (!crc.chunk_bytes) return run_compress(t, w, stream, ev) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
+  if (!crc.chunk_bytes) return run_compress(t, w, stream, ev, one_stream) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 
   // compress_with_crc32: when checksum chunks are whole 1 KiB frames, k_scan
   // and k_pack accumulate the remainders of the blob's frames as they write
@@ -369,7 +373,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   }
   a.total_chunks = ccur;
   hipError_t err = fused ? launch_zero_u32(frames, fcur, stream) : hipSuccess;
-  if (err == hipSuccess) err = run_compress(t, w, stream, ev);
+  if (err == hipSuccess) err = run_compress(t, w, stream, ev, one_stream);
   if (err == hipSuccess) err = fused ? launch_crc32_frames(a, stream) : launch_crc32(a, stream);
   if (ev) record(ev, 5, stream);
   return err == hipSuccess ? LTC_OK : LTC_ERR_HIP;
@@ -531,7 +535,9 @@ uint64_t ltc_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
 }
 
 uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes, uint32_t flags) {
-  if (check_shape(nbytes, dtype, chunk_bytes) || (flags & ~LTC_FLAG_SHARED_TABLES)) return 0;
+  if (check_shape(nbytes, dtype, chunk_bytes) ||
+      (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY)))
+    return 0;
   return bound_flags(nbytes, elem_bytes(dtype), chunk_bytes, flags);
 }
 

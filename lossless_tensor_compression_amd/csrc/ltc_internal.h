@@ -9,15 +9,10 @@
 #include <utility>
 
 #include "ltc.h"
+#include "ltc_format.h"
 
 namespace ltc {
 
-constexpr uint32_t kTotal = 4096;       // normalised frequency total (2^12)
-constexpr uint32_t kLanes = 64;         // interleaved rANS lanes = one wave64
-constexpr uint32_t kRansLow = 65536;    // state lower bound 2^16
-constexpr uint32_t kHeader = 64;
-constexpr uint32_t kDirEntry = 16;
-constexpr uint32_t kRansFixed = 272;    // 16-byte prefix + 64 u32 states
 constexpr uint32_t kModeCand = 0xFF;    // internal: histogram done, encode pending (no blob mode)
 constexpr uint32_t kRawStaged = 1;      // internal: a RAW stream's bytes wait in its workspace slot
 constexpr int kMaxJobs = LTC_BATCH_MAX;

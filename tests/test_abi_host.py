@@ -120,3 +120,13 @@ def test_argument_errors_before_any_launch():
                need, fake, 1 << 30, null) == -1
     assert cwc(fake, 4096, 9, 131072, 0.95, fake, bound, fake, 1024, fake, need, fake, 1 << 30, null) == -2
     assert cwc(fake, 4096, 1, 131072, 0.95, fake, bound, fake, 1024, fake, need, fake, 16, null) == -7
+
+
+def test_caller_stream_flag_does_not_change_the_bound():
+    _lib()
+    for dtype in (0, 1, 3):
+        n = 131072 * 5 + 8
+        base = ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, 0)
+        assert base == ltc.compress_bound(n, dtype)
+        assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, ltc.FLAG_CALLER_STREAM_ONLY) == base
+        assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, 8) == 0  # unknown flag

@@ -314,13 +314,14 @@ def test_staged_raw_streams_with_abandoned_neighbours(ltc, dtype, thr):
     assert modes[:, e - 1].tolist() == top
 
 
-# ---- pipelined compression: calls over 512 chunks or more run in four
-# chunk-ordered groups on several streams; blobs must not change.
+# ---- pipelined compression: calls over 512 chunks or more run in two
+# chunk-ordered groups on two streams (the caller's and one internal
+# stream); blobs must not change.
 
 @pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (2, 2048), (0, 512)])
 def test_grouped_single_tensor(ltc, dtype, chunk):
     rng = np.random.default_rng(100 + dtype)
-    nbytes = 700 * chunk + 3 * 8  # 701 chunks, a ragged last one: four uneven groups
+    nbytes = 700 * chunk + 3 * 8  # 701 chunks, a ragged last one: two uneven groups (350 + 351)
     if dtype == 0:
         data = rng.integers(0, 6, nbytes, dtype=np.uint8)
         data[: nbytes // 3] = 7  # const chunks too
@@ -364,6 +365,42 @@ def test_grouped_batch_with_empty_and_tiny(ltc):
     again = ltc.compress_batch(ts, chunk)
     for b1, b2 in zip(blobs, again):
         assert torch.equal(b1, b2)
+
+
+def test_caller_stream_only_equals_grouped(ltc):
+    """LTC_FLAG_CALLER_STREAM_ONLY: a call over more than 512 chunks (which
+    otherwise runs in two groups on two streams) runs every kernel on the
+    caller's stream and gives the same blobs, plain and with checksums."""
+    rng = np.random.default_rng(88)
+    chunk = 4096
+    arrs = [(rng.standard_normal(n) * s).astype(np.float32) for n, s in
+            ((300000, 0.02), (5, 1.0), (250003, 1e-3))]
+    ts = [to_gpu(a, 3) for a in arrs]
+    nbytes = [a.nbytes for a in arrs]
+    assert sum((n + chunk - 1) // chunk for n in nbytes) >= 512
+    caps = [ltc.compress_bound(n, 3, chunk) for n in nbytes]
+    ws_n = ltc.workspace_size(nbytes, 3, chunk)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    got = {}
+    for flags in (0, ltc.FLAG_CALLER_STREAM_ONLY):
+        for crc in (0, 16384):
+            blobs = [torch.empty(c, dtype=torch.uint8, device="cuda") for c in caps]
+            sizes = torch.zeros(len(ts), dtype=torch.int64, device="cuda")
+            ccap = [(c + 16383) // 16384 for c in caps]
+            crcs = [torch.empty(n, dtype=torch.int32, device="cuda") for n in ccap]
+            ltc.compress_ex_raw([t.data_ptr() for t in ts], nbytes, 3, chunk, 0.95, flags,
+                                [b.data_ptr() for b in blobs], caps, sizes.data_ptr(), ws.data_ptr(), ws_n,
+                                crc, [c.data_ptr() for c in crcs] if crc else None, ccap if crc else None)
+            torch.cuda.synchronize()
+            sz = sizes.cpu().tolist()
+            got[(flags, crc)] = ([to_np_bytes(b[:s]) for b, s in zip(blobs, sz)],
+                                 [c[:(s + 16383) // 16384].cpu().numpy() for c, s in zip(crcs, sz)] if crc else None)
+    for a, i in zip(arrs, range(len(arrs))):
+        want = oracle.compress(a, 3, chunk)
+        for key, (blobs, crcs) in got.items():
+            assert np.array_equal(blobs[i], want), (key, i)
+            if crcs is not None:
+                assert np.array_equal(crcs[i].view(np.uint32), oracle.crc32_chunks(want, 16384)), (key, i)
 
 
 @pytest.mark.parametrize("dtype", [0, 1])
