@@ -52,7 +52,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: all, max 16)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads of the multi-threaded baseline (0: the host's CPU share)")
+    ap.add_argument("--configs", default="c1,c2,c4,c5",
+                    help="other workloads also measured and reported under 'configs' (comma list of "
+                         "c1, c2, c4, c5; empty for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB (HBM counter calibration)")
     ap.add_argument("--isolated", action="store_true",
@@ -293,36 +297,205 @@ def delta_bench(args, hip, sptr, torch):
             "stream_modes": modes}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, ts, torch):
+    """The oracle (plain scalar C, OpenMP over chunks) on the host cores:
+    compress + decompress + CRC-32 of the blob, on a bounded sample of the
+    workload, best of 3 runs, once on one thread and once on the host's CPU
+    share.  The share is the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when set (a GPU machine gives one GPU's process 16)."""
     import numpy as np
 
     import oracle
-    threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-    # bounded sample: whole tensors from the start of the workload, at most 2 GiB
-    cap = 2 << 30
-    sample, taken = [], 0
-    for t in ts:
-        b = t.contiguous().view(-1).view(torch.uint8)
-        if taken and taken + b.numel() > cap:
-            break
-        take = min(b.numel(), cap)
-        sample.append(b[:take].cpu().numpy())
-        taken += take
-        if taken >= cap:
-            break
+    affinity = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    share = min(affinity, int(omp)) if omp.isdigit() and int(omp) > 0 else affinity
+    threads = args.cpu_threads or share
     code = {torch.bfloat16: 1, torch.float16: 2, torch.float32: 3, torch.uint8: 0}[ts[0].dtype]
-    t0 = time.time()
-    total = 0
-    for s in sample:
-        blob = oracle.compress(s, code, CHUNK, THRESHOLD, nthreads=threads)
-        rc, out = oracle.decompress(blob, nthreads=threads)
-        assert rc == 0 and np.array_equal(out, s)
-        oracle.crc32_chunks(blob, CRC_CHUNK)
-        total += s.size
-    dt = time.time() - t0
-    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {total / 2**20:.0f} MiB of the workload: compress + decompress + "
-                      f"CRC-32 per step, OpenMP over chunks, {dt:.1f} s"}
+
+    def sample(cap):  # whole tensors from the start of the workload, at most cap bytes
+        out, taken = [], 0
+        for t in ts:
+            b = t.contiguous().view(-1).view(torch.uint8)
+            if taken and taken + b.numel() > cap:
+                break
+            take = min(b.numel(), cap)
+            out.append(b[:take].cpu().numpy())
+            taken += take
+            if taken >= cap:
+                break
+        return out
+
+    def best_of_3(parts, nthreads):
+        best = None
+        for _ in range(3):
+            t0 = time.time()
+            for s in parts:
+                blob = oracle.compress(s, code, CHUNK, THRESHOLD, nthreads=nthreads)
+                rc, out = oracle.decompress(blob, nthreads=nthreads)
+                assert rc == 0 and np.array_equal(out, s)
+                oracle.crc32_chunks(blob, CRC_CHUNK)
+            dt = time.time() - t0
+            best = dt if best is None else min(best, dt)
+        return best
+
+    many = sample(1664 << 20)
+    one = sample(32 << 20)
+    n_many = sum(s.size for s in many)
+    n_one = sum(s.size for s in one)
+    t_many = best_of_3(many, threads)
+    t_one = best_of_3(one, 1)
+    return {"value": round(n_many / t_many / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_many / 2**20:.0f} MiB of the workload: compress + decompress + CRC-32, "
+                      f"OpenMP over chunks on {threads} threads, best of 3 ({t_many:.2f} s)",
+            "single_thread": {"value": round(n_one / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"first {n_one / 2**20:.0f} MiB of the workload, best of 3 "
+                                        f"({t_one:.2f} s)"},
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_num_threads": omp or None,
+            "speedup_threads_vs_one": round(t_one / n_one * n_many / t_many, 2)}
+
+
+def digests(torch, tensors, sizes=None):
+    """SHA-256 of each tensor's bytes (the first sizes[i] bytes when given)."""
+    out = []
+    for i, t in enumerate(tensors):
+        b = t.contiguous().view(-1).view(torch.uint8)
+        if sizes is not None:
+            b = b[:sizes[i]]
+        out.append(hashlib.sha256(b.cpu().numpy().tobytes()).hexdigest())
+    return out
+
+
+def config_figures(name, ts, hip, sptr, torch, reps, hashes=True):
+    """Compress, compress_with_crc32, decompress and the CRC-32 kernel over
+    one workload's tensors (batch calls, inputs in HBM), each call repeated
+    back to back between two events; the exact round trip and the device
+    status are checked first.  Roofline fractions count N + B per call."""
+    import lossless_tensor_compression_amd as ltc
+    code = ltc.DTYPE_CODE[ts[0].dtype]
+    count = len(ts)
+    nbytes = [t.numel() * t.element_size() for t in ts]
+    N = sum(nbytes)
+    caps = [ltc.compress_bound(n, code, CHUNK) for n in nbytes]
+    blobs = [torch.empty(c, dtype=torch.uint8, device="cuda") for c in caps]
+    ws_n = ltc.workspace_size(nbytes, code, CHUNK)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    sizes = torch.zeros(count, dtype=torch.int64, device="cuda")
+    outs = [torch.empty(n, dtype=torch.uint8, device="cuda") for n in nbytes]
+    status = torch.zeros(count, dtype=torch.int32, device="cuda")
+    src_ptrs = [t.data_ptr() for t in ts]
+    blob_ptrs = [b.data_ptr() for b in blobs]
+    out_ptrs = [o.data_ptr() for o in outs]
+    fcap = [(c + CRC_CHUNK - 1) // CRC_CHUNK for c in caps]
+    fcrcs = [torch.empty(n, dtype=torch.int32, device="cuda") for n in fcap]
+
+    def comp():
+        ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, 0, blob_ptrs, caps, sizes.data_ptr(),
+                            ws.data_ptr(), ws_n)
+
+    def comp_crc():
+        ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, 0, blob_ptrs, caps, sizes.data_ptr(),
+                            ws.data_ptr(), ws_n, CRC_CHUNK, [c.data_ptr() for c in fcrcs], fcap)
+
+    comp()
+    bsz = sizes.cpu().tolist()
+    headers = [bytes(b[:64].cpu().numpy().tobytes()) for b in blobs]
+    B = sum(bsz)
+    ncrc = [(s + CRC_CHUNK - 1) // CRC_CHUNK for s in bsz]
+    crcs = [torch.empty(max(n, 1), dtype=torch.int32, device="cuda") for n in ncrc]
+
+    def dec():
+        ltc.decompress_raw(headers, blob_ptrs, bsz, out_ptrs, nbytes, status.data_ptr())
+
+    def crc():
+        ltc.crc32_raw(blob_ptrs, bsz, CRC_CHUNK, [c.data_ptr() for c in crcs])
+
+    for fn in (comp_crc, dec, crc):
+        fn()
+    torch.cuda.synchronize()
+    assert sizes.cpu().tolist() == bsz, f"{name}: blob sizes changed"
+    assert status.cpu().tolist() == [0] * count, f"{name}: decode status"
+    for t, o in zip(ts, outs):
+        assert torch.equal(t.contiguous().view(-1).view(torch.uint8), o), f"{name}: round trip"
+    for a, b, n in zip(crcs, fcrcs, ncrc):
+        assert torch.equal(a[:n], b[:n]), f"{name}: CRC-32 paths differ"
+    ev = hip.events(2)
+
+    def timed(fn):
+        fn()
+        hip.record(ev[0], sptr)
+        for _ in range(reps):
+            fn()
+        hip.record(ev[1], sptr)
+        torch.cuda.synchronize()
+        return hip.ms(ev[0], ev[1]) / reps
+
+    t_c, t_cc, t_d, t_x = timed(comp), timed(comp_crc), timed(dec), timed(crc)
+    nck = sum(ncrc)
+
+    def gbs(nb, ms):
+        return round(nb / (ms * 1e-3) / 1e9, 2)
+
+    def frac(nb, ms):
+        return round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+    sha = ({"inputs": digests(torch, ts), "blobs": digests(torch, blobs, bsz)} if hashes else
+           "not taken (8 GiB; the full-size GPU test compares the whole blob with the oracle's)")
+    return {"orig_bytes": N, "blob_bytes": B, "ratio": round(B / N, 5), "tensors": count, "sha256": sha,
+            "dtype": {1: "bf16", 2: "fp16", 3: "fp32", 0: "u8"}[code],
+            "compress_ms": round(t_c, 4), "decompress_ms": round(t_d, 4),
+            "compress_with_crc32_ms": round(t_cc, 4), "crc32_ms": round(t_x, 4),
+            "compress_gbs": gbs(N, t_c), "decompress_gbs": gbs(N, t_d),
+            "compress_with_crc32_gbs": gbs(N, t_cc), "crc32_blob_gbs": gbs(B, t_x),
+            "compress_roofline_frac": frac(N + B, t_c), "decompress_roofline_frac": frac(N + B, t_d),
+            "crc32_roofline_frac": frac(B + 4 * nck, t_x)}
+
+
+def other_configs(which, hip, sptr, torch, reps):
+    """The figures of the other workloads, one after another (each freed
+    before the next is generated): C1, C2, the two parts of C4 and their
+    combination, and C5 (8 GiB)."""
+    import numpy as np
+
+    import workloads
+    res = {}
+    for name in which:
+        if name == "c1":
+            ts = [torch.from_numpy(workloads.c1().view(np.int16)).cuda().view(torch.bfloat16)]
+            res["C1"] = config_figures(name, ts, hip, sptr, torch, reps)
+        elif name == "c2":
+            ts = [torch.from_numpy(workloads.c2()).cuda()]
+            res["C2"] = config_figures(name, ts, hip, sptr, torch, reps)
+        elif name == "c4":
+            clean, h = workloads.c4()
+            a = config_figures("c4a", [torch.from_numpy(clean).cuda()], hip, sptr, torch, reps)
+            b = config_figures("c4b", [torch.from_numpy(h).cuda()], hip, sptr, torch, reps)
+            res["C4a"], res["C4b"] = a, b
+            n, bb = a["orig_bytes"] + b["orig_bytes"], a["blob_bytes"] + b["blob_bytes"]
+            tc, td = a["compress_ms"] + b["compress_ms"], a["decompress_ms"] + b["decompress_ms"]
+            res["C4"] = {"orig_bytes": n, "blob_bytes": bb, "ratio": round(bb / n, 5),
+                         "compress_gbs": round(n / (tc * 1e-3) / 1e9, 2),
+                         "decompress_gbs": round(n / (td * 1e-3) / 1e9, 2),
+                         "compress_roofline_frac": round((n + bb) / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "decompress_roofline_frac": round((n + bb) / (td * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "note": "C4a then C4b, one call each"}
+        elif name == "c5":
+            buf = workloads.c5_gpu("cuda")
+            res["C5"] = config_figures(name, [buf.view(torch.bfloat16)], hip, sptr, torch, reps, hashes=False)
+            del buf
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -560,12 +733,19 @@ def main():
         "roofline": roof,
         "wall_s_timed": round(wall, 3),
     }
+    rec["sha256"] = {"inputs": digests(torch, ts), "blobs": digests(torch, blobs, bsz)}
     if args.host_path:
         rec["host_path"] = host_path(ts, blobs, bsz, outs, nbytes, N, B, hip, sptr, torch)
     if args.delta:
         rec["delta"] = delta_bench(args, hip, sptr, torch)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args, ts, torch)
+    which = [w for w in args.configs.split(",") if w and w != args.workload]
+    if which:
+        del ts, blobs, ws, outs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        rec["configs"] = other_configs(which, hip, sptr, torch, reps)
     print(json.dumps(rec), flush=True)
 
 
