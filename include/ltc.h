@@ -193,6 +193,26 @@ int ltc_compress(const void* d_src, uint64_t nbytes, int dtype, uint32_t chunk_b
                  uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes,
                  hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * blob as ltc_compress, with the workspace taken from a device array the
+ * library holds on each GPU it runs on (LTC_NOALLOC_SCRATCH_BYTES = 64 MiB,
+ * kept until the process ends; its address is looked up once per device, on
+ * the first call there).  The call allocates nothing and uses no internal
+ * stream: every kernel runs on `stream`, which must belong to the current
+ * device.  The input is limited to what that workspace covers,
+ * ltc_compress_workspace_size() <= LTC_NOALLOC_SCRATCH_BYTES (about 60 MB of
+ * BF16 at the default chunk size); larger inputs return LTC_ERR_WORKSPACE
+ * before anything is enqueued.  All calls on one GPU share its array: calls
+ * whose work overlaps on that GPU (on different streams, or from several
+ * threads) race and give undefined blobs; calls in order on one stream are
+ * safe, since every call writes each workspace field it reads.  Other errors
+ * as ltc_compress, plus INVALID_ARGUMENT for a stream of another device. */
+#define LTC_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int ltc_compress_noalloc(const void* d_src, uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                         double passthrough_threshold, void* d_blob, uint64_t blob_capacity,
+                         uint64_t* d_blob_nbytes, hipStream_t stream);
+
 /* Batch of `count` (1..LTC_BATCH_MAX) tensors of one dtype, one launch
  * sequence; each blob is identical to what ltc_compress gives for that
  * tensor alone.  Host arrays hold the per-tensor device pointers and sizes;

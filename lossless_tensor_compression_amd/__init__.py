@@ -83,6 +83,7 @@ def lib():
         L.ltc_compress_workspace_size.argtypes = [u64, i32, u32, pu64]
         L.ltc_compress_batch_workspace_size.argtypes = [i32, pu64, i32, u32, pu64]
         L.ltc_compress.argtypes = [vp, u64, i32, u32, dbl, vp, u64, vp, vp, u64, vp]
+        L.ltc_compress_noalloc.argtypes = [vp, u64, i32, u32, dbl, vp, u64, vp, vp]
         L.ltc_compress_batch.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp, vp, u64, vp]
         L.ltc_compress_batch_prof.argtypes = [i32, pvp, pu64, i32, u32, dbl, pvp, pu64, vp, vp,
                                               u64, vp, pvp]
@@ -110,7 +111,8 @@ def lib():
         L.ltc_crc32_chunks_batch.argtypes = [i32, pvp, pu64, u32, pvp, vp]
         L.ltc_blob_stats.argtypes = [ctypes.c_char_p, u64, ctypes.POINTER(Stats)]
         for name in ("ltc_compress_workspace_size", "ltc_compress_batch_workspace_size",
-                     "ltc_compress", "ltc_compress_batch", "ltc_compress_batch_prof",
+                     "ltc_compress", "ltc_compress_noalloc", "ltc_compress_batch",
+                     "ltc_compress_batch_prof",
                      "ltc_compress_with_crc32", "ltc_compress_batch_with_crc32", "ltc_compress_batch_ex",
                      "ltc_compress_batch_with_crc32_prof",
                      "ltc_blob_info", "ltc_decompress", "ltc_decompress_batch",
@@ -152,6 +154,7 @@ def _flat_bytes(t):
 FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
 FLAG_DELTA = 2          # header flag: the blob codes src XOR base
 FLAG_CALLER_STREAM_ONLY = 4  # compress flag: every kernel on the caller's stream
+NOALLOC_SCRATCH_BYTES = 64 << 20  # workspace limit of ltc_compress_noalloc
 
 
 def compress_bound(nbytes, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES, shared_tables=False):
@@ -177,6 +180,17 @@ def compress_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blob_ptrs
         _check(lib().ltc_compress_batch(*args), "compress")
     else:
         _check(lib().ltc_compress_batch_prof(*args, _ptrs(events)), "compress")
+
+
+def compress_noalloc_raw(src_ptr, nbytes, dtype_code, chunk_bytes, threshold, blob_ptr, cap,
+                         nbytes_out_ptr, stream=None):
+    """Pointer-level ltc_compress_noalloc on `stream`: the workspace is the
+    library's own device array (inputs up to NOALLOC_SCRATCH_BYTES of
+    workspace), nothing is allocated."""
+    _check(lib().ltc_compress_noalloc(ctypes.c_void_p(src_ptr), nbytes, dtype_code, chunk_bytes,
+                                      threshold, ctypes.c_void_p(blob_ptr), cap,
+                                      ctypes.c_void_p(nbytes_out_ptr), _stream(stream)),
+           "compress_noalloc")
 
 
 def compress_ex_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, flags, blob_ptrs, caps,

@@ -10,6 +10,12 @@
 #include "ltc_internal.h"
 #include "ltc_launch.h"
 
+// Workspace of ltc_compress_noalloc: one copy on each GPU the library runs
+// on, held until the process ends.  Host code never uses this name as an
+// address (on the host it is only a stand-in for the device symbol); it uses
+// the per-device pointer from hipGetSymbolAddress (scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[LTC_NOALLOC_SCRATCH_BYTES];
+
 namespace ltc {
 namespace {
 
@@ -105,6 +111,35 @@ hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipE
   }
   for (int g = 1; g < kPipeGroups && err == hipSuccess; ++g) err = hipStreamWaitEvent(stream, r->done[g], 0);
   return err;
+}
+
+// ---- the scratch array of ltc_compress_noalloc
+// Its device address, looked up once per device (with that device current)
+// on the first call there, and kept; a fixed table, so no call allocates.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// the current device's scratch address, or null (stream of another device,
+// or the lookup failed: *err tells which)
+void* scratch_ptr(hipStream_t stream, int* err) {
+  int dev = 0;
+  *err = LTC_ERR_HIP;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  *err = LTC_ERR_INVALID_ARGUMENT;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  hipDevice_t sdev = 0;
+  if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *err = LTC_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
 }
 
 uint64_t round_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
@@ -589,6 +624,21 @@ int ltc_compress(const void* d_src, uint64_t nbytes, int dtype, uint32_t chunk_b
                  uint64_t* d_blob_nbytes, void* d_ws, uint64_t ws_nbytes, hipStream_t stream) {
   return compress_impl(1, &d_src, &nbytes, dtype, chunk_bytes, passthrough_threshold, &d_blob,
                        &blob_capacity, d_blob_nbytes, d_ws, ws_nbytes, stream, nullptr);
+}
+
+int ltc_compress_noalloc(const void* d_src, uint64_t nbytes, int dtype, uint32_t chunk_bytes,
+                         double passthrough_threshold, void* d_blob, uint64_t blob_capacity,
+                         uint64_t* d_blob_nbytes, hipStream_t stream) {
+  uint64_t need = 0;
+  const int rc = ltc_compress_workspace_size(nbytes, dtype, chunk_bytes, &need);
+  if (rc) return rc;
+  if (need > LTC_NOALLOC_SCRATCH_BYTES) return LTC_ERR_WORKSPACE;
+  int err = LTC_OK;
+  void* ws = scratch_ptr(stream, &err);
+  if (!ws) return err;
+  return compress_impl(1, &d_src, &nbytes, dtype, chunk_bytes, passthrough_threshold, &d_blob,
+                       &blob_capacity, d_blob_nbytes, ws, LTC_NOALLOC_SCRATCH_BYTES, stream, nullptr,
+                       CrcReq{0, nullptr, nullptr}, LTC_FLAG_CALLER_STREAM_ONLY);
 }
 
 int ltc_compress_batch(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,

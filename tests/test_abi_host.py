@@ -122,6 +122,32 @@ def test_argument_errors_before_any_launch():
     assert cwc(fake, 4096, 1, 131072, 0.95, fake, bound, fake, 1024, fake, need, fake, 16, null) == -7
 
 
+def test_noalloc_limits_before_any_launch():
+    """ltc_compress_noalloc checks its arguments and the size of its fixed
+    workspace on the host, before touching the device: an input whose
+    workspace exceeds LTC_NOALLOC_SCRATCH_BYTES is refused with WORKSPACE."""
+    L = _lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_uint64(0)
+    limit = ltc.NOALLOC_SCRATCH_BYTES
+    # the largest BF16 input (whole chunks) whose workspace fits, and one chunk more
+    per = 1
+    while True:
+        assert L.ltc_compress_workspace_size(per * 131072, 1, 131072, ctypes.byref(ws)) == 0
+        if ws.value > limit:
+            break
+        per += 1
+    assert per > 400  # about 60 MB of BF16
+    big = per * 131072
+    bound = L.ltc_compress_bound(big, 1, 131072)
+    assert L.ltc_compress_noalloc(fake, big, 1, 131072, 0.95, fake, bound, fake, null) == -7
+    assert L.ltc_compress_noalloc(fake, 1 << 40, 1, 131072, 0.95, fake, 1 << 41, fake, null) == -7
+    assert L.ltc_compress_noalloc(fake, 16, 9, 131072, 0.95, fake, 1 << 20, fake, null) == -2
+    assert L.ltc_compress_noalloc(fake, 15, 1, 131072, 0.95, fake, 1 << 20, fake, null) == -1
+    assert L.ltc_compress_noalloc(fake, 16, 1, 12, 0.95, fake, 1 << 20, fake, null) == -1
+
+
 def test_caller_stream_flag_does_not_change_the_bound():
     _lib()
     for dtype in (0, 1, 3):
