@@ -493,7 +493,7 @@ static int check_args(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
   if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8)
     return LTCO_ERR_INVALID_ARGUMENT;
   if (!(theta > 0.0 && theta <= 1.0)) return LTCO_ERR_INVALID_ARGUMENT;
-  if ((nbytes + chunk_bytes - 1) / chunk_bytes >= (1ull << 32))
+  if (nbytes / chunk_bytes + (nbytes % chunk_bytes != 0) >= (1ull << 32))
     return LTCO_ERR_INVALID_ARGUMENT;
   return LTCO_OK;
 }
@@ -948,7 +948,8 @@ static int decompress_impl(const uint8_t* blob, uint64_t blob_nbytes, const uint
   if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8)
     return LTCO_ERR_CORRUPT;
   if (nbytes % (uint64_t)e) return LTCO_ERR_CORRUPT;
-  if (k != (nbytes + chunk_bytes - 1) / chunk_bytes) return LTCO_ERR_CORRUPT;
+  /* K = ceil(N / C) as an exact integer (no wrap for N near 2^64) */
+  if (k != nbytes / chunk_bytes + (nbytes % chunk_bytes != 0)) return LTCO_ERR_CORRUPT;
   uint64_t s = k * (uint64_t)e;
   uint64_t base = HDR_BYTES + DIR_BYTES * s;
   if (get_u64(blob + 32) != blob_nbytes) return LTCO_ERR_CORRUPT;

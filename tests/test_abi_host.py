@@ -86,6 +86,15 @@ def test_blob_info_errors_match_oracle():
         assert got == want, (got, want)
     assert _info_rc(blob[:63]) == ltc.lib().ltc_blob_info(bytes(blob[:63]), 63, ctypes.byref(ltc.Info()))
     assert _info_rc(blob[:40]) == -5
+    # a 64-byte blob claiming N = 2^64 - 8 in K = 0 chunks: ceil(N / C) must
+    # not wrap around to K (otherwise the header is consistent: empty
+    # directory, payload_base = blob_nbytes = 64)
+    b = blob[:64].copy()
+    b[8:16] = np.frombuffer((2**64 - 8).to_bytes(8, "little"), dtype=np.uint8)
+    b[20:24] = 0
+    b[32:40] = np.frombuffer((64).to_bytes(8, "little"), dtype=np.uint8)
+    b[40:48] = np.frombuffer((64).to_bytes(8, "little"), dtype=np.uint8)
+    assert _info_rc(b) == oracle.decompress(b, capacity=0)[0] == -5
 
 
 def test_argument_errors_before_any_launch():
