@@ -15,7 +15,12 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libltc.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["ltc_compress.hip", "ltc_decompress.hip", "ltc_crc32.hip", "ltc_api.hip"]
+# plain C++ (no device code): the host-side parsing of blob bytes
+HOST_SOURCES = ["ltc_host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+              "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 # Packed FP32 instructions (v_pk_*_f32) stay off in device code.  hipcc's
 # driver cannot forward -Xclang options to the device pass alone (-Xarch_device
 # refuses options that take an argument), so the feature goes to both passes
@@ -41,10 +46,20 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _compile_host(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    objs += [_compile_host(s, verbose) for s in HOST_SOURCES]
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

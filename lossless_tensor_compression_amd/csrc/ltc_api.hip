@@ -7,6 +7,7 @@
 #include <mutex>
 #include <vector>
 
+#include "ltc_host.h"
 #include "ltc_internal.h"
 #include "ltc_launch.h"
 
@@ -187,16 +188,6 @@ uint32_t xpow8(uint64_t n) {
 }
 
 
-uint32_t elem_bytes(int dtype) {
-  switch (dtype) {
-    case LTC_U8: return 1;
-    case LTC_BF16: return 2;
-    case LTC_FP16: return 2;
-    case LTC_FP32: return 4;
-    default: return 0;
-  }
-}
-
 // Largest integer P with (double)P < theta * (double)n: cuZipNN 0.1.0, "API":
 // a chunk stays compressed only if it shrinks below the threshold fraction.
 uint32_t p_max(uint64_t n, double theta) {
@@ -212,7 +203,7 @@ int check_shape(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
   if (!e) return LTC_ERR_UNSUPPORTED_DTYPE;
   if (nbytes % e) return LTC_ERR_INVALID_ARGUMENT;
   if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8) return LTC_ERR_INVALID_ARGUMENT;
-  const uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
+  const uint64_t k = nbytes / chunk_bytes + (nbytes % chunk_bytes != 0);  // no wrap for any N
   if (k >= (1ull << 32)) return LTC_ERR_INVALID_ARGUMENT;
   return LTC_OK;
 }
@@ -416,25 +407,6 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
 
 uint32_t rd_flags(const void* header) { return static_cast<const uint8_t*>(header)[27]; }
 
-uint64_t rd64(const uint8_t* p) {
-  uint64_t v;
-  memcpy(&v, p, 8);
-  return v;
-}
-uint32_t rd32(const uint8_t* p) {
-  uint32_t v;
-  memcpy(&v, p, 4);
-  return v;
-}
-uint16_t rd16(const uint8_t* p) {
-  uint16_t v;
-  memcpy(&v, p, 2);
-  return v;
-}
-
-// byte offset of stream s in a blob's directory, read from host memory
-uint64_t dir_offset(const uint8_t* h_blob, uint64_t s) { return rd64(h_blob + kHeader + kDirEntry * s); }
-
 // Copies and decodes blobs held in host memory (t's blobs are the staging
 // buffers; every header was checked).  Group g holds global chunks
 // [T*g/G, T*(g+1)/G); its bytes of blob j are that tensor's directory (first
@@ -447,36 +419,32 @@ hipError_t decode_from_host(int dtype, const DTable& t, uint32_t e, const void* 
                             hipStream_t stream) {
   const uint64_t T = t.total_chunks;
   if (T == 0) return launch_decompress_range(dtype, t, stream, nullptr, 0, 0, true);
+  HostBlob hb[kMaxJobs];
   uint64_t total = 0;
-  for (uint32_t j = 0; j < t.count; ++j) total += t.jobs[j].blob_nbytes;
-  uint64_t G = total / kCopyGroupBytes;
-  G = G < 1 ? 1 : (G > (uint64_t)kCopyGroupsMax ? kCopyGroupsMax : G);
-  if (G > T) G = T;
+  for (uint32_t j = 0; j < t.count; ++j) {
+    const DJob& jb = t.jobs[j];
+    hb[j] = HostBlob{static_cast<const uint8_t*>(host_blobs[j]), jb.blob_nbytes, jb.chunk0, jb.nchunks};
+    total += jb.blob_nbytes;
+  }
+  const uint64_t G = host_copy_groups(total, T, kCopyGroupBytes, kCopyGroupsMax);
   std::lock_guard<std::mutex> lock(g_pipe_mu);
   PipeRes* r = pipe_res(stream);
   if (!r) return hipErrorInvalidValue;
   hipStream_t cs = r->s[1];
   hipError_t err = hipEventRecord(r->fork, stream);
   if (err == hipSuccess) err = hipStreamWaitEvent(cs, r->fork, 0);
+  HostRange rg[kMaxJobs];
   for (uint64_t g = 0; g < G && err == hipSuccess; ++g) {
-    const uint64_t c0 = T * g / G, c1 = T * (g + 1) / G;
-    for (uint32_t j = 0; j < t.count && err == hipSuccess; ++j) {
-      const DJob& jb = t.jobs[j];
-      if (c1 <= jb.chunk0 || c0 >= jb.chunk0 + jb.nchunks) continue;  // no chunk of blob j here
-      const uint64_t lo_c = c0 > jb.chunk0 ? c0 - jb.chunk0 : 0;
-      const uint64_t hi_c = c1 - jb.chunk0 < jb.nchunks ? c1 - jb.chunk0 : jb.nchunks;
-      const uint8_t* hb = static_cast<const uint8_t*>(host_blobs[j]);
-      const uint64_t B = jb.blob_nbytes;
-      uint64_t lo = lo_c == 0 ? 0 : dir_offset(hb, lo_c * e);
-      uint64_t hi = hi_c == jb.nchunks ? B : dir_offset(hb, hi_c * e);
-      lo = lo < B ? lo : B;
-      hi = hi < lo ? lo : (hi < B ? hi : B);
-      if (hi > lo)
-        err = hipMemcpyAsync(const_cast<uint8_t*>(jb.blob) + lo, hb + lo, hi - lo, hipMemcpyHostToDevice, cs);
+    const uint32_t nr = host_group_ranges(hb, t.count, e, T, G, g, rg);
+    for (uint32_t q = 0; q < nr && err == hipSuccess; ++q) {
+      const HostRange& x = rg[q];
+      err = hipMemcpyAsync(const_cast<uint8_t*>(t.jobs[x.job].blob) + x.lo, hb[x.job].data + x.lo, x.hi - x.lo,
+                           hipMemcpyHostToDevice, cs);
     }
     if (err == hipSuccess) err = hipEventRecord(r->copied[g], cs);
     if (err == hipSuccess) err = hipStreamWaitEvent(stream, r->copied[g], 0);
-    if (err == hipSuccess) err = launch_decompress_range(dtype, t, stream, nullptr, c0, c1, g == 0);
+    if (err == hipSuccess)
+      err = launch_decompress_range(dtype, t, stream, nullptr, T * g / G, T * (g + 1) / G, g == 0);
   }
   return err;
 }
@@ -561,8 +529,6 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
 using namespace ltc;
 
 extern "C" {
-
-uint32_t ltc_elem_bytes(int dtype) { return elem_bytes(dtype); }
 
 uint64_t ltc_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
   if (check_shape(nbytes, dtype, chunk_bytes)) return 0;
@@ -697,48 +663,6 @@ int ltc_compress_batch_with_crc32_prof(int count, const void* const* h_src_ptrs,
                        crc);
 }
 
-int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {
-  if (!h_header || !out) return LTC_ERR_INVALID_ARGUMENT;
-  if (h_nbytes < kHeader) return LTC_ERR_CORRUPT;
-  const uint8_t* h = static_cast<const uint8_t*>(h_header);
-  if (memcmp(h, "LTCB", 4) != 0) return LTC_ERR_BAD_MAGIC;
-  const uint32_t version = rd16(h + 4);
-  if (version != 1 && version != 2) return LTC_ERR_BAD_VERSION;
-  const int dtype = h[6];
-  const uint32_t e = elem_bytes(dtype);
-  if (!e) return LTC_ERR_UNSUPPORTED_DTYPE;
-  if (h[7] != e) return LTC_ERR_CORRUPT;
-  const uint64_t nbytes = rd64(h + 8);
-  const uint32_t chunk_bytes = rd32(h + 16);
-  const uint64_t k = rd32(h + 20);
-  if (rd16(h + 24) != kLanes || h[26] != 12 ||
-      (h[27] & ~LTC_FLAG_DELTA) != (version == 2 ? LTC_FLAG_SHARED_TABLES : 0u) || rd32(h + 28) != 0)
-    return LTC_ERR_CORRUPT;
-  for (int i = 48; i < 64; ++i)
-    if (h[i]) return LTC_ERR_CORRUPT;
-  if (chunk_bytes < 8 || chunk_bytes > (1u << 24) || chunk_bytes % 8) return LTC_ERR_CORRUPT;
-  if (nbytes % e) return LTC_ERR_CORRUPT;
-  if (k != (nbytes + chunk_bytes - 1) / chunk_bytes) return LTC_ERR_CORRUPT;
-  // v2: E table records of 16 to 528 bytes between the directory and the payloads
-  const uint64_t dir_end = kHeader + kDirEntry * k * e;
-  const uint64_t base = rd64(h + 40);
-  const uint64_t blob_nbytes = rd64(h + 32);
-  if (version == 1 ? base != dir_end
-                   : (base < dir_end + 16ull * e || base > dir_end + 528ull * e || base % 16))
-    return LTC_ERR_CORRUPT;
-  if (blob_nbytes < base || blob_nbytes % 16) return LTC_ERR_CORRUPT;
-  out->dtype = dtype;
-  out->elem_bytes = e;
-  out->nbytes = nbytes;
-  out->chunk_bytes = chunk_bytes;
-  out->nchunks = (uint32_t)k;
-  out->blob_nbytes = blob_nbytes;
-  out->payload_base = base;
-  out->version = version;
-  out->flags = h[27];
-  return LTC_OK;
-}
-
 int ltc_decompress(const void* h_header, const void* d_blob, uint64_t blob_nbytes, void* d_dst,
                    uint64_t dst_capacity, int32_t* d_status, hipStream_t stream) {
   return decompress_impl(1, &h_header, &d_blob, &blob_nbytes, &d_dst, &dst_capacity, d_status,
@@ -843,32 +767,6 @@ int ltc_crc32_chunks(const void* d_src, uint64_t nbytes, uint32_t chunk_bytes, u
   if (nbytes == 0) return LTC_OK;
   if (!d_src || !d_crc) return LTC_ERR_INVALID_ARGUMENT;
   return ltc_crc32_chunks_batch(1, &d_src, &nbytes, chunk_bytes, &d_crc, stream);
-}
-
-int ltc_blob_stats(const void* h_prefix, uint64_t h_nbytes, ltc_stats* out) {
-  ltc_info info;
-  const int rc = ltc_blob_info(h_prefix, h_nbytes, &info);
-  if (rc) return rc;
-  if (!out || h_nbytes < info.payload_base) return LTC_ERR_INVALID_ARGUMENT;
-  memset(out, 0, sizeof(*out));
-  out->elem_bytes = info.elem_bytes;
-  out->nbytes = info.nbytes;
-  out->blob_nbytes = info.blob_nbytes;
-  const uint8_t* d = static_cast<const uint8_t*>(h_prefix) + kHeader;
-  const uint32_t e = info.elem_bytes;
-  for (uint64_t c = 0; c < info.nchunks; ++c) {
-    const uint64_t len = c + 1 < info.nchunks ? info.chunk_bytes : info.nbytes - c * (uint64_t)info.chunk_bytes;
-    for (uint32_t k = 0; k < e; ++k) {
-      const uint8_t* ent = d + kDirEntry * (c * e + k);
-      const uint32_t mode = ent[12];
-      if (mode > ((static_cast<const uint8_t*>(h_prefix)[27] & LTC_FLAG_DELTA) ? 3u : 2u))
-        return LTC_ERR_CORRUPT;
-      out->mode_count[k][mode] += 1;
-      out->payload_bytes[k] += rd32(ent + 8);
-      out->stream_bytes[k] += len / e;
-    }
-  }
-  return LTC_OK;
 }
 
 }  // extern "C"

@@ -38,9 +38,12 @@ def _u8p(a):
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        # LTC_ORACLE_LIB: another build of the same source (the sanitized one
+        # of tests/test_host_sanitized.py)
+        path = os.environ.get("LTC_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         u8p = ctypes.POINTER(ctypes.c_uint8)
         u16p = ctypes.POINTER(ctypes.c_uint16)
         u32p = ctypes.POINTER(ctypes.c_uint32)
