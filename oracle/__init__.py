@@ -19,6 +19,7 @@ ELEM_BYTES = {0: 1, 1: 2, 2: 2, 3: 4}
 MODE_RAW, MODE_RANS, MODE_CONST, MODE_ZRUN = 0, 1, 2, 3
 FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
 FLAG_DELTA = 2          # header flag: XOR delta against a base
+FLAG_TOP_LAST = 8       # layout: top-stream payloads after all others
 
 OK = 0
 ERR_INVALID_ARGUMENT = -1
@@ -162,9 +163,15 @@ def compress_bound(nbytes, dtype, chunk_bytes=131072, shared_tables=False):
                                         FLAG_SHARED_TABLES if shared_tables else 0)
 
 
-def compress(src, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None, shared_tables=False):
+def _flags(shared_tables, top_last):
+    return (FLAG_SHARED_TABLES if shared_tables else 0) | (FLAG_TOP_LAST if top_last else 0)
+
+
+def compress(src, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None, shared_tables=False,
+             top_last=False):
     """Blob (np.uint8) of the bytes of `src` read as `dtype` (a code);
-    shared_tables: format v2 (one frequency table per stream index)."""
+    shared_tables: format v2 (one frequency table per stream index);
+    top_last: the top stream of every chunk placed after all other payloads."""
     b = _as_bytes(src)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
@@ -172,7 +179,7 @@ def compress(src, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None, shar
     blob = np.zeros(cap, dtype=np.uint8)
     nb = ctypes.c_uint64(0)
     rc = lib().ltco_compress_ex(_u8p(b), b.size, dtype, chunk_bytes, threshold,
-                                FLAG_SHARED_TABLES if shared_tables else 0,
+                                _flags(shared_tables, top_last),
                                 _u8p(blob), blob.size, ctypes.byref(nb), int(nthreads))
     if rc:
         raise ValueError(f"oracle compress: status {rc}")
@@ -180,7 +187,7 @@ def compress(src, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None, shar
 
 
 def compress_delta(src, base, dtype, chunk_bytes=131072, threshold=0.95, nthreads=None,
-                   shared_tables=False):
+                   shared_tables=False, top_last=False):
     """Blob of src XOR base (same byte size), with ZipNN's zero-run rule."""
     b = _as_bytes(src)
     bb = _as_bytes(base)
@@ -192,7 +199,7 @@ def compress_delta(src, base, dtype, chunk_bytes=131072, threshold=0.95, nthread
     blob = np.zeros(cap, dtype=np.uint8)
     nb = ctypes.c_uint64(0)
     rc = lib().ltco_compress_delta(_u8p(b), _u8p(bb), b.size, dtype, chunk_bytes, threshold,
-                                   FLAG_SHARED_TABLES if shared_tables else 0,
+                                   _flags(shared_tables, top_last),
                                    _u8p(blob), blob.size, ctypes.byref(nb), int(nthreads))
     if rc:
         raise ValueError(f"oracle compress_delta: status {rc}")

@@ -25,6 +25,16 @@
 
 static uint64_t align16(uint64_t v) { return (v + 15u) & ~(uint64_t)15u; }
 
+/* Directory index of the t-th payload in blob order, for k chunks of e
+ * streams: directory order, or with the top-last layout (ltc_oracle.h) the
+ * k*(e-1) lower streams in directory order followed by the k top streams. */
+static uint64_t placed(uint64_t t, uint64_t k, int e, int top_last) {
+  if (!top_last || e == 1) return t;
+  uint64_t lower = k * (uint64_t)(e - 1);
+  if (t < lower) return t / (uint64_t)(e - 1) * (uint64_t)e + t % (uint64_t)(e - 1);
+  return (t - lower) * (uint64_t)e + (uint64_t)(e - 1);
+}
+
 int ltco_elem_bytes(int dtype) {
   switch (dtype) {
     case 0: return 1;
@@ -531,7 +541,7 @@ int ltco_encode_chunk(const uint8_t* src, uint64_t nbytes, int dtype,
 static int compress_v1(const uint8_t* src, uint64_t nbytes, int dtype,
                        uint32_t chunk_bytes, double theta, uint8_t* blob,
                        uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads,
-                       int delta) {
+                       int delta, int top_last) {
   int rc = LTCO_OK;
   int e = ltco_elem_bytes(dtype);
   uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
@@ -567,11 +577,12 @@ static int compress_v1(const uint8_t* src, uint64_t nbytes, int dtype,
     put_u32(blob + 20, (uint32_t)k);
     put_u16(blob + 24, LANES);
     blob[26] = 12;
-    blob[27] = (uint8_t)(delta ? LTCO_FLAG_DELTA : 0);
+    blob[27] = (uint8_t)((delta ? LTCO_FLAG_DELTA : 0) | (top_last ? LTCO_FLAG_TOP_LAST : 0));
     put_u64(blob + 32, cursor);
     put_u64(blob + 40, base);
     uint64_t cur = base;
-    for (uint64_t i = 0; i < s; i++) {
+    for (uint64_t t = 0; t < s; t++) {
+      uint64_t i = placed(t, k, e, top_last);
       uint8_t* d = blob + HDR_BYTES + DIR_BYTES * i;
       put_u64(d, cur);
       put_u32(d + 8, res[i].size);
@@ -593,7 +604,7 @@ int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
   int rc = check_args(nbytes, dtype, chunk_bytes, theta);
   if (rc) return rc;
   return compress_v1(src, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity, blob_nbytes,
-                     nthreads, 0);
+                     nthreads, 0, 0);
 }
 
 /* ---- format v2: one frequency table per stream index (shared tables) ---- */
@@ -677,7 +688,7 @@ uint64_t ltco_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes
 static int compress_shared(const uint8_t* src, uint64_t nbytes, int dtype,
                            uint32_t chunk_bytes, double theta, uint8_t* blob,
                            uint64_t blob_capacity, uint64_t* blob_nbytes,
-                           int nthreads, int delta) {
+                           int nthreads, int delta, int top_last) {
   int e = ltco_elem_bytes(dtype);
   uint64_t k = (nbytes + chunk_bytes - 1) / chunk_bytes;
   uint64_t s = k * (uint64_t)e;
@@ -749,7 +760,8 @@ static int compress_shared(const uint8_t* src, uint64_t nbytes, int dtype,
     put_u32(blob + 20, (uint32_t)k);
     put_u16(blob + 24, LANES);
     blob[26] = 12;
-    blob[27] = (uint8_t)(LTCO_FLAG_SHARED_TABLES | (delta ? LTCO_FLAG_DELTA : 0));
+    blob[27] = (uint8_t)(LTCO_FLAG_SHARED_TABLES | (delta ? LTCO_FLAG_DELTA : 0) |
+                         (top_last ? LTCO_FLAG_TOP_LAST : 0));
     put_u64(blob + 32, cursor);
     put_u64(blob + 40, base);
     uint64_t t = HDR_BYTES + DIR_BYTES * s;
@@ -760,7 +772,8 @@ static int compress_shared(const uint8_t* src, uint64_t nbytes, int dtype,
       t += record_bytes(lo[q], hi[q]);
     }
     uint64_t cur = base;
-    for (uint64_t i = 0; i < s; i++) {
+    for (uint64_t t = 0; t < s; t++) {
+      uint64_t i = placed(t, k, e, top_last);
       uint8_t* d = blob + HDR_BYTES + DIR_BYTES * i;
       put_u64(d, cur);
       put_u32(d + 8, res[i].size);
@@ -780,32 +793,36 @@ int ltco_compress_ex(const uint8_t* src, uint64_t nbytes, int dtype,
                      uint32_t chunk_bytes, double theta, uint32_t flags,
                      uint8_t* blob, uint64_t blob_capacity, uint64_t* blob_nbytes,
                      int nthreads) {
-  if (flags & ~(uint32_t)LTCO_FLAG_SHARED_TABLES) return LTCO_ERR_INVALID_ARGUMENT;
-  if (!(flags & LTCO_FLAG_SHARED_TABLES))
-    return ltco_compress(src, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity,
-                         blob_nbytes, nthreads);
+  if (flags & ~(uint32_t)(LTCO_FLAG_SHARED_TABLES | LTCO_FLAG_TOP_LAST))
+    return LTCO_ERR_INVALID_ARGUMENT;
   int rc = check_args(nbytes, dtype, chunk_bytes, theta);
   if (rc) return rc;
+  int top_last = (flags & LTCO_FLAG_TOP_LAST) != 0;
+  if (!(flags & LTCO_FLAG_SHARED_TABLES))
+    return compress_v1(src, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity, blob_nbytes,
+                       nthreads, 0, top_last);
   return compress_shared(src, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity,
-                         blob_nbytes, nthreads, 0);
+                         blob_nbytes, nthreads, 0, top_last);
 }
 
 int ltco_compress_delta(const uint8_t* src, const uint8_t* base, uint64_t nbytes, int dtype,
                         uint32_t chunk_bytes, double theta, uint32_t flags, uint8_t* blob,
                         uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads) {
-  if (flags & ~(uint32_t)LTCO_FLAG_SHARED_TABLES) return LTCO_ERR_INVALID_ARGUMENT;
+  if (flags & ~(uint32_t)(LTCO_FLAG_SHARED_TABLES | LTCO_FLAG_TOP_LAST))
+    return LTCO_ERR_INVALID_ARGUMENT;
   int rc = check_args(nbytes, dtype, chunk_bytes, theta);
   if (rc) return rc;
+  int top_last = (flags & LTCO_FLAG_TOP_LAST) != 0;
   /* NOTE-241: ZipNN, "Method" item 6: XOR against the base, then as usual */
   uint8_t* x = (uint8_t*)malloc(nbytes ? nbytes : 1);
   if (!x) return LTCO_ERR_INVALID_ARGUMENT;
   for (uint64_t i = 0; i < nbytes; i++) x[i] = src[i] ^ base[i];
   if (flags & LTCO_FLAG_SHARED_TABLES)
     rc = compress_shared(x, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity, blob_nbytes,
-                         nthreads, 1);
+                         nthreads, 1, top_last);
   else
     rc = compress_v1(x, nbytes, dtype, chunk_bytes, theta, blob, blob_capacity, blob_nbytes,
-                     nthreads, 1);
+                     nthreads, 1, top_last);
   free(x);
   return rc;
 }
@@ -938,8 +955,10 @@ static int decompress_impl(const uint8_t* blob, uint64_t blob_nbytes, const uint
   uint32_t chunk_bytes = get_u32(blob + 16);
   uint64_t k = get_u32(blob + 20);
   const int delta = (blob[27] & LTCO_FLAG_DELTA) != 0;
+  const int top_last = (blob[27] & LTCO_FLAG_TOP_LAST) != 0;
   if (get_u16(blob + 24) != LANES || blob[26] != 12 ||
-      (blob[27] & ~LTCO_FLAG_DELTA) != (version == 2 ? LTCO_FLAG_SHARED_TABLES : 0) ||
+      (blob[27] & ~(LTCO_FLAG_DELTA | LTCO_FLAG_TOP_LAST)) !=
+          (version == 2 ? LTCO_FLAG_SHARED_TABLES : 0) ||
       get_u32(blob + 28) != 0)
     return LTCO_ERR_CORRUPT;
   if (delta != (xbase != NULL)) return LTCO_ERR_INVALID_ARGUMENT; /* a delta blob needs its base */
@@ -990,7 +1009,6 @@ static int decompress_impl(const uint8_t* blob, uint64_t blob_nbytes, const uint
 
   dir_entry* ent = (dir_entry*)malloc((s ? s : 1) * sizeof(dir_entry));
   if (!ent) return LTCO_ERR_INVALID_ARGUMENT;
-  uint64_t cursor = base;
   for (uint64_t i = 0; i < s; i++) {
     const uint8_t* d = blob + HDR_BYTES + DIR_BYTES * i;
     ent[i].off = get_u64(d);
@@ -1001,13 +1019,23 @@ static int decompress_impl(const uint8_t* blob, uint64_t blob_nbytes, const uint
     uint64_t len = nbytes - c * (uint64_t)chunk_bytes;
     if (len > chunk_bytes) len = chunk_bytes;
     uint64_t n = len / (uint64_t)e;
-    int bad = ent[i].off != cursor || get_u16(d + 14) != 0 ||
+    int bad = get_u16(d + 14) != 0 ||
               ent[i].mode > (delta ? LTCO_MODE_ZRUN : LTCO_MODE_CONST) ||
               (ent[i].mode != LTCO_MODE_CONST && ent[i].cval != 0) ||
               (ent[i].mode == LTCO_MODE_RAW && ent[i].size != n) ||
               (ent[i].mode == LTCO_MODE_CONST && ent[i].size != 0) ||
-              ent[i].size > blob_nbytes - ent[i].off;
+              ent[i].off > blob_nbytes || ent[i].size > blob_nbytes - ent[i].off;
     if (bad) {
+      free(ent);
+      return LTCO_ERR_CORRUPT;
+    }
+  }
+  /* the offsets: each payload starts where the one before it in blob order
+     ends (rounded up to 16), the first at payload_base, the last ends the blob */
+  uint64_t cursor = base;
+  for (uint64_t t = 0; t < s; t++) {
+    uint64_t i = placed(t, k, e, top_last);
+    if (ent[i].off != cursor) {
       free(ent);
       return LTCO_ERR_CORRUPT;
     }

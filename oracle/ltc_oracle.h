@@ -90,6 +90,15 @@
  *    64-byte blocks (ceil(n/64) bits, LSB first), zero pad to 16 | nblk u64
  *    masks (bit i = byte i of the block is nonzero), zero pad to 16 | the
  *    nnz nonzero bytes in order.
+ *
+ * Top streams last (header flag bit 3, value 8; with v1, v2 and deltas):
+ * NOTE-241: ZipNN, "Method" item 5 keeps a map of the variable-size
+ * compressed pieces so each can be found on its own; the directory is that
+ * map, which leaves the order of the payloads free (READING).  In this layout
+ * the cursor first walks every stream k < E-1 in directory order, then every
+ * stream k = E-1 (the exponent byte of BF16 and FP32, "Method" item 1) in
+ * chunk order.  Entries, payloads, gaps and blob_nbytes are otherwise those
+ * of the same blob without the flag; for E = 1 the two orders coincide.
  */
 #ifndef LTC_ORACLE_H
 #define LTC_ORACLE_H
@@ -112,6 +121,7 @@ extern "C" {
 
 #define LTCO_FLAG_SHARED_TABLES 1u /* compress_ex: format v2 */
 #define LTCO_FLAG_DELTA 2u         /* header flag: XOR delta against a base */
+#define LTCO_FLAG_TOP_LAST 8u      /* payloads of stream E-1 after all others */
 
 #define LTCO_MODE_RAW 0
 #define LTCO_MODE_RANS 1
@@ -140,7 +150,8 @@ uint64_t ltco_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes);
 int ltco_compress(const uint8_t* src, uint64_t nbytes, int dtype,
                   uint32_t chunk_bytes, double theta, uint8_t* blob,
                   uint64_t blob_capacity, uint64_t* blob_nbytes, int nthreads);
-/* flags 0: ltco_compress (v1); LTCO_FLAG_SHARED_TABLES: format v2 */
+/* flags 0: ltco_compress (v1); LTCO_FLAG_SHARED_TABLES: format v2;
+ * LTCO_FLAG_TOP_LAST (with either): top streams placed last */
 uint64_t ltco_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
                                 uint32_t flags);
 int ltco_compress_ex(const uint8_t* src, uint64_t nbytes, int dtype,
@@ -155,7 +166,7 @@ int ltco_encode_chunk(const uint8_t* src, uint64_t nbytes, int dtype,
                       uint8_t* out, uint64_t out_cap, uint64_t* nout);
 int ltco_decompress(const uint8_t* blob, uint64_t blob_nbytes, uint8_t* dst,
                     uint64_t dst_capacity, uint64_t* out_nbytes, int nthreads);
-/* deltas: compress src XOR base (flags 0 or LTCO_FLAG_SHARED_TABLES); decode
+/* deltas: compress src XOR base (flags: LTCO_FLAG_SHARED_TABLES, LTCO_FLAG_TOP_LAST); decode
  * and XOR the base back in.  A delta blob needs its base and only then. */
 int ltco_compress_delta(const uint8_t* src, const uint8_t* base, uint64_t nbytes, int dtype,
                         uint32_t chunk_bytes, double theta, uint32_t flags, uint8_t* blob,
