@@ -63,6 +63,10 @@ def parse():
                     help="run every step kernel by kernel on one stream (for per-kernel profiles)")
     ap.add_argument("--crc", default="fused", choices=["fused", "beside"],
                     help="CRC-32 of the blobs computed while packing, or by its own kernel")
+    ap.add_argument("--layout", default="top-last", choices=["top-last", "directory"],
+                    help="payload order: top streams after all others (LTC_FLAG_TOP_LAST, the "
+                         "compressor then writes RAW streams straight into the blob) or directory "
+                         "order; the other one's compress times are reported beside")
     ap.add_argument("--tables", default="own", choices=["own", "shared"],
                     help="blob format: v1 (a frequency table per coded stream) or v2 (one per "
                          "stream index, shared by all chunks of a tensor)")
@@ -376,7 +380,7 @@ def digests(torch, tensors, sizes=None):
     return out
 
 
-def config_figures(name, ts, hip, sptr, torch, reps, hashes=True):
+def config_figures(name, ts, hip, sptr, torch, reps, flags, hashes=True):
     """Compress, compress_with_crc32, decompress and the CRC-32 kernel over
     one workload's tensors (batch calls, inputs in HBM), each call repeated
     back to back between two events; the exact round trip and the device
@@ -400,12 +404,13 @@ def config_figures(name, ts, hip, sptr, torch, reps, hashes=True):
     fcrcs = [torch.empty(n, dtype=torch.int32, device="cuda") for n in fcap]
 
     def comp():
-        ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, 0, blob_ptrs, caps, sizes.data_ptr(),
-                            ws.data_ptr(), ws_n)
+        ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, flags, blob_ptrs, caps,
+                            sizes.data_ptr(), ws.data_ptr(), ws_n)
 
     def comp_crc():
-        ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, 0, blob_ptrs, caps, sizes.data_ptr(),
-                            ws.data_ptr(), ws_n, CRC_CHUNK, [c.data_ptr() for c in fcrcs], fcap)
+        ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, flags, blob_ptrs, caps,
+                            sizes.data_ptr(), ws.data_ptr(), ws_n, CRC_CHUNK, [c.data_ptr() for c in fcrcs],
+                            fcap)
 
     comp()
     bsz = sizes.cpu().tolist()
@@ -461,7 +466,7 @@ def config_figures(name, ts, hip, sptr, torch, reps, hashes=True):
             "crc32_roofline_frac": frac(B + 4 * nck, t_x)}
 
 
-def other_configs(which, hip, sptr, torch, reps):
+def other_configs(which, hip, sptr, torch, reps, flags):
     """The figures of the other workloads, one after another (each freed
     before the next is generated): C1, C2, the two parts of C4 and their
     combination, and C5 (8 GiB)."""
@@ -472,14 +477,14 @@ def other_configs(which, hip, sptr, torch, reps):
     for name in which:
         if name == "c1":
             ts = [torch.from_numpy(workloads.c1().view(np.int16)).cuda().view(torch.bfloat16)]
-            res["C1"] = config_figures(name, ts, hip, sptr, torch, reps)
+            res["C1"] = config_figures(name, ts, hip, sptr, torch, reps, flags)
         elif name == "c2":
             ts = [torch.from_numpy(workloads.c2()).cuda()]
-            res["C2"] = config_figures(name, ts, hip, sptr, torch, reps)
+            res["C2"] = config_figures(name, ts, hip, sptr, torch, reps, flags)
         elif name == "c4":
             clean, h = workloads.c4()
-            a = config_figures("c4a", [torch.from_numpy(clean).cuda()], hip, sptr, torch, reps)
-            b = config_figures("c4b", [torch.from_numpy(h).cuda()], hip, sptr, torch, reps)
+            a = config_figures("c4a", [torch.from_numpy(clean).cuda()], hip, sptr, torch, reps, flags)
+            b = config_figures("c4b", [torch.from_numpy(h).cuda()], hip, sptr, torch, reps, flags)
             res["C4a"], res["C4b"] = a, b
             n, bb = a["orig_bytes"] + b["orig_bytes"], a["blob_bytes"] + b["blob_bytes"]
             tc, td = a["compress_ms"] + b["compress_ms"], a["decompress_ms"] + b["decompress_ms"]
@@ -491,7 +496,8 @@ def other_configs(which, hip, sptr, torch, reps):
                          "note": "C4a then C4b, one call each"}
         elif name == "c5":
             buf = workloads.c5_gpu("cuda")
-            res["C5"] = config_figures(name, [buf.view(torch.bfloat16)], hip, sptr, torch, reps, hashes=False)
+            res["C5"] = config_figures(name, [buf.view(torch.bfloat16)], hip, sptr, torch, reps, flags,
+                                       hashes=False)
             del buf
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -521,7 +527,8 @@ def main():
     nbytes = [t.numel() * t.element_size() for t in ts]
     N = sum(nbytes)
     shared = args.tables == "shared"
-    flags = ltc.FLAG_SHARED_TABLES if shared else 0
+    layout_flag = ltc.FLAG_TOP_LAST if args.layout == "top-last" else 0
+    flags = (ltc.FLAG_SHARED_TABLES if shared else 0) | layout_flag
     caps = [ltc.compress_bound(n, code, CHUNK, shared) for n in nbytes]
     blobs = [torch.empty(c, dtype=torch.uint8, device="cuda") for c in caps]
     ws_n = ltc.workspace_size(nbytes, code, CHUNK)
@@ -667,11 +674,28 @@ def main():
         kf["k_pack_crc"] += hip.ms(ev_f[3], ev_f[4]) / reps
         kf["k_crc32_finish"] += hip.ms(ev_f[4], ev_f[5]) / reps
 
+    # the other payload order, same inputs and buffers (its blobs have the
+    # same sizes); then the measured layout's blobs are written again
+    oflags = flags ^ ltc.FLAG_TOP_LAST
+    t_ocomp = timed(lambda: ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, oflags, blob_ptrs,
+                                                caps, sizes.data_ptr(), ws.data_ptr(), ws_n))
+    t_ofused = timed(lambda: ltc.compress_ex_raw(src_ptrs, nbytes, code, CHUNK, THRESHOLD, oflags, blob_ptrs,
+                                                 caps, sizes.data_ptr(), ws.data_ptr(), ws_n, CRC_CHUNK,
+                                                 fcrc_ptrs, fcap))
+    compress_plain()
+    torch.cuda.synchronize()
+    assert sizes.cpu().tolist() == bsz
+    other = {"layout": "directory" if layout_flag else "top-last",
+             "compress_ms": round(t_ocomp, 4), "compress_with_crc32_ms": round(t_ofused, 4),
+             "compress_roofline_frac": round((N + B) / (t_ocomp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     # algorithmic bytes per launch (what the method must move):
     #   k_decode reads the blob and writes the original bytes: B + N
     #   k_hist reads the input once: N;  k_crc32 reads the blobs: B
     #   k_encode reads the elements of the streams it codes; k_pack writes
-    #   the blob and reads the input for RAW streams: B + N
+    #   the blob and reads the input for RAW streams: B + N (in the top-last
+    #   layout k_encode writes the RAW streams it staged, so this overstates
+    #   k_pack's share; it only matters if k_pack were the dominant kernel)
     algo = {"k_decode": B + N, "k_hist": N, "k_pack": B + N, "k_crc32": B, "k_encode": N,
             "k_scan": 0, "k_decode_multi": 0}
     dom = max((n for n in k if algo[n]), key=lambda n: k[n])
@@ -717,6 +741,7 @@ def main():
                    "crc": "computed while packing (compress_with_crc32)" if fused
                           else "own kernel beside decompress",
                    "format": "v2, one table per stream index" if shared else "v1, a table per coded stream",
+                   "layout": "top streams last (LTC_FLAG_TOP_LAST)" if layout_flag else "directory order",
                    "launch": "kernel by kernel, one stream" if args.isolated
                              else "compress in 2 chunk groups on 2 streams"},
         "decompress_gbs": round(N / (t_dec * 1e-3) / 1e9, 2),
@@ -731,6 +756,7 @@ def main():
         "kernel_ms": {**{n: round(v, 4) for n, v in k.items()},
                       **{n: round(v, 4) for n, v in kf.items()}},
         "roofline": roof,
+        "other_layout": other,
         "wall_s_timed": round(wall, 3),
     }
     rec["sha256"] = {"inputs": digests(torch, ts), "blobs": digests(torch, blobs, bsz)}
@@ -745,7 +771,7 @@ def main():
         del ts, blobs, ws, outs
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        rec["configs"] = other_configs(which, hip, sptr, torch, reps)
+        rec["configs"] = other_configs(which, hip, sptr, torch, reps, flags)
     print(json.dumps(rec), flush=True)
 
 

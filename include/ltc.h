@@ -33,7 +33,8 @@
  * before anything enqueued after the call, so the call still behaves as work
  * on `stream`.  One group's compute-bound encoding then overlaps another's
  * memory-bound passes.  The groups' offset scans run in chunk order, so blobs
- * are the same as from one group.  A caller that owns every stream (or
+ * are the same as from one group (in the top-last layout the top streams'
+ * scans start after every group's lower-stream scan).  A caller that owns every stream (or
  * captures the call into a graph) passes LTC_FLAG_CALLER_STREAM_ONLY to
  * ltc_compress_batch_ex, and every kernel of the call then runs on `stream`
  * alone (measured on 28 BF16 tensors, 1.74 GB: 1.60 ms on one stream against
@@ -118,6 +119,20 @@
  *   stored (RANS on a tie); RAW if neither fits.  Decoding a delta blob
  *   needs the same base; without it, or with a base for a plain blob, the
  *   call returns INVALID_ARGUMENT.
+ *
+ * TOP-LAST LAYOUT (header flag LTC_FLAG_TOP_LAST, with v1, v2 and deltas;
+ * "NOTE-241: ZipNN", section "Method" item 5: a map of the variable-size
+ * compressed pieces lets each be found on its own -- here the directory,
+ * whose offsets leave the order of the payloads free):
+ *   Everything as without the flag except the order in which the cursor
+ *   places payloads: first every stream k < E-1 in directory order (chunk
+ *   by chunk), then every stream k = E-1 in chunk order.  Sizes, modes,
+ *   payload bytes, gaps and blob_nbytes do not change; for E = 1 the two
+ *   orders coincide.  The point is the compressor's memory traffic: the
+ *   lower streams (for BF16 and FP32 mostly RAW sign/mantissa bytes, sized
+ *   by the histogram pass) get their offsets before the top streams are
+ *   coded, so the wave that codes a chunk's top stream, which loads every
+ *   byte of its elements anyway, writes them straight into the blob.
  */
 #ifndef LTC_H
 #define LTC_H
@@ -149,6 +164,7 @@ enum { LTC_MODE_RAW = 0, LTC_MODE_RANS = 1, LTC_MODE_CONST = 2, LTC_MODE_ZRUN = 
 #define LTC_FLAG_SHARED_TABLES 1u      /* compress flags: format v2 */
 #define LTC_FLAG_DELTA 2u              /* header flag: XOR delta against a base */
 #define LTC_FLAG_CALLER_STREAM_ONLY 4u /* compress flags: no internal stream, all on `stream` */
+#define LTC_FLAG_TOP_LAST 8u           /* compress flags and header flag: top-last layout */
 
 #define LTC_HEADER_BYTES 64
 #define LTC_DEFAULT_CHUNK_BYTES 131072u
@@ -166,7 +182,8 @@ typedef struct {
   uint64_t blob_nbytes;
   uint64_t payload_base;
   uint32_t version;      /* 1, or 2 (shared tables) */
-  uint32_t flags;        /* header byte 27: LTC_FLAG_SHARED_TABLES | LTC_FLAG_DELTA */
+  uint32_t flags;        /* header byte 27: LTC_FLAG_SHARED_TABLES | LTC_FLAG_DELTA |
+                            LTC_FLAG_TOP_LAST */
 } ltc_info;
 
 /* Element size of a dtype code, 0 if unknown. */
@@ -290,14 +307,16 @@ int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint6
 
 /* Upper bound of the blob size with compress flags (0: ltc_compress_bound;
  * LTC_FLAG_SHARED_TABLES adds E table records of at most 528 bytes;
- * LTC_FLAG_CALLER_STREAM_ONLY changes nothing).  0 on bad arguments. */
+ * LTC_FLAG_CALLER_STREAM_ONLY and LTC_FLAG_TOP_LAST change nothing).  0 on
+ * bad arguments. */
 uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes, uint32_t flags);
 
 /* The general compress call: ltc_compress_batch plus
- *   flags: 0 (format v1) or LTC_FLAG_SHARED_TABLES (format v2); capacities
- *     are checked against ltc_compress_bound_ex; with
- *     LTC_FLAG_CALLER_STREAM_ONLY added, the call uses no internal stream
- *     (same blobs, all kernels on `stream` one after another);
+ *   flags: 0 (format v1) or LTC_FLAG_SHARED_TABLES (format v2), either with
+ *     LTC_FLAG_TOP_LAST (the top-last layout); capacities are checked
+ *     against ltc_compress_bound_ex; with LTC_FLAG_CALLER_STREAM_ONLY added,
+ *     the call uses no internal stream (same blobs, all kernels on `stream`
+ *     one after another);
  *   h_base_ptrs: NULL, or per tensor the device pointer of its delta base
  *     (nbytes bytes, aligned like the source): the blobs are XOR deltas
  *     (LTC_FLAG_DELTA set in the header; with checksums the CRC kernel reads
@@ -318,7 +337,8 @@ int ltc_compress_batch_ex(int count, const void* const* h_src_ptrs, const uint64
 
 /* XOR delta of d_src against d_base ("NOTE-241: ZipNN", "Method" item 6;
  * format above, DELTAS): both nbytes bytes of `dtype`, aligned to the
- * element size.  flags: 0 or LTC_FLAG_SHARED_TABLES.  Capacity, workspace
+ * element size.  flags: 0, LTC_FLAG_SHARED_TABLES, LTC_FLAG_TOP_LAST, or
+ * both.  Capacity, workspace
  * (ltc_compress_workspace_size) and errors as ltc_compress, plus
  * INVALID_ARGUMENT for a NULL or misaligned base. */
 int ltc_compress_delta(const void* d_src, const void* d_base, uint64_t nbytes, int dtype,

@@ -154,7 +154,12 @@ def _flat_bytes(t):
 FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
 FLAG_DELTA = 2          # header flag: the blob codes src XOR base
 FLAG_CALLER_STREAM_ONLY = 4  # compress flag: every kernel on the caller's stream
+FLAG_TOP_LAST = 8       # compress and header flag: top-stream payloads after all others
 NOALLOC_SCRATCH_BYTES = 64 << 20  # workspace limit of ltc_compress_noalloc
+
+
+def _flags(shared_tables, top_last):
+    return (FLAG_SHARED_TABLES if shared_tables else 0) | (FLAG_TOP_LAST if top_last else 0)
 
 
 def compress_bound(nbytes, dtype_code, chunk_bytes=DEFAULT_CHUNK_BYTES, shared_tables=False):
@@ -240,29 +245,31 @@ def decompress_raw(headers, blob_ptrs, blob_nbytes, dst_ptrs, caps, status_ptr, 
 
 
 def compress_batch(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
-                   passthrough_threshold=DEFAULT_THRESHOLD, shared_tables=False):
+                   passthrough_threshold=DEFAULT_THRESHOLD, shared_tables=False, top_last=False):
     """Blobs (uint8 GPU tensors) for up to 32 tensors of one dtype;
-    shared_tables: format v2 (one frequency table per stream index)."""
-    return _compress_batch(tensors, None, chunk_bytes, passthrough_threshold, shared_tables)
+    shared_tables: format v2 (one frequency table per stream index);
+    top_last: the top-last payload layout (LTC_FLAG_TOP_LAST)."""
+    return _compress_batch(tensors, None, chunk_bytes, passthrough_threshold, shared_tables, top_last)
 
 
 def compress_batch_delta(tensors, bases, chunk_bytes=DEFAULT_CHUNK_BYTES,
-                         passthrough_threshold=DEFAULT_THRESHOLD, shared_tables=False):
+                         passthrough_threshold=DEFAULT_THRESHOLD, shared_tables=False, top_last=False):
     """XOR-delta blobs of up to 32 tensors against their bases (same dtype
     and size each): ZipNN's delta compression of a fine-tuned model against
     its base model."""
     if len(bases) != len(tensors):
         raise ValueError("one base per tensor")
-    return _compress_batch(tensors, bases, chunk_bytes, passthrough_threshold, shared_tables)
+    return _compress_batch(tensors, bases, chunk_bytes, passthrough_threshold, shared_tables, top_last)
 
 
 def compress_delta(t, base, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
-                   shared_tables=False):
+                   shared_tables=False, top_last=False):
     """XOR-delta blob of a GPU tensor against a base of the same dtype and size."""
-    return compress_batch_delta([t], [base], chunk_bytes, passthrough_threshold, shared_tables)[0]
+    return compress_batch_delta([t], [base], chunk_bytes, passthrough_threshold, shared_tables,
+                                top_last)[0]
 
 
-def _compress_batch(tensors, bases, chunk_bytes, passthrough_threshold, shared_tables):
+def _compress_batch(tensors, bases, chunk_bytes, passthrough_threshold, shared_tables, top_last=False):
     if not 1 <= len(tensors) <= BATCH_MAX:
         raise ValueError(f"1..{BATCH_MAX} tensors per batch")
     ts = [_flat_bytes(t) for t in tensors]
@@ -285,7 +292,7 @@ def _compress_batch(tensors, bases, chunk_bytes, passthrough_threshold, shared_t
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
     sizes = torch.zeros(len(ts), dtype=torch.int64, device=dev)
     compress_ex_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
-                    FLAG_SHARED_TABLES if shared_tables else 0, [b.data_ptr() for b in blobs], caps,
+                    _flags(shared_tables, top_last), [b.data_ptr() for b in blobs], caps,
                     sizes.data_ptr(), ws.data_ptr(), ws.numel(),
                     base_ptrs=[b.data_ptr() for b in bs] if bs is not None else None)
     host_sizes = sizes.cpu().tolist()
@@ -294,7 +301,8 @@ def _compress_batch(tensors, bases, chunk_bytes, passthrough_threshold, shared_t
 
 def compress_batch_with_crc32(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
                               passthrough_threshold=DEFAULT_THRESHOLD,
-                              checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES, shared_tables=False):
+                              checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES, shared_tables=False,
+                              top_last=False):
     """(blobs, checksums): the blobs of compress_batch and, per blob, the
     CRC-32 of each checksum_chunk_bytes-byte chunk (int32 GPU tensors holding
     the CRC bits)."""
@@ -318,7 +326,7 @@ def compress_batch_with_crc32(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
     sizes = torch.zeros(len(ts), dtype=torch.int64, device=dev)
     compress_ex_raw([t.data_ptr() for t in ts], nbytes, code, chunk_bytes, passthrough_threshold,
-                    FLAG_SHARED_TABLES if shared_tables else 0, [b.data_ptr() for b in blobs], caps,
+                    _flags(shared_tables, top_last), [b.data_ptr() for b in blobs], caps,
                     sizes.data_ptr(), ws.data_ptr(), ws.numel(), checksum_chunk_bytes,
                     [c.data_ptr() for c in crcs], ccaps)
     host_sizes = sizes.cpu().tolist()
@@ -327,17 +335,18 @@ def compress_batch_with_crc32(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
 
 
 def compress_with_crc32(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
-                        checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES, shared_tables=False):
+                        checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES, shared_tables=False,
+                        top_last=False):
     """(blob, checksums) of one GPU tensor (cuZipNN's compress_tensor_with_crc32)."""
     blobs, crcs = compress_batch_with_crc32([t], chunk_bytes, passthrough_threshold,
-                                            checksum_chunk_bytes, shared_tables)
+                                            checksum_chunk_bytes, shared_tables, top_last)
     return blobs[0], crcs[0]
 
 
 def compress(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
-             shared_tables=False):
+             shared_tables=False, top_last=False):
     """Blob (1-D uint8 tensor on t's device) of a GPU tensor's bytes."""
-    return compress_batch([t], chunk_bytes, passthrough_threshold, shared_tables)[0]
+    return compress_batch([t], chunk_bytes, passthrough_threshold, shared_tables, top_last)[0]
 
 
 def blob_info(blob_or_header):
@@ -486,10 +495,10 @@ def decompress_from_host(blob, shape=None, device=None):
 
 
 def compress_to_host(t, chunk_bytes=DEFAULT_CHUNK_BYTES, passthrough_threshold=DEFAULT_THRESHOLD,
-                     pin_memory=True, shared_tables=False):
+                     pin_memory=True, shared_tables=False, top_last=False):
     """cuZipNN's compress_tensor: the blob of a GPU tensor as a 1-D uint8 CPU
     tensor (pinned by default, ready for decompress_from_host)."""
-    blob = compress(t, chunk_bytes, passthrough_threshold, shared_tables)
+    blob = compress(t, chunk_bytes, passthrough_threshold, shared_tables, top_last)
     out = torch.empty(blob.numel(), dtype=torch.uint8, pin_memory=pin_memory)
     out.copy_(blob)
     return out

@@ -51,7 +51,7 @@ constexpr uint64_t kCopyGroupBytes = 16ull << 20;
 
 struct PipeRes {
   hipStream_t s[kPipeGroups] = {};
-  hipEvent_t fork = nullptr, scan[kPipeGroups] = {}, done[kPipeGroups] = {};
+  hipEvent_t fork = nullptr, scan[kPipeGroups] = {}, top[kPipeGroups] = {}, done[kPipeGroups] = {};
   hipEvent_t copied[kCopyGroupsMax] = {};
   bool ok = false;
 };
@@ -71,6 +71,7 @@ PipeRes* pipe_res(hipStream_t stream) {
     for (int g = 0; g < kPipeGroups; ++g) {
       if (g > 0) ok = ok && hipStreamCreateWithFlags(&r->s[g], hipStreamNonBlocking) == hipSuccess;
       ok = ok && hipEventCreateWithFlags(&r->scan[g], hipEventDisableTiming) == hipSuccess;
+      ok = ok && hipEventCreateWithFlags(&r->top[g], hipEventDisableTiming) == hipSuccess;
       ok = ok && hipEventCreateWithFlags(&r->done[g], hipEventDisableTiming) == hipSuccess;
     }
     for (int g = 0; g < kCopyGroupsMax; ++g)
@@ -95,20 +96,43 @@ hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipE
     const hipError_t err = launch_v2_tables(t, w, stream, ev);
     if (err != hipSuccess) return err;
   }
-  if (ev || one_stream || total < kPipeMinChunks)
-    return launch_compress(t, w, stream, ev, nullptr, nullptr, staged);
+  // one stream: the two halves of the top-last schedule back to back
+  auto whole = [&](const hipEvent_t* e) -> hipError_t {
+    if (!t.top_last) return launch_compress(t, w, stream, e, nullptr, nullptr, staged);
+    const hipError_t err = launch_compress_front(t, w, stream, e, nullptr, nullptr, staged);
+    return err == hipSuccess ? launch_compress_back(t, w, stream, e, nullptr, nullptr) : err;
+  };
+  if (ev || one_stream || total < kPipeMinChunks) return whole(ev);
   std::lock_guard<std::mutex> lock(g_pipe_mu);
   PipeRes* r = pipe_res(stream);
-  if (!r) return launch_compress(t, w, stream, nullptr, nullptr, nullptr, staged);
+  if (!r) return whole(nullptr);
   hipError_t err = hipEventRecord(r->fork, stream);
   for (int g = 1; g < kPipeGroups && err == hipSuccess; ++g) err = hipStreamWaitEvent(r->s[g], r->fork, 0);
-  for (int g = 0; g < kPipeGroups && err == hipSuccess; ++g) {
+  auto group = [&](int g) {
     CTable tg = t;
     tg.c_begin = total * g / kPipeGroups;
     tg.c_end = total * (g + 1) / kPipeGroups;
-    hipStream_t st = g == 0 ? stream : r->s[g];
-    err = launch_compress(tg, w, st, nullptr, g > 0 ? r->scan[g - 1] : nullptr, r->scan[g], staged);
-    if (err == hipSuccess && g > 0) err = hipEventRecord(r->done[g], st);
+    return tg;
+  };
+  auto gstream = [&](int g) { return g == 0 ? stream : r->s[g]; };
+  if (!t.top_last) {
+    for (int g = 0; g < kPipeGroups && err == hipSuccess; ++g) {
+      err = launch_compress(group(g), w, gstream(g), nullptr, g > 0 ? r->scan[g - 1] : nullptr, r->scan[g], staged);
+      if (err == hipSuccess && g > 0) err = hipEventRecord(r->done[g], gstream(g));
+    }
+  } else {
+    // front halves (lower scans chained in chunk order), then back halves:
+    // the first top scan waits for the last lower scan, each later one for
+    // the top scan before it.  Every event is recorded (enqueued) before a
+    // wait on it is enqueued.
+    for (int g = 0; g < kPipeGroups && err == hipSuccess; ++g)
+      err = launch_compress_front(group(g), w, gstream(g), nullptr, g > 0 ? r->scan[g - 1] : nullptr,
+                                  r->scan[g], staged);
+    for (int g = 0; g < kPipeGroups && err == hipSuccess; ++g) {
+      err = launch_compress_back(group(g), w, gstream(g), nullptr,
+                                 g == 0 ? r->scan[kPipeGroups - 1] : r->top[g - 1], r->top[g]);
+      if (err == hipSuccess && g > 0) err = hipEventRecord(r->done[g], gstream(g));
+    }
   }
   for (int g = 1; g < kPipeGroups && err == hipSuccess; ++g) err = hipStreamWaitEvent(stream, r->done[g], 0);
   return err;
@@ -217,7 +241,7 @@ uint32_t words_capacity(uint32_t chunk_bytes, uint32_t e) {
 }
 
 struct Layout {
-  uint64_t sinfo, freq, hist, plane, ptab, pbase, zinfo, states, offsets, blobn, frames, words, total;
+  uint64_t sinfo, freq, hist, plane, ptab, pbase, zinfo, states, offsets, blobn, toprun, frames, words, total;
 };
 
 // frames: one u32 per KiB of every blob's bound (compress_with_crc32);
@@ -235,6 +259,7 @@ Layout layout(uint64_t streams, int count, uint32_t wcap, uint64_t frames, uint3
   l.states = cur;  cur = round_up(cur + 256 * streams, kAlign);
   l.offsets = cur; cur = round_up(cur + 8 * streams, kAlign);
   l.blobn = cur;   cur = round_up(cur + 8 * (uint64_t)count, kAlign);
+  l.toprun = cur;  cur = round_up(cur + 8 * (uint64_t)count, kAlign);
   l.frames = cur;  cur = round_up(cur + 4 * frames, kAlign);
   l.words = cur;   cur = round_up(cur + 2ull * wcap * streams, kAlign);
   l.total = cur;
@@ -286,7 +311,8 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
                   uint32_t flags = 0, const void* const* bases = nullptr) {
   if (count < 1 || count > kMaxJobs || !srcs || !nbytes || !blobs || !caps || !d_blob_nbytes)
     return LTC_ERR_INVALID_ARGUMENT;
-  if (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY)) return LTC_ERR_INVALID_ARGUMENT;
+  if (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY | LTC_FLAG_TOP_LAST))
+    return LTC_ERR_INVALID_ARGUMENT;
   if (!(theta > 0.0 && theta <= 1.0)) return LTC_ERR_INVALID_ARGUMENT;
   const bool one_stream = (flags & LTC_FLAG_CALLER_STREAM_ONLY) != 0;
   const uint32_t e = elem_bytes(dtype);
@@ -325,6 +351,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   t.dtype = (uint32_t)dtype;
   t.v2 = (flags & LTC_FLAG_SHARED_TABLES) ? 1u : 0u;
   t.delta = bases ? 1u : 0u;
+  t.top_last = (flags & LTC_FLAG_TOP_LAST) ? 1u : 0u;
   bool vec = chunk_bytes % 16 == 0;
   uint64_t chunk0 = 0;
   for (int i = 0; i < count; ++i) {
@@ -358,6 +385,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   w.states = reinterpret_cast<uint32_t*>(ws + l.states);
   w.offsets = reinterpret_cast<uint64_t*>(ws + l.offsets);
   w.blob_nbytes = reinterpret_cast<uint64_t*>(ws + l.blobn);
+  w.top_run = reinterpret_cast<uint64_t*>(ws + l.toprun);
   w.words = reinterpret_cast<uint16_t*>(ws + l.words);
   if (!crc.chunk_bytes) return run_compress(t, w, stream, ev, one_stream) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 
@@ -412,7 +440,8 @@ uint32_t rd_flags(const void* header) { return static_cast<const uint8_t*>(heade
 // [T*g/G, T*(g+1)/G); its bytes of blob j are that tensor's directory (first
 // group of the tensor) and the payloads from the first stream of its first
 // chunk to the first stream of the next group's (or the blob's end), clamped
-// to the blob.  The decoder validates every offset it uses, so a corrupt
+// to the blob; for a top-last blob, that span for its lower streams and
+// another for its top streams (host_group_ranges).  The decoder validates every offset it uses, so a corrupt
 // directory can only leave bytes of the staging buffer stale, never lead to
 // an access outside it.
 hipError_t decode_from_host(int dtype, const DTable& t, uint32_t e, const void* const* host_blobs,
@@ -423,7 +452,8 @@ hipError_t decode_from_host(int dtype, const DTable& t, uint32_t e, const void* 
   uint64_t total = 0;
   for (uint32_t j = 0; j < t.count; ++j) {
     const DJob& jb = t.jobs[j];
-    hb[j] = HostBlob{static_cast<const uint8_t*>(host_blobs[j]), jb.blob_nbytes, jb.chunk0, jb.nchunks};
+    hb[j] = HostBlob{static_cast<const uint8_t*>(host_blobs[j]), jb.blob_nbytes, jb.chunk0, jb.nchunks,
+                     jb.top_last != 0};
     total += jb.blob_nbytes;
   }
   const uint64_t G = host_copy_groups(total, T, kCopyGroupBytes, kCopyGroupsMax);
@@ -433,7 +463,7 @@ hipError_t decode_from_host(int dtype, const DTable& t, uint32_t e, const void* 
   hipStream_t cs = r->s[1];
   hipError_t err = hipEventRecord(r->fork, stream);
   if (err == hipSuccess) err = hipStreamWaitEvent(cs, r->fork, 0);
-  HostRange rg[kMaxJobs];
+  HostRange rg[2 * kMaxJobs];
   for (uint64_t g = 0; g < G && err == hipSuccess; ++g) {
     const uint32_t nr = host_group_ranges(hb, t.count, e, T, G, g, rg);
     for (uint32_t q = 0; q < nr && err == hipSuccess; ++q) {
@@ -497,6 +527,7 @@ int decompress_impl(int count, const void* const* headers, const void* const* bl
     jb.status = d_status + i;
     jb.payload_base = info.payload_base;
     jb.v2 = info.version == 2 ? 1u : 0u;
+    jb.top_last = (info.flags & LTC_FLAG_TOP_LAST) ? 1u : 0u;
     jb.blob_nbytes = info.blob_nbytes;
     jb.nbytes = info.nbytes;
     jb.chunk0 = chunk0;
@@ -537,7 +568,7 @@ uint64_t ltc_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
 
 uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes, uint32_t flags) {
   if (check_shape(nbytes, dtype, chunk_bytes) ||
-      (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY)))
+      (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY | LTC_FLAG_TOP_LAST)))
     return 0;
   return bound_flags(nbytes, elem_bytes(dtype), chunk_bytes, flags);
 }

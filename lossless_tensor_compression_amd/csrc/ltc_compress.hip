@@ -694,14 +694,21 @@ template <int DT> __device__ __forceinline__ uint2 stream_bytes8(const uint32_t*
 //
 // Staging.  The wave coding a chunk's top byte loads every byte of its
 // elements, so it also writes the chunk's RAW streams (those k_hist decided,
-// named in its record's third word), in blob order, into their own
-// workspace slots, which nothing else uses; k_pack then copies them instead
-// of regrouping the input again.  Only whole chunks of full 8-step blocks
-// coded in lock step are staged, and a stream is marked staged (fourth word
-// of its record) once every block is written and the top stream was not
-// abandoned.
+// named in its record's third word).  In the top-last layout their blob
+// offsets are known by then (the lower streams are scanned before the top
+// streams are coded), so the bytes go straight to their place in the blob;
+// otherwise they go, in blob order, into the streams' own workspace slots,
+// which nothing else uses, and k_pack copies them instead of regrouping the
+// input again.  Only whole chunks of full 8-step blocks coded in lock step
+// are staged, and a stream is marked staged (fourth word of its record) once
+// every block is written and the top stream was not abandoned; k_pack writes
+// the others whole.
+//
+// A launch codes the stream indices kfirst, kfirst - 1, ... (nplanes of
+// them): all E at once, or in the top-last layout the lower ones and then,
+// after their scan, the top one.
 template <int DT, bool DELTA>
-__global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
+__global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirst, uint32_t nplanes) {
   constexpr int E = Dt<DT>::E;
   constexpr int U = kEncStreams;
   __shared__ uint4 tab[U][256];
@@ -722,12 +729,12 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   uint32_t k;
   uint64_t g0;
   if constexpr (DELTA) {
-    const uint32_t grp = blockIdx.x / (8u * E), r = blockIdx.x % (8u * E);
-    k = (uint32_t)(E - 1) - r / 8u;
+    const uint32_t grp = blockIdx.x / (8u * nplanes), r = blockIdx.x % (8u * nplanes);
+    k = kfirst - r / 8u;
     g0 = t.c_begin + (uint64_t)(grp * 8u + r % 8u) * U;
   } else {
-    const uint32_t pairs = gridDim.x / E;
-    k = (uint32_t)(E - 1) - blockIdx.x / pairs;
+    const uint32_t pairs = gridDim.x / nplanes;
+    k = kfirst - blockIdx.x / pairs;
     g0 = t.c_begin + (uint64_t)(blockIdx.x % pairs) * U;
   }
   const uint32_t wcap = t.wcap;
@@ -739,6 +746,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
   const uint8_t* bsrc[U];
   const uint16_t* ftab[U];
   uint4 fallback[U];  // the stream's directory info if coding it does not pay
+  uint8_t* rdst[U][E > 1 ? E - 1 : 1];  // where staged RAW stream j of the chunk goes
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     on[u] = false;
@@ -748,6 +756,8 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     bsrc[u] = nullptr;
     ftab[u] = nullptr;
     fallback[u] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < (E > 1 ? E - 1 : 1); ++q) rdst[u][q] = nullptr;
     const uint64_t g = g0 + u;
     if (g >= t.c_end) continue;
     const uint64_t s = g * E + k;
@@ -763,8 +773,14 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
     full[u] = n[u] / 64;
     lo[u] = (info >> 16) & 0xFFu;
     hi[u] = info >> 24;
-    if (E > 1 && k == (uint32_t)(E - 1) && n[u] % (64u * kEncBlock) == 0 && n[u] <= 2u * wcap)
+    if (E > 1 && k == (uint32_t)(E - 1) && n[u] % (64u * kEncBlock) == 0 && n[u] <= 2u * wcap) {
       smask[u] = w.sinfo[4 * s + 2];
+#pragma unroll
+      for (int q = 0; q < E - 1; ++q)
+        if (smask[u] & (1u << q))
+          rdst[u][q] = t.top_last ? job.blob + w.offsets[s - k + q]
+                                  : reinterpret_cast<uint8_t*>(w.words + (s - k + q) * wcap);
+    }
     // v2: the plane's table and no table in the payload
     wo[u] = t.v2 ? kRansFixed : (uint32_t)align16(kRansFixed + 2u * (hi[u] - lo[u] + 1u));
     ftab[u] = t.v2 ? w.ptab + ((uint64_t)j * E + k) * 256 : w.freq + 256 * s;
@@ -981,8 +997,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w) {
 #pragma unroll
         for (int j = 0; j < E - 1; ++j)
           if (smask[u] & (1u << j)) {  // a uniform block address and a lane offset
-            uint8_t* blk = reinterpret_cast<uint8_t*>(w.words + (sid[u] - k + j) * wcap) +
-                           64u * (full[u] - kEncBlock * (bi + 1));
+            uint8_t* blk = rdst[u][j] + 64u * (full[u] - kEncBlock * (bi + 1));
             *reinterpret_cast<uint2*>(blk + 8u * lane) = rw[u][j];
           }
     };
@@ -1089,11 +1104,15 @@ __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int o) {
 }
 
 // One workgroup per tensor: exclusive scan of the 16-byte-aligned payload
-// sizes of the tensor's streams inside this launch's chunk range.  A
+// sizes of the tensor's streams inside this launch's chunk range, in blob
+// order.  part 0: every stream (directory order); top-last layout: part 1
+// the lower streams k < E-1 (directory order), part 2 the top streams (chunk
+// order), which start where the tensor's last lower stream ends.  A
 // pipelined call scans its groups in chunk order; the running offset passes
-// from one group to the next through blob_nbytes[j], and the group holding
-// the tensor's last chunk writes the blob size and the header.
-__global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32_t E) {
+// from one group to the next through blob_nbytes[j] (parts 0 and 1) or
+// top_run[j] (part 2), and the group holding the tensor's last chunk writes
+// the blob size and the header (parts 0 and 2).
+__global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32_t E, uint32_t part) {
   __shared__ uint64_t wave_tot[kScanThreads / 64];
   const int j = blockIdx.x;
   const CJob& job = t.jobs[j];
@@ -1107,16 +1126,23 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
   }
   const bool first = c_lo == job.chunk0, final = c_hi == job.chunk0 + job.nchunks;
   const uint64_t s0 = c_lo * E;
-  const uint64_t S = (c_hi - c_lo) * E;
+  // streams per chunk in this part, and the first of them
+  const uint32_t per = part == 0 ? E : part == 1 ? E - 1 : 1u;
+  const uint32_t k0 = part == 2 ? E - 1 : 0u;
+  const uint64_t S = (c_hi - c_lo) * per;
   const uint64_t base = t.v2 ? w.pbase[j] : kHeader + kDirEntry * (uint64_t)job.nchunks * E;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64;
-  uint64_t running = first ? base : w.blob_nbytes[j];
+  uint64_t running = part == 2 ? (first ? w.blob_nbytes[j] : w.top_run[j]) : first ? base : w.blob_nbytes[j];
+  // global stream index of the idx-th stream of this part in the range
+  auto sidx = [&](uint64_t idx) -> uint64_t {
+    return per == E ? s0 + idx : s0 + (idx / per) * E + k0 + idx % per;
+  };
   for (uint64_t tile = 0; tile < S; tile += 4 * kScanThreads) {
     uint64_t sz[4], local = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint64_t idx = tile + 4 * tid + i;
-      sz[i] = idx < S ? align16(w.sinfo[4 * (s0 + idx)]) : 0;
+      sz[i] = idx < S ? align16(w.sinfo[4 * sidx(idx)]) : 0;
       local += sz[i];
     }
     uint64_t inc = local;
@@ -1136,14 +1162,17 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint64_t idx = tile + 4 * tid + i;
-      if (idx < S) w.offsets[s0 + idx] = off;
+      if (idx < S) w.offsets[sidx(idx)] = off;
       off += sz[i];
     }
     running += tile_total;
     __syncthreads();
   }
-  if (tid == 0) w.blob_nbytes[j] = running;
-  if (!final) return;
+  if (tid == 0) {
+    if (part == 2) w.top_run[j] = running;
+    else w.blob_nbytes[j] = running;
+  }
+  if (!final || part == 1) return;
   if (tid == 0) *job.blob_nbytes_out = running;
   if (tid < 4) {  // header
     uint4 v;
@@ -1153,7 +1182,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
     else if (tid == 1)
       v = make_uint4(t.chunk_bytes, job.nchunks,
                      64u | (12u << 16) | ((t.v2 ? LTC_FLAG_SHARED_TABLES : 0u) << 24) |
-                         ((t.delta ? LTC_FLAG_DELTA : 0u) << 24),
+                         ((t.delta ? LTC_FLAG_DELTA : 0u) << 24) | ((t.top_last ? LTC_FLAG_TOP_LAST : 0u) << 24),
                      0u);
     else if (tid == 2)
       v = make_uint4((uint32_t)running, (uint32_t)(running >> 32), (uint32_t)base,
@@ -1462,8 +1491,9 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
       split_frames(cr, (uint32_t)(a & 63), a >> 6, job.frames, pos, lane);
     }
   }
-  // RAW streams: copied from their workspace slots when k_encode staged
-  // them (stmask), else regrouped from the input
+  // RAW streams: when k_encode staged them (stmask), already in place
+  // (top-last layout; only read back for the checksums) or copied from their
+  // workspace slots; else regrouped from the input
   uint32_t rawmask = 0, stmask = 0;
   uint64_t raw_off[E];
 #pragma unroll
@@ -1482,13 +1512,17 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
       write_zrun<DT, DELTA>(blob + raw_off[k], src, job.base + c * t.chunk_bytes, n, k, si.z, si.w, si.x,
                             t.vec16 != 0, red);
   }
+  const bool inplace = t.top_last != 0;
+  if (!CRC && inplace) rawmask &= ~stmask;
   if (!rawmask) return;
   const uint32_t units = (n + 15) / 16;
   const bool regroup = (rawmask & ~stmask) != 0;
   // unit u of RAW stream k; y: the regrouped elements when not staged
   auto raw_unit = [&](int k, uint32_t u, const uint32_t* y) -> uint4 {
     if (stmask & (1u << k))
-      return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(w.words + (s0 + k) * t.wcap) + 16 * u);
+      return *reinterpret_cast<const uint4*>(
+          inplace ? blob + raw_off[k] + 16 * u
+                  : reinterpret_cast<const uint8_t*>(w.words + (s0 + k) * t.wcap) + 16 * u);
     return make_uint4(pack4(y, k), pack4(y + 4, k), pack4(y + 8, k), pack4(y + 12, k));
   };
   if constexpr (!CRC) {
@@ -1545,7 +1579,7 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
         uint32_t cr = 0;
         if (have) {
           const uint4 v = (kAhead && (stmask & (1u << k))) ? cv[k] : raw_unit(k, u, y);
-          *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = v;
+          if (!(inplace && (stmask & (1u << k)))) *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = v;
           cr = crc_step16(L.c, 0u, v);
         }
         const uint64_t d = raw_off[k] / 16 - a0;  // >= 0: streams are laid out in order
@@ -1580,6 +1614,33 @@ __attribute__((amdgpu_waves_per_eu(CRC ? 4 : 1))) void k_pack(CTable t, CWork w)
 
 // ------------------------------------------------------------------ launch
 
+// k_encode for stream indices kfirst, kfirst - 1, ... (nplanes of them) of
+// chunks [t.c_begin, t.c_end)
+template <int DT, bool DELTA>
+static void launch_encode(const CTable& t, const CWork& w, hipStream_t st, uint32_t kfirst,
+                          uint32_t nplanes) {
+  constexpr uint64_t U = kEncStreams;
+  const uint64_t chunks = t.c_end - t.c_begin;
+  if (!chunks || !nplanes) return;
+  const uint32_t grid = DELTA ? (uint32_t)((chunks + 8 * U - 1) / (8 * U) * 8 * nplanes)
+                              : (uint32_t)((chunks + U - 1) / U * nplanes);
+  hipLaunchKernelGGL((k_encode<DT, DELTA>), dim3(grid), dim3(64), 0, st, t, w, kfirst, nplanes);
+}
+
+template <int DT, bool DELTA>
+static void launch_pack(const CTable& t, const CWork& w, hipStream_t st) {
+  const uint64_t chunks = t.c_end - t.c_begin;
+  if (!chunks) return;
+  if constexpr (DELTA) {  // the blob is read back for checksums (no CRC variant)
+    hipLaunchKernelGGL((k_pack<DT, false, true>), dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
+  } else {
+    if (t.crc)
+      hipLaunchKernelGGL((k_pack<DT, true, false>), dim3((uint32_t)chunks), dim3(kPackCrcThreads), 0, st, t, w);
+    else
+      hipLaunchKernelGGL((k_pack<DT, false, false>), dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
+  }
+}
+
 template <int DT, bool DELTA>
 static hipError_t launch_compress_d(const CTable& t, const CWork& w, hipStream_t st,
                                     const hipEvent_t* ev, hipEvent_t scan_after,
@@ -1591,24 +1652,50 @@ static hipError_t launch_compress_d(const CTable& t, const CWork& w, hipStream_t
     if (chunks) hipLaunchKernelGGL((k_hist<DT, DELTA>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
     record(ev, 1, st);
   }
-  if (chunks)
-    hipLaunchKernelGGL((k_encode<DT, DELTA>),
-                       dim3(DELTA ? (uint32_t)((chunks + 8 * kEncStreams - 1) / (8 * kEncStreams) * 8 * E)
-                                  : (uint32_t)((chunks + kEncStreams - 1) / kEncStreams * E)),
-                       dim3(64), 0, st, t, w);
+  launch_encode<DT, DELTA>(t, w, st, E - 1, E);
   record(ev, 2, st);
   if (scan_after) (void)hipStreamWaitEvent(st, scan_after, 0);
-  hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E);
+  hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E, 0u);
   if (scan_done) (void)hipEventRecord(scan_done, st);
   record(ev, 3, st);
-  if constexpr (DELTA) {  // the blob is read back for checksums (no CRC variant)
-    if (chunks) hipLaunchKernelGGL((k_pack<DT, false, true>), dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
-  } else {
-    if (chunks && t.crc)
-      hipLaunchKernelGGL((k_pack<DT, true, false>), dim3((uint32_t)chunks), dim3(kPackCrcThreads), 0, st, t, w);
-    else if (chunks)
-      hipLaunchKernelGGL((k_pack<DT, false, false>), dim3((uint32_t)chunks), dim3(kPackThreads), 0, st, t, w);
+  launch_pack<DT, DELTA>(t, w, st);
+  record(ev, 4, st);
+  return hipGetLastError();
+}
+
+// Top-last layout, first half for chunks [c_begin, c_end): k_hist, the lower
+// streams' coding, their scan, then the top streams' coding, which writes
+// the staged RAW streams at the offsets that scan gave.
+template <int DT, bool DELTA>
+static hipError_t launch_front_d(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                                 hipEvent_t scan_after, hipEvent_t scan_done, bool staged) {
+  constexpr int E = Dt<DT>::E;
+  const uint64_t chunks = t.c_end - t.c_begin;
+  if (!staged) {
+    record(ev, 0, st);
+    if (chunks) hipLaunchKernelGGL((k_hist<DT, DELTA>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
+    record(ev, 1, st);
   }
+  if (E > 1) launch_encode<DT, DELTA>(t, w, st, E - 2, E - 1);
+  if (scan_after) (void)hipStreamWaitEvent(st, scan_after, 0);
+  hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E, 1u);
+  if (scan_done) (void)hipEventRecord(scan_done, st);
+  launch_encode<DT, DELTA>(t, w, st, E - 1, 1);
+  record(ev, 2, st);
+  return hipGetLastError();
+}
+
+// second half: the top streams' scan (the first group's needs every
+// group's lower scan) and k_pack
+template <int DT, bool DELTA>
+static hipError_t launch_back_d(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                                hipEvent_t scan_after, hipEvent_t scan_done) {
+  constexpr int E = Dt<DT>::E;
+  if (scan_after) (void)hipStreamWaitEvent(st, scan_after, 0);
+  hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E, 2u);
+  if (scan_done) (void)hipEventRecord(scan_done, st);
+  record(ev, 3, st);
+  launch_pack<DT, DELTA>(t, w, st);
   record(ev, 4, st);
   return hipGetLastError();
 }
@@ -1619,6 +1706,20 @@ static hipError_t launch_compress_t(const CTable& t, const CWork& w, hipStream_t
                                     hipEvent_t scan_done, bool staged) {
   return t.delta ? launch_compress_d<DT, true>(t, w, st, ev, scan_after, scan_done, staged)
                  : launch_compress_d<DT, false>(t, w, st, ev, scan_after, scan_done, staged);
+}
+
+template <int DT>
+static hipError_t launch_front_t(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                                 hipEvent_t scan_after, hipEvent_t scan_done, bool staged) {
+  return t.delta ? launch_front_d<DT, true>(t, w, st, ev, scan_after, scan_done, staged)
+                 : launch_front_d<DT, false>(t, w, st, ev, scan_after, scan_done, staged);
+}
+
+template <int DT>
+static hipError_t launch_back_t(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                                hipEvent_t scan_after, hipEvent_t scan_done) {
+  return t.delta ? launch_back_d<DT, true>(t, w, st, ev, scan_after, scan_done)
+                 : launch_back_d<DT, false>(t, w, st, ev, scan_after, scan_done);
 }
 
 // v2, all chunks of t: histograms (summed per plane), plane tables and
@@ -1648,6 +1749,28 @@ hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, cons
     case LTC_BF16: return launch_compress_t<LTC_BF16>(t, w, st, ev, scan_after, scan_done, staged);
     case LTC_FP16: return launch_compress_t<LTC_FP16>(t, w, st, ev, scan_after, scan_done, staged);
     case LTC_FP32: return launch_compress_t<LTC_FP32>(t, w, st, ev, scan_after, scan_done, staged);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_compress_front(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                                 hipEvent_t scan_after, hipEvent_t scan_done, bool staged) {
+  switch (t.dtype) {
+    case LTC_U8: return launch_front_t<LTC_U8>(t, w, st, ev, scan_after, scan_done, staged);
+    case LTC_BF16: return launch_front_t<LTC_BF16>(t, w, st, ev, scan_after, scan_done, staged);
+    case LTC_FP16: return launch_front_t<LTC_FP16>(t, w, st, ev, scan_after, scan_done, staged);
+    case LTC_FP32: return launch_front_t<LTC_FP32>(t, w, st, ev, scan_after, scan_done, staged);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_compress_back(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                                hipEvent_t scan_after, hipEvent_t scan_done) {
+  switch (t.dtype) {
+    case LTC_U8: return launch_back_t<LTC_U8>(t, w, st, ev, scan_after, scan_done);
+    case LTC_BF16: return launch_back_t<LTC_BF16>(t, w, st, ev, scan_after, scan_done);
+    case LTC_FP16: return launch_back_t<LTC_FP16>(t, w, st, ev, scan_after, scan_done);
+    case LTC_FP32: return launch_back_t<LTC_FP32>(t, w, st, ev, scan_after, scan_done);
     default: return hipErrorInvalidValue;
   }
 }

@@ -133,11 +133,27 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
            (mode[k] == LTC_MODE_RAW && size[k] != n) || (mode[k] == LTC_MODE_CONST && size[k] != 0) ||
            (mode[k] == LTC_MODE_RANS && size[k] < kRansFixed + (job.v2 ? 0u : 16u)) || off[k] > B ||
            (uint64_t)size[k] > B - off[k];
-    if (k == 0 && c == 0) bad |= off[0] != job.payload_base;
-    if (k > 0) bad |= off[k] != align16(off[k - 1] + size[k - 1]);
     nr += mode[k] == LTC_MODE_RANS;
   }
-  {
+  // the offset chain: every payload starts where the one before it in blob
+  // order ends, rounded up to 16; the first at payload_base, the last ends
+  // the blob.  Directory order: the chunk's own links and the link to the
+  // next chunk.  Top-last: the link into each of the chunk's streams.
+  if (E > 1 && job.top_last) {
+    auto end_of = [&](uint64_t si) -> uint64_t {  // where entry si's payload ends
+      const uint4 e = dir[si];
+      return align16(((uint64_t)e.x | ((uint64_t)e.y << 32)) + e.z);
+    };
+    bad |= off[0] != (c == 0 ? job.payload_base : end_of(s0 - 2));  // after stream E-2 of chunk c-1
+#pragma unroll
+    for (int k = 1; k < E - 1; ++k) bad |= off[k] != align16(off[k - 1] + size[k - 1]);
+    // after the last lower stream of the blob, or the top stream of chunk c-1
+    bad |= off[E - 1] != (c == 0 ? end_of(S - 2) : end_of(s0 - 1));
+    if (last) bad |= align16(off[E - 1] + size[E - 1]) != B;
+  } else {
+    if (c == 0) bad |= off[0] != job.payload_base;
+#pragma unroll
+    for (int k = 1; k < E; ++k) bad |= off[k] != align16(off[k - 1] + size[k - 1]);
     const uint64_t end = align16(off[E - 1] + size[E - 1]);
     if (s0 + E < S) {
       const uint4 e = dir[s0 + E];

@@ -70,11 +70,21 @@ uint32_t host_group_ranges(const HostBlob* blobs, uint32_t count, uint32_t e, ui
     const uint64_t lo_c = c0 > b.chunk0 ? c0 - b.chunk0 : 0;
     const uint64_t hi_c = c1 - b.chunk0 < b.nchunks ? c1 - b.chunk0 : b.nchunks;
     const uint64_t B = b.nbytes;
-    uint64_t lo = lo_c == 0 ? 0 : dir_offset(b.data, lo_c * e);
-    uint64_t hi = hi_c == b.nchunks ? B : dir_offset(b.data, hi_c * e);
-    lo = lo < B ? lo : B;
-    hi = hi < lo ? lo : (hi < B ? hi : B);
-    if (hi > lo) out[n++] = HostRange{j, lo, hi};
+    auto put = [&](uint64_t lo, uint64_t hi) {
+      lo = lo < B ? lo : B;
+      hi = hi < lo ? lo : (hi < B ? hi : B);
+      if (hi > lo) out[n++] = HostRange{j, lo, hi};
+    };
+    if (!b.top_last || e == 1) {
+      put(lo_c == 0 ? 0 : dir_offset(b.data, lo_c * e), hi_c == b.nchunks ? B : dir_offset(b.data, hi_c * e));
+    } else {
+      // lower streams from stream 0 of the first chunk; top streams from
+      // stream E-1 of the first chunk; each up to the same stream of the
+      // next group's first chunk, or to where the part ends
+      const uint64_t top0 = dir_offset(b.data, e - 1);  // the first top stream
+      put(lo_c == 0 ? 0 : dir_offset(b.data, lo_c * e), hi_c == b.nchunks ? top0 : dir_offset(b.data, hi_c * e));
+      put(dir_offset(b.data, lo_c * e + e - 1), hi_c == b.nchunks ? B : dir_offset(b.data, hi_c * e + e - 1));
+    }
   }
   return n;
 }
@@ -106,7 +116,8 @@ int ltc_blob_info(const void* h_header, uint64_t h_nbytes, ltc_info* out) {
   const uint32_t chunk_bytes = ltc::rd32(h + 16);
   const uint64_t k = ltc::rd32(h + 20);
   if (ltc::rd16(h + 24) != kLanes || h[26] != kProbBits ||
-      (h[27] & ~LTC_FLAG_DELTA) != (version == 2 ? LTC_FLAG_SHARED_TABLES : 0u) || ltc::rd32(h + 28) != 0)
+      (h[27] & ~(LTC_FLAG_DELTA | LTC_FLAG_TOP_LAST)) != (version == 2 ? LTC_FLAG_SHARED_TABLES : 0u) ||
+      ltc::rd32(h + 28) != 0)
     return LTC_ERR_CORRUPT;
   for (int i = 48; i < 64; ++i)
     if (h[i]) return LTC_ERR_CORRUPT;

@@ -14,7 +14,8 @@
 namespace ltc {
 
 constexpr uint32_t kModeCand = 0xFF;    // internal: histogram done, encode pending (no blob mode)
-constexpr uint32_t kRawStaged = 1;      // internal: a RAW stream's bytes wait in its workspace slot
+constexpr uint32_t kRawStaged = 1;      // internal: a RAW stream's bytes are written (top-last: in
+                                        // the blob at their offset; else in the stream's workspace slot)
 constexpr int kMaxJobs = LTC_BATCH_MAX;
 
 __host__ __device__ constexpr uint64_t align16(uint64_t v) { return (v + 15) & ~uint64_t(15); }
@@ -69,6 +70,7 @@ struct CTable {
   uint32_t dtype;
   uint32_t v2;         // format v2: one table per (tensor, stream index)
   uint32_t delta;      // XOR deltas: every job has a base; ZRUN candidates
+  uint32_t top_last;   // layout flag LTC_FLAG_TOP_LAST: stream E-1 of every chunk after the others
   // the launch covers global chunks [c_begin, c_end) (a group of a pipelined
   // call, or all of them)
   uint64_t c_begin, c_end;
@@ -93,7 +95,8 @@ struct CWork {
   uint32_t* states;     // [S][64]
   uint16_t* words;      // [S][wcap]  (a stream's words end at its slot's end)
   uint64_t* offsets;    // [S]
-  uint64_t* blob_nbytes;  // [count]
+  uint64_t* blob_nbytes;  // [count] running offset of the scans (top-last: of the lower streams)
+  uint64_t* top_run;      // [count] top-last: running offset of the top streams' scan
 };
 
 struct DJob {
@@ -103,6 +106,7 @@ struct DJob {
   int32_t* status;
   uint64_t payload_base;  // from the header (v1: the end of the directory)
   uint32_t v2;            // table records between the directory and payload_base
+  uint32_t top_last;      // header flag LTC_FLAG_TOP_LAST: payload order
   uint64_t blob_nbytes;
   uint64_t nbytes;
   uint64_t chunk0;

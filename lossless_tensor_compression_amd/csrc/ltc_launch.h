@@ -17,6 +17,17 @@ hipError_t launch_compress(const CTable& t, const CWork& w, hipStream_t st, cons
                            hipEvent_t scan_after = nullptr, hipEvent_t scan_done = nullptr,
                            bool staged = false);
 
+// The same for the top-last layout (t.top_last), in two halves.  Front:
+// k_hist (unless staged), k_encode of the lower streams, their scan (after
+// scan_after, then scan_done), k_encode of the top streams; events 0-2.
+// Back: the top streams' scan (after scan_after, then scan_done) and k_pack;
+// events 3-4.  The first group's back half must wait for the last group's
+// lower scan: it starts the top streams where the lower ones end.
+hipError_t launch_compress_front(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                                 hipEvent_t scan_after, hipEvent_t scan_done, bool staged);
+hipError_t launch_compress_back(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
+                                hipEvent_t scan_after, hipEvent_t scan_done);
+
 // Format v2 for all chunks of t (c_begin = 0, c_end = total): k_hist (which
 // then sums each plane's histograms), k_share (tables, records, payload
 // base), k_decide (skip bound per stream).  ev (optional): events 0 and 1.

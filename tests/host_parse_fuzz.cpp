@@ -63,17 +63,17 @@ void exercise(const uint8_t* src, uint64_t len) {
       ltc::HostBlob hb[3];
       uint64_t chunk0 = 0, total = 0;
       for (int j = 0; j < 3; ++j) {  // three copies of the blob in one call
-        hb[j] = ltc::HostBlob{p, len, chunk0, info.nchunks};
+        hb[j] = ltc::HostBlob{p, len, chunk0, info.nchunks, (info.flags & LTC_FLAG_TOP_LAST) != 0};
         chunk0 += info.nchunks;
         total += len;
       }
-      ltc::HostRange rg[3];
+      ltc::HostRange rg[6];
       for (uint64_t gb : {1ull << 10, 1ull << 20, 16ull << 20}) {
         const uint64_t G = ltc::host_copy_groups(total, chunk0, gb, 8);
         if (G < 1 || G > 8 || G > chunk0) fail("group count", G, chunk0);
         for (uint64_t g = 0; g < G; ++g) {
           const uint32_t n = ltc::host_group_ranges(hb, 3, info.elem_bytes, chunk0, G, g, rg);
-          if (n > 3) fail("range count", n, g);
+          if (n > 6) fail("range count", n, g);
           for (uint32_t q = 0; q < n; ++q) {
             ++g_ranges;
             if (rg[q].job >= 3 || rg[q].lo >= rg[q].hi || rg[q].hi > len) fail("range", rg[q].lo, rg[q].hi);

@@ -65,6 +65,16 @@ def test_blob_info_and_stats_on_oracle_blob():
     assert 0.30 < stats.payload_bytes[1] / stats.stream_bytes[1] < 0.35
 
 
+def test_blob_info_top_last():
+    _lib()
+    x = workloads.c1()
+    blob = oracle.compress(x, 1, top_last=True)
+    info = ltc.blob_info(bytes(blob[:64]))
+    assert info["flags"] == 8 and info["version"] == 1 and info["blob_nbytes"] == blob.size
+    v2 = oracle.compress(x, 1, shared_tables=True, top_last=True)
+    assert ltc.blob_info(bytes(v2[:64]))["flags"] == 9
+
+
 def _info_rc(hdr):
     out = ltc.Info()
     return ltc.lib().ltc_blob_info(bytes(hdr), len(hdr), ctypes.byref(out))
@@ -76,7 +86,7 @@ def test_blob_info_errors_match_oracle():
     assert _info_rc(blob[:64]) == 0
     cases = []
     for pos, val in ((0, 0x4D), (4, 2), (4, 3), (6, 7), (7, 4), (24, 32), (26, 11), (27, 1),
-                     (28, 1), (50, 1), (16, 0), (20, 99), (40, 0)):
+                     (27, 9), (27, 16), (28, 1), (50, 1), (16, 0), (20, 99), (40, 0)):
         b = blob.copy()
         b[pos] = val
         cases.append(b)
@@ -157,11 +167,12 @@ def test_noalloc_limits_before_any_launch():
     assert L.ltc_compress_noalloc(fake, 16, 1, 12, 0.95, fake, 1 << 20, fake, null) == -1
 
 
-def test_caller_stream_flag_does_not_change_the_bound():
+def test_stream_and_layout_flags_do_not_change_the_bound():
     _lib()
     for dtype in (0, 1, 3):
         n = 131072 * 5 + 8
         base = ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, 0)
         assert base == ltc.compress_bound(n, dtype)
         assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, ltc.FLAG_CALLER_STREAM_ONLY) == base
-        assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, 8) == 0  # unknown flag
+        assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, ltc.FLAG_TOP_LAST) == base
+        assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, 16) == 0  # unknown flag

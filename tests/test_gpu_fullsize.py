@@ -1,6 +1,7 @@
 """GPU parity at the benchmark sizes, in the launch configuration bench.py
-times: C3 (28 BF16 tensors, 1.74 GB, one batch call; format v1, format v2
-and XOR deltas against the C3D base) and C5 (one 8 GiB BF16 buffer, 1/8
+times: C3 (28 BF16 tensors, 1.74 GB, one batch call; format v1, the
+top-last layout with checksums, format v2 and XOR deltas against the C3D
+base) and C5 (one 8 GiB BF16 buffer, 1/8
 random bytes) plus CRC-32 of the C5 blob.
 
 Every blob is compared byte for byte with the oracle's blob of the same
@@ -107,6 +108,35 @@ def test_c3_compress_with_crc32_full_size(ltc):
         got = c.cpu().numpy().view(np.uint32)
         assert got.size == want.size and np.array_equal(got, want), i
     banner(f"C3 {sum(c.numel() for c in crcs)} checksums equal to the oracle's")
+
+
+def test_c3_top_last_full_size(ltc):
+    """The top-last layout over the C3 batch, as bench.py times it
+    (compress_with_crc32, K = 16 KiB, then decompress): all 28 blobs byte
+    for byte against the oracle's top-last blobs, every checksum against the
+    oracle's CRC-32 of those blobs, the plain call's blobs equal, and the
+    exact round trip."""
+    banner("C3 generate")
+    ts = workloads.c3_gpu()
+    banner("C3 compress_batch_with_crc32, top-last (K = 16 KiB)")
+    blobs, crcs = ltc.compress_batch_with_crc32(ts, CHUNK, 0.95, 16384, top_last=True)
+    plain = ltc.compress_batch(ts, top_last=True)
+    for i, (b, p) in enumerate(zip(blobs, plain)):
+        assert torch.equal(b, p), i
+    del plain
+    banner("C3 top-last decompress_batch")
+    outs = ltc.decompress_batch(blobs)
+    for t, o in zip(ts, outs):
+        assert torch.equal(t.view(-1).view(torch.int16), o.view(torch.int16))
+    del outs
+    banner(f"C3 top-last oracle parity, all 28 tensors, {THREADS} host threads")
+    for i, (t, bl, c) in enumerate(zip(ts, blobs, crcs)):
+        want = oracle.compress(_host(t), 1, CHUNK, 0.95, nthreads=THREADS, top_last=True)
+        _assert_blob_equal(bl, want, f"C3 top-last tensor {i} {workloads.C3_SHAPES[i]}")
+        wcrc = oracle.crc32_chunks(want, 16384)
+        got = c.cpu().numpy().view(np.uint32)
+        assert got.size == wcrc.size and np.array_equal(got, wcrc), i
+    banner("C3 top-last parity done")
 
 
 def test_c3_shared_tables_full_size(ltc):

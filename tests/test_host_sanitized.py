@@ -54,6 +54,9 @@ def _blobs():
         "v2_fp32": oracle.compress(f32, 3, 1024, shared_tables=True),
         "delta_v1": oracle.compress_delta(x, base, 1, 4096),
         "delta_v2": oracle.compress_delta(x, base, 1, 4096, shared_tables=True),
+        "top_last_bf16": oracle.compress(x, 1, 4096, top_last=True),
+        "top_last_fp32_v2": oracle.compress(f32, 3, 1024, shared_tables=True, top_last=True),
+        "top_last_delta": oracle.compress_delta(x, base, 1, 4096, top_last=True),
         "empty": oracle.compress(np.zeros(0, np.uint8), 0, 4096),
         "one_chunk": oracle.compress(x[:100], 1, 131072),
     }
