@@ -421,3 +421,46 @@ def test_largest_chunk_many_histogram_segments(ltc, dtype):
         x[: nbytes // 4] = 0.015625  # one bit pattern over half of the first chunk
         arr = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
     check_case(ltc, arr, dtype, chunk, label="16 MiB chunks")
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 3])
+@pytest.mark.parametrize("top_last", [False, True], ids=["dir", "top-last"])
+def test_wide_and_narrow_symbol_ranges(ltc, dtype, top_last):
+    """The encoder keeps a 128-entry table for pairs of streams that span at
+    most 128 symbols and a 256-entry one otherwise.  Chunks alternate
+    between a narrow coded stream (values 60..75) and a wide one (mostly 5
+    and 240, a few in between), so pairs are narrow, wide, and mixed; the
+    boundary spans 127, 128 and 129 values appear too."""
+    rng = np.random.default_rng(60 + dtype)
+    e = oracle.ELEM_BYTES[dtype]
+    chunk = 8192
+    n = chunk // e
+    kinds = ["narrow", "wide", "wide", "narrow", "narrow", "s127", "s128", "s129", "wide"]
+    parts = []
+    for kind in kinds:
+        if kind == "narrow":
+            v = rng.integers(60, 76, n)
+        elif kind == "wide":
+            v = np.where(rng.random(n) < 0.5, 5, 240)
+            v[rng.integers(0, n, 40)] = rng.integers(5, 241, 40)
+        else:
+            span = int(kind[1:])
+            v = rng.integers(70, 75, n)
+            v[:2] = (10, 10 + span - 1)  # lowest and highest symbol: hi - lo = span - 1
+        v = v.astype(np.uint64)
+        if dtype == 0:
+            parts.append(v.astype(np.uint8))
+        elif dtype == 1:  # v is the exponent byte; random sign and mantissa
+            low = rng.integers(0, 256, n).astype(np.uint64)
+            parts.append((((low >> 7) << 15) | (v << 7) | (low & 0x7F)).astype(np.uint16))
+        else:
+            m = rng.integers(0, 1 << 24, n).astype(np.uint64)
+            parts.append((((m >> 23) << 31) | (v << 23) | (m & 0x7FFFFF)).astype(np.uint32))
+    x = np.concatenate(parts)
+    src = x.view(np.uint8)
+    want = oracle.compress(src, dtype, chunk, top_last=top_last)
+    got = to_np_bytes(ltc.compress(to_gpu(src, dtype), chunk, top_last=top_last))
+    assert got.size == want.size and np.array_equal(got, want)
+    assert np.array_equal(gpu_decode(ltc, want), src)
+    st = ltc.blob_stats(torch.from_numpy(want))
+    assert st["modes"][e - 1]["rans"] == len(kinds)
