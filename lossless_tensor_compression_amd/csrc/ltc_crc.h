@@ -31,7 +31,6 @@ template <int L> struct CrcLdsT {
   uint32_t tl[L][4][256];
   uint32_t basis[L][32];
 };
-using CrcLds = CrcLdsT<kCrcLevels>;
 
 // a * b mod P with bit 31 - d of a word holding the coefficient of x^d
 __device__ __forceinline__ uint32_t gf2_mulmod(uint32_t a, uint32_t b) {
@@ -85,39 +84,6 @@ __device__ __forceinline__ uint32_t crc_step16(const CrcLdsT<L>& s, uint32_t c, 
   return c;
 }
 
-// Slicing-by-16: th[m][b] is the register after byte b and 8 + m zero
-// bytes, so with t8 a 16-byte unit takes one round of 16 independent
-// lookups instead of two rounds of 8.  Every thread of the workgroup calls
-// the builder (after crc_build_tables); it ends with a workgroup barrier.
-template <int L>
-__device__ __forceinline__ void crc_build_th(const CrcLdsT<L>& s, uint32_t (*th)[256], uint32_t tid,
-                                             uint32_t nthreads) {
-  for (uint32_t b = tid; b < 256; b += nthreads) {
-    uint32_t c = s.t8[7][b];
-    for (int m = 0; m < 8; ++m) {
-      for (int k = 0; k < 8; ++k) c = (c >> 1) ^ (kPoly & (0u - (c & 1u)));
-      th[m][b] = c;
-    }
-  }
-  __syncthreads();
-}
-
-template <int L>
-__device__ __forceinline__ uint32_t crc_step16x(const CrcLdsT<L>& s, const uint32_t (*th)[256], uint32_t c,
-                                                const uint4 q) {
-  c ^= q.x;
-  return th[7][c & 0xFFu] ^ th[6][(c >> 8) & 0xFFu] ^ th[5][(c >> 16) & 0xFFu] ^ th[4][c >> 24] ^
-         th[3][q.y & 0xFFu] ^ th[2][(q.y >> 8) & 0xFFu] ^ th[1][(q.y >> 16) & 0xFFu] ^ th[0][q.y >> 24] ^
-         s.t8[7][q.z & 0xFFu] ^ s.t8[6][(q.z >> 8) & 0xFFu] ^ s.t8[5][(q.z >> 16) & 0xFFu] ^
-         s.t8[4][q.z >> 24] ^ s.t8[3][q.w & 0xFFu] ^ s.t8[2][(q.w >> 8) & 0xFFu] ^
-         s.t8[1][(q.w >> 16) & 0xFFu] ^ s.t8[0][q.w >> 24];
-}
-
-template <int L>
-__device__ __forceinline__ uint32_t crc_step1(const CrcLdsT<L>& s, uint32_t c, uint32_t byte) {
-  return s.t8[0][(c ^ byte) & 0xFFu] ^ (c >> 8);
-}
-
 // c * lvl[l] mod P
 template <int L>
 __device__ __forceinline__ uint32_t crc_mul_level(const CrcLdsT<L>& s, int l, uint32_t c) {
@@ -125,15 +91,81 @@ __device__ __forceinline__ uint32_t crc_mul_level(const CrcLdsT<L>& s, int l, ui
          s.tl[l][3][c >> 24];
 }
 
+// ---- bank-interleaved tables (k_crc32)
+// A lookup indexed by data is a random LDS access: 64 lanes reading one
+// 1 KiB table collide on most banks (the k_crc32 of a 1.2 GB blob with
+// slicing-by-16 tables of this kind spent about half its time stalled on bank
+// conflicts).  Here every slicing-by-4 table (bank[m][b]: the register after
+// byte b and m zero bytes) is stored as 32 copies interleaved by bank: entry
+// b of copy j is dword 32 * b + j, and lane l reads copy l % 32, so the 32
+// lanes an LDS cycle serves hit 32 different banks.  The four tables fill
+// 128 KiB, so a workgroup that holds them has a CU to itself.
+struct CrcBankLds {
+  uint32_t bank[4][256][32];
+  uint32_t tl[kCrcLevels][4][256];
+  uint32_t basis[kCrcLevels][32];
+};
+
+// Fills the tables (tl and basis as crc_build_tables); every thread of the
+// workgroup calls it; it ends with a workgroup barrier.
+__device__ __forceinline__ void crc_build_bank(CrcBankLds& s, const uint32_t* lvl, uint32_t tid,
+                                               uint32_t nthreads) {
+  for (uint32_t b = tid; b < 256; b += nthreads) {  // copy 0
+    uint32_t c = b;
+    for (int m = 0; m < 4; ++m) {
+      for (int k = 0; k < 8; ++k) c = (c >> 1) ^ (kPoly & (0u - (c & 1u)));
+      s.bank[m][b][0] = c;
+    }
+  }
+  for (uint32_t i = tid; i < kCrcLevels * 32; i += nthreads)
+    s.basis[i / 32][i % 32] = gf2_mulmod(1u << (i % 32), lvl[i / 32]);
+  __syncthreads();
+  for (uint32_t idx = tid; idx < 4 * 256 * 32; idx += nthreads) {  // copies 1..31
+    const uint32_t j = idx & 31;
+    if (j) (&s.bank[0][0][0])[idx] = (&s.bank[0][0][0])[idx - j];
+  }
+  for (uint32_t idx = tid; idx < kCrcLevels * 4 * 256; idx += nthreads) {
+    const uint32_t l = idx / 1024, p = (idx / 256) & 3, b = idx & 255;
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (b & (1u << i)) v ^= s.basis[l][8 * p + i];
+    s.tl[l][p][b] = v;
+  }
+  __syncthreads();
+}
+
+// register c advanced over the 4 bytes of little-endian word w; bl: the
+// lane's table copy (lane % 32)
+__device__ __forceinline__ uint32_t crc_word_bank(const CrcBankLds& s, uint32_t c, uint32_t w, uint32_t bl) {
+  c ^= w;
+  return s.bank[3][c & 0xFFu][bl] ^ s.bank[2][(c >> 8) & 0xFFu][bl] ^ s.bank[1][(c >> 16) & 0xFFu][bl] ^
+         s.bank[0][c >> 24][bl];
+}
+
+__device__ __forceinline__ uint32_t crc_step16_bank(const CrcBankLds& s, uint32_t c, const uint4 q,
+                                                    uint32_t bl) {
+  c = crc_word_bank(s, c, q.x, bl);
+  c = crc_word_bank(s, c, q.y, bl);
+  c = crc_word_bank(s, c, q.z, bl);
+  return crc_word_bank(s, c, q.w, bl);
+}
+
+__device__ __forceinline__ uint32_t crc_step1_bank(const CrcBankLds& s, uint32_t c, uint32_t byte,
+                                                   uint32_t bl) {
+  return s.bank[0][(c ^ byte) & 0xFFu][bl] ^ (c >> 8);
+}
+
 // Lane i holds the remainder of segment i of 64 equal consecutive segments
 // (level l's constant shifts by 2^l segments).  Returns, in lane 0, the
 // remainder of the concatenation; every lane of the wave must call it.
-template <int L>
-__device__ __forceinline__ uint32_t crc_tree64(const CrcLdsT<L>& s, uint32_t c, uint32_t lane) {
+__device__ __forceinline__ uint32_t crc_tree64_bank(const CrcBankLds& s, uint32_t c, uint32_t lane) {
 #pragma unroll
   for (int l = 0; l < kCrcLevels; ++l) {
     const uint32_t right = __shfl_down(c, 1u << l, 64);
-    if ((lane & ((2u << l) - 1u)) == 0) c = crc_mul_level(s, l, c) ^ right;
+    if ((lane & ((2u << l) - 1u)) == 0)
+      c = (s.tl[l][0][c & 0xFFu] ^ s.tl[l][1][(c >> 8) & 0xFFu] ^ s.tl[l][2][(c >> 16) & 0xFFu] ^
+           s.tl[l][3][c >> 24]) ^ right;
   }
   return c;
 }

@@ -4,9 +4,9 @@
 // zlib CRC-32 of every checksum_chunk_bytes-byte chunk, the last one
 // possibly shorter.  One wave per chunk: the chunk is split into 64 lane
 // segments, each lane runs a table-driven CRC over its segment with the
-// register starting at zero (slicing-by-16 with sixteen 256-entry tables in LDS;
-// Kounavis & Berry, "A Systematic Approach to Building High Performance
-// Software-based CRC Generators", 2005), and the 64 partial remainders are
+// register starting at zero (slicing-by-4 from bank-interleaved tables in
+// LDS, ltc_crc.h; Kounavis & Berry, "A Systematic Approach to Building High
+// Performance Software-based CRC Generators", 2005), and the 64 partial remainders are
 // combined in a 6-level tree whose level l multiplies the left partial by
 // x^(8 * seg * 2^l) mod P (the linearity rules are in ltc_crc.h).  A short
 // chunk is aligned to the END of its 64-segment frame (leading zero bytes do
@@ -24,34 +24,50 @@
 
 namespace ltc {
 
-constexpr int kCrcThreads = 256;
+// The tables take 153 KiB of LDS, so one workgroup of 16 waves holds a CU;
+// the grid is at most one workgroup per CU and its waves walk the chunks.
+constexpr int kCrcThreads = 1024;
+constexpr int kCrcGridMax = 256;
 
-// DEVLEN: buffer lengths are read on the device (compress_with_crc32)
+// DEVLEN: buffer lengths are read on the device (compress_with_crc32).  The
+// workgroup then reads each buffer's length once and numbers only the chunks
+// that exist (the job table counts chunks of the capacity, about a third
+// more for a blob of two thirds of its input).
 template <bool DEVLEN>
 __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
-  __shared__ CrcLds s;
-  __shared__ uint32_t th[8][256];
+  __shared__ CrcBankLds s;
+  __shared__ uint64_t lens[kMaxJobs];         // DEVLEN: the buffers' lengths
+  __shared__ uint64_t first[kMaxJobs + 1];    // DEVLEN: their first chunk's index
   const uint32_t tid = threadIdx.x;
-  crc_build_tables(s, a.lvl, tid, kCrcThreads);
-  crc_build_th(s, th, tid, kCrcThreads);
-
-  const uint32_t lane = lane_id(), wave = tid / 64;
-  const uint64_t frame = 64 * a.seg;
-  for (uint64_t gi = (uint64_t)blockIdx.x * 4 + wave; gi < a.total_chunks;
-       gi += (uint64_t)gridDim.x * 4) {
-    int jb = 0;
-    while (jb + 1 < (int)a.count && gi >= a.jobs[jb + 1].chunk0) ++jb;
-    const CrcJob& job = a.jobs[jb];
-    const uint64_t i = gi - job.chunk0;
-    uint64_t len;
-    if constexpr (DEVLEN) {  // length known on the device only
-      const uint64_t total = *job.len;
-      const uint64_t n = (total + a.chunk_bytes - 1) / a.chunk_bytes;
-      if (i >= n) continue;
-      len = i + 1 == n ? total - i * a.chunk_bytes : a.chunk_bytes;
-    } else {
-      len = i + 1 == job.nchunks ? job.tail_len : a.chunk_bytes;
+  if (DEVLEN && tid < a.count) lens[tid] = *a.jobs[tid].len;
+  if (DEVLEN) __syncthreads();
+  if (DEVLEN && tid == 0) {
+    uint64_t c = 0;
+    for (uint32_t j = 0; j < a.count; ++j) {
+      first[j] = c;
+      c += (lens[j] + a.chunk_bytes - 1) / a.chunk_bytes;
     }
+    first[a.count] = c;
+  }
+  crc_build_bank(s, a.lvl, tid, kCrcThreads);  // ends with a barrier
+
+  const uint32_t lane = lane_id(), wave = tid / 64, bl = lane & 31u;
+  constexpr uint32_t kWaves = kCrcThreads / 64;
+  const uint64_t frame = 64 * a.seg;
+  const uint64_t total = DEVLEN ? first[a.count] : a.total_chunks;
+  for (uint64_t gi = (uint64_t)blockIdx.x * kWaves + wave; gi < total; gi += (uint64_t)gridDim.x * kWaves) {
+    int jb = 0;
+    uint64_t i, len;
+    if constexpr (DEVLEN) {
+      while (jb + 1 < (int)a.count && gi >= first[jb + 1]) ++jb;
+      i = gi - first[jb];
+      len = gi + 1 == first[jb + 1] ? lens[jb] - i * a.chunk_bytes : a.chunk_bytes;
+    } else {
+      while (jb + 1 < (int)a.count && gi >= a.jobs[jb + 1].chunk0) ++jb;
+      i = gi - a.jobs[jb].chunk0;
+      len = i + 1 == a.jobs[jb].nchunks ? a.jobs[jb].tail_len : a.chunk_bytes;
+    }
+    const CrcJob& job = a.jobs[jb];
     const uint64_t pad = frame - len;  // leading virtual zero bytes
     const uint64_t vs = lane * a.seg, ve = vs + a.seg;
     const uint8_t* base = job.src + i * a.chunk_bytes;
@@ -62,18 +78,18 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
       end = base + (ve - pad);
     }
     uint32_t crc = vs <= pad && pad < ve ? 0xFFFFFFFFu : 0u;  // zlib's preset at the first byte
-    while (p < end && (reinterpret_cast<uintptr_t>(p) & 15)) crc = crc_step1(s, crc, *p++);
+    while (p < end && (reinterpret_cast<uintptr_t>(p) & 15)) crc = crc_step1_bank(s, crc, *p++, bl);
     // all sixteen 16-byte loads of a 256-byte segment are in flight together
     for (; p + 256 <= end; p += 256) {
       uint4 q[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) q[u] = reinterpret_cast<const uint4*>(p)[u];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) crc = crc_step16x(s, th, crc, q[u]);
+      for (int u = 0; u < 16; ++u) crc = crc_step16_bank(s, crc, q[u], bl);
     }
-    for (; p + 16 <= end; p += 16) crc = crc_step16x(s, th, crc, *reinterpret_cast<const uint4*>(p));
-    for (; p < end; ++p) crc = crc_step1(s, crc, *p);
-    crc = crc_tree64(s, crc, lane);
+    for (; p + 16 <= end; p += 16) crc = crc_step16_bank(s, crc, *reinterpret_cast<const uint4*>(p), bl);
+    for (; p < end; ++p) crc = crc_step1_bank(s, crc, *p, bl);
+    crc = crc_tree64_bank(s, crc, lane);
     if (lane == 0) job.out[i] = crc ^ 0xFFFFFFFFu;
   }
 }
@@ -149,8 +165,8 @@ hipError_t launch_zero_u32(uint32_t* p, uint64_t n, hipStream_t st) {
 
 hipError_t launch_crc32(const CrcArgs& a, hipStream_t st) {
   if (a.total_chunks == 0) return hipSuccess;
-  const uint64_t want = (a.total_chunks + 3) / 4;
-  const uint32_t grid = (uint32_t)(want < 1280 ? want : 1280);
+  const uint64_t want = (a.total_chunks + kCrcThreads / 64 - 1) / (kCrcThreads / 64);
+  const uint32_t grid = (uint32_t)(want < kCrcGridMax ? want : kCrcGridMax);
   if (a.jobs[0].len)
     hipLaunchKernelGGL(k_crc32<true>, dim3(grid), dim3(kCrcThreads), 0, st, a);
   else
