@@ -26,7 +26,7 @@
  * launch failure returns LTC_ERR_HIP.  Calls on different streams are
  * independent.
  *
- * PIPELINED COMPRESSION.  A compress call over 512 chunks or more (all
+ * PIPELINED COMPRESSION.  A compress call over 4096 chunks or more (all
  * tensors of a batch together) splits its chunks into two
  * chunk-ordered groups: the first runs on `stream`, the second on an internal
  * stream that waits for `stream` at the call and that `stream` waits for

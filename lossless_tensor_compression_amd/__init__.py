@@ -130,6 +130,25 @@ def _check(rc, what):
         raise LTCError(rc, what)
 
 
+class Prepared:
+    """One C ABI call with its arguments marshalled once, for loops that
+    repeat the same call (the host then pays only the foreign call).  keep:
+    objects the marshalled pointers refer to."""
+
+    def __init__(self, fn, args, what, keep=None):
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args), self._what)
+
+
+def _run(fn, args, what, prepare, keep=None):
+    if prepare:
+        return Prepared(fn, args, what, keep)
+    _check(fn(*args), what)
+    return None
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -200,20 +219,20 @@ def compress_noalloc_raw(src_ptr, nbytes, dtype_code, chunk_bytes, threshold, bl
 
 def compress_ex_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, flags, blob_ptrs, caps,
                     nbytes_out_ptr, ws_ptr, ws_nbytes, crc_chunk_bytes=0, crc_ptrs=None,
-                    crc_caps=None, stream=None, events=None, base_ptrs=None):
+                    crc_caps=None, stream=None, events=None, base_ptrs=None, prepare=False):
     """Pointer-level ltc_compress_batch_ex: format flags, optional checksums
     (crc_chunk_bytes > 0), optional events (5, or 6 with checksums) and
-    optional delta bases (XOR deltas)."""
+    optional delta bases (XOR deltas).  prepare: return a Prepared call
+    instead of calling."""
     count = len(src_ptrs)
     crc_ptrs = crc_ptrs or [0] * count
     crc_caps = crc_caps or [0] * count
     ev = _ptrs(events) if events is not None else None
     bases = _ptrs(base_ptrs) if base_ptrs is not None else None
-    _check(lib().ltc_compress_batch_ex(count, _ptrs(src_ptrs), _u64s(nbytes), dtype_code, chunk_bytes,
-                                       threshold, flags, bases, _ptrs(blob_ptrs), _u64s(caps),
-                                       ctypes.c_void_p(nbytes_out_ptr), crc_chunk_bytes, _ptrs(crc_ptrs),
-                                       _u64s(crc_caps), ctypes.c_void_p(ws_ptr), ws_nbytes,
-                                       _stream(stream), ev), "compress")
+    args = (count, _ptrs(src_ptrs), _u64s(nbytes), dtype_code, chunk_bytes, threshold, flags, bases,
+            _ptrs(blob_ptrs), _u64s(caps), ctypes.c_void_p(nbytes_out_ptr), crc_chunk_bytes, _ptrs(crc_ptrs),
+            _u64s(crc_caps), ctypes.c_void_p(ws_ptr), ws_nbytes, _stream(stream), ev)
+    return _run(lib().ltc_compress_batch_ex, args, "compress", prepare)
 
 
 def compress_crc32_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blob_ptrs, caps,
@@ -232,16 +251,17 @@ def compress_crc32_raw(src_ptrs, nbytes, dtype_code, chunk_bytes, threshold, blo
 
 
 def decompress_raw(headers, blob_ptrs, blob_nbytes, dst_ptrs, caps, status_ptr, stream=None,
-                   events=None):
-    """Pointer-level batch decompress on `stream`; headers are 64-byte host bytes."""
+                   events=None, prepare=False):
+    """Pointer-level batch decompress on `stream`; headers are 64-byte host
+    bytes.  prepare: return a Prepared call instead of calling."""
     count = len(blob_ptrs)
     hdr = (ctypes.c_void_p * count)(*[ctypes.cast(ctypes.c_char_p(h), ctypes.c_void_p) for h in headers])
     args = [count, hdr, _ptrs(blob_ptrs), _u64s(blob_nbytes), _ptrs(dst_ptrs), _u64s(caps),
             ctypes.c_void_p(status_ptr), _stream(stream)]
     if events is None:
-        _check(lib().ltc_decompress_batch(*args), "decompress")
-    else:
-        _check(lib().ltc_decompress_batch_prof(*args, _ptrs(events)), "decompress")
+        return _run(lib().ltc_decompress_batch, args, "decompress", prepare, keep=list(headers))
+    return _run(lib().ltc_decompress_batch_prof, args + [_ptrs(events)], "decompress", prepare,
+                keep=list(headers))
 
 
 def compress_batch(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
@@ -517,10 +537,11 @@ def crc32_chunks(t, chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):
     return out[:count]
 
 
-def crc32_raw(src_ptrs, nbytes, chunk_bytes, crc_ptrs, stream=None):
-    """Pointer-level batch CRC-32 on `stream` (no allocation, no sync)."""
-    _check(lib().ltc_crc32_chunks_batch(len(src_ptrs), _ptrs(src_ptrs), _u64s(nbytes), chunk_bytes,
-                                        _ptrs(crc_ptrs), _stream(stream)), "crc32_chunks_batch")
+def crc32_raw(src_ptrs, nbytes, chunk_bytes, crc_ptrs, stream=None, prepare=False):
+    """Pointer-level batch CRC-32 on `stream` (no allocation, no sync).
+    prepare: return a Prepared call instead of calling."""
+    args = (len(src_ptrs), _ptrs(src_ptrs), _u64s(nbytes), chunk_bytes, _ptrs(crc_ptrs), _stream(stream))
+    return _run(lib().ltc_crc32_chunks_batch, args, "crc32_chunks_batch", prepare)
 
 
 def crc32_chunks_batch(tensors, chunk_bytes=DEFAULT_CRC_CHUNK_BYTES):

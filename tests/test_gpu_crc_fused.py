@@ -104,12 +104,12 @@ def test_small_and_ragged(ltc, dtype, nelem, chunk):
     check_crc_case(ltc, arr, dtype, chunk, [1024, 16384, 1000], label=f"small n={nelem}")
 
 
-@pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (0, 2048)])
+@pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 1024), (0, 1024)])
 def test_grouped_call(ltc, dtype, chunk):
-    """Over 512 chunks: two chunk groups on two streams add into frames that
+    """Over 4096 chunks: two chunk groups on two streams add into frames that
     straddle the group border; every 5th chunk is random bytes."""
     rng = np.random.default_rng(300 + dtype)
-    nbytes = 700 * chunk + 24
+    nbytes = 4200 * chunk + 24
     if dtype == 0:
         data = rng.integers(0, 6, nbytes, dtype=np.uint8)
     else:

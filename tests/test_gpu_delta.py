@@ -165,14 +165,14 @@ def test_staged_raw_xor_streams(ltc, dtype):
     assert (modes[:, e - 1] == oracle.MODE_RANS).all()
 
 
-@pytest.mark.parametrize("dtype,chunk,shared", [(1, 4096, False), (1, 4096, True), (3, 1024, False),
-                                                (0, 2048, True)])
+@pytest.mark.parametrize("dtype,chunk,shared", [(1, 1024, False), (1, 1024, True), (3, 512, False),
+                                                (0, 512, True)])
 def test_grouped(ltc, dtype, chunk, shared):
-    """Over 512 chunks: two chunk groups on two streams (v2: after the
+    """Over 4096 chunks: two chunk groups on two streams (v2: after the
     tables), ZRUN chunks in every group."""
     rng = np.random.default_rng(500 + dtype)
     e = oracle.ELEM_BYTES[dtype]
-    n = (700 * chunk + 24) // e
+    n = (4200 * chunk + 24) // e
     src, base = _pair(dtype, n, "nudge", rng)
     sv = src.view(np.uint8)
     for c in range(0, sv.size // chunk, 7):  # some chunks changed everywhere

@@ -314,14 +314,14 @@ def test_staged_raw_streams_with_abandoned_neighbours(ltc, dtype, thr):
     assert modes[:, e - 1].tolist() == top
 
 
-# ---- pipelined compression: calls over 512 chunks or more run in two
-# chunk-ordered groups on two streams (the caller's and one internal
-# stream); blobs must not change.
+# ---- pipelined compression: calls over 4096 chunks or more (the library's
+# threshold) run in two chunk-ordered groups on two streams (the caller's and
+# one internal stream); blobs must not change.
 
-@pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (2, 2048), (0, 512)])
+@pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 512), (2, 512), (0, 256)])
 def test_grouped_single_tensor(ltc, dtype, chunk):
     rng = np.random.default_rng(100 + dtype)
-    nbytes = 700 * chunk + 3 * 8  # 701 chunks, a ragged last one: two uneven groups (350 + 351)
+    nbytes = 4200 * chunk + 3 * 8  # 4201 chunks, a ragged last one: two uneven groups (2100 + 2101)
     if dtype == 0:
         data = rng.integers(0, 6, nbytes, dtype=np.uint8)
         data[: nbytes // 3] = 7  # const chunks too
@@ -346,11 +346,11 @@ def test_grouped_batch_with_empty_and_tiny(ltc):
     """A batch whose tensors straddle the group boundaries, with an empty and
     a one-element tensor; every blob must equal the single-tensor oracle blob."""
     rng = np.random.default_rng(77)
-    chunk = 1024
+    chunk = 512
     sizes = (90000, 0, 1, 123457, 2, 40000, 250001, 17, 60000)
     arrs = [(rng.standard_normal(n) * rng.choice([0.02, 1.0, 1e-4])).astype(np.float32) for n in sizes]
     total_chunks = sum((a.nbytes + chunk - 1) // chunk for a in arrs)
-    assert total_chunks >= 512
+    assert total_chunks >= 4096
     ts = [to_gpu(a, 3) for a in arrs]
     banner(f"grouped batch: {len(arrs)} tensors, {total_chunks} chunks")
     blobs = ltc.compress_batch(ts, chunk)
@@ -368,16 +368,16 @@ def test_grouped_batch_with_empty_and_tiny(ltc):
 
 
 def test_caller_stream_only_equals_grouped(ltc):
-    """LTC_FLAG_CALLER_STREAM_ONLY: a call over more than 512 chunks (which
+    """LTC_FLAG_CALLER_STREAM_ONLY: a call over more than 4096 chunks (which
     otherwise runs in two groups on two streams) runs every kernel on the
     caller's stream and gives the same blobs, plain and with checksums."""
     rng = np.random.default_rng(88)
-    chunk = 4096
+    chunk = 512
     arrs = [(rng.standard_normal(n) * s).astype(np.float32) for n, s in
             ((300000, 0.02), (5, 1.0), (250003, 1e-3))]
     ts = [to_gpu(a, 3) for a in arrs]
     nbytes = [a.nbytes for a in arrs]
-    assert sum((n + chunk - 1) // chunk for n in nbytes) >= 512
+    assert sum((n + chunk - 1) // chunk for n in nbytes) >= 4096
     caps = [ltc.compress_bound(n, 3, chunk) for n in nbytes]
     ws_n = ltc.workspace_size(nbytes, 3, chunk)
     ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")

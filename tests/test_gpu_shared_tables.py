@@ -85,11 +85,11 @@ def test_thresholds(ltc, thr):
     check_v2(ltc, x, 3, 65536, thr, label="threshold")
 
 
-@pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (0, 2048)])
+@pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 512), (0, 512)])
 def test_grouped_with_random_chunks(ltc, dtype, chunk):
-    """Over 512 chunks: the tables come first, then two chunk groups."""
+    """Over 4096 chunks: the tables come first, then two chunk groups."""
     rng = np.random.default_rng(400 + dtype)
-    nbytes = 700 * chunk + 24
+    nbytes = 4200 * chunk + 24
     if dtype == 0:
         data = rng.integers(0, 6, nbytes, dtype=np.uint8)
     else:

@@ -101,12 +101,13 @@ def test_abandoned_top_streams(ltc, dtype, thr):
     check(ltc, x, dtype, 131072, thr, label="abandoned exponent streams")
 
 
-@pytest.mark.parametrize("dtype,chunk", [(1, 4096), (3, 1024), (2, 2048), (0, 512)])
+@pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 512), (2, 512), (0, 256)])
 def test_grouped_single_tensor(ltc, dtype, chunk):
-    """701 chunks: two groups on two streams; the first group's top scan
-    starts where the second group's lower scan ended."""
+    """4201 chunks (over the library's pipelining threshold of 4096): two
+    groups on two streams; the first group's top scan starts where the second
+    group's lower scan ended."""
     rng = np.random.default_rng(200 + dtype)
-    nbytes = 700 * chunk + 24
+    nbytes = 4200 * chunk + 24
     e = oracle.ELEM_BYTES[dtype]
     if dtype == 0:
         data = rng.integers(0, 6, nbytes, dtype=np.uint8)
@@ -122,10 +123,10 @@ def test_grouped_single_tensor(ltc, dtype, chunk):
 @pytest.mark.parametrize("shared", [False, True], ids=["v1", "v2"])
 def test_grouped_batch_with_empty_and_tiny(ltc, shared):
     rng = np.random.default_rng(78)
-    chunk = 1024
+    chunk = 512
     sizes = (90000, 0, 1, 123457, 2, 40000, 250001, 17, 60000)
     arrs = [(rng.standard_normal(n) * rng.choice([0.02, 1.0, 1e-4])).astype(np.float32) for n in sizes]
-    assert sum((a.nbytes + chunk - 1) // chunk for a in arrs) >= 512
+    assert sum((a.nbytes + chunk - 1) // chunk for a in arrs) >= 4096
     banner(f"top-last grouped batch v2={shared}")
     blobs = ltc.compress_batch([to_gpu(a, 3) for a in arrs], chunk, shared_tables=shared, top_last=True)
     for i, (a, b) in enumerate(zip(arrs, blobs)):
@@ -139,7 +140,7 @@ def test_stream_modes_checksums_and_events(ltc):
     with fused checksums (K = 16 KiB: k_pack reads the placed RAW streams
     back) and with read-back checksums (K = 1000)."""
     rng = np.random.default_rng(89)
-    chunk = 4096
+    chunk = 512
     arrs = [(rng.standard_normal(n) * s).astype(np.float32) for n, s in
             ((300000, 0.02), (5, 1.0), (250003, 1e-3))]
     ts = [to_gpu(a, 3) for a in arrs]
