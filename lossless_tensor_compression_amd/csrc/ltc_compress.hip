@@ -1516,8 +1516,9 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
     }
   }
   // RAW streams: when k_encode staged them (stmask), already in place
-  // (top-last layout; only read back for the checksums) or copied from their
-  // workspace slots; else regrouped from the input
+  // (top-last layout, which the checksumming variant never packs: its
+  // checksums are read back) or copied from their workspace slots; else
+  // regrouped from the input
   uint32_t rawmask = 0, stmask = 0;
   uint64_t raw_off[E];
 #pragma unroll
@@ -1536,17 +1537,14 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
       write_zrun<DT, DELTA>(blob + raw_off[k], src, job.base + c * t.chunk_bytes, n, k, si.z, si.w, si.x,
                             t.vec16 != 0, red);
   }
-  const bool inplace = t.top_last != 0;
-  if (!CRC && inplace) rawmask &= ~stmask;
+  if (t.top_last) rawmask &= ~stmask;
   if (!rawmask) return;
   const uint32_t units = (n + 15) / 16;
   const bool regroup = (rawmask & ~stmask) != 0;
   // unit u of RAW stream k; y: the regrouped elements when not staged
   auto raw_unit = [&](int k, uint32_t u, const uint32_t* y) -> uint4 {
     if (stmask & (1u << k))
-      return *reinterpret_cast<const uint4*>(
-          inplace ? blob + raw_off[k] + 16 * u
-                  : reinterpret_cast<const uint8_t*>(w.words + (s0 + k) * t.wcap) + 16 * u);
+      return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(w.words + (s0 + k) * t.wcap) + 16 * u);
     return make_uint4(pack4(y, k), pack4(y + 4, k), pack4(y + 8, k), pack4(y + 12, k));
   };
   if constexpr (!CRC) {
@@ -1603,7 +1601,7 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
         uint32_t cr = 0;
         if (have) {
           const uint4 v = (kAhead && (stmask & (1u << k))) ? cv[k] : raw_unit(k, u, y);
-          if (!(inplace && (stmask & (1u << k)))) *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = v;
+          *reinterpret_cast<uint4*>(blob + raw_off[k] + 16 * u) = v;
           cr = crc_step16(L.c, 0u, v);
         }
         const uint64_t d = raw_off[k] / 16 - a0;  // >= 0: streams are laid out in order
