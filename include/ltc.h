@@ -27,8 +27,9 @@
  * independent.
  *
  * PIPELINED COMPRESSION.  A compress call over 4096 chunks or more (all
- * tensors of a batch together) splits its chunks into two
- * chunk-ordered groups: the first runs on `stream`, the second on an internal
+ * tensors of a batch together) in directory order, or of deltas, splits its
+ * chunks into two chunk-ordered groups (a top-last call of that size runs on
+ * `stream` alone: its encoder writes the top streams' payloads in place): the first runs on `stream`, the second on an internal
  * stream that waits for `stream` at the call and that `stream` waits for
  * before anything enqueued after the call, so the call still behaves as work
  * on `stream`.  One group's compute-bound encoding then overlaps another's

@@ -37,7 +37,11 @@ constexpr uint32_t kWordsGranule = 1024;
 // groups 1.60 ms against 1.66 on one stream.  Below 4096 chunks the fork,
 // the cross-stream waits and the doubled launches cost more than the
 // overlap: a 64 MiB FP32 tensor (512 chunks) compresses in 0.15 ms on one
-// stream against 0.21 ms in two groups.
+// stream against 0.21 ms in two groups.  Top-last calls (no deltas) of that
+// size do not pipeline: their encoder places the top streams' payloads
+// itself (k_encode), whose look-back runs within one launch; on C3 that is
+// 2-3% faster than the two groups (1.31 against 1.33-1.36 ms on one box, C5
+// 5.49-5.52 against 5.65-5.68 ms).
 constexpr int kPipeGroups = 2;
 constexpr uint64_t kPipeMinChunks = 4096;
 
@@ -105,7 +109,7 @@ hipError_t run_compress(CTable t, const CWork& w, hipStream_t stream, const hipE
     const hipError_t err = launch_compress_front(t, w, stream, e, nullptr, nullptr, staged);
     return err == hipSuccess ? launch_compress_back(t, w, stream, e, nullptr, nullptr) : err;
   };
-  if (ev || one_stream || total < kPipeMinChunks) return whole(ev);
+  if (ev || one_stream || total < kPipeMinChunks || t.place) return whole(ev);
   std::lock_guard<std::mutex> lock(g_pipe_mu);
   PipeRes* r = pipe_res(stream);
   if (!r) return whole(nullptr);
@@ -244,7 +248,7 @@ uint32_t words_capacity(uint32_t chunk_bytes, uint32_t e) {
 }
 
 struct Layout {
-  uint64_t sinfo, freq, hist, plane, ptab, pbase, zinfo, states, offsets, blobn, toprun, frames, words, total;
+  uint64_t sinfo, freq, hist, plane, ptab, pbase, zinfo, states, offsets, blobn, toprun, tstat, frames, words, total;
 };
 
 // frames: one u32 per KiB of every blob's bound (compress_with_crc32);
@@ -263,6 +267,7 @@ Layout layout(uint64_t streams, int count, uint32_t wcap, uint64_t frames, uint3
   l.offsets = cur; cur = round_up(cur + 8 * streams, kAlign);
   l.blobn = cur;   cur = round_up(cur + 8 * (uint64_t)count, kAlign);
   l.toprun = cur;  cur = round_up(cur + 8 * (uint64_t)count, kAlign);
+  l.tstat = cur;   cur = round_up(cur + 8 * streams, kAlign);  // one per chunk suffices
   l.frames = cur;  cur = round_up(cur + 4 * frames, kAlign);
   l.words = cur;   cur = round_up(cur + 2ull * wcap * streams, kAlign);
   l.total = cur;
@@ -376,6 +381,10 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   }
   t.total_chunks = chunk0;
   t.vec16 = vec ? 1u : 0u;
+  // top-last calls large enough to pipeline: k_encode places the top
+  // streams' payloads instead, on one stream (a smaller call waits longer in
+  // the look-back than packing takes)
+  t.place = t.top_last && !bases && chunk0 >= kPipeMinChunks ? 1u : 0u;
   uint8_t* ws = static_cast<uint8_t*>(d_ws);
   CWork w;
   w.sinfo = reinterpret_cast<uint32_t*>(ws + l.sinfo);
@@ -389,6 +398,7 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   w.offsets = reinterpret_cast<uint64_t*>(ws + l.offsets);
   w.blob_nbytes = reinterpret_cast<uint64_t*>(ws + l.blobn);
   w.top_run = reinterpret_cast<uint64_t*>(ws + l.toprun);
+  w.tstat = reinterpret_cast<uint64_t*>(ws + l.tstat);
   w.words = reinterpret_cast<uint16_t*>(ws + l.words);
   if (!crc.chunk_bytes) return run_compress(t, w, stream, ev, one_stream) == hipSuccess ? LTC_OK : LTC_ERR_HIP;
 

@@ -666,6 +666,88 @@ template <int DT> __device__ __forceinline__ uint2 stream_bytes8(const uint32_t*
   }
 }
 
+// ---- placing the top streams' RANS payloads (top-last layout)
+//
+// In the top-last layout a tensor's top streams follow its lower streams in
+// chunk order, so the payload of chunk g's top stream starts where the lower
+// streams end (k_scan part 1) plus the aligned sizes of the top streams of
+// the tensor's chunks before g ("NOTE-241: ZipNN", Method item 5: the
+// directory says where each payload is; the order is the layout's).  Every
+// chunk's top stream has a status word in the workspace: 0 while its size is
+// unknown, kStAgg | size once it is coded, kStInc | (bytes of the tensor's top
+// streams up to and including it) once that sum is known, and kStLater while
+// the 256-entry launch has yet to code it.  k_scan (part 1) sets the status of
+// every top stream that needs no coding (its size is final), the tensor's
+// first chunk as an inclusive count.  A wave that codes a top stream
+// publishes its size, walks back over the statuses of the chunks before it,
+// 64 at a time, summing sizes down to the nearest inclusive count, publishes
+// its own inclusive count, and writes the payload into the blob itself,
+// marking the stream kPlaced so that k_pack skips it.
+//
+// Waiting.  A wave waits only for chunks with smaller indices, and only after
+// publishing its own size.  Workgroups start in index order on each XCD, so
+// the lowest-indexed wave not yet started has only running or finished waves
+// of lower index on its XCD, which wait for nothing it holds: every chain of
+// waits ends at a running wave.  The 128-entry launch runs first and never
+// waits for a kStLater chunk (the 256-entry launch codes it later); in the
+// 256-entry launch such a chunk belongs to an earlier wave of the launch.
+// Every wait is also bounded by the device clock.  A wave that gives up
+// leaves its payload to k_pack: the walk decides only who writes the payload
+// (offsets, directory and blob size still come from k_scan), so a slow or
+// missing status costs time, never a wrong blob.  The status words are the
+// only data the waves exchange, so they are read and written with relaxed
+// device-scope atomics, coherent across the XCDs' L2 caches without cache
+// maintenance (acquire and release forms write back or invalidate the
+// XCD's whole L2 at every poll: C3's encoder took 2.47 instead of 0.6 ms).
+constexpr uint64_t kStAgg = 1ull << 62, kStInc = 2ull << 62, kStLater = 3ull << 62;
+constexpr uint64_t kStVal = (1ull << 62) - 1;
+
+// Bytes of the top streams of chunks [f, g) (f < g: the first chunk of g's
+// tensor) from their status words (one wave).  false: a kStLater chunk
+// without wait_later, or no answer within `limit` ticks of the device clock.
+__device__ bool top_prefix(const uint64_t* st, uint64_t g, uint64_t f, bool wait_later, uint64_t limit,
+                           uint64_t& out) {
+  const uint32_t lane = lane_id();
+  const uint64_t t0 = (uint64_t)wall_clock64();
+  uint64_t acc = 0, hi = g;  // chunks [f, hi) are still to add
+  while (true) {
+    const uint64_t span = hi - f;
+    const uint32_t nin = span < 64 ? (uint32_t)span : 64u;  // lane l reads chunk hi - 1 - l
+    const bool in = lane < nin;
+    const uint64_t v =
+        in ? __hip_atomic_load(st + (hi - 1 - lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    const uint64_t fl = v >> 62;
+    const uint64_t incm = ballot(in && fl == 2);
+    const uint32_t last = incm ? (uint32_t)__builtin_ctzll(incm) : nin - 1;  // the lanes needed: 0..last
+    const uint64_t need = last == 63 ? ~0ull : (2ull << last) - 1;
+    if (!wait_later && (ballot(in && fl == 3) & need)) return false;
+    if ((ballot(in && (fl == 1 || fl == 2)) & need) != need) {
+      if ((uint64_t)wall_clock64() - t0 > limit) return false;
+      __builtin_amdgcn_s_sleep(4);
+      continue;  // read the window again
+    }
+    acc += wave_sum_u64(lane <= last ? (v & kStVal) : 0ull);
+    if (incm || span <= 64) {
+      out = acc;
+      return true;
+    }
+    hi -= 64;
+  }
+}
+
+// bytes [sh, sh + 16) of the 32 bytes a, b (sh even, below 16)
+__device__ __forceinline__ uint4 shift_blocks(const uint4 a, const uint4 b, uint32_t sh) {
+  const uint32_t q = sh >> 2;
+  const uint32_t w0 = q == 0 ? a.x : q == 1 ? a.y : q == 2 ? a.z : a.w;
+  const uint32_t w1 = q == 0 ? a.y : q == 1 ? a.z : q == 2 ? a.w : b.x;
+  const uint32_t w2 = q == 0 ? a.z : q == 1 ? a.w : q == 2 ? b.x : b.y;
+  const uint32_t w3 = q == 0 ? a.w : q == 1 ? b.x : q == 2 ? b.y : b.z;
+  if (!(sh & 2u)) return make_uint4(w0, w1, w2, w3);
+  const uint32_t w4 = q == 0 ? b.x : q == 1 ? b.y : q == 2 ? b.z : b.w;
+  return make_uint4(__builtin_amdgcn_alignbyte(w1, w0, 2), __builtin_amdgcn_alignbyte(w2, w1, 2),
+                    __builtin_amdgcn_alignbyte(w3, w2, 2), __builtin_amdgcn_alignbyte(w4, w3, 2));
+}
+
 // One wave codes stream k of two neighbouring chunks, interleaving their
 // independent state chains (instruction-level parallelism for a loop whose
 // every step is a dependent chain).
@@ -752,6 +834,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
   const uint8_t* bsrc[U];
   const uint16_t* ftab[U];
   uint4 fallback[U];  // the stream's directory info if coding it does not pay
+  int jb[U];          // the chunk's tensor
   uint8_t* rdst[U][E > 1 ? E - 1 : 1];  // where staged RAW stream j of the chunk goes
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -762,6 +845,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
     bsrc[u] = nullptr;
     ftab[u] = nullptr;
     fallback[u] = make_uint4(0, 0, 0, 0);
+    jb[u] = 0;
 #pragma unroll
     for (int q = 0; q < (E > 1 ? E - 1 : 1); ++q) rdst[u][q] = nullptr;
     const uint64_t g = g0 + u;
@@ -774,6 +858,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
     const uint64_t c = g - job.chunk0;
     const bool last = c + 1 == job.nchunks;
     on[u] = true;
+    jb[u] = j;
     sid[u] = s;
     n[u] = last ? job.n_tail : t.n_full;
     full[u] = n[u] / 64;
@@ -822,8 +907,20 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (on[u] && hi[u] - lo[u] >= 128u) small = false;
-    if (small != (TABN < 256)) return;
+    if (small != (TABN < 256)) {
+      // placement: the 128-entry launch runs first and marks the top streams
+      // it leaves to the 256-entry one, so that no wave of it waits for them
+      if (TABN < 256 && t.place && k == (uint32_t)(E - 1) && lane == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (on[u]) __hip_atomic_store(w.tstat + g0 + u, kStLater, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return;
+    }
   }
+  bool mine[U];  // the top streams this wave codes (placement)
+#pragma unroll
+  for (int u = 0; u < U; ++u) mine[u] = on[u];
   uint32_t toff[U];  // the symbol of table entry 0
 #pragma unroll
   for (int u = 0; u < U; ++u) toff[u] = TABN < 256 ? lo[u] : 0u;
@@ -1117,6 +1214,84 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
   const bool topexp = (DT == LTC_BF16 || DT == LTC_FP32) && k == (uint32_t)(E - 1);
   if (topexp) body(std::true_type{});
   else body(std::false_type{});
+
+  if constexpr (!DELTA) {
+    if (!t.place || k != (uint32_t)(E - 1)) return;
+    // sizes first (a coded stream's payload, or the RAW fallback of one
+    // that did not pay), then each stream's walk
+    uint64_t fsz[U], pre[U];
+    bool got[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      got[u] = false;
+      fsz[u] = pre[u] = 0;
+      if (!mine[u]) continue;
+      fsz[u] = align16(on[u] ? wo[u] + 2ull * (wcap - top[u]) : (uint64_t)fallback[u].x);
+      const bool first = g0 + u == t.jobs[jb[u]].chunk0;
+      if (lane == 0)
+        __hip_atomic_store(w.tstat + g0 + u, (first ? kStInc : kStAgg) | fsz[u], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // ticks of the 100 MHz device clock: 1 ms plus 20 ns per element of a
+    // chunk, several times the coding time of a stream
+    const uint64_t limit = 100000ull + 2ull * t.n_full;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!mine[u]) continue;
+      const uint64_t g = g0 + u, f = t.jobs[jb[u]].chunk0;
+      if (g == f) {
+        got[u] = true;
+      } else if (u == 1 && mine[0] && got[0] && jb[0] == jb[1]) {
+        pre[u] = pre[0] + fsz[0];
+        got[u] = true;
+      } else {
+        got[u] = top_prefix(w.tstat, g, f, TABN == 256, limit, pre[u]);
+      }
+      if (got[u] && g != f && lane == 0)
+        __hip_atomic_store(w.tstat + g, kStInc | (pre[u] + fsz[u]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the payloads: prefix, the 64 final states, v1's table, the words from
+    // the stream's workspace slot (the drains of this wave; the slot ends on
+    // a 16-byte boundary, so they are read as aligned blocks shifted into
+    // place, blocks past the end as zeros) and zeros to the next 16 bytes.
+    // The words were stored by other lanes of this one-wave workgroup: a
+    // workgroup-scope fence orders them before the loads.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!got[u] || !on[u]) continue;
+      const uint32_t nw = wcap - top[u];
+      uint8_t* dst = t.jobs[jb[u]].blob + w.blob_nbytes[jb[u]] + pre[u];
+      if (lane == 0) *reinterpret_cast<uint4*>(dst) = make_uint4(nw, t.v2 ? 0u : lo[u] | (hi[u] << 8), 0u, 0u);
+      reinterpret_cast<uint32_t*>(dst + 16)[lane] = x[u];
+      const uint32_t tcount = t.v2 ? 0u : hi[u] - lo[u] + 1u;
+      const uint16_t* fr = w.freq + 256 * sid[u] + lo[u];
+      for (uint32_t i = lane; i < (wo[u] - kRansFixed) / 2; i += 64)
+        reinterpret_cast<uint16_t*>(dst + kRansFixed)[i] = i < tcount ? fr[i] : (uint16_t)0;
+      const uint8_t* ws = reinterpret_cast<const uint8_t*>(w.words + sid[u] * wcap + (wcap - nw));
+      const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(ws) & 15u);
+      const uint4* ab = reinterpret_cast<const uint4*>(ws - sh);
+      const uint32_t nsrc = (sh + 2u * nw) / 16u, wunits = (2u * nw + 15u) / 16u;
+      uint4* wd = reinterpret_cast<uint4*>(dst + wo[u]);
+      for (uint32_t i0 = lane; i0 < wunits; i0 += 256) {
+        uint4 va[4], vb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // clamped loads, then selects (block i < wunits <= nsrc)
+          const uint32_t i = i0 + 64 * q;
+          const uint4 a = ab[min(i, wunits - 1u)], b = ab[min(i + 1u, nsrc - 1u)];
+          va[q] = i < wunits ? a : z;
+          vb[q] = sh && i + 1 < nsrc ? b : z;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t i = i0 + 64 * q;
+          if (i < wunits) wd[i] = shift_blocks(va[q], vb[q], sh);
+        }
+      }
+      if (lane == 0) w.sinfo[4 * sid[u] + 3] = kPlaced;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ k_scan
@@ -1149,6 +1324,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(CTable t, CWork w, uint32
     return;  // no chunk of this tensor in this launch
   }
   const bool first = c_lo == job.chunk0, final = c_hi == job.chunk0 + job.nchunks;
+  // placement: the status of every chunk's top stream, its size when it
+  // needs no coding (CONST, RAW), unknown (0) when k_encode codes it
+  if (part == 1 && t.place) {
+    for (uint64_t g = c_lo + threadIdx.x; g < c_hi; g += kScanThreads) {
+      const uint64_t s = g * E + E - 1;
+      const bool cand = (w.sinfo[4 * s + 1] & 0xFFu) == kModeCand;
+      w.tstat[g] = cand ? 0ull : (g == job.chunk0 ? kStInc : kStAgg) | align16(w.sinfo[4 * s]);
+    }
+  }
   const uint64_t s0 = c_lo * E;
   // streams per chunk in this part, and the first of them
   const uint32_t per = part == 0 ? E : part == 1 ? E - 1 : 1u;
@@ -1531,7 +1715,7 @@ __device__ __forceinline__ void pack_chunk(const CTable& t, const CWork& w, uint
       rawmask |= 1u << k;
       if (si.w == kRawStaged) stmask |= 1u << k;
     }
-    else if (mode == LTC_MODE_RANS)
+    else if (mode == LTC_MODE_RANS && si.w != kPlaced)  // k_encode wrote the placed ones
       write_rans<CRC>(blob, raw_off[k], s, si.y, si.x, si.z, t, w, job.frames, L, pos);
     else if (DELTA && mode == LTC_MODE_ZRUN)
       write_zrun<DT, DELTA>(blob + raw_off[k], src, job.base + c * t.chunk_bytes, n, k, si.z, si.w, si.x,

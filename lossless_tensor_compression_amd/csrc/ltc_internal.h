@@ -16,6 +16,7 @@ namespace ltc {
 constexpr uint32_t kModeCand = 0xFF;    // internal: histogram done, encode pending (no blob mode)
 constexpr uint32_t kRawStaged = 1;      // internal: a RAW stream's bytes are written (top-last: in
                                         // the blob at their offset; else in the stream's workspace slot)
+constexpr uint32_t kPlaced = 2;         // internal: k_encode wrote this RANS payload into the blob
 constexpr int kMaxJobs = LTC_BATCH_MAX;
 
 __host__ __device__ constexpr uint64_t align16(uint64_t v) { return (v + 15) & ~uint64_t(15); }
@@ -71,6 +72,8 @@ struct CTable {
   uint32_t v2;         // format v2: one table per (tensor, stream index)
   uint32_t delta;      // XOR deltas: every job has a base; ZRUN candidates
   uint32_t top_last;   // layout flag LTC_FLAG_TOP_LAST: stream E-1 of every chunk after the others
+  uint32_t place;      // top-last, one group, no deltas: k_encode writes the top streams' RANS
+                       // payloads into the blob (offsets from a look-back over CWork::tstat)
   // the launch covers global chunks [c_begin, c_end) (a group of a pipelined
   // call, or all of them)
   uint64_t c_begin, c_end;
@@ -97,6 +100,7 @@ struct CWork {
   uint64_t* offsets;    // [S]
   uint64_t* blob_nbytes;  // [count] running offset of the scans (top-last: of the lower streams)
   uint64_t* top_run;      // [count] top-last: running offset of the top streams' scan
+  uint64_t* tstat;        // CTable::place: [chunks] status of each chunk's top stream (k_encode)
 };
 
 struct DJob {
@@ -181,6 +185,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    v += ((uint64_t)hi << 32) | lo;
+  }
   return v;
 }
 
