@@ -9,8 +9,10 @@ Blobs must equal the oracle's top-last blobs byte for byte, checksums the
 oracle's CRC-32 of those blobs, decodes the input, and verdicts on corrupted
 blobs the oracle's.  Cases cover every dtype, ragged and tiny inputs, chunks
 whose top stream is abandoned part way (so their RAW streams are written
-whole by the packing pass instead), pipelined calls whose top-stream scans
-wait on both groups' lower scans, batches with empty tensors, format v2,
+whole by the packing pass instead), calls of 4096 chunks or more (whose
+encoder places the top streams' payloads itself; pipelined for deltas, whose
+top-stream scans wait on both groups' lower scans), batches with empty
+tensors, format v2,
 deltas, the fused and the read-back checksums, the per-kernel (event) path
 and the host-blob decode.
 """
@@ -103,9 +105,10 @@ def test_abandoned_top_streams(ltc, dtype, thr):
 
 @pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 512), (2, 512), (0, 256)])
 def test_grouped_single_tensor(ltc, dtype, chunk):
-    """4201 chunks (over the library's pipelining threshold of 4096): two
-    groups on two streams; the first group's top scan starts where the second
-    group's lower scan ended."""
+    """4201 chunks (the library's threshold is 4096): the encoder places the
+    top streams' payloads, each after the sizes of the top streams before it
+    in the tensor; every fifth chunk is random (a RAW top stream settled
+    before coding, inside the sums)."""
     rng = np.random.default_rng(200 + dtype)
     nbytes = 4200 * chunk + 24
     e = oracle.ELEM_BYTES[dtype]
@@ -193,10 +196,12 @@ def test_deltas(ltc, shared):
 
 
 def test_grouped_deltas_fp32(ltc):
+    """Deltas over 4096 chunks run in two groups on two streams: the first
+    group's top scan starts where the second group's lower scan ended."""
     rng = np.random.default_rng(13)
-    base = (rng.standard_normal(600 * 256) * 0.02).astype(np.float32)  # 600 chunks of 1 KiB
+    base = (rng.standard_normal(4200 * 256) * 0.02).astype(np.float32)  # 4200 chunks of 1 KiB
     src = base.copy()
-    src.view(np.uint32)[rng.integers(0, src.size, 3000)] ^= 3
+    src.view(np.uint32)[rng.integers(0, src.size, 21000)] ^= 3
     want = oracle.compress_delta(src, base, 3, 1024, top_last=True)
     got = ltc.compress_delta(to_gpu(src, 3), to_gpu(base, 3), 1024, top_last=True)
     _equal(to_np_bytes(got), want, "grouped fp32 delta")
