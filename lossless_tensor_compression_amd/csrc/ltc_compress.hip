@@ -43,7 +43,7 @@ constexpr int kScanThreads = 1024;
 constexpr uint32_t kRingWords = 512;    // encoder word ring per stream (LDS)
 constexpr uint32_t kFlushWords = 256;   // one drain = 64 lanes x 8 bytes
 constexpr int kEncBlock = 8;            // steps per prefetched block (a multiple of 4)
-constexpr int kEncStreams = 2;          // streams one wave codes, interleaved
+constexpr int kEncStreams = 2;          // streams one wave codes, interleaved (large calls)
 
 __device__ __forceinline__ uint32_t pack_info(uint32_t mode, uint32_t cval, uint32_t lo,
                                               uint32_t hi) {
@@ -748,9 +748,10 @@ __device__ __forceinline__ uint4 shift_blocks(const uint4 a, const uint4 b, uint
                     __builtin_amdgcn_alignbyte(w3, w2, 2), __builtin_amdgcn_alignbyte(w4, w3, 2));
 }
 
-// One wave codes stream k of two neighbouring chunks, interleaving their
-// independent state chains (instruction-level parallelism for a loop whose
-// every step is a dependent chain).
+// One wave codes stream k of U neighbouring chunks: in large calls two,
+// interleaving their independent state chains (instruction-level parallelism
+// for a loop whose every step is a dependent chain), in smaller ones one
+// (more waves in flight; see launch_encode).
 //
 // Division.  A coding step needs q = floor(x / f) for a 32-bit x and
 // 1 <= f <= 4095.  With r = 1/f rounded up to a double, x * r >= x / f, and
@@ -795,10 +796,9 @@ __device__ __forceinline__ uint4 shift_blocks(const uint4 a, const uint4 b, uint
 // A launch codes the stream indices kfirst, kfirst - 1, ... (nplanes of
 // them): all E at once, or in the top-last layout the lower ones and then,
 // after their scan, the top one.
-template <int DT, bool DELTA, int TABN>
+template <int DT, bool DELTA, int TABN, int U>
 __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirst, uint32_t nplanes) {
   constexpr int E = Dt<DT>::E;
-  constexpr int U = kEncStreams;
   __shared__ uint4 tab[U][TABN];
   __shared__ __attribute__((aligned(16))) uint32_t stg[U][256];  // 512 u16 entry offsets
   __shared__ __attribute__((aligned(16))) uint16_t ring[U][kRingWords + 64];
@@ -899,7 +899,12 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
     wlimit[u] = (limit - wo[u]) / 2;
     src[u] = job.src + c * t.chunk_bytes;
   }
-  if (!on[0] && !on[1]) return;
+  {
+    bool any = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) any = any || on[u];
+    if (!any) return;
+  }
   // the short-table instantiation takes the pairs whose coded streams use at
   // most TABN consecutive symbols (v1 tables); the full one the others
   {
@@ -1023,7 +1028,9 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
     // wide load, the block goes through the LDS tile, and every lane reads
     // back its own element of each step at a fixed offset.
     uint32_t done = 0;  // full steps coded, counted from the last one down
-    const bool lock = on[0] && on[1] && full[0] == full[1] && t.vec16 != 0;
+    bool lock = t.vec16 != 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) lock = lock && on[u] && full[u] == full[0];
     const uint32_t nfb = lock ? full[0] / kEncBlock : 0u;
     uint32_t pf[U][2 * E];
     auto fetch = [&](int u, uint32_t bi) {  // block bi: elements 64*(full - 8(bi+1)) + 8 lane ...
@@ -1176,13 +1183,18 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
 #pragma unroll
           for (int q = 0; q < kEncBlock; ++q) sy[u][q] = sn[u][q];
         done = kEncBlock * (bi + 1);
-        if (!on[0] || !on[1]) break;  // the survivor finishes below
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < U; ++u) all = all && on[u];
+        if (!all) break;  // the survivor finishes below
       }
     }
     // General path: whatever the fast loop left (streams of different
     // lengths, unaligned inputs, the last full % 8 steps, the partner of a
     // stream that aborted), one step at a time with direct element loads.
-    const uint32_t rest = max(on[0] ? full[0] - done : 0u, on[1] ? full[1] - done : 0u);
+    uint32_t rest = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) rest = max(rest, on[u] ? full[u] - done : 0u);
     for (uint32_t i = 0; i < rest; ++i) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -1241,8 +1253,8 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
       const uint64_t g = g0 + u, f = t.jobs[jb[u]].chunk0;
       if (g == f) {
         got[u] = true;
-      } else if (u == 1 && mine[0] && got[0] && jb[0] == jb[1]) {
-        pre[u] = pre[0] + fsz[0];
+      } else if (u > 0 && mine[u - 1] && got[u - 1] && jb[u - 1] == jb[u]) {
+        pre[u] = pre[u - 1] + fsz[u - 1];
         got[u] = true;
       } else {
         got[u] = top_prefix(w.tstat, g, f, TABN == 256, limit, pre[u]);
@@ -1821,17 +1833,32 @@ __attribute__((amdgpu_waves_per_eu(CRC ? 4 : 1))) void k_pack(CTable t, CWork w)
 // ------------------------------------------------------------------ launch
 
 // k_encode for stream indices kfirst, kfirst - 1, ... (nplanes of them) of
-// chunks [t.c_begin, t.c_end)
+// chunks [t.c_begin, t.c_end), U streams per wave
+template <int DT, bool DELTA, int U>
+static void launch_encode_u(const CTable& t, const CWork& w, hipStream_t st, uint32_t kfirst,
+                            uint32_t nplanes, uint64_t chunks) {
+  const uint32_t grid = DELTA ? (uint32_t)((chunks + 8 * U - 1) / (8 * U) * 8 * nplanes)
+                              : (uint32_t)((chunks + U - 1) / U * nplanes);
+  hipLaunchKernelGGL((k_encode<DT, DELTA, 128, U>), dim3(grid), dim3(64), 0, st, t, w, kfirst, nplanes);
+  hipLaunchKernelGGL((k_encode<DT, DELTA, 256, U>), dim3(grid), dim3(64), 0, st, t, w, kfirst, nplanes);
+}
+
+// Two interleaved streams per wave suit a call of many rounds of resident
+// waves; a smaller call codes one stream per wave (54 instead of 101 VGPRs
+// and half the LDS for BF16: 32 waves per CU instead of 16), so twice as many
+// chains run at once and the last round is half as long.  Measured (top-last
+// compress, one box): C2 (512 chunks) 0.154 -> 0.109 ms, C4b (1024) 0.291 ->
+// 0.201 ms, C3 (13,312) 1.30 -> 1.27 ms; C5 (65,536) 5.45-5.49 ms with two
+// streams against 5.59 with one.
+constexpr uint64_t kEncPairMinChunks = 16384;
+
 template <int DT, bool DELTA>
 static void launch_encode(const CTable& t, const CWork& w, hipStream_t st, uint32_t kfirst,
                           uint32_t nplanes) {
-  constexpr uint64_t U = kEncStreams;
   const uint64_t chunks = t.c_end - t.c_begin;
   if (!chunks || !nplanes) return;
-  const uint32_t grid = DELTA ? (uint32_t)((chunks + 8 * U - 1) / (8 * U) * 8 * nplanes)
-                              : (uint32_t)((chunks + U - 1) / U * nplanes);
-  hipLaunchKernelGGL((k_encode<DT, DELTA, 128>), dim3(grid), dim3(64), 0, st, t, w, kfirst, nplanes);
-  hipLaunchKernelGGL((k_encode<DT, DELTA, 256>), dim3(grid), dim3(64), 0, st, t, w, kfirst, nplanes);
+  if (chunks < kEncPairMinChunks) launch_encode_u<DT, DELTA, 1>(t, w, st, kfirst, nplanes, chunks);
+  else launch_encode_u<DT, DELTA, kEncStreams>(t, w, st, kfirst, nplanes, chunks);
 }
 
 template <int DT, bool DELTA>
