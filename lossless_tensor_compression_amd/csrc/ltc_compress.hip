@@ -30,7 +30,7 @@
 
 namespace ltc {
 
-constexpr int kHistThreads = 256;
+constexpr int kHistThreads = 512;
 constexpr int kHistCopyShift = 4;
 constexpr int kHistCopies = 1 << kHistCopyShift;  // sub-histograms, picked by lane & 15
 constexpr uint32_t kHistSeg = 1u << 19;  // elements between sub-histogram flushes
@@ -93,8 +93,11 @@ __device__ __forceinline__ uint4 load_x16(const uint8_t* src, const uint8_t* bas
 // lanes hit 16 different banks whatever their bins.  Two bins share a word as
 // 16-bit counters; a copy counts at most kHistSeg/16 = 32768 elements between
 // flushes into the 32-bit histogram, so no counter overflows.  16 copies
-// rather than 32 halve the LDS of a workgroup, so 8 of them (the 32-wave
-// limit) fit on a CU instead of 4: 0.37 against 0.40 ms for 1.7 GB of BF16.
+// rather than 32 halve the LDS of a workgroup (16 KiB), so a CU holds its
+// 32-wave limit of them (with 256-thread workgroups: 0.37 against 0.40 ms for
+// 1.7 GB of BF16).  512-thread workgroups measured 1-3% faster than 256 on
+// calls of 512-1024 chunks and no slower on 13,312; 1024 threads were 5%
+// slower there.
 template <int DT>
 __device__ __forceinline__ void hist_elem(uint32_t* hs, uint32_t y, uint32_t copy) {
   constexpr int E = Dt<DT>::E;
