@@ -38,6 +38,9 @@ constexpr uint32_t kMirror = 64;     // words after the ring: a copy of its firs
 // slowest chunk ends).
 constexpr uint32_t kDecWaves = 1;
 constexpr uint32_t kHalf = 256;     // words per refill (64 lanes x 8 bytes)
+// Launches of at most this many chunks decode with the fused slot table
+// (8 waves per CU: every chunk of such a launch is resident at once).
+constexpr uint64_t kDecFusedMaxChunks = 2048;
 
 // Words 256h + 4l .. +3 of a coded stream (lane l).  An 8-byte read that
 // starts at a word index below W stays inside the payload's 16-byte padded
@@ -91,11 +94,18 @@ template <int DT> __device__ __forceinline__ void planes_to_words(const uint32_t
   }
 }
 
-template <int DT, int MAXR, bool DELTA>
+// FUSED (one coded stream per chunk, small calls): one 32-bit entry per slot,
+// symbol | f << 8 | (slot - cum) << 20 (a coded stream has two or more
+// symbols, so f and slot - cum stay below 4096), read once per step instead
+// of the slot's symbol and then the symbol's (f, cum).  The 16 KiB table
+// leaves room for 8 waves per CU instead of 20, which a call of at most
+// kDecFusedMaxChunks chunks does not fill anyway.
+template <int DT, int MAXR, bool DELTA, bool FUSED = false>
 __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
   constexpr int E = Dt<DT>::E;
-  __shared__ uint8_t lut_w[kDecWaves][MAXR][4096];
-  __shared__ uint32_t symt_w[kDecWaves][MAXR][256];
+  static_assert(!FUSED || MAXR == 1, "the fused table serves one coded stream");
+  __shared__ uint8_t lut_w[kDecWaves][MAXR][FUSED ? 4 : 4096];
+  __shared__ uint32_t symt_w[kDecWaves][MAXR][FUSED ? 4096 : 256];
   __shared__ __attribute__((aligned(16))) uint16_t ring_w[kDecWaves][MAXR][kDecRing + kMirror];
   const uint32_t wslot = kDecWaves > 1 ? threadIdx.x / 64 : 0u;
   auto& lut = lut_w[wslot];
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
     for (int q = 0; q < 4; ++q) {
       const uint32_t i = 4 * lane + q;
       if (i < tcount) {
-        symt[rr][lo + i] = f[q] | ((base + cum[q]) << 16);
+        if constexpr (!FUSED) symt[rr][lo + i] = f[q] | ((base + cum[q]) << 16);
         cumt[i] = (uint16_t)(base + cum[q]);
       }
     }
@@ -326,12 +336,33 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
     return;
   }
   wave_sync();
-  // slot -> symbol table: lane l fills slots 64l .. 64l+63
+  // slot -> symbol table: lane l fills slots 64l .. 64l+63 (FUSED: the slot
+  // entries, lane l slots l, l + 64, ..., so that consecutive lanes write
+  // consecutive words)
 #pragma unroll
   for (int rr = 0; rr < MAXR; ++rr) {
     if (rr >= nr) continue;
     const uint32_t lo = tlo[rr], tcount = tcnt[rr];
     const uint16_t* cumt = ring[rr];
+    if constexpr (FUSED) {
+      uint32_t a = 0, z = tcount - 1;  // largest i with cumt[i] <= lane
+      while (a < z) {
+        const uint32_t mid = (a + z + 1) / 2;
+        if (cumt[mid] <= lane) a = mid;
+        else z = mid - 1;
+      }
+      uint32_t v = a, curc = cumt[a], nextc = cumt[a + 1];  // cumt[tcount] = 4096 ends every walk
+      for (uint32_t j = 0; j < 64; ++j) {
+        const uint32_t sl = lane + 64 * j;
+        while (nextc <= sl) {
+          ++v;
+          curc = nextc;
+          nextc = cumt[v + 1];
+        }
+        symt[rr][sl] = (lo + v) | ((nextc - curc) << 8) | ((sl - curc) << 20);
+      }
+      continue;
+    }
     const uint32_t slot0 = 64 * lane;
     uint32_t a = 0, z = tcount - 1;  // largest i with cumt[i] <= slot0
     while (a < z) {
@@ -425,9 +456,16 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode(DTable t) {
     const bool active = !G || 64 * full + lane < n;
     const uint32_t xs = x[rr];
     const uint32_t sl = xs & (kTotal - 1);
-    const uint32_t v = lut[rr][sl];
-    const uint32_t e = symt[rr][v];
-    const uint32_t xd = __umul24(e & 0xFFFFu, xs >> 12) + sl - (e >> 16);
+    uint32_t v, xd;
+    if constexpr (FUSED) {
+      const uint32_t e = symt[rr][sl];
+      v = e & 0xFFu;
+      xd = __umul24((e >> 8) & 0xFFFu, xs >> 12) + (e >> 20);
+    } else {
+      v = lut[rr][sl];
+      const uint32_t e = symt[rr][v];
+      xd = __umul24(e & 0xFFFFu, xs >> 12) + sl - (e >> 16);
+    }
     const bool need = active && xd < kRansLow;
     const uint64_t mask = ballot(need);
     uint32_t wv = ring_word(rr, mask);
@@ -818,7 +856,8 @@ static hipError_t launch_decompress_d(DTable t, hipStream_t st, const hipEvent_t
   if (init_status) hipLaunchKernelGGL(k_status_init, dim3(1), dim3(64), 0, st, t);
   if (DELTA && n) hipLaunchKernelGGL(k_zrun_expand<DT>, dim3((uint32_t)(n * E)), dim3(256), 0, st, t);
   record(ev, 0, st);
-  if (n) hipLaunchKernelGGL((k_decode<DT, 1, DELTA>), dgrid, dblock, 0, st, t);
+  if (n && n <= kDecFusedMaxChunks) hipLaunchKernelGGL((k_decode<DT, 1, DELTA, true>), dgrid, dblock, 0, st, t);
+  else if (n) hipLaunchKernelGGL((k_decode<DT, 1, DELTA>), dgrid, dblock, 0, st, t);
   record(ev, 1, st);
   if constexpr (E > 1) {
     if (n) hipLaunchKernelGGL((k_decode<DT, E, DELTA>), dgrid, dblock, 0, st, t);
