@@ -225,3 +225,35 @@ def test_c5_full_size_with_crc(ltc):
     bad = np.nonzero(crc != wcrc)[0]
     assert bad.size == 0, f"{bad.size} CRC chunks differ, first {int(bad[0])}"
     banner(f"C5 {crc.size} checksums equal to the oracle's")
+
+
+def test_c5_top_last_full_size(ltc):
+    """C5 as bench.py times it: compress_with_crc32 in the top-last layout
+    (65,536 chunks: two streams per encoder wave, payloads placed by the
+    encoder, checksums read back), the whole blob against the oracle's
+    top-last blob, every checksum against the oracle's CRC-32 of it, and the
+    exact round trip."""
+    banner("C5 generate (8 GiB)")
+    buf = workloads.c5_gpu()
+    t = buf.view(torch.bfloat16)
+    banner("C5 compress_with_crc32, top-last")
+    blob, crc = ltc.compress_with_crc32(t, CHUNK, 0.95, 16384, top_last=True)
+    banner("C5 top-last decompress")
+    out = ltc.decompress(blob)
+    assert torch.equal(out.view(torch.uint8), buf)
+    del out
+    crc = crc.cpu().numpy().view(np.uint32)
+    got = blob.cpu().numpy()
+    del blob
+    torch.cuda.empty_cache()
+    src = buf.cpu().numpy()
+    del buf, t
+    torch.cuda.empty_cache()
+    banner(f"C5 oracle compress, top-last (8 GiB, {THREADS} host threads)")
+    want = oracle.compress(src, 1, CHUNK, 0.95, nthreads=THREADS, top_last=True)
+    del src
+    _assert_blob_equal(got, want, "C5 top-last blob")
+    del got
+    wcrc = oracle.crc32_chunks(want, 16384)
+    assert crc.size == wcrc.size and np.array_equal(crc, wcrc)
+    banner(f"C5 top-last: blob and {crc.size} checksums equal to the oracle's")

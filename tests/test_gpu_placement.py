@@ -150,3 +150,16 @@ def test_abandon_mix_full_chunks(ltc):
     bits = [7, 5, 5, 7, 7, 5, 7, 5, 5] * 456
     x = _abandon_mix(1, bits, 131072, rng)
     _batch(ltc, [x], 1, 131072, thr=0.88, label="512 MiB abandon mix")
+
+
+def test_two_streams_per_wave(ltc):
+    """16,384 chunks or more: the encoder codes two chunks' streams per wave
+    and places both payloads (the second takes the first's prefix when both
+    are in one tensor); narrow, wide, abandoned, constant and RAW top
+    streams, and tensors that end on odd chunks."""
+    rng = np.random.default_rng(620)
+    chunk = 1024
+    kinds = ["narrow", "narrow", "wide", "a7", "narrow", "const", "uniform", "narrow", "narrow", "a7", "narrow"]
+    x = _exp_chunks(1, kinds * 1500, chunk, rng)  # 16,500 chunks
+    cut = [0, 4001 * 512, 4002 * 512, 11001 * 512, x.size]
+    _batch(ltc, [x[a:b] for a, b in zip(cut, cut[1:])], 1, chunk, thr=0.88, label="two streams per wave")
