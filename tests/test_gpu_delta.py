@@ -40,13 +40,15 @@ def _modes(blob):
     return blob[64 + 12:64 + 16 * k * e:16]
 
 
-def check_delta(ltc, src, base, dtype, chunk=131072, thr=0.95, shared=False, label=""):
+def check_delta(ltc, src, base, dtype, chunk=131072, thr=0.95, shared=False, label="", top_last=False):
     sb = np.ascontiguousarray(src).reshape(-1).view(np.uint8)
     bb = np.ascontiguousarray(base).reshape(-1).view(np.uint8)
-    banner(f"delta case {label} dtype={dtype} chunk={chunk} thr={thr} v2={shared} bytes={sb.size}")
-    want = oracle.compress_delta(sb, bb, dtype, chunk, thr, shared_tables=shared)
+    banner(f"delta case {label} dtype={dtype} chunk={chunk} thr={thr} v2={shared} top_last={top_last} "
+           f"bytes={sb.size}")
+    want = oracle.compress_delta(sb, bb, dtype, chunk, thr, shared_tables=shared, top_last=top_last)
     tb = to_gpu(bb, dtype)
-    got = to_np_bytes(ltc.compress_delta(to_gpu(sb, dtype), tb, chunk, thr, shared_tables=shared))
+    got = to_np_bytes(ltc.compress_delta(to_gpu(sb, dtype), tb, chunk, thr, shared_tables=shared,
+                                         top_last=top_last))
     assert got.size == want.size, (got.size, want.size)
     if not np.array_equal(got, want):
         bad = np.nonzero(got != want)[0]
@@ -178,6 +180,21 @@ def test_grouped(ltc, dtype, chunk, shared):
     for c in range(0, sv.size // chunk, 7):  # some chunks changed everywhere
         sv[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
     check_delta(ltc, src, base, dtype, chunk, shared=shared, label=f"grouped {dtype}")
+
+
+@pytest.mark.parametrize("top_last", [False, True], ids=["dir", "top-last"])
+def test_two_streams_per_wave(ltc, top_last):
+    """33,000 chunks: each pipeline group holds 16,384 chunks or more, so the
+    encoder codes two chunks' streams per wave (the workgroups of a chunk pair
+    8 apart for the XCDs), with ZRUN, RANS and RAW streams in every group."""
+    rng = np.random.default_rng(530)
+    chunk = 512
+    n = (33000 * chunk) // 4
+    src, base = _pair(3, n, "nudge", rng)
+    sv = src.view(np.uint8)
+    for c in range(0, sv.size // chunk, 11):
+        sv[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
+    check_delta(ltc, src, base, 3, chunk, top_last=top_last, label="two streams per wave")
 
 
 def test_misaligned_base_and_source(ltc):
