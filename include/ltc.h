@@ -166,6 +166,8 @@ enum { LTC_MODE_RAW = 0, LTC_MODE_RANS = 1, LTC_MODE_CONST = 2, LTC_MODE_ZRUN = 
 #define LTC_FLAG_DELTA 2u              /* header flag: XOR delta against a base */
 #define LTC_FLAG_CALLER_STREAM_ONLY 4u /* compress flags: no internal stream, all on `stream` */
 #define LTC_FLAG_TOP_LAST 8u           /* compress flags and header flag: top-last layout */
+#define LTC_FLAG_PLACE_NO_WAIT 16u     /* compress flags, top-last: the encoder waits for no earlier
+                                          payload size (see ltc_compress_batch_ex) */
 
 #define LTC_HEADER_BYTES 64
 #define LTC_DEFAULT_CHUNK_BYTES 131072u
@@ -308,8 +310,8 @@ int ltc_crc32_chunks_batch(int count, const void* const* h_src_ptrs, const uint6
 
 /* Upper bound of the blob size with compress flags (0: ltc_compress_bound;
  * LTC_FLAG_SHARED_TABLES adds E table records of at most 528 bytes;
- * LTC_FLAG_CALLER_STREAM_ONLY and LTC_FLAG_TOP_LAST change nothing).  0 on
- * bad arguments. */
+ * LTC_FLAG_CALLER_STREAM_ONLY, LTC_FLAG_TOP_LAST and LTC_FLAG_PLACE_NO_WAIT
+ * change nothing).  0 on bad arguments. */
 uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes, uint32_t flags);
 
 /* The general compress call: ltc_compress_batch plus
@@ -317,7 +319,12 @@ uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes,
  *     LTC_FLAG_TOP_LAST (the top-last layout); capacities are checked
  *     against ltc_compress_bound_ex; with LTC_FLAG_CALLER_STREAM_ONLY added,
  *     the call uses no internal stream (same blobs, all kernels on `stream`
- *     one after another);
+ *     one after another); with LTC_FLAG_PLACE_NO_WAIT added to a top-last
+ *     call, the encoder waves that place top-stream payloads (calls of 4096
+ *     chunks or more, no deltas) wait for no earlier payload's size: a wave
+ *     whose offset is not known the moment it looks leaves its payload to
+ *     the packing pass, the fallback a slow predecessor otherwise triggers.
+ *     Same blobs; for testing that path;
  *   h_base_ptrs: NULL, or per tensor the device pointer of its delta base
  *     (nbytes bytes, aligned like the source): the blobs are XOR deltas
  *     (LTC_FLAG_DELTA set in the header; with checksums the CRC kernel reads

@@ -174,6 +174,7 @@ FLAG_SHARED_TABLES = 1  # format v2: one frequency table per stream index
 FLAG_DELTA = 2          # header flag: the blob codes src XOR base
 FLAG_CALLER_STREAM_ONLY = 4  # compress flag: every kernel on the caller's stream
 FLAG_TOP_LAST = 8       # compress and header flag: top-stream payloads after all others
+FLAG_PLACE_NO_WAIT = 16  # compress flag, top-last: placing encoder waves never wait (tests)
 NOALLOC_SCRATCH_BYTES = 64 << 20  # workspace limit of ltc_compress_noalloc
 
 

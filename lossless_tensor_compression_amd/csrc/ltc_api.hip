@@ -319,7 +319,8 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
                   uint32_t flags = 0, const void* const* bases = nullptr) {
   if (count < 1 || count > kMaxJobs || !srcs || !nbytes || !blobs || !caps || !d_blob_nbytes)
     return LTC_ERR_INVALID_ARGUMENT;
-  if (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY | LTC_FLAG_TOP_LAST))
+  if (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY | LTC_FLAG_TOP_LAST |
+                LTC_FLAG_PLACE_NO_WAIT))
     return LTC_ERR_INVALID_ARGUMENT;
   if (!(theta > 0.0 && theta <= 1.0)) return LTC_ERR_INVALID_ARGUMENT;
   const bool one_stream = (flags & LTC_FLAG_CALLER_STREAM_ONLY) != 0;
@@ -385,6 +386,9 @@ int compress_impl(int count, const void* const* srcs, const uint64_t* nbytes, in
   // streams' payloads instead, on one stream (a smaller call waits longer in
   // the look-back than packing takes)
   t.place = t.top_last && !bases && chunk0 >= kPipeMinChunks ? 1u : 0u;
+  // device-clock ticks (100 MHz) a placing wave waits for the sizes before
+  // its chunk: about 1 ms plus the time to code one chunk's stream
+  t.place_wait = (flags & LTC_FLAG_PLACE_NO_WAIT) ? 0 : 100000ull + 2ull * t.n_full;
   uint8_t* ws = static_cast<uint8_t*>(d_ws);
   CWork w;
   w.sinfo = reinterpret_cast<uint32_t*>(ws + l.sinfo);
@@ -584,7 +588,8 @@ uint64_t ltc_compress_bound(uint64_t nbytes, int dtype, uint32_t chunk_bytes) {
 
 uint64_t ltc_compress_bound_ex(uint64_t nbytes, int dtype, uint32_t chunk_bytes, uint32_t flags) {
   if (check_shape(nbytes, dtype, chunk_bytes) ||
-      (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY | LTC_FLAG_TOP_LAST)))
+      (flags & ~(LTC_FLAG_SHARED_TABLES | LTC_FLAG_CALLER_STREAM_ONLY | LTC_FLAG_TOP_LAST |
+                 LTC_FLAG_PLACE_NO_WAIT)))
     return 0;
   return bound_flags(nbytes, elem_bytes(dtype), chunk_bytes, flags);
 }

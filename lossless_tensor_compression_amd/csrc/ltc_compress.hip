@@ -1252,9 +1252,10 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
         __hip_atomic_store(w.tstat + g0 + u, (first ? kStInc : kStAgg) | fsz[u], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    // ticks of the 100 MHz device clock: 1 ms plus 20 ns per element of a
-    // chunk, several times the coding time of a stream
-    const uint64_t limit = 100000ull + 2ull * t.n_full;
+    // ticks of the 100 MHz device clock (the host sets 1 ms plus 20 ns per
+    // element of a chunk, several times the coding time of a stream; 0 with
+    // LTC_FLAG_PLACE_NO_WAIT: give up at the first unknown size)
+    const uint64_t limit = t.place_wait;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!mine[u]) continue;

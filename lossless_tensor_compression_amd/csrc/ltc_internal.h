@@ -74,6 +74,7 @@ struct CTable {
   uint32_t top_last;   // layout flag LTC_FLAG_TOP_LAST: stream E-1 of every chunk after the others
   uint32_t place;      // top-last, one group, no deltas: k_encode writes the top streams' RANS
                        // payloads into the blob (offsets from a look-back over CWork::tstat)
+  uint64_t place_wait; // with place: device-clock ticks a wave waits for the sizes before it
   // the launch covers global chunks [c_begin, c_end) (a group of a pipelined
   // call, or all of them)
   uint64_t c_begin, c_end;

@@ -19,3 +19,17 @@ def to_np_bytes(t):
 
 def banner(msg):
     print(f"[gpu] {msg}", flush=True)
+
+
+def stream_modes(blob):
+    """Directory modes of a blob (public format): array [K, E] of mode bytes."""
+    b = np.asarray(blob, dtype=np.uint8)
+    e = int(b[7])
+    k = int(b[20:24].view(np.uint32)[0])
+    return b[64:64 + 16 * k * e].reshape(k, e, 16)[:, :, 12].copy()
+
+
+def rans_streams(blob):
+    """Number of RANS (mode 1) streams in a blob's directory."""
+    b = np.asarray(blob, dtype=np.uint8)
+    return int((stream_modes(b) == 1).sum()) if b.size > 64 else 0

@@ -175,4 +175,5 @@ def test_stream_and_layout_flags_do_not_change_the_bound():
         assert base == ltc.compress_bound(n, dtype)
         assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, ltc.FLAG_CALLER_STREAM_ONLY) == base
         assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, ltc.FLAG_TOP_LAST) == base
-        assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, 16) == 0  # unknown flag
+        assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, ltc.FLAG_PLACE_NO_WAIT) == base
+        assert ltc.lib().ltc_compress_bound_ex(n, dtype, 131072, 32) == 0  # unknown flag

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import banner, to_gpu, to_np_bytes
+from gpu_util import banner, rans_streams, to_gpu, to_np_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -104,10 +104,11 @@ def test_small_and_ragged(ltc, dtype, nelem, chunk):
     check_crc_case(ltc, arr, dtype, chunk, [1024, 16384, 1000], label=f"small n={nelem}")
 
 
-@pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 1024), (0, 1024)])
+@pytest.mark.parametrize("dtype,chunk", [(1, 8192), (3, 4096), (0, 2048)])
 def test_grouped_call(ltc, dtype, chunk):
     """Over 4096 chunks: two chunk groups on two streams add into frames that
-    straddle the group border; every 5th chunk is random bytes."""
+    straddle the group border; every 5th chunk is random bytes; chunks of a
+    few thousand elements, so that RANS payloads are checksummed too."""
     rng = np.random.default_rng(300 + dtype)
     nbytes = 4200 * chunk + 24
     if dtype == 0:
@@ -123,14 +124,16 @@ def test_grouped_call(ltc, dtype, chunk):
         data[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
     e = oracle.ELEM_BYTES[dtype]
     data = data[: nbytes // e * e]
-    check_crc_case(ltc, data, dtype, chunk, [1024, 16384, 131072, 5000], label=f"grouped {dtype}")
+    want = check_crc_case(ltc, data, dtype, chunk, [1024, 16384, 131072, 5000], label=f"grouped {dtype}")
+    assert rans_streams(want) > 2000, rans_streams(want)
 
 
 def test_batch_with_empty_and_tiny(ltc):
     rng = np.random.default_rng(78)
-    chunk = 1024
+    chunk = 4096
     sizes = (90000, 0, 1, 123457, 2, 40000, 250001, 17, 60000)
     arrs = [(rng.standard_normal(n) * rng.choice([0.02, 1.0, 1e-4])).astype(np.float32) for n in sizes]
+    assert sum(rans_streams(oracle.compress(a, 3, chunk)) for a in arrs) > 300
     ts = [to_gpu(a, 3) for a in arrs]
     for k in (16384, 2048, 999):
         banner(f"crc batch K={k}")

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import banner, to_gpu, to_np_bytes
+from gpu_util import banner, stream_modes, to_gpu, to_np_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -186,15 +186,25 @@ def test_grouped(ltc, dtype, chunk, shared):
 def test_two_streams_per_wave(ltc, top_last):
     """33,000 chunks: each pipeline group holds 16,384 chunks or more, so the
     encoder codes two chunks' streams per wave (the workgroups of a chunk pair
-    8 apart for the XCDs), with ZRUN, RANS and RAW streams in every group."""
+    8 apart for the XCDs), with ZRUN, RANS and RAW streams in every group.
+    8 KiB chunks (2048 elements per stream), so that a RANS payload fits: every
+    fifth chunk XORs small nonzero values into its low bytes (no zero runs,
+    three bits a symbol), every eleventh is random bytes."""
     rng = np.random.default_rng(530)
-    chunk = 512
+    chunk = 8192
     n = (33000 * chunk) // 4
     src, base = _pair(3, n, "nudge", rng)
+    per = chunk // 4
+    for c in range(2, n // per, 5):
+        src[c * per:(c + 1) * per] = base[c * per:(c + 1) * per] ^ rng.integers(1, 8, per, dtype=np.uint32)
     sv = src.view(np.uint8)
     for c in range(0, sv.size // chunk, 11):
         sv[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
-    check_delta(ltc, src, base, 3, chunk, top_last=top_last, label="two streams per wave")
+    want = check_delta(ltc, src, base, 3, chunk, top_last=top_last, label="two streams per wave")
+    modes = stream_modes(want)
+    for half in (modes[: modes.shape[0] // 2], modes[modes.shape[0] // 2:]):
+        counts = np.bincount(half.reshape(-1), minlength=4)
+        assert counts[0] > 0 and counts[1] > 1000 and counts[3] > 1000, counts  # RAW, RANS, ZRUN
 
 
 def test_misaligned_base_and_source(ltc):

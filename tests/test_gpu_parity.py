@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import banner, to_gpu, to_np_bytes
+from gpu_util import banner, rans_streams, to_gpu, to_np_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -316,9 +316,11 @@ def test_staged_raw_streams_with_abandoned_neighbours(ltc, dtype, thr):
 
 # ---- pipelined compression: calls over 4096 chunks or more (the library's
 # threshold) run in two chunk-ordered groups on two streams (the caller's and
-# one internal stream); blobs must not change.
+# one internal stream); blobs must not change.  Chunks of a few thousand
+# elements, so that top streams are coded (a RANS payload carries 272 bytes
+# of states and its table, more than a stream of 512 bytes may take).
 
-@pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 512), (2, 512), (0, 256)])
+@pytest.mark.parametrize("dtype,chunk", [(1, 8192), (3, 4096), (2, 4096), (0, 2048)])
 def test_grouped_single_tensor(ltc, dtype, chunk):
     rng = np.random.default_rng(100 + dtype)
     nbytes = 4200 * chunk + 3 * 8  # 4201 chunks, a ragged last one: two uneven groups (2100 + 2101)
@@ -339,25 +341,29 @@ def test_grouped_single_tensor(ltc, dtype, chunk):
         for c in range(0, nbytes // chunk, 5):
             data[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
     data = data[: nbytes // oracle.ELEM_BYTES[dtype] * oracle.ELEM_BYTES[dtype]]
-    check_case(ltc, data, dtype, chunk, label=f"grouped dtype {dtype}")
+    want = check_case(ltc, data, dtype, chunk, label=f"grouped dtype {dtype}")
+    assert rans_streams(want) > 2000, rans_streams(want)
 
 
 def test_grouped_batch_with_empty_and_tiny(ltc):
     """A batch whose tensors straddle the group boundaries, with an empty and
     a one-element tensor; every blob must equal the single-tensor oracle blob."""
     rng = np.random.default_rng(77)
-    chunk = 512
-    sizes = (90000, 0, 1, 123457, 2, 40000, 250001, 17, 60000)
+    chunk = 4096
+    sizes = (720000, 0, 1, 987657, 2, 320000, 2000001, 17, 480000)
     arrs = [(rng.standard_normal(n) * rng.choice([0.02, 1.0, 1e-4])).astype(np.float32) for n in sizes]
     total_chunks = sum((a.nbytes + chunk - 1) // chunk for a in arrs)
     assert total_chunks >= 4096
     ts = [to_gpu(a, 3) for a in arrs]
     banner(f"grouped batch: {len(arrs)} tensors, {total_chunks} chunks")
     blobs = ltc.compress_batch(ts, chunk)
+    coded = 0
     for a, b in zip(arrs, blobs):
         want = oracle.compress(a, 3, chunk)
         got = to_np_bytes(b)
         assert got.size == want.size and np.array_equal(got, want)
+        coded += rans_streams(want)
+    assert coded > 2000, coded
     outs = ltc.decompress_batch(blobs)
     for a, o in zip(arrs, outs):
         assert np.array_equal(to_np_bytes(o), a.view(np.uint8))
@@ -372,9 +378,9 @@ def test_caller_stream_only_equals_grouped(ltc):
     otherwise runs in two groups on two streams) runs every kernel on the
     caller's stream and gives the same blobs, plain and with checksums."""
     rng = np.random.default_rng(88)
-    chunk = 512
+    chunk = 4096
     arrs = [(rng.standard_normal(n) * s).astype(np.float32) for n, s in
-            ((300000, 0.02), (5, 1.0), (250003, 1e-3))]
+            ((2400000, 0.02), (5, 1.0), (2000003, 1e-3))]
     ts = [to_gpu(a, 3) for a in arrs]
     nbytes = [a.nbytes for a in arrs]
     assert sum((n + chunk - 1) // chunk for n in nbytes) >= 4096
@@ -395,12 +401,15 @@ def test_caller_stream_only_equals_grouped(ltc):
             sz = sizes.cpu().tolist()
             got[(flags, crc)] = ([to_np_bytes(b[:s]) for b, s in zip(blobs, sz)],
                                  [c[:(s + 16383) // 16384].cpu().numpy() for c, s in zip(crcs, sz)] if crc else None)
+    coded = 0
     for a, i in zip(arrs, range(len(arrs))):
         want = oracle.compress(a, 3, chunk)
+        coded += rans_streams(want)
         for key, (blobs, crcs) in got.items():
             assert np.array_equal(blobs[i], want), (key, i)
             if crcs is not None:
                 assert np.array_equal(crcs[i].view(np.uint32), oracle.crc32_chunks(want, 16384)), (key, i)
+    assert coded > 2000, coded
 
 
 @pytest.mark.parametrize("dtype", [0, 1])

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import banner, to_gpu, to_np_bytes
+from gpu_util import banner, rans_streams, to_gpu, to_np_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -85,9 +85,10 @@ def test_thresholds(ltc, thr):
     check_v2(ltc, x, 3, 65536, thr, label="threshold")
 
 
-@pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 512), (0, 512)])
+@pytest.mark.parametrize("dtype,chunk", [(1, 8192), (3, 4096), (0, 2048)])
 def test_grouped_with_random_chunks(ltc, dtype, chunk):
-    """Over 4096 chunks: the tables come first, then two chunk groups."""
+    """Over 4096 chunks: the tables come first, then two chunk groups.
+    Chunks of a few thousand elements, so that streams are coded."""
     rng = np.random.default_rng(400 + dtype)
     nbytes = 4200 * chunk + 24
     if dtype == 0:
@@ -99,7 +100,8 @@ def test_grouped_with_random_chunks(ltc, dtype, chunk):
     for c in range(0, nbytes // chunk, 5):
         data[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
     e = oracle.ELEM_BYTES[dtype]
-    check_v2(ltc, data[: nbytes // e * e], dtype, chunk, label=f"grouped {dtype}")
+    want = check_v2(ltc, data[: nbytes // e * e], dtype, chunk, label=f"grouped {dtype}")
+    assert rans_streams(want) > 2000, rans_streams(want)
 
 
 def test_batch_with_empty_and_tiny(ltc):

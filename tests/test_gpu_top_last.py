@@ -22,7 +22,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import banner, to_gpu, to_np_bytes
+from gpu_util import banner, rans_streams, to_gpu, to_np_bytes
 from test_gpu_parity import _abandon_mix, _pattern
 
 pytestmark = pytest.mark.gpu
@@ -103,12 +103,14 @@ def test_abandoned_top_streams(ltc, dtype, thr):
     check(ltc, x, dtype, 131072, thr, label="abandoned exponent streams")
 
 
-@pytest.mark.parametrize("dtype,chunk", [(1, 1024), (3, 512), (2, 512), (0, 256)])
+@pytest.mark.parametrize("dtype,chunk", [(1, 8192), (3, 4096), (2, 4096), (0, 2048)])
 def test_grouped_single_tensor(ltc, dtype, chunk):
     """4201 chunks (the library's threshold is 4096): the encoder places the
     top streams' payloads, each after the sizes of the top streams before it
     in the tensor; every fifth chunk is random (a RAW top stream settled
-    before coding, inside the sums)."""
+    before coding, inside the sums).  Chunks of a few thousand elements, so
+    that the top streams are coded (a RANS payload carries 272 bytes of
+    states and its table, more than a stream of 512 bytes may take)."""
     rng = np.random.default_rng(200 + dtype)
     nbytes = 4200 * chunk + 24
     e = oracle.ELEM_BYTES[dtype]
@@ -120,38 +122,45 @@ def test_grouped_single_tensor(ltc, dtype, chunk):
         data = data.copy()
         for c in range(0, nbytes // chunk, 5):  # random chunks: RAW top streams too
             data[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
-    check(ltc, data[: nbytes // e * e], dtype, chunk, label=f"grouped dtype {dtype}")
+    want = check(ltc, data[: nbytes // e * e], dtype, chunk, label=f"grouped dtype {dtype}")
+    assert rans_streams(want) > 2000, rans_streams(want)
 
 
 @pytest.mark.parametrize("shared", [False, True], ids=["v1", "v2"])
 def test_grouped_batch_with_empty_and_tiny(ltc, shared):
     rng = np.random.default_rng(78)
-    chunk = 512
-    sizes = (90000, 0, 1, 123457, 2, 40000, 250001, 17, 60000)
+    chunk = 4096
+    sizes = (720000, 0, 1, 987657, 2, 320000, 2000001, 17, 480000)
     arrs = [(rng.standard_normal(n) * rng.choice([0.02, 1.0, 1e-4])).astype(np.float32) for n in sizes]
     assert sum((a.nbytes + chunk - 1) // chunk for a in arrs) >= 4096
     banner(f"top-last grouped batch v2={shared}")
     blobs = ltc.compress_batch([to_gpu(a, 3) for a in arrs], chunk, shared_tables=shared, top_last=True)
+    coded = 0
     for i, (a, b) in enumerate(zip(arrs, blobs)):
-        _equal(to_np_bytes(b), oracle.compress(a, 3, chunk, shared_tables=shared, top_last=True), f"tensor {i}")
+        want = oracle.compress(a, 3, chunk, shared_tables=shared, top_last=True)
+        _equal(to_np_bytes(b), want, f"tensor {i}")
+        coded += rans_streams(want)
+    assert coded > 2000, coded
     for a, o in zip(arrs, ltc.decompress_batch(blobs)):
         assert np.array_equal(to_np_bytes(o), a.view(np.uint8))
 
 
 def test_stream_modes_checksums_and_events(ltc):
-    """Grouped, caller-stream-only and per-kernel (events) calls, each plain,
-    with fused checksums (K = 16 KiB: k_pack reads the placed RAW streams
-    back) and with read-back checksums (K = 1000)."""
+    """Calls of 4096 chunks or more (the encoder placing the coded payloads),
+    on the caller's stream only or not, and per kernel (events), each plain
+    and with checksums of 16 KiB and 1000-byte chunks (in the top-last layout
+    the CRC kernel reads the finished blobs back)."""
     rng = np.random.default_rng(89)
-    chunk = 512
+    chunk = 4096
     arrs = [(rng.standard_normal(n) * s).astype(np.float32) for n, s in
-            ((300000, 0.02), (5, 1.0), (250003, 1e-3))]
+            ((2400000, 0.02), (5, 1.0), (2000003, 1e-3))]
     ts = [to_gpu(a, 3) for a in arrs]
     nbytes = [a.nbytes for a in arrs]
     caps = [ltc.compress_bound(n, 3, chunk) for n in nbytes]
     ws_n = ltc.workspace_size(nbytes, 3, chunk)
     ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
     wants = [oracle.compress(a, 3, chunk, top_last=True) for a in arrs]
+    assert sum(rans_streams(w) for w in wants) > 2000
     for flags in (ltc.FLAG_TOP_LAST, ltc.FLAG_TOP_LAST | ltc.FLAG_CALLER_STREAM_ONLY):
         for crc in (0, 16384, 1000):
             for prof in (False, True):
