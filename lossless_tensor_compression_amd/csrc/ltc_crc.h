@@ -95,16 +95,24 @@ __device__ __forceinline__ uint32_t crc_mul_level(const CrcLdsT<L>& s, int l, ui
 // A lookup indexed by data is a random LDS access: 64 lanes reading one
 // 1 KiB table collide on most banks (the k_crc32 of a 1.2 GB blob with
 // slicing-by-16 tables of this kind spent about half its time stalled on bank
-// conflicts).  Here every slicing-by-4 table (bank[m][b]: the register after
-// byte b and m zero bytes) is stored as 32 copies interleaved by bank: entry
-// b of copy j is dword 32 * b + j, and lane l reads copy l % 32, so the 32
-// lanes an LDS cycle serves hit 32 different banks.  The four tables fill
-// 128 KiB, so a workgroup that holds them has a CU to itself.
+// conflicts).  Here every slicing-by-4 table (table m, entry b: the register
+// after byte b and m zero bytes) is stored as 32 copies interleaved by bank,
+// and lane l reads copy l % 32, so the 32 lanes an LDS cycle serves hit 32
+// different banks.  Copy j of entry b of table m sits at byte address
+//   (m >> 1) << 16 | b << 8 | (m & 1) << 7 | j << 2,
+// so a lookup's address is one byte permute: the data byte goes to address
+// byte 1, the lane's (m >> 1) << 16 | j << 2 supplies bytes 0 and 2, and
+// (m & 1) << 7 is the load's immediate offset.  The four tables fill 128 KiB,
+// so a workgroup that holds them has a CU to itself.
 struct CrcBankLds {
-  uint32_t bank[4][256][32];
+  uint32_t bank[4 * 256 * 32];
   uint32_t tl[kCrcLevels][4][256];
   uint32_t basis[kCrcLevels][32];
 };
+
+__host__ __device__ constexpr uint32_t crc_bank_index(uint32_t m, uint32_t b, uint32_t j) {
+  return (m >> 1) << 14 | b << 6 | (m & 1) << 5 | j;
+}
 
 // Fills the tables (tl and basis as crc_build_tables); every thread of the
 // workgroup calls it; it ends with a workgroup barrier.
@@ -114,7 +122,7 @@ __device__ __forceinline__ void crc_build_bank(CrcBankLds& s, const uint32_t* lv
     uint32_t c = b;
     for (int m = 0; m < 4; ++m) {
       for (int k = 0; k < 8; ++k) c = (c >> 1) ^ (kPoly & (0u - (c & 1u)));
-      s.bank[m][b][0] = c;
+      s.bank[crc_bank_index(m, b, 0)] = c;
     }
   }
   for (uint32_t i = tid; i < kCrcLevels * 32; i += nthreads)
@@ -122,7 +130,7 @@ __device__ __forceinline__ void crc_build_bank(CrcBankLds& s, const uint32_t* lv
   __syncthreads();
   for (uint32_t idx = tid; idx < 4 * 256 * 32; idx += nthreads) {  // copies 1..31
     const uint32_t j = idx & 31;
-    if (j) (&s.bank[0][0][0])[idx] = (&s.bank[0][0][0])[idx - j];
+    if (j) s.bank[idx] = s.bank[idx - j];
   }
   for (uint32_t idx = tid; idx < kCrcLevels * 4 * 256; idx += nthreads) {
     const uint32_t l = idx / 1024, p = (idx / 256) & 3, b = idx & 255;
@@ -135,12 +143,21 @@ __device__ __forceinline__ void crc_build_bank(CrcBankLds& s, const uint32_t* lv
   __syncthreads();
 }
 
+// entry of table m (immediate (m & 1) << 7) at address a (one byte permute)
+__device__ __forceinline__ uint32_t crc_bank_at(const CrcBankLds& s, uint32_t a, uint32_t half) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(s.bank) + a + (half << 7));
+}
+
 // register c advanced over the 4 bytes of little-endian word w; bl: the
-// lane's table copy (lane % 32)
+// lane's table copy (lane % 32).  v_perm_b32 selector bytes 0-3 pick bytes
+// of the second operand, 4-7 of the first.
 __device__ __forceinline__ uint32_t crc_word_bank(const CrcBankLds& s, uint32_t c, uint32_t w, uint32_t bl) {
+  const uint32_t lb0 = bl << 2, lb1 = lb0 | 0x10000u;  // tables 0-1, tables 2-3
   c ^= w;
-  return s.bank[3][c & 0xFFu][bl] ^ s.bank[2][(c >> 8) & 0xFFu][bl] ^ s.bank[1][(c >> 16) & 0xFFu][bl] ^
-         s.bank[0][c >> 24][bl];
+  return crc_bank_at(s, __builtin_amdgcn_perm(c, lb1, 0x03020400u), 1) ^  // byte 0: table 3
+         crc_bank_at(s, __builtin_amdgcn_perm(c, lb1, 0x03020500u), 0) ^  // byte 1: table 2
+         crc_bank_at(s, __builtin_amdgcn_perm(c, lb0, 0x03020600u), 1) ^  // byte 2: table 1
+         crc_bank_at(s, __builtin_amdgcn_perm(c, lb0, 0x03020700u), 0);   // byte 3: table 0
 }
 
 __device__ __forceinline__ uint32_t crc_step16_bank(const CrcBankLds& s, uint32_t c, const uint4 q,
@@ -153,7 +170,7 @@ __device__ __forceinline__ uint32_t crc_step16_bank(const CrcBankLds& s, uint32_
 
 __device__ __forceinline__ uint32_t crc_step1_bank(const CrcBankLds& s, uint32_t c, uint32_t byte,
                                                    uint32_t bl) {
-  return s.bank[0][(c ^ byte) & 0xFFu][bl] ^ (c >> 8);
+  return crc_bank_at(s, __builtin_amdgcn_perm(c ^ byte, bl << 2, 0x03020400u), 0) ^ (c >> 8);
 }
 
 // Lane i holds the remainder of segment i of 64 equal consecutive segments
