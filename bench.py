@@ -319,7 +319,8 @@ def cpu_baseline(args, ts, torch):
     compress + decompress + CRC-32 of the blob, on a bounded sample of the
     workload, best of 3 runs, once on one thread and once on the host's CPU
     share.  The share is the CPUs this process may run on, capped by
-    OMP_NUM_THREADS when set (a GPU machine gives one GPU's process 16)."""
+    OMP_NUM_THREADS when set (a machine that shares its cores among its GPUs
+    sets it to one GPU's share)."""
     import numpy as np
 
     import oracle
