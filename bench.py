@@ -62,7 +62,8 @@ def parse():
     ap.add_argument("--isolated", action="store_true",
                     help="run every step kernel by kernel on one stream (for per-kernel profiles)")
     ap.add_argument("--crc", default="fused", choices=["fused", "beside"],
-                    help="CRC-32 of the blobs computed while packing, or by its own kernel")
+                    help="CRC-32 of the blobs in the compress call (compress_with_crc32), or by its "
+                         "own kernel after a plain compress")
     ap.add_argument("--layout", default="top-last", choices=["top-last", "directory"],
                     help="payload order: top streams after all others (LTC_FLAG_TOP_LAST, the "
                          "compressor then writes RAW streams straight into the blob) or directory "
@@ -726,7 +727,8 @@ def main():
     #   blob's payloads, the RAW lower streams and the coded top streams:
     #   N + B, the compress path's bytes; otherwise it writes only the
     #   workspace, and integer issue bounds it (below)
-    placed = bool(layout_flag) and sum((n + CHUNK - 1) // CHUNK for n in nbytes) >= 4096
+    total_chunks = sum((n + CHUNK - 1) // CHUNK for n in nbytes)
+    placed = bool(layout_flag) and total_chunks >= 4096
     algo = {"k_decode": B + N, "k_hist": N, "k_pack": B + N, "k_crc32": B,
             "k_encode": N + B if placed else N, "k_scan": 0, "k_decode_multi": 0}
     dom = max((n for n in k if algo[n]), key=lambda n: k[n])
@@ -774,12 +776,15 @@ def main():
         "config": {**desc, "global_batch": count, "orig_bytes": N, "blob_bytes": B,
                    "chunk_bytes": CHUNK, "passthrough_threshold": THRESHOLD,
                    "crc_chunk_bytes": CRC_CHUNK, "parallelism": "single GPU",
-                   "crc": "computed while packing (compress_with_crc32)" if fused
-                          else "own kernel beside decompress",
+                   "crc": ("in the compress call (compress_with_crc32): " +
+                           ("k_crc32 reads the finished blobs" if layout_flag else "accumulated while packing"))
+                          if fused else "own kernel beside decompress",
                    "format": "v2, one table per stream index" if shared else "v1, a table per coded stream",
                    "layout": "top streams last (LTC_FLAG_TOP_LAST)" if layout_flag else "directory order",
                    "launch": "kernel by kernel, one stream" if args.isolated
-                             else "compress in 2 chunk groups on 2 streams"},
+                             else "one stream, the encoder placing the top streams' payloads" if placed
+                             else "compress in 2 chunk groups on 2 streams" if total_chunks >= 4096
+                             else "one stream"},
         "decompress_gbs": round(N / (t_dec * 1e-3) / 1e9, 2),
         "compress_gbs": round(N / (t_comp * 1e-3) / 1e9, 2),
         "crc32_blob_gbs": round(B / (t_crc * 1e-3) / 1e9, 2),
