@@ -423,8 +423,10 @@ int ltc_blob_stats(const void* h_prefix, uint64_t h_nbytes, ltc_stats* out);
  * kernel (never pipelined), plus hipEventRecord on `stream` around each kernel
  * so a caller can time one kernel alone.
  * Compress: 5 events (before k_hist, before k_encode, before k_scan, before
- * k_pack, after k_pack); compress with CRC-32: 6, the sixth after the CRC
- * kernel that finishes the checksums.  Decompress: 3 events (before the
+ * k_pack, after k_pack; in the top-last layout, format v1, the lower streams'
+ * k_encode and scan come before the second event, so that the second
+ * interval holds the top streams' k_encode alone); compress with CRC-32: 6,
+ * the sixth after the CRC kernel that finishes the checksums.  Decompress: 3 events (before the
  * single-table decode kernel, between it and the multi-table one, after). */
 int ltc_compress_batch_prof(int count, const void* const* h_src_ptrs, const uint64_t* h_nbytes,
                             int dtype, uint32_t chunk_bytes, double passthrough_threshold,

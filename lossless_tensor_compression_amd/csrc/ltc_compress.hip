@@ -1908,7 +1908,9 @@ static hipError_t launch_compress_d(const CTable& t, const CWork& w, hipStream_t
 
 // Top-last layout, first half for chunks [c_begin, c_end): k_hist, the lower
 // streams' coding, their scan, then the top streams' coding, which writes
-// the staged RAW streams at the offsets that scan gave.
+// the staged RAW streams at the offsets that scan gave.  The profiling
+// events put the lower streams' pass with k_hist, so that the second
+// interval holds the top streams' coding alone.
 template <int DT, bool DELTA>
 static hipError_t launch_front_d(const CTable& t, const CWork& w, hipStream_t st, const hipEvent_t* ev,
                                  hipEvent_t scan_after, hipEvent_t scan_done, bool staged) {
@@ -1917,12 +1919,12 @@ static hipError_t launch_front_d(const CTable& t, const CWork& w, hipStream_t st
   if (!staged) {
     record(ev, 0, st);
     if (chunks) hipLaunchKernelGGL((k_hist<DT, DELTA>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
-    record(ev, 1, st);
   }
   if (E > 1) launch_encode<DT, DELTA>(t, w, st, E - 2, E - 1);
   if (scan_after) (void)hipStreamWaitEvent(st, scan_after, 0);
   hipLaunchKernelGGL(k_scan, dim3(t.count), dim3(kScanThreads), 0, st, t, w, (uint32_t)E, 1u);
   if (scan_done) (void)hipEventRecord(scan_done, st);
+  if (!staged) record(ev, 1, st);
   launch_encode<DT, DELTA>(t, w, st, E - 1, 1);
   record(ev, 2, st);
   return hipGetLastError();
