@@ -13,8 +13,8 @@
  * CRC-32 per 16 KiB matching zlib.crc32, the last chunk shorter); the blob is
  * versioned and other versions are rejected (same page, "Blob format").  The
  * device-pointer, caller-stream, no-allocation convention follows lmz's
- * device entry point (lmz README, section "Building on lmz": "The caller owns
- * the device").
+ * device entry point (lmz README, section "Building on lmz": the device
+ * stays the caller's).
  *
  * OWNERSHIP AND ASYNCHRONY.  Arguments named d_* are device pointers, h_*
  * host pointers.  The caller allocates every buffer and owns the stream.
