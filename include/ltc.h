@@ -377,9 +377,9 @@ int ltc_decompress_delta(const void* h_header, const void* d_blob, uint64_t blob
 
 /* Compress and checksum the blob in one call (cuZipNN 0.1.0 "API",
  * compress_tensor_with_crc32): the same blob as ltc_compress, and in d_crc
- * the CRC-32 of every checksum_chunk_bytes-byte chunk of the blob, the last
- * one possibly shorter, exactly as ltc_crc32_chunks would give for the
- * finished blob.  The blob size is known only on the device, so d_crc must
+ * one CRC-32 per consecutive checksum_chunk_bytes bytes of the blob (a
+ * shorter final piece included), exactly as ltc_crc32_chunks would give for
+ * the finished blob.  The blob size is known only on the device, so d_crc must
  * hold crc_capacity >= ceil(ltc_compress_bound() / checksum_chunk_bytes)
  * u32 values; the first ceil(*d_blob_nbytes / checksum_chunk_bytes) are
  * written and the rest are left as they were.  When checksum_chunk_bytes is a

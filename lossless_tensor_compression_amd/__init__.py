@@ -324,8 +324,8 @@ def compress_batch_with_crc32(tensors, chunk_bytes=DEFAULT_CHUNK_BYTES,
                               passthrough_threshold=DEFAULT_THRESHOLD,
                               checksum_chunk_bytes=DEFAULT_CRC_CHUNK_BYTES, shared_tables=False,
                               top_last=False):
-    """(blobs, checksums): the blobs of compress_batch and, per blob, the
-    CRC-32 of each checksum_chunk_bytes-byte chunk (int32 GPU tensors holding
+    """(blobs, checksums): the blobs of compress_batch and, per blob, one
+    CRC-32 per checksum_chunk_bytes bytes of it (int32 GPU tensors holding
     the CRC bits)."""
     if not 1 <= len(tensors) <= BATCH_MAX:
         raise ValueError(f"1..{BATCH_MAX} tensors per batch")

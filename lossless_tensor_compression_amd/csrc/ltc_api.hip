@@ -220,7 +220,7 @@ uint32_t xpow8(uint64_t n) {
 
 
 // Largest integer P with (double)P < theta * (double)n: cuZipNN 0.1.0, "API":
-// a chunk stays compressed only if it shrinks below the threshold fraction.
+// coding is kept only when the coded size is under that fraction of the raw one.
 uint32_t p_max(uint64_t n, double theta) {
   const double lim = theta * (double)n;
   if (!(lim > 0.0)) return 0;

@@ -1,7 +1,7 @@
 // ltc_crc32.hip -- per-chunk CRC-32 (zlib's) on gfx950.
 //
-// cuZipNN 0.1.0 ("API", hash_tensor_with_crc32) defines the checksum as the
-// zlib CRC-32 of every checksum_chunk_bytes-byte chunk, the last one
+// cuZipNN 0.1.0 ("API", hash_tensor_with_crc32) defines the checksum as one
+// zlib CRC-32 per checksum_chunk_bytes bytes of the buffer, the final piece
 // possibly shorter.  One wave per chunk: the chunk is split into 64 lane
 // segments, each lane runs a table-driven CRC over its segment with the
 // register starting at zero (slicing-by-4 from bank-interleaved tables in

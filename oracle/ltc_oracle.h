@@ -13,10 +13,10 @@
  *    order-0 entropy coding per stream, all-zero (here: single-valued)
  *    streams reduced to a header, independent fixed-size chunks with a map.
  *  - cuZipNN 0.1.0 (PyPI page), section "API": chunk_bytes (multiple of 8,
- *    at most 16 MiB), passthrough_threshold in (0, 1] ("stays compressed
- *    only if it shrinks below this fraction"), per-chunk CRC-32 that matches
- *    zlib.crc32 with a shorter last chunk; section "Blob format": a versioned
- *    blob, other versions rejected.
+ *    at most 16 MiB), passthrough_threshold in (0, 1] (coding is kept only
+ *    when it makes a stream smaller than that fraction of its size),
+ *    per-chunk CRC-32 that matches zlib.crc32 with a shorter last chunk;
+ *    section "Blob format": a versioned blob, other versions rejected.
  *  - lmz (lmzip 1.3.0 README), sections "On a GPU" and "Building on lmz":
  *    rANS with several interleaved states as lanes of work, and a frequency
  *    table carried per rANS stream.
