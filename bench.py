@@ -176,10 +176,14 @@ def traffic_from_profiles(kernel, workload):
     rec = json.load(open(path))
     if rec.get("bench_workload") != workload:
         return None
-    src = os.path.join(ROOT, rec.get("source", ""))
-    if not os.path.exists(src):
+    # the kernel's source file and the headers it includes, hashed together
+    srcs = [os.path.join(ROOT, f) for f in rec.get("sources", [])]
+    if not srcs or not all(os.path.exists(f) for f in srcs):
         return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != rec.get("sources_sha256"):
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -767,11 +767,12 @@ __device__ __forceinline__ uint4 shift_blocks(const uint4 a, const uint4 b, uint
 // Per stream, in LDS:
 //   tab   one 16-byte entry per symbol: {r (double), 4096 - f, cum}.  A
 //         second instantiation holds 128 entries from the stream's lowest
-//         symbol and takes the pairs whose coded streams span at most 128
-//         symbols (exponent streams of trained weights span about 40): its
-//         8,448 bytes of LDS let 16 waves share a CU (then the 99 VGPRs
-//         bound it) instead of 12, and the encoder runs about 7% faster.
-//         Both are launched; each leaves the other's pairs alone.
+//         symbol and takes the waves whose coded streams all span at most
+//         128 symbols (exponent streams of trained weights span about 40):
+//         with two streams a wave, its 8,448 bytes of LDS let 16 waves share
+//         a CU (then the 99 VGPRs bound it) instead of 12, and the encoder
+//         ran about 7% faster.  Both are launched; each leaves the other's
+//         waves alone.
 //   stg   one block of 512 elements, loaded with wide coalesced loads one
 //         block ahead, stored as their symbols' table offsets and read back
 //         transposed to lane order;
@@ -812,8 +813,8 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
   // BF16 tensor to half of the XCDs (of an FP32 tensor, to a quarter) while
   // the rest only receive streams that exit at once.
   // Deltas usually code every stream of a chunk, and each wave reads whole
-  // elements of source and base: there the E workgroups of a chunk pair sit
-  // 8 apart (blocks of 8 pairs), so they reach the same XCD together and walk
+  // elements of source and base: there the E workgroups of a wave's chunks
+  // sit 8 apart (blocks of 8), so they reach the same XCD together and walk
   // the same elements in the same order, and the later reads hit its L2.
   // The launch rounds the grid up to whole blocks; the spare workgroups find
   // no chunk and exit.
@@ -824,9 +825,9 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
     k = kfirst - r / 8u;
     g0 = t.c_begin + (uint64_t)(grp * 8u + r % 8u) * U;
   } else {
-    const uint32_t pairs = gridDim.x / nplanes;
-    k = kfirst - blockIdx.x / pairs;
-    g0 = t.c_begin + (uint64_t)(blockIdx.x % pairs) * U;
+    const uint32_t per_plane = gridDim.x / nplanes;  // workgroups per stream index
+    k = kfirst - blockIdx.x / per_plane;
+    g0 = t.c_begin + (uint64_t)(blockIdx.x % per_plane) * U;
   }
   const uint32_t wcap = t.wcap;
 
@@ -908,7 +909,7 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
     for (int u = 0; u < U; ++u) any = any || on[u];
     if (!any) return;
   }
-  // the short-table instantiation takes the pairs whose coded streams use at
+  // the short-table instantiation takes the waves whose coded streams use at
   // most TABN consecutive symbols (v1 tables); the full one the others
   {
     bool small = !t.v2;
