@@ -233,7 +233,7 @@ __device__ uint32_t normalize_stream(const uint32_t* h, uint32_t n, uint32_t pma
   if (plane) {  // v2: decided once the plane's table exists (k_decide)
     *reinterpret_cast<uint4*>(w.hist + 256 * s + 4 * lane) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     if (lane == 0)
-      *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(kModeCand, 0, 0, 0), 0, 0);
+      *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(kModeCand, 0, lo, hi), 0, 0);
     return kModeCand;
   }
   normalize_wave(hv, n, f);
@@ -479,7 +479,8 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(CTable t, CWork w) {
   }
   // A coded top byte stages the chunk's RAW streams (see k_encode): its
   // record's third word carries their mask.  The wave that wrote the record
-  // adds it, so the two stores keep their order.
+  // adds it, so the two stores keep their order.  v2 decides its streams in
+  // k_decide, which sets the mask there.
   if constexpr (E > 1) {
     __syncthreads();
     if (!t.v2 && wave == (uint32_t)(E - 1) && lane == 0 && modes[E - 1] == kModeCand) {
@@ -593,31 +594,53 @@ __global__ __launch_bounds__(256) void k_share(CTable t, CWork w) {
 template <int DT>
 __global__ __launch_bounds__(256) void k_decide(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
-  const uint64_t s = (t.c_begin * E) + (uint64_t)blockIdx.x * 4 + threadIdx.x / 64;
-  if (s >= t.c_end * E) return;
-  const uint32_t info = w.sinfo[4 * s + 1];
-  if ((info & 0xFFu) != kModeCand) return;
-  const uint64_t g = s / E;
-  const uint32_t k = (uint32_t)(s % E);
-  const int j = find_job(t, g);
-  const CJob& job = t.jobs[j];
-  const bool last = g - job.chunk0 + 1 == job.nchunks;
-  const uint32_t n = last ? job.n_tail : t.n_full;
-  const uint32_t lane = lane_id();
-  const uint4 hq = *reinterpret_cast<const uint4*>(w.hist + 256 * s + 4 * lane);
-  const uint64_t fq = *reinterpret_cast<const uint64_t*>(w.ptab + ((uint64_t)j * E + k) * 256 + 4 * lane);
-  const uint32_t hv[4] = {hq.x, hq.y, hq.z, hq.w};
-  const uint32_t f[4] = {(uint32_t)fq & 0xFFFFu, (uint32_t)(fq >> 16) & 0xFFFFu,
-                         (uint32_t)(fq >> 32) & 0xFFFFu, (uint32_t)(fq >> 48)};
-  const uint32_t pmax = last ? job.pmax_tail : job.pmax_full;
-  if (raw_by_bound(hv, f, n, kRansFixed, pmax) && lane == 0) {
-    uint4 v = make_uint4(n, pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
-    if (t.delta) {  // a delta stream ZipNN's rule fired for: ZRUN if it fits
-      const uint2 zi = w.zinfo[s];
-      const uint32_t pz = zrun_bytes(n, zi.x, zi.y & 0x7FFFFFFFu);
-      if ((zi.y >> 31) && pz <= pmax) v = make_uint4(pz, pack_info(LTC_MODE_ZRUN, 0, 0, 0), zi.x, zi.y & 0x7FFFFFFFu);
+  // Each wave decides one stream; the four streams of a workgroup are whole
+  // chunks (the launch covers all chunks from chunk 0, four streams per
+  // workgroup, E in {1, 2, 4}), so the wave of a chunk's top stream can name
+  // the chunk's RAW streams for k_encode to write (as k_hist does in v1).
+  __shared__ uint32_t fmode[4];  // each wave's stream: its mode once decided
+  const uint32_t wave = threadIdx.x / 64, lane = lane_id();
+  const uint64_t s = (t.c_begin * E) + (uint64_t)blockIdx.x * 4 + wave;
+  const bool in = s < t.c_end * E;
+  uint32_t mode = 0xFFu;
+  if (in) {
+    const uint32_t info = w.sinfo[4 * s + 1];
+    mode = info & 0xFFu;
+  }
+  if (in && mode == kModeCand) {
+    const uint64_t g = s / E;
+    const uint32_t k = (uint32_t)(s % E);
+    const int j = find_job(t, g);
+    const CJob& job = t.jobs[j];
+    const bool last = g - job.chunk0 + 1 == job.nchunks;
+    const uint32_t n = last ? job.n_tail : t.n_full;
+    const uint4 hq = *reinterpret_cast<const uint4*>(w.hist + 256 * s + 4 * lane);
+    const uint64_t fq = *reinterpret_cast<const uint64_t*>(w.ptab + ((uint64_t)j * E + k) * 256 + 4 * lane);
+    const uint32_t hv[4] = {hq.x, hq.y, hq.z, hq.w};
+    const uint32_t f[4] = {(uint32_t)fq & 0xFFFFu, (uint32_t)(fq >> 16) & 0xFFFFu,
+                           (uint32_t)(fq >> 32) & 0xFFFFu, (uint32_t)(fq >> 48)};
+    const uint32_t pmax = last ? job.pmax_tail : job.pmax_full;
+    if (raw_by_bound(hv, f, n, kRansFixed, pmax)) {
+      uint4 v = make_uint4(n, pack_info(LTC_MODE_RAW, 0, 0, 0), 0, 0);
+      if (t.delta) {  // a delta stream ZipNN's rule fired for: ZRUN if it fits
+        const uint2 zi = w.zinfo[s];
+        const uint32_t pz = zrun_bytes(n, zi.x, zi.y & 0x7FFFFFFFu);
+        if ((zi.y >> 31) && pz <= pmax) v = make_uint4(pz, pack_info(LTC_MODE_ZRUN, 0, 0, 0), zi.x, zi.y & 0x7FFFFFFFu);
+      }
+      if (lane == 0) *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = v;
+      mode = v.y & 0xFFu;
     }
-    *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = v;
+  }
+  if constexpr (E > 1) {
+    if (lane == 0) fmode[wave] = mode;
+    __syncthreads();
+    if (in && lane == 0 && s % E == (uint64_t)(E - 1) && mode == kModeCand) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int q = 0; q < E - 1; ++q)
+        if (fmode[wave - (E - 1) + q] == LTC_MODE_RAW) m |= 1u << q;
+      if (m) w.sinfo[4 * s + 2] = m;
+    }
   }
 }
 
@@ -910,9 +933,10 @@ __global__ __launch_bounds__(64) void k_encode(CTable t, CWork w, uint32_t kfirs
     if (!any) return;
   }
   // the short-table instantiation takes the waves whose coded streams use at
-  // most TABN consecutive symbols (v1 tables); the full one the others
+  // most TABN consecutive symbols (filled from the stream's lowest symbol, v1
+  // or v2 tables alike); the full one the others
   {
-    bool small = !t.v2;
+    bool small = true;
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (on[u] && hi[u] - lo[u] >= 128u) small = false;

@@ -4,14 +4,14 @@ its top streams' sizes and walks back over the statuses of the chunks before
 them to find their offsets ("NOTE-241: ZipNN", Method item 5: the directory
 maps every payload, so a payload's place follows from the sizes before it).
 
-The cases make the walk meet everything it handles: chunk pairs coded by the
+The cases make the walk meet everything it handles: chunks coded by the
 128-entry and the 256-entry table launches in one tensor (the first launch
 gives up behind a chunk left to the second, and k_pack writes those
 payloads), top streams abandoned part way (their RAW fallback size enters
 the sums), settled top streams (CONST, RAW by the size bound) published
-before coding, tensors of one chunk and pairs that straddle two tensors,
-format v2 (all pairs in the 256-entry launch), every dtype, and the
-checksummed call.  Blobs must equal the oracle's byte for byte.  Chunks hold
+before coding, tensors of one chunk and waves whose two chunks straddle two
+tensors, format v2, every dtype, and the checksummed call.  Blobs must
+equal the oracle's byte for byte.  Chunks hold
 thousands of elements so that top streams are coded (a RANS payload carries
 272 bytes of states and its table: a stream of 512 bytes never fits), and
 each test checks in the oracle's directory that coded top streams are there.
@@ -138,7 +138,9 @@ def test_tensor_boundaries_and_tiny_tensors(ltc):
 
 
 @pytest.mark.parametrize("dtype", [1, 2])
-def test_v2_all_pairs_in_the_second_launch(ltc, dtype):
+def test_v2(ltc, dtype):
+    """Format v2: the plane tables, the RAW streams named by k_decide and
+    written by the encoder, the 128-entry launch for narrow streams."""
     rng = np.random.default_rng(560 + dtype)
     chunk = 8192
     n = 4100 * chunk // 2
