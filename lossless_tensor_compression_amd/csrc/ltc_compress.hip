@@ -202,7 +202,7 @@ __device__ __forceinline__ bool raw_by_bound(const uint32_t hv[4], const uint32_
 
 // Normalise one stream's histogram (one wave; lane l owns symbols 4l..4l+3),
 // pick CONST / RAW / encode, write the frequency table and the stream info.
-// v2: keep the histogram for k_decide and add it to the plane's instead.
+// v2 (plane non-null): keep the histogram for k_planesum and k_decide.
 __device__ uint32_t normalize_stream(const uint32_t* h, uint32_t n, uint32_t pmax, uint64_t s,
                                      const CWork& w, uint64_t* plane) {
   const uint32_t lane = lane_id();
@@ -220,11 +220,6 @@ __device__ uint32_t normalize_stream(const uint32_t* h, uint32_t n, uint32_t pma
   nz = wave_sum_u32(nz);
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
-  if (plane) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (hv[i]) atomicAdd(reinterpret_cast<unsigned long long*>(plane + 4 * lane + i), (unsigned long long)hv[i]);
-  }
   if (nz == 1) {  // a single value: the stream is a header ("NOTE-241", Method item 3)
     if (lane == 0)
       *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(LTC_MODE_CONST, lo, 0, 0), 0, 0);
@@ -509,6 +504,40 @@ __device__ __forceinline__ uint32_t unit_remainder_bitwise(uint4 v) {
       for (int k = 0; k < 8; ++k) r = (r >> 1) ^ (kPoly & (0u - (r & 1u)));
     }
   return r;
+}
+
+// v2 plane histograms: thread b sums bin b of stream index k over a block of
+// kPlaneBlock chunks (the kept histograms of coded streams; a CONST stream
+// counts its n elements at its value) and adds each tensor's share to that
+// tensor's plane with one atomic.  Grid: E x ceil(chunks / kPlaneBlock).
+constexpr uint32_t kPlaneBlock = 64;
+template <int DT>
+__global__ __launch_bounds__(256) void k_planesum(CTable t, CWork w) {
+  constexpr int E = Dt<DT>::E;
+  const uint32_t nblk = (uint32_t)((t.total_chunks + kPlaneBlock - 1) / kPlaneBlock);
+  const uint32_t k = blockIdx.x / nblk, bin = threadIdx.x;
+  const uint64_t g0 = (uint64_t)(blockIdx.x % nblk) * kPlaneBlock;
+  const uint64_t g1 = min(g0 + kPlaneBlock, t.total_chunks);
+  int j = find_job(t, g0);
+  uint64_t acc = 0;
+  for (uint64_t g = g0; g < g1; ++g) {
+    if (g >= t.jobs[j].chunk0 + t.jobs[j].nchunks) {  // the next tensor: flush this one's share
+      if (acc) atomicAdd(reinterpret_cast<unsigned long long*>(w.plane + ((uint64_t)j * E + k) * 256 + bin),
+                         (unsigned long long)acc);
+      acc = 0;
+      j = find_job(t, g);
+    }
+    const uint64_t s = g * E + k;
+    const uint32_t info = w.sinfo[4 * s + 1];
+    if ((info & 0xFFu) == LTC_MODE_CONST) {
+      const bool last = g + 1 == t.jobs[j].chunk0 + t.jobs[j].nchunks;
+      if (((info >> 8) & 0xFFu) == bin) acc += last ? t.jobs[j].n_tail : t.n_full;
+    } else {
+      acc += w.hist[256 * s + bin];
+    }
+  }
+  if (acc) atomicAdd(reinterpret_cast<unsigned long long*>(w.plane + ((uint64_t)j * E + k) * 256 + bin),
+                     (unsigned long long)acc);
 }
 
 // One workgroup per tensor, wave k for stream index k: the plane's table
@@ -2006,6 +2035,9 @@ static hipError_t launch_v2_tables_t(const CTable& t, const CWork& w, hipStream_
     hipLaunchKernelGGL((k_hist<DT, true>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
   else if (chunks)
     hipLaunchKernelGGL((k_hist<DT, false>), dim3((uint32_t)chunks), dim3(kHistThreads), 0, st, t, w);
+  if (chunks)
+    hipLaunchKernelGGL(k_planesum<DT>, dim3((uint32_t)(E * ((chunks + kPlaneBlock - 1) / kPlaneBlock))),
+                       dim3(256), 0, st, t, w);
   hipLaunchKernelGGL(k_share<DT>, dim3(t.count), dim3(256), 0, st, t, w);
   if (chunks) hipLaunchKernelGGL(k_decide<DT>, dim3((uint32_t)((chunks * E + 3) / 4)), dim3(256), 0, st, t, w);
   record(ev, 1, st);
