@@ -220,13 +220,14 @@ __device__ uint32_t normalize_stream(const uint32_t* h, uint32_t n, uint32_t pma
   nz = wave_sum_u32(nz);
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
+  if (plane)  // v2: every stream's histogram, a CONST stream's too, for k_planesum
+    *reinterpret_cast<uint4*>(w.hist + 256 * s + 4 * lane) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
   if (nz == 1) {  // a single value: the stream is a header ("NOTE-241", Method item 3)
     if (lane == 0)
       *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(LTC_MODE_CONST, lo, 0, 0), 0, 0);
     return LTC_MODE_CONST;
   }
   if (plane) {  // v2: decided once the plane's table exists (k_decide)
-    *reinterpret_cast<uint4*>(w.hist + 256 * s + 4 * lane) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     if (lane == 0)
       *reinterpret_cast<uint4*>(w.sinfo + 4 * s) = make_uint4(0, pack_info(kModeCand, 0, lo, hi), 0, 0);
     return kModeCand;
@@ -507,37 +508,27 @@ __device__ __forceinline__ uint32_t unit_remainder_bitwise(uint4 v) {
 }
 
 // v2 plane histograms: thread b sums bin b of stream index k over a block of
-// kPlaneBlock chunks (the kept histograms of coded streams; a CONST stream
-// counts its n elements at its value) and adds each tensor's share to that
-// tensor's plane with one atomic.  Grid: E x ceil(chunks / kPlaneBlock).
-constexpr uint32_t kPlaneBlock = 64;
+// kPlaneBlock chunks (k_hist keeps every stream's histogram in v2) and adds
+// each tensor's share to that tensor's plane with one atomic.  The loads of
+// a block are independent, so they are in flight together.  Grid:
+// E x ceil(chunks / kPlaneBlock).
+constexpr uint32_t kPlaneBlock = 16;
 template <int DT>
 __global__ __launch_bounds__(256) void k_planesum(CTable t, CWork w) {
   constexpr int E = Dt<DT>::E;
   const uint32_t nblk = (uint32_t)((t.total_chunks + kPlaneBlock - 1) / kPlaneBlock);
   const uint32_t k = blockIdx.x / nblk, bin = threadIdx.x;
-  const uint64_t g0 = (uint64_t)(blockIdx.x % nblk) * kPlaneBlock;
-  const uint64_t g1 = min(g0 + kPlaneBlock, t.total_chunks);
-  int j = find_job(t, g0);
-  uint64_t acc = 0;
-  for (uint64_t g = g0; g < g1; ++g) {
-    if (g >= t.jobs[j].chunk0 + t.jobs[j].nchunks) {  // the next tensor: flush this one's share
-      if (acc) atomicAdd(reinterpret_cast<unsigned long long*>(w.plane + ((uint64_t)j * E + k) * 256 + bin),
-                         (unsigned long long)acc);
-      acc = 0;
-      j = find_job(t, g);
-    }
-    const uint64_t s = g * E + k;
-    const uint32_t info = w.sinfo[4 * s + 1];
-    if ((info & 0xFFu) == LTC_MODE_CONST) {
-      const bool last = g + 1 == t.jobs[j].chunk0 + t.jobs[j].nchunks;
-      if (((info >> 8) & 0xFFu) == bin) acc += last ? t.jobs[j].n_tail : t.n_full;
-    } else {
-      acc += w.hist[256 * s + bin];
-    }
+  uint64_t g = (uint64_t)(blockIdx.x % nblk) * kPlaneBlock;
+  const uint64_t g1 = min(g + kPlaneBlock, t.total_chunks);
+  while (g < g1) {
+    const int j = find_job(t, g);
+    const uint64_t gend = min(g1, t.jobs[j].chunk0 + t.jobs[j].nchunks);
+    uint64_t acc = 0;
+#pragma unroll 8
+    for (; g < gend; ++g) acc += w.hist[256 * (g * E + k) + bin];
+    if (acc) atomicAdd(reinterpret_cast<unsigned long long*>(w.plane + ((uint64_t)j * E + k) * 256 + bin),
+                       (unsigned long long)acc);
   }
-  if (acc) atomicAdd(reinterpret_cast<unsigned long long*>(w.plane + ((uint64_t)j * E + k) * 256 + bin),
-                     (unsigned long long)acc);
 }
 
 // One workgroup per tensor, wave k for stream index k: the plane's table
