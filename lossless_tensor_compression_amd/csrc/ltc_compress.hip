@@ -6,8 +6,9 @@
 //             sub-histograms against same-bin contention), then one wave per
 //             stream normalises its histogram to a 4096 total and decides
 //             CONST / RAW (by an exact lower bound on the rANS size) / encode.
-//   k_encode  one wave per two streams still to encode: 64-lane interleaved
-//             rANS from the last step to the first, exact division by one
+//   k_encode  one wave per stream index of a chunk still to encode (of two
+//             chunks from 16,384 chunks on): 64-lane interleaved rANS from
+//             the last step to the first, exact division by one
 //             double multiply, words staged in an LDS ring and drained 512
 //             bytes at a time to the workspace in decoder order; aborts to
 //             RAW as soon as the payload can no longer beat the threshold.
@@ -19,6 +20,9 @@
 //             staged RAW streams from the workspace, other RAW streams
 //             regrouped from the input; every byte of the blob, padding
 //             included, is written exactly once.
+// Format v2 (one table per tensor and stream index) puts k_planesum, k_share
+// and k_decide between k_hist and k_encode: plane sums of the kept
+// histograms, the plane tables, then each stream's skip bound.
 // Method: "NOTE-241: ZipNN", Method items 1-3 and 5; chunk size and
 // passthrough rule: cuZipNN 0.1.0, API; interleaved rANS lanes and a table per
 // stream: lmz README, "On a GPU" and "Building on lmz".
