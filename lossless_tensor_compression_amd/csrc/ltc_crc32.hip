@@ -55,8 +55,8 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
   constexpr uint32_t kWaves = kCrcThreads / 64;
   const uint64_t frame = 64 * a.seg;
   const uint64_t total = DEVLEN ? first[a.count] : a.total_chunks;
+  int jb = 0;  // a wave's chunk indices only grow, so its buffer index only moves forward
   for (uint64_t gi = (uint64_t)blockIdx.x * kWaves + wave; gi < total; gi += (uint64_t)gridDim.x * kWaves) {
-    int jb = 0;
     uint64_t i, len;
     if constexpr (DEVLEN) {
       while (jb + 1 < (int)a.count && gi >= first[jb + 1]) ++jb;
