@@ -28,6 +28,7 @@ namespace ltc {
 // the grid is at most one workgroup per CU and its waves walk the chunks.
 constexpr int kCrcThreads = 1024;
 constexpr int kCrcGridMax = 256;
+static_assert(kMaxJobs <= 64, "one lane per buffer in k_crc32's prologue");
 
 // DEVLEN: buffer lengths are read on the device (compress_with_crc32).  The
 // workgroup then reads each buffer's length once and numbers only the chunks
@@ -38,20 +39,24 @@ __global__ __launch_bounds__(kCrcThreads) void k_crc32(CrcArgs a) {
   __shared__ CrcBankLds s;
   __shared__ uint64_t lens[kMaxJobs];         // DEVLEN: the buffers' lengths
   __shared__ uint64_t first[kMaxJobs + 1];    // DEVLEN: their first chunk's index
-  const uint32_t tid = threadIdx.x;
-  if (DEVLEN && tid < a.count) lens[tid] = *a.jobs[tid].len;
-  if (DEVLEN) __syncthreads();
-  if (DEVLEN && tid == 0) {
-    uint64_t c = 0;
-    for (uint32_t j = 0; j < a.count; ++j) {
-      first[j] = c;
-      c += (lens[j] + a.chunk_bytes - 1) / a.chunk_bytes;
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid / 64, bl = lane & 31u;
+  if (DEVLEN && wave == 0) {  // lane j: buffer j's length and chunk count; their prefix sums
+    const uint64_t L = lane < a.count ? *a.jobs[lane].len : 0;
+    const uint64_t c = (L + a.chunk_bytes - 1) / a.chunk_bytes;
+    uint64_t inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t up = __shfl_up(inc, o, 64);
+      if (lane >= (uint32_t)o) inc += up;
     }
-    first[a.count] = c;
+    if (lane < a.count) {
+      lens[lane] = L;
+      first[lane] = inc - c;
+    }
+    if (lane + 1 == a.count) first[a.count] = inc;
   }
   crc_build_bank(s, a.lvl, tid, kCrcThreads);  // ends with a barrier
 
-  const uint32_t lane = lane_id(), wave = tid / 64, bl = lane & 31u;
   constexpr uint32_t kWaves = kCrcThreads / 64;
   const uint64_t frame = 64 * a.seg;
   const uint64_t total = DEVLEN ? first[a.count] : a.total_chunks;
