@@ -147,6 +147,31 @@ def test_batch_with_empty_and_tiny(ltc):
             assert torch.equal(b1, b2)
 
 
+@pytest.mark.parametrize("top_last", [False, True])
+def test_full_batch_of_ragged_blobs(ltc, top_last):
+    """BATCH_MAX tensors, empty ones among them: the checksum kernel numbers
+    the chunks of every blob (in the top-last layout from the lengths the
+    compressor wrote on the device) and must find each chunk's blob."""
+    rng = np.random.default_rng(93)
+    chunk = 2048
+    sizes = [0 if i % 7 == 3 else int(rng.integers(1, 40000)) for i in range(ltc.BATCH_MAX)]
+    arrs = [(rng.standard_normal(n) * 0.02).astype(np.float32) for n in sizes]
+    ts = [to_gpu(a, 3) for a in arrs]
+    wants = [oracle.compress(a, 3, chunk, top_last=top_last) for a in arrs]
+    for k in (1024, 5000):
+        banner(f"crc full batch top_last={top_last} K={k}")
+        blobs, crcs = ltc.compress_batch_with_crc32(ts, chunk, 0.95, k, top_last=top_last)
+        for i, (want, b, c) in enumerate(zip(wants, blobs, crcs)):
+            assert np.array_equal(to_np_bytes(b), want), i
+            assert np.array_equal(_u32(c), np.array(oracle.crc32_chunks(want, k), dtype=np.uint32)), i
+    # the checksum entry point alone, empty buffers first and last
+    empty = torch.empty(0, dtype=torch.uint8, device="cuda")
+    got = ltc.crc32_chunks_batch([empty] + blobs[1:-1] + [empty], 5000)
+    assert got[0].numel() == 0 and got[-1].numel() == 0
+    for want, c in zip(wants[1:-1], got[1:-1]):
+        assert np.array_equal(_u32(c), np.array(oracle.crc32_chunks(want, 5000), dtype=np.uint32))
+
+
 def test_repeat_calls_and_untouched_tail(ltc):
     """Frames are cleared at every call: a second call gives the same
     checksums; entries past ceil(blob / K) keep what the caller put there."""
