@@ -17,7 +17,7 @@ from gpu_util import banner, to_gpu, to_np_bytes
 
 pytestmark = pytest.mark.gpu
 
-NCASES = 240
+NCASES = 1200
 
 
 @pytest.fixture(scope="module")
